@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused SwiGLU gate/up stage on one MI355X.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+
+Headline workload: one training step of the fused stage at M=8192 tokens,
+K=4096, N=14336 in bf16 (fp32 accumulation): the fused forward
+h = SiLU(x Wg^T) * (x Wu^T) followed by the backward (dX, dWg, dWu).
+value = algorithmic TFLOP/s of that step, 12 M N K flops per step (4 M N K
+forward, 8 M N K for dX and dW; the recompute of g and u in the backward is
+not credited).  Inputs are synthetic (seed 0) and resident in HBM before the
+timed region starts.
+
+The same run also measures, after the timed region and outside `value`:
+  decode   the M=1..8 weight-streaming forward at (N,K)=(6912,1536) with 16
+           rotated weight copies and (11008,4096) with 4 copies (each call
+           reads cold weights), in GB/s, beside a pure dual-stream read of
+           the same buffers (the cold-read floor);
+  act_quant the elementwise SwiGLU + FP8 block quantisation of [4001, 3584]
+           fp32 inputs (4 rotated copies), in GB/s;
+  fp32     the IEEE-fp32 fused forward at M=4001, K=2048, N=3584, in TFLOP/s;
+  cpu_baseline  the fp64 oracle on a row sample of the headline workload,
+           timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # dense bf16 MFMA, MI355X
+PEAK_FP32_TFLOPS = 157.3      # dense fp32 matrix, MI355X
+PEAK_HBM_GBS = 8000.0         # HBM3E, MI355X
+
+M4, N4, K4 = 8192, 14336, 4096
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target host time of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the decode / act_quant / fp32 legs")
+    p.add_argument("--only", choices=["step", "fwd", "decode", "act_quant", "fp32"], default=None,
+                   help="profiling aid: run one leg only (no JSON contract)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "swiglu_mlp_fwd_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name: str):
+    """HBM traffic per launch measured by rocprofv3 counters for `name`, if the
+    committed measurement was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(name)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the current stream (the stream the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+
+def graph_time_per_call(torch, calls, reps=5):
+    """Capture `calls` (a list of closures launching one library call each) in
+    one HIP graph, replay it `reps` times, return seconds per call."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in calls:  # warm once outside capture
+            c()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    samples = []
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        samples.append(e0.elapsed_time(e1) * 1e-3 / len(calls))
+    del g
+    samples.sort()
+    return samples[len(samples) // 2], samples
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the library runs on one GPU and has no "
+              "multi-GPU path; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from swiglu_mlp_fwd_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    import swiglu_mlp_fwd_amd as S
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ------------------------------------------------------------ headline
+    t0 = time.time()
+    d4 = synth.train_bf16(M4, N4, K4, seed=0)
+    x, wg, wu, dh = (to_dev_bf16(d4[k]) for k in ("x", "wg", "wu", "dh"))
+    ws = torch.empty(S.bwd_workspace_bytes(torch.bfloat16, M4, N4, K4), dtype=torch.uint8, device=dev)
+    h = torch.empty((M4, N4), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    def step():
+        S.fwd(x, wg, wu, out=h)
+        return S.bwd(x, wg, wu, dh, workspace=ws)
+
+    if args.only in ("step", "fwd"):
+        for _ in range(args.warmup + args.steps):
+            if args.only == "fwd":
+                S.fwd(x, wg, wu, out=h)
+            else:
+                step()
+        torch.cuda.synchronize()
+        log("done")
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    fwd_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        fwd_ev[i][0].record()
+        S.fwd(x, wg, wu, out=h)
+        fwd_ev[i][1].record()
+        S.bwd(x, wg, wu, dh, workspace=ws)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    t_step = start.elapsed_time(end) * 1e-3 / args.steps
+    t_fwd = sum(a.elapsed_time(b) for a, b in fwd_ev) * 1e-3 / args.steps
+    flops_step = 12.0 * M4 * N4 * K4
+    value = flops_step / t_step / 1e12
+    fwd_tflops = 4.0 * M4 * N4 * K4 / t_fwd / 1e12
+    log(f"step {t_step * 1e3:.3f} ms ({value:.1f} TFLOP/s); fwd {t_fwd * 1e3:.3f} ms ({fwd_tflops:.1f} TFLOP/s); "
+        f"host wall {wall:.2f}s")
+
+    traffic = load_traffic("fwd_dual_gemm_bf16_8192x14336x4096")
+    result = {
+        "metric": "fused SwiGLU TFLOP/s (M=8192) + cold GB/s (M=1..8), % of roofline",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seed 0): x~N(0,1), Wg,Wu~N(0,0.02), dh~N(0,0.01)",
+        "config": {"workload": "fused SwiGLU gate/up training step (forward + backward), bf16, fp32 accumulation",
+                   "M": M4, "K": K4, "N": N4, "flops_per_step": "12*M*N*K (recompute not credited)",
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "kernel": "fused dual GEMM forward (x Wg^T, x Wu^T, SiLU-gate epilogue)",
+            "bound": "mfma",
+            "achieved": round(fwd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(t_fwd * 1e3, 4),
+        },
+        "fwd_ms": round(t_fwd * 1e3, 4),
+        "bwd_ms": round((t_step - t_fwd) * 1e3, 4),
+        "bwd_tflops_8MNK": round(8.0 * M4 * N4 * K4 / (t_step - t_fwd) / 1e12, 2),
+    }
+    del h
+    sample_inputs = {k: d4[k] for k in ("x", "wg", "wu", "dh")}
+    del x, wg, wu, dh, ws
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ extra legs
+    if not args.no_extra:
+        result["decode"] = decode_leg(torch, S, synth, np, dev, to_dev_bf16)
+        result["act_quant"] = act_quant_leg(torch, S, synth, np, dev)
+        result["fp32"] = fp32_leg(torch, S, synth, np, dev)
+
+    # ------------------------------------------------------------ cpu baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(np, synth, sample_inputs, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def decode_leg(torch, S, synth, np, dev, to_dev_bf16):
+    out = {"unit": "GB/s", "bytes": "2*N*K*2 + M*K*2 + M*N*2 per call", "shapes": []}
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    for (N, K, copies) in ((6912, 1536, 16), (11008, 4096, 4)):
+        d = synth.decode_bf16(8, N, K, seed=0)
+        wg0, wu0 = to_dev_bf16(d["wg"]), to_dev_bf16(d["wu"])
+        W = [(wg0.clone(), wu0.clone()) for _ in range(copies)]
+        del wg0, wu0
+        reps_per_graph = 4
+        probe_calls = [(lambda a=a, b=b: S.probe_read2(a, b, sink)) for _ in range(reps_per_graph) for (a, b) in W]
+        t_probe, _ = graph_time_per_call(torch, probe_calls)
+        floor = 2 * N * K * 2 / t_probe / 1e9
+        entry = {"N": N, "K": K, "copies": copies,
+                 "working_set_MB": round(copies * 2 * N * K * 2 / 1e6, 1),
+                 "read_floor_GBs": round(floor, 1), "per_M": []}
+        for M in (1, 2, 4, 8):
+            x = to_dev_bf16(d["x"][:M].copy())
+            outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+            calls = [(lambda a=a, b=b, o=o: S.gemv_fwd(x, a, b, out=o))
+                     for _ in range(reps_per_graph) for (a, b), o in zip(W, outs)]
+            t, _ = graph_time_per_call(torch, calls)
+            nbytes = 2 * N * K * 2 + M * K * 2 + M * N * 2
+            gbs = nbytes / t / 1e9
+            entry["per_M"].append({"M": M, "us": round(t * 1e6, 3), "GBs": round(gbs, 1),
+                                   "frac_of_floor": round(gbs / floor, 4), "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)})
+            log(f"decode N={N} K={K} M={M}: {t * 1e6:.2f} us, {gbs:.0f} GB/s ({gbs / floor:.1%} of read floor {floor:.0f})")
+        out["shapes"].append(entry)
+        del W
+        torch.cuda.empty_cache()
+    return out
+
+
+def act_quant_leg(torch, S, synth, np, dev):
+    R, C = 4001, 3584
+    d = synth.act_quant_f32(R, C, seed=0)
+    g0, u0 = torch.from_numpy(d["gate"]).to(dev), torch.from_numpy(d["up"]).to(dev)
+    copies = 4
+    G = [g0.clone() for _ in range(copies)]
+    U = [u0.clone() for _ in range(copies)]
+    del g0, u0
+    outs = [(torch.empty((R, C), dtype=torch.uint8, device=dev), torch.empty((R, C // 32), dtype=torch.uint8, device=dev),
+             torch.empty(1, dtype=torch.int64, device=dev), None) for _ in range(copies)]
+    nbytes = 2 * R * C * 4 + R * C + R * C // 32
+    res = {"rows": R, "cols": C, "copies": copies, "bytes_per_call": nbytes, "unit": "GB/s"}
+    for L in (math.inf, 7.0):
+        calls = [(lambda i=i: S.act_quant(G[i], U[i], L, out=outs[i])) for _ in range(4) for i in range(copies)]
+        t, _ = graph_time_per_call(torch, calls)
+        gbs = nbytes / t / 1e9
+        key = "no_clamp" if math.isinf(L) else "clamp_7"
+        res[key] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"act_quant {R}x{C} {key}: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
+    del G, U, outs
+    torch.cuda.empty_cache()
+    return res
+
+
+def fp32_leg(torch, S, synth, np, dev):
+    M, N, K = 4001, 3584, 2048
+    d = synth.gemm_fp32(M, N, K, seed=0)
+    x, wg, wu = (torch.from_numpy(d[k]).to(dev) for k in ("x", "wg", "wu"))
+    h = torch.empty((M, N), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        S.fwd(x, wg, wu, out=h)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    e0.record()
+    for _ in range(n):
+        S.fwd(x, wg, wu, out=h)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / n
+    tf = 4.0 * M * N * K / t / 1e12
+    log(f"fp32 fwd {M}x{N}x{K}: {t * 1e3:.3f} ms, {tf:.1f} TFLOP/s")
+    del x, wg, wu, h
+    torch.cuda.empty_cache()
+    return {"M": M, "N": N, "K": K, "ms": round(t * 1e3, 4), "TFLOPs": round(tf, 2),
+            "frac_of_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4)}
+
+
+def cpu_baseline(np, synth, d, target_s):
+    """The fp64 oracle, as it stands, on the first m rows of the headline
+    workload: forward for those rows and the backward contributions of those
+    rows (dX rows, and dWg/dWu summed over the m rows only)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    wg = synth.bf16_bits_to_f32(d["wg"]).astype(np.float64)
+    wu = synth.bf16_bits_to_f32(d["wu"]).astype(np.float64)
+
+    def run(m):
+        x = synth.bf16_bits_to_f32(d["x"][:m]).astype(np.float64)
+        dh = synth.bf16_bits_to_f32(d["dh"][:m]).astype(np.float64)
+        t = time.perf_counter()
+        oracle.swiglu_fwd(x, wg, wu)
+        oracle.swiglu_bwd(x, wg, wu, dh)
+        return time.perf_counter() - t
+
+    m0 = 64
+    run(m0)                       # warm the BLAS thread pool
+    t0 = run(m0)
+    m = int(max(m0, min(M4, m0 * target_s / max(t0, 1e-3))))
+    t = run(m)
+    flops = 12.0 * m * N4 * K4
+    log(f"cpu oracle: {m} rows in {t:.1f}s on {cores} threads -> {flops / t / 1e12:.4f} TFLOP/s")
+    return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy oracle forward + backward on the first {m} of {M4} rows of the headline "
+                      f"workload (12*m*N*K flops credited, as for value); {t:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

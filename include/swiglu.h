@@ -1,0 +1,161 @@
+/*
+ * libswiglu -- the fused SwiGLU gate/up stage on AMD Instinct MI355X (gfx950).
+ *
+ *   h = SiLU(x Wg^T) (*) (x Wu^T),  SiLU(z) = z * sigmoid(z)
+ *
+ * Plain C ABI: device pointers, sizes and a HIP stream passed as void*.  No
+ * torch types, no allocation, no synchronisation: every call validates its
+ * arguments on the host and then only enqueues kernels on `stream`.
+ *
+ * Common conventions
+ *   - All tensor pointers are DEVICE pointers to dense row-major arrays.
+ *   - Weights use the nn.Linear layout Wg, Wu [N, K] and are applied as
+ *     x @ W^T ("VisualGen MLP: cublasLt GELU-tanh epilogue for the
+ *     unquantized bf16 path", TensorRT-LLM PR 17693, section Change: the
+ *     up-projection is addmm(bias, x2d, weight.t()) on a [M, in] view).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is ordered on
+ *     it; the call returns before the work is done.
+ *   - The caller owns every buffer.  Outputs must not alias inputs or each
+ *     other.  Every pointer must be 16-byte aligned (the kernels use 128-bit
+ *     loads and stores).
+ *   - Return value: SWIGLU_OK or an error code.  On an error nothing has been
+ *     enqueued and no output has been written.  Sizes of zero are valid and
+ *     enqueue only what is needed to give the outputs their defined values.
+ *   - Calls are thread-safe: the library holds no mutable global state apart
+ *     from a thread-local record of the last HIP error.
+ */
+#ifndef SWIGLU_H_
+#define SWIGLU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum swiglu_status {
+  SWIGLU_OK = 0,
+  SWIGLU_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  SWIGLU_ERR_SHAPE = 2,       /* a size is negative or breaks a layout rule     */
+  SWIGLU_ERR_DTYPE = 3,       /* unknown dtype code                             */
+  SWIGLU_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
+  SWIGLU_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
+  SWIGLU_ERR_ARG = 6,         /* any other invalid argument (e.g. clamp limit)  */
+  SWIGLU_ERR_UNSUPPORTED = 7, /* valid request this build does not implement    */
+  SWIGLU_ERR_HIP = 8          /* a HIP launch failed; see swiglu_last_hip_error */
+};
+
+/* Element type of x, Wg, Wu, dh and of every output of a call.  Accumulation
+ * is always fp32.  SWIGLU_F32 is true IEEE fp32 on the fp32 matrix cores (no
+ * reduced-precision operand truncation): "[RFC] Testing Methodology for FP32
+ * Convergence Tests on Fused SwiGLU/dSwiGLU Kernels" (Liger-Kernel issue
+ * 1383), section Root Cause, traces fp32 convergence failures to TF32. */
+enum swiglu_dtype { SWIGLU_F32 = 0, SWIGLU_BF16 = 1 };
+
+/* Forward of the fused gate/up stage: the dual GEMM g = x Wg^T, u = x Wu^T
+ * with the SiLU-gate epilogue applied to the fp32 accumulators and one
+ * rounding of h to `dtype`; g and u are never written to memory.
+ * Sources: Liger-Kernel issue 1383, Background (gate/up GEMM + SwiGLU fused
+ * in one kernel to cut intermediate-tensor traffic); "Another MLP
+ * implementation along with multiplier support" (Liger-Kernel issue 937),
+ * TL;DR approach 3 (dual GEMM with activation); TensorRT-LLM PR 17693,
+ * follow-up commit on numerics (activation on the fp32 accumulator).
+ *
+ *   x  [M, K], wg [N, K], wu [N, K]  (inputs, dtype)
+ *   h  [M, N]                        (output, dtype)
+ * Layout rule: K % 8 == 0 for bf16 and K % 4 == 0 for fp32 (16-byte rows).
+ * K == 0 gives h = 0. */
+int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K,
+               const void* x, const void* wg, const void* wu, void* h,
+               void* stream);
+
+/* Bytes of device workspace swiglu_bwd needs for these sizes (0 on invalid
+ * sizes).  The workspace holds dg and du, their transposes, x^T and the
+ * transposed weight pair. */
+size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K);
+
+/* Backward of the fused stage ("Fused SwiGLU/dSwiGLU", Liger-Kernel issue
+ * 1383, Background: the full forward and backward dataflow).  With
+ * s = sigmoid(g) and g, u recomputed from x, Wg, Wu:
+ *   du = dh * g * s,   dg = dh * u * s * (1 + g * (1 - s))
+ *   dx = dg Wg + du Wu,   dwg = dg^T x,   dwu = du^T x
+ * dg and du are rounded to `dtype` once (they are matrix-core operands);
+ * every contraction accumulates in fp32 and rounds its output once.
+ * Five kernels run in order on `stream`: the recompute dual GEMM with the
+ * dSwiGLU epilogue, transposes of x, the weights and [dg | du], then the dX
+ * GEMM and the stacked dW GEMM.
+ *
+ *   x [M, K], wg/wu [N, K], dh [M, N]         (inputs, dtype)
+ *   dx [M, K], dwg [N, K], dwu [N, K]         (outputs, dtype; overwritten)
+ *   workspace: device buffer of at least swiglu_bwd_workspace_bytes(...)
+ *              bytes, 256-byte aligned; contents are scratch.
+ * Layout rule: K % 8 == 0 for bf16, K % 4 == 0 for fp32; M and N are free
+ * (the transposed operands are zero-padded to 16-byte rows). */
+int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K,
+               const void* x, const void* wg, const void* wu, const void* dh,
+               void* dx, void* dwg, void* dwu,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode forward for 1 <= M <= 8 tokens, bf16 only: the same h as
+ * swiglu_fwd, computed by a weight-streaming kernel that reads each row of
+ * Wg and Wu from HBM once for all M tokens and reduces on the vector units
+ * ("Fused SwiGLU benchmark", AstrAI docs/developer/swiglu_benchmark.md,
+ * sections L20 findings and HBM re-measurement: a fused BF16 SwiGLU
+ * primitive for M = 1, 2, 4, 8 bound by the cold weight read).
+ *
+ *   x [M, K], wg/wu [N, K] (bf16 inputs), h [M, N] (bf16 output)
+ * Layout rule: K % 8 == 0 and M * K * 2 <= 65536 (x is staged in LDS);
+ * larger x gives SWIGLU_ERR_UNSUPPORTED. */
+int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K,
+                    const void* x, const void* wg, const void* wu, void* h,
+                    void* stream);
+
+/* Elementwise SwiGLU with FP8 block quantisation, one pass ("quant: add
+ * SwiGLU forward/backward VMI kernels", TileKernels-PTO PR 20, sections
+ * overview and implementation notes):
+ *   g' = clamp(gate, -L, L), u' = clamp(up, -L, L)   (NaN passes through)
+ *   h  = SiLU(g') * u'                               (fp32)
+ *   per row and 1x32 block along cols: amax = max |h| ignoring NaN,
+ *   E = smallest integer with amax <= 448 * 2^E, clamped to [-127, 127]
+ *       (E = 128 when amax is +inf), scale byte = E + 127 (UE8M0),
+ *   q = E4M3FN(h * 2^-E), round to nearest even, no saturation,
+ *       NaN and +-inf -> NaN.
+ *
+ *   gate, up     [rows, cols] fp32 inputs
+ *   clamp_limit  L > 0, or +INFINITY for no clamp (NaN or L <= 0: error)
+ *   q            [rows, cols] uint8 E4M3FN codes (output)
+ *   scale        [rows, cols / 32] uint8 UE8M0 bytes (output)
+ *   clamp_count  NULL, or one uint64 overwritten with the number of gate and
+ *                up values with |v| > L (NaN not counted)
+ *   h_out        NULL, or [rows, cols] fp32 that also receives h itself (the
+ *                page's kernel likewise keeps a non-quantised output mode)
+ * Layout rule: cols % 32 == 0 (the 1x32 blocks tile each row). */
+int swiglu_act_quant(int64_t rows, int64_t cols,
+                     const float* gate, const float* up, float clamp_limit,
+                     uint8_t* q, uint8_t* scale, uint64_t* clamp_count,
+                     float* h_out, void* stream);
+
+/* Measurement aid: a pure streaming read of two device buffers of `bytes`
+ * bytes each (16-byte multiples), the cold-read floor against which the
+ * decode kernel is judged ("Fused SwiGLU benchmark", section HBM
+ * re-measurement: the fused kernel is compared with a dual-stream pure-read
+ * loop over rotated weight copies).  Writes one word per workgroup to `sink`
+ * (>= 4096 uint32 words) so the reads cannot be elided. */
+int swiglu_probe_read2(const void* a, const void* b, size_t bytes,
+                       uint32_t* sink, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* swiglu_status_str(int status);
+
+/* hipError_t of the last SWIGLU_ERR_HIP returned on this thread (0 if none). */
+int swiglu_last_hip_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int swiglu_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIGLU_H_ */

@@ -264,6 +264,16 @@ def act_quant(gate, up, clamp_limit=np.inf):
     with np.errstate(over="ignore", invalid="ignore"):
         h64 = silu(g) * u
         h32 = h64.astype(np.float32)
+    q, scale = quantize_1x32(h32)
+    return q, scale, count, h32
+
+
+def quantize_1x32(h32):
+    """1x32 block quantisation of fp32 activations h32 [rows, cols]:
+    amax per block (NaN ignored, all-NaN -> 0), UE8M0 byte, E4M3FN codes of
+    h * 2^-E.  Returns (q uint8 [rows, cols], scale uint8 [rows, cols/32])."""
+    h32 = np.asarray(h32, dtype=np.float32)
+    rows, cols = h32.shape
     blocks = h32.astype(np.float64).reshape(rows, cols // 32, 32)
     mag = np.abs(blocks)
     amax = np.where(np.isnan(mag), -np.inf, mag).max(axis=2)   # NaN ignored
@@ -271,7 +281,7 @@ def act_quant(gate, up, clamp_limit=np.inf):
     E = ue8m0_exponent(amax)
     scaled = np.ldexp(blocks, -E[:, :, None])                   # exact in float64
     q = e4m3_encode(scaled).reshape(rows, cols)
-    return q, ue8m0_byte(E), count, h32
+    return q, ue8m0_byte(E)
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,153 @@
+// The C ABI of libswiglu: validation on the host, then kernel launches on the
+// caller's stream.  No allocation, no synchronisation.
+#include <math.h>
+
+#include "gemm.hpp"
+#include "swiglu.h"
+#include "validate.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return SWIGLU_OK;
+  g_last_hip_error = (int)e;
+  return SWIGLU_ERR_HIP;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+swg::Dt as_dt(int dtype) { return dtype == SWIGLU_BF16 ? swg::Dt::kBF16 : swg::Dt::kF32; }
+
+// Zero-fill of a dense output through the transpose kernel's padding path
+// (a kernel, not a memset node, so callers may capture it in a graph).
+hipError_t fill_zero(int dtype, void* p, int64_t rows, int64_t cols, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  // Transposing a [0, rows] input with rows_pad = cols writes zeros into
+  // out[c, r] for c < rows, r < cols, i.e. the whole [rows, cols] array.
+  return swg::launch_transpose(as_dt(dtype), nullptr, 0, 0, (int)rows, p, cols, 0, (int)cols, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+               const void* wu, void* h, void* stream) {
+  int st = swg::validate_fwd(dtype, M, N, K, x, wg, wu, h);
+  if (st != SWIGLU_OK || M == 0 || N == 0) return st;
+  swg::GemmArgs a{};
+  a.a = x; a.b0 = wg; a.b1 = wu;
+  a.lda = K; a.ldb = K;
+  a.arows = (int)M; a.brows = (int)N;
+  a.m = (int)M; a.n = (int)N; a.r = (int)K;
+  a.out0 = h; a.ldo = N; a.ncols = (int)N;
+  return hip_status(swg::launch_fwd_dual(as_dt(dtype), a, as_stream(stream)));
+}
+
+size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K) {
+  if (swg::check_dtype(dtype) != SWIGLU_OK || swg::check_dims(M, N, K) != SWIGLU_OK) return 0;
+  return swg::bwd_layout(dtype, M, N, K).total;
+}
+
+int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+               const void* wu, const void* dh, void* dx, void* dwg, void* dwu, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  int st = swg::validate_bwd(dtype, M, N, K, x, wg, wu, dh, dx, dwg, dwu, workspace,
+                             workspace_bytes);
+  if (st != SWIGLU_OK || K == 0) return st;
+  hipStream_t s = as_stream(stream);
+  const swg::Dt dt = as_dt(dtype);
+  if (M == 0 || N == 0) {
+    // Empty sums: dx = 0 when N == 0, dWg = dWu = 0 when M == 0.
+    hipError_t e = hipSuccess;
+    if (N == 0) e = fill_zero(dtype, dx, M, K, s);
+    if (e == hipSuccess && M == 0) e = fill_zero(dtype, dwg, N, K, s);
+    if (e == hipSuccess && M == 0) e = fill_zero(dtype, dwu, N, K, s);
+    return hip_status(e);
+  }
+  const swg::BwdLayout L = swg::bwd_layout(dtype, M, N, K);
+  char* ws = static_cast<char*>(workspace);
+  void* D = ws + L.off_d;
+  void* DT = ws + L.off_dt;
+  void* XT = ws + L.off_xt;
+  void* WT = ws + L.off_wt;
+  const int Mi = (int)M, Ni = (int)N, Ki = (int)K, Mp = (int)L.Mp, Np = (int)L.Np;
+  hipError_t e;
+
+  // 1. Recompute g, u and form D = [dg | du] (columns N..Np-1 of each half are zero).
+  swg::GemmArgs b1{};
+  b1.a = x; b1.b0 = wg; b1.b1 = wu; b1.lda = K; b1.ldb = K;
+  b1.arows = Mi; b1.brows = Ni; b1.m = Mi; b1.n = Np; b1.r = Ki;
+  b1.out0 = D; b1.ldo = 2 * (int64_t)Np; b1.ncols = Ni;
+  b1.dh = dh; b1.lddh = N; b1.du_off = Np;
+  if ((e = swg::launch_bwd_dswiglu(dt, b1, s)) != hipSuccess) return hip_status(e);
+
+  // 2. Transposes: x -> XT [K, Mp]; Wg, Wu -> WT [K, 2 Np]; D -> DT [2 Np, Mp].
+  if ((e = swg::launch_transpose(dt, x, K, Mi, Ki, XT, Mp, 0, Mp, s)) != hipSuccess) return hip_status(e);
+  if ((e = swg::launch_transpose(dt, wg, K, Ni, Ki, WT, 2 * (int64_t)Np, 0, Np, s)) != hipSuccess) return hip_status(e);
+  if ((e = swg::launch_transpose(dt, wu, K, Ni, Ki, WT, 2 * (int64_t)Np, Np, Np, s)) != hipSuccess) return hip_status(e);
+  if ((e = swg::launch_transpose(dt, D, 2 * (int64_t)Np, Mi, 2 * Np, DT, Mp, 0, Mp, s)) != hipSuccess) return hip_status(e);
+
+  // 3. dX [M, K] = D [M, 2 Np] . WT [K, 2 Np]^T  (reduction over the stacked N).
+  swg::GemmArgs b2{};
+  b2.a = D; b2.b0 = WT; b2.lda = 2 * (int64_t)Np; b2.ldb = 2 * (int64_t)Np;
+  b2.arows = Mi; b2.brows = Ki; b2.m = Mi; b2.n = Ki; b2.r = 2 * Np;
+  b2.out0 = dx; b2.ldo = K; b2.split = Mi; b2.lim0 = Mi; b2.lim1 = 0; b2.ncols = Ki;
+  if ((e = swg::launch_gemm_store(dt, b2, s)) != hipSuccess) return hip_status(e);
+
+  // 4. [dWg; dWu] [2 Np, K] = DT [2 Np, Mp] . XT [K, Mp]^T  (reduction over M).
+  swg::GemmArgs b3{};
+  b3.a = DT; b3.b0 = XT; b3.lda = Mp; b3.ldb = Mp;
+  b3.arows = 2 * Np; b3.brows = Ki; b3.m = 2 * Np; b3.n = Ki; b3.r = Mp;
+  b3.out0 = dwg; b3.out1 = dwu; b3.ldo = K; b3.split = Np; b3.lim0 = Ni; b3.lim1 = Ni;
+  b3.ncols = Ki;
+  return hip_status(swg::launch_gemm_store(dt, b3, s));
+}
+
+int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                    const void* wu, void* h, void* stream) {
+  int st = swg::validate_gemv(M, N, K, x, wg, wu, h);
+  if (st != SWIGLU_OK || M == 0 || N == 0) return st;
+  return hip_status(swg::launch_gemv((int)M, (int)N, (int)K, x, wg, wu, h, as_stream(stream)));
+}
+
+int swiglu_act_quant(int64_t rows, int64_t cols, const float* gate, const float* up,
+                     float clamp_limit, uint8_t* q, uint8_t* scale, uint64_t* clamp_count,
+                     float* h_out, void* stream) {
+  int st = swg::validate_act_quant(rows, cols, gate, up, clamp_limit, q, scale, clamp_count, h_out);
+  if (st != SWIGLU_OK) return st;
+  const bool clamp = !isinf(clamp_limit);
+  return hip_status(swg::launch_act_quant(rows, cols, gate, up, clamp_limit, clamp, q, scale,
+                                          clamp_count, h_out, as_stream(stream)));
+}
+
+int swiglu_probe_read2(const void* a, const void* b, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes % 16 != 0) return SWIGLU_ERR_SHAPE;
+  if (bytes == 0) return SWIGLU_OK;
+  if (a == nullptr || b == nullptr || sink == nullptr) return SWIGLU_ERR_NULL;
+  if (!swg::aligned(a, 16) || !swg::aligned(b, 16) || !swg::aligned(sink, 4)) return SWIGLU_ERR_ALIGN;
+  return hip_status(swg::launch_probe_read2(a, b, bytes, sink, as_stream(stream)));
+}
+
+const char* swiglu_status_str(int status) {
+  switch (status) {
+    case SWIGLU_OK: return "ok";
+    case SWIGLU_ERR_NULL: return "null pointer";
+    case SWIGLU_ERR_SHAPE: return "invalid shape";
+    case SWIGLU_ERR_DTYPE: return "invalid dtype";
+    case SWIGLU_ERR_ALIGN: return "misaligned pointer";
+    case SWIGLU_ERR_WORKSPACE: return "workspace missing or too small";
+    case SWIGLU_ERR_ARG: return "invalid argument";
+    case SWIGLU_ERR_UNSUPPORTED: return "unsupported size";
+    case SWIGLU_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int swiglu_last_hip_error(void) { return g_last_hip_error; }
+
+int swiglu_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// Elementwise SwiGLU with FP8 (E4M3FN) 1x32 block quantisation, one pass.
+//
+// "quant: add SwiGLU forward/backward VMI kernels" (TileKernels-PTO PR 20),
+// overview and implementation notes: an optional clamp with a count of the
+// clamped values, h = SiLU(gate) * up, one scale per 32 consecutive elements
+// of a row stored packed as a UE8M0 byte, and an E4M3 cast without
+// saturation that keeps NaN; validation covers subnormal inputs, non-finite
+// inputs and the packed scale of a block whose amax is infinite.
+//
+// Mapping: with cols % 32 == 0 the 1x32 blocks tile the flattened
+// [rows, cols] array, so block b covers elements [32 b, 32 b + 32) and its
+// scale byte sits at scale[b].  Each lane handles 8 consecutive elements
+// (two 16-byte loads per input), a quad of 4 lanes covers one block, and the
+// block amax is reduced across the quad with two xor-shuffles.  The block
+// exponent comes from the bits of amax (integer logic); the codes from the
+// hardware FP8 conversion of h * 2^-E.
+#include "common.hpp"
+#include "gemm.hpp"
+
+namespace swg {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxBlocks = 1024;   // 4 workgroups per CU, grid-stride beyond
+
+// UE8M0 exponent of a block: smallest E with amax <= 448 * 2^E, clamped to
+// [-127, 127]; E = 128 when amax is +inf.  amax is finite-or-inf, >= 0.
+// With amax = 1.f * 2^ea: 448 * 2^E = 1.75 * 2^(E + 8), so E = ea - 8 when
+// 1.f <= 1.75 and ea - 7 otherwise.
+__device__ __forceinline__ int block_exponent(float amax) {
+  const uint32_t a = f32_bits(amax);
+  if (a >= 0x7F800000u) return 128;
+  if (a == 0) return -127;
+  int ea;
+  uint32_t frac;
+  if (a >= 0x00800000u) {
+    ea = (int)(a >> 23) - 127;
+    frac = a & 0x7FFFFFu;
+  } else {                                  // subnormal: normalise the mantissa
+    const int lz = __clz(a);                // a < 2^23, so lz >= 9
+    ea = (31 - lz) - 149;
+    frac = (a << (lz - 8)) & 0x7FFFFFu;
+  }
+  int E = ea - 8 + (frac > 0x600000u ? 1 : 0);
+  return E < -127 ? -127 : E;
+}
+
+// E4M3FN codes of RNE(h * 2^-E) for two values, no saturation, NaN/inf ->
+// NaN, using the gfx950 conversion v_cvt_pk_fp8_f32 (OCP E4M3FN, current
+// rounding mode = nearest even, no clamp).  The scale 2^-E is exact in fp32
+// for E in [-127, 128] (2^-128 is a subnormal) and the product h * 2^-E is
+// exact whenever it is a normal number; when it is below 2^-126 it is far
+// below half the smallest E4M3 step (2^-10), so any rounding of the product
+// cannot change the code.
+__device__ __forceinline__ uint32_t e4m3_pair(float h0, float h1, float s) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(h0 * s, h1 * s, 0, false) & 0xFFFFu;
+}
+
+// h = SiLU(g) * u rounded once to fp32.
+//
+// e^-|g| = p 2^n (exp_neg_split); sigma(|g|) = 1 / (1 + e) and
+// sigma(-|g|) = p r 2^n with r = 1 / (1 + e).  The product g u sigma is
+// formed in fp64, where g * u is exact and the scale 2^n is applied by
+// ldexp, and is rounded to fp32 once.  So no intermediate is ever an fp32
+// subnormal: a subnormal gate times a large up, or a very negative gate
+// (sigma below 2^-126), keeps its precision.  fp64 multiplies run at the fp32
+// rate on this chip.  Special values follow IEEE: g = -inf gives 2^n -> 0 and
+// -inf * 0 = NaN; g = +inf gives inf * u; NaN propagates.
+__device__ __forceinline__ float swiglu_value(float g, float u) {
+#pragma clang fp contract(off)
+  float p;
+  int n;
+  exp_neg_split(fminf(fabsf(g), 1024.0f), p, n);  // e^-1024 is 0 even in fp64
+  const float d = 1.0f + ldexpf(p, n);
+  float r = __builtin_amdgcn_rcpf(d);
+  r = __builtin_fmaf(r, __builtin_fmaf(-d, r, 1.0f), r);
+  const bool pos = g >= 0.0f;
+  const double sig = ldexp((double)(pos ? r : p * r), pos ? 0 : n);
+  return (float)(((double)g * (double)u) * sig);
+}
+
+template <bool kClamp, bool kCount, bool kHout>
+__global__ __launch_bounds__(kThreads) void act_quant_kernel(const float* __restrict__ gate,
+                                                             const float* __restrict__ up, float L,
+                                                             uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ scale,
+                                                             unsigned long long* __restrict__ count,
+                                                             float* __restrict__ hout,
+                                                             int64_t nchunks) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t cnt = 0;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += stride) {
+    const f32x4* gp = reinterpret_cast<const f32x4*>(gate) + 2 * c;
+    const f32x4* up4 = reinterpret_cast<const f32x4*>(up) + 2 * c;
+    const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
+    const f32x4 u0 = __builtin_nontemporal_load(up4), u1 = __builtin_nontemporal_load(up4 + 1);
+    float h[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float g = e < 4 ? g0[e] : g1[e - 4];
+      float u = e < 4 ? u0[e] : u1[e - 4];
+      if (kClamp) {
+        // |v| > L is false for NaN, so NaN passes through uncounted.
+        const bool cg = fabsf(g) > L, cu = fabsf(u) > L;
+        if (kCount) cnt += (uint32_t)cg + (uint32_t)cu;
+        g = cg ? copysignf(L, g) : g;
+        u = cu ? copysignf(L, u) : u;
+      }
+      h[e] = swiglu_value(g, u);
+      amax = fmaxf(amax, fabsf(h[e]));  // maxNum: NaN operands are ignored
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const int E = block_exponent(amax);
+    const float sc = ldexpf(1.0f, -E);
+    const uint32_t lo = e4m3_pair(h[0], h[1], sc) | (e4m3_pair(h[2], h[3], sc) << 16);
+    const uint32_t hi = e4m3_pair(h[4], h[5], sc) | (e4m3_pair(h[6], h[7], sc) << 16);
+    *reinterpret_cast<u32x2*>(q + 8 * c) = u32x2{lo, hi};
+    if ((threadIdx.x & 3) == 0) scale[c >> 2] = (uint8_t)(E + 127);
+    if (kHout) {
+      f32x4* hp = reinterpret_cast<f32x4*>(hout) + 2 * c;
+      hp[0] = f32x4{h[0], h[1], h[2], h[3]};
+      hp[1] = f32x4{h[4], h[5], h[6], h[7]};
+    }
+  }
+  if (kCount) {
+    // Wave sums, then one atomic per workgroup (same-address atomics from
+    // every XCD are serialised; keep them few).
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+    __shared__ uint32_t wsum[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) t += wsum[w];
+      if (t != 0) atomicAdd(count, (unsigned long long)t);
+    }
+  }
+}
+
+__global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
+
+template <bool kClamp, bool kCount, bool kHout>
+void launch_aq(unsigned grid, const float* gate, const float* up, float L, uint8_t* q,
+               uint8_t* scale, uint64_t* count, float* hout, int64_t nchunks, hipStream_t s) {
+  hipLaunchKernelGGL((act_quant_kernel<kClamp, kCount, kHout>), dim3(grid), dim3(kThreads), 0, s,
+                     gate, up, L, q, scale, reinterpret_cast<unsigned long long*>(count), hout,
+                     nchunks);
+}
+
+}  // namespace
+
+hipError_t launch_act_quant(int64_t rows, int64_t cols, const float* gate, const float* up,
+                            float limit, bool clamp, uint8_t* q, uint8_t* scale, uint64_t* count,
+                            float* hout, hipStream_t s) {
+  const bool counting = clamp && count != nullptr;
+  if (count != nullptr) {
+    hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s,
+                       reinterpret_cast<unsigned long long*>(count));
+  }
+  const int64_t nchunks = rows * cols / 8;
+  if (nchunks > 0) {
+    int64_t want = (nchunks + kThreads - 1) / kThreads;
+    const unsigned grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);
+    // The count is only accumulated when a counter is given and the clamp is
+    // on; with the clamp off no value can exceed the limit.
+    if (counting) {
+      if (hout) launch_aq<true, true, true>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
+      else launch_aq<true, true, false>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
+    } else if (clamp) {
+      if (hout) launch_aq<true, false, true>(grid, gate, up, limit, q, scale, nullptr, hout, nchunks, s);
+      else launch_aq<true, false, false>(grid, gate, up, limit, q, scale, nullptr, hout, nchunks, s);
+    } else {
+      if (hout) launch_aq<false, false, true>(grid, gate, up, limit, q, scale, nullptr, hout, nchunks, s);
+      else launch_aq<false, false, false>(grid, gate, up, limit, q, scale, nullptr, hout, nchunks, s);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace swg

@@ -1,0 +1,92 @@
+// Shared device-side definitions for libswiglu (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swg {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Reinterpret one 32-bit word as two bf16 (element 0 = low half).  Takes the
+// word by value: bit-casting a vector element lvalue directly reads element 0.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16 to_bf16(float f) { return (bf16)f; }
+__device__ __forceinline__ float from_bf16(bf16 b) { return (float)b; }
+
+// e^-a for a >= 0 as p * 2^n with p in [1, 2) (up to one ulp of slack at
+// the ends) and integer n:  e^-a = 2^t, t = -a log2(e).  n = floor of the
+// rounded product; f = t - n is formed by one fused multiply-add from the
+// exact product -a * L2E_hi (L2E_hi = log2(e) rounded to fp32), and the tail
+// -a * (log2(e) - L2E_hi) is applied to first order:
+//   2^t = 2^f * 2^tail ~ 2^f * (1 + tail ln 2),  |tail| < 2^-17.
+// With the hardware exp2 (v_exp_f32) on f in [0, 1) the result is good to
+// about two ulps for every a.  Contraction is off so the compiler cannot
+// fold the rounding of the product used for floor() into f.
+__device__ __forceinline__ void exp_neg_split(float a, float& p, int& n) {
+#pragma clang fp contract(off)
+  constexpr float kL2eHi = 1.44269502162933349609375f;      // fp32(log2 e)
+  constexpr float kL2eLo = 1.925963033500011079e-08f;       // log2 e - kL2eHi
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float nf = floorf(-a * kL2eHi);
+  const float f = __builtin_fmaf(-a, kL2eHi, -nf);
+  const float tail = -a * kL2eLo;
+  const float e2 = __builtin_amdgcn_exp2f(f);
+  p = __builtin_fmaf(e2 * tail, kLn2, e2);
+  n = (int)nf;
+}
+
+// sigma(z) and SiLU(z) = z * sigma(z) in fp32, from e = exp(-|z|) in (0, 1]
+// so no step overflows:  sigma(|z|) = 1 / (1 + e),  sigma(-|z|) = e / (1 + e).
+// The reciprocal is the hardware v_rcp_f32 refined by one Newton step.
+// IEEE rules carry the special values: SiLU(+inf) = +inf,
+// SiLU(-inf) = -inf * 0 = NaN, SiLU(NaN) = NaN.  For z below about -87 the
+// fp32 value of e flushes to zero and SiLU(z) returns -0 (|true value| is
+// below 1e-36); the elementwise kernel, whose output is fp32, handles that
+// range exactly on its own.
+__device__ __forceinline__ void sigmoid_silu_f32(float z, float& s, float& silu) {
+#pragma clang fp contract(off)
+  float p;
+  int n;
+  exp_neg_split(fminf(fabsf(z), 128.0f), p, n);   // fminf drops NaN: z = NaN handled below
+  const float e = ldexpf(p, n);
+  const float d = 1.0f + e;
+  float r = __builtin_amdgcn_rcpf(d);
+  r = __builtin_fmaf(r, __builtin_fmaf(-d, r, 1.0f), r);
+  s = (z >= 0.0f) ? r : e * r;
+  if (z != z) s = z;
+  silu = z * s;
+}
+
+__device__ __forceinline__ float silu_f32(float z) {
+  float s, silu;
+  sigmoid_silu_f32(z, s, silu);
+  return silu;
+}
+
+// Bijection from the hardware workgroup index to a logical tile index such
+// that each XCD (workgroups are dealt to the 8 XCDs round-robin) receives a
+// contiguous range of logical tiles, so tiles that share operands share an
+// L2.
+__device__ __forceinline__ int xcd_remap(int bid, int ntiles) {
+  constexpr int kXcds = 8;
+  int q = ntiles / kXcds, r = ntiles % kXcds;
+  int x = bid % kXcds, j = bid / kXcds;
+  int start = x * q + (x < r ? x : r);
+  return start + j;
+}
+
+}  // namespace swg

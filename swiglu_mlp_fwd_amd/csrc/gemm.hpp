@@ -1,0 +1,52 @@
+// Internal launch interface of the GEMM-shaped kernels (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swg {
+
+// C[m, n] = sum_r A[m, r] * B[n, r]: both operands have the reduction index
+// contiguous (the nn.Linear layout), so one kernel family serves the forward
+// dual GEMM and, after transposes, every backward contraction.
+struct GemmArgs {
+  const void* a;       // A [arows, r], row stride lda (elements)
+  const void* b0;      // B0 [brows, r], row stride ldb
+  const void* b1;      // B1 [brows, r] (dual only)
+  int64_t lda, ldb;
+  int arows, brows;    // rows of A / B that exist; rows beyond read as zero
+  int m, n, r;         // output tile space m x n; reduction length r
+  // epilogue
+  void* out0;
+  void* out1;
+  int64_t ldo;         // row stride of outputs (elements)
+  int split;           // store: rows < split go to out0, others to out1 (row - split)
+  int lim0, lim1;      // store: rows of out0 / out1 that exist
+  int ncols;           // columns of the output that exist (store / swiglu)
+  const void* dh;      // dswiglu: upstream gradient [arows, ncols], row stride lddh
+  int64_t lddh;
+  int du_off;          // dswiglu: du is written at column du_off + n of out0
+};
+
+enum class Dt { kF32 = 0, kBF16 = 1 };
+
+hipError_t launch_fwd_dual(Dt dt, const GemmArgs& a, hipStream_t s);      // h = silu(g) * u
+hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s);   // D = [dg | du]
+hipError_t launch_gemm_store(Dt dt, const GemmArgs& a, hipStream_t s);    // C = A B^T
+
+// out[c, col_off + r] = in[r, c] for r < rows, 0 for rows <= r < rows_pad.
+hipError_t launch_transpose(Dt dt, const void* in, int64_t ld_in, int rows, int cols,
+                            void* out, int64_t ld_out, int col_off, int rows_pad,
+                            hipStream_t s);
+
+hipError_t launch_gemv(int M, int N, int K, const void* x, const void* wg, const void* wu,
+                       void* h, hipStream_t s);
+
+hipError_t launch_act_quant(int64_t rows, int64_t cols, const float* gate, const float* up,
+                            float limit, bool clamp, uint8_t* q, uint8_t* scale,
+                            uint64_t* count, float* hout, hipStream_t s);
+
+hipError_t launch_probe_read2(const void* a, const void* b, size_t bytes, uint32_t* sink,
+                              hipStream_t s);
+
+}  // namespace swg

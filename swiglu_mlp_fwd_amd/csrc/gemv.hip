@@ -1,0 +1,106 @@
+// Decode forward, 1 <= M <= 8 tokens, bf16: h = SiLU(x Wg^T) * (x Wu^T).
+//
+// The work is bound by reading Wg and Wu from HBM once ("Fused SwiGLU
+// benchmark", AstrAI docs/developer/swiglu_benchmark.md, sections L20
+// findings and HBM re-measurement: the wide shapes are weight-bandwidth
+// dominated and the fused kernel sits at the dual-stream cold-read floor).
+// No matrix cores: the dot products run on the vector ALU with the bf16 dot2
+// instruction (two bf16 products accumulated into fp32 per lane-op).
+//
+// Mapping: each half-wave (32 lanes) owns one output column n and streams
+// the rows Wg[n, :] and Wu[n, :] with 16-byte loads (lane j reads chunks
+// j, j+32, ...); x [M, K] is staged once per workgroup in LDS and each 16-byte
+// chunk of it is reused for both weights.  Per lane the 2M partial sums are
+// reduced across the half-wave with butterfly shuffles; lane 0 of the half
+// applies SiLU(g) * u and stores the M outputs of its column.
+#include "common.hpp"
+#include "gemm.hpp"
+
+namespace swg {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kColsPerBlock = 8;  // 4 waves x 2 half-waves
+
+template <int M>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__ x,
+                                                        const bf16* __restrict__ wg,
+                                                        const bf16* __restrict__ wu,
+                                                        bf16* __restrict__ h, int N, int K) {
+  extern __shared__ u32x4 xs[];  // [M][K / 8]
+  const int nch = K >> 3;
+  const int tid = threadIdx.x;
+  const u32x4* xg = reinterpret_cast<const u32x4*>(x);
+  for (int i = tid; i < M * nch; i += kThreads) xs[i] = xg[i];
+  __syncthreads();
+
+  const int lane = tid & 63;
+  const int hl = lane & 31;
+  const int col = (blockIdx.x * (kThreads / 64) + (tid >> 6)) * 2 + (lane >> 5);
+  if (col >= N) return;
+
+  const u32x4* rg = reinterpret_cast<const u32x4*>(wg + (int64_t)col * K);
+  const u32x4* ru = reinterpret_cast<const u32x4*>(wu + (int64_t)col * K);
+  float ag[M], au[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) ag[m] = au[m] = 0.0f;
+
+#pragma unroll 4
+  for (int c = hl; c < nch; c += 32) {
+    const u32x4 vg = __builtin_nontemporal_load(rg + c);
+    const u32x4 vu = __builtin_nontemporal_load(ru + c);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const u32x4 xv = xs[m * nch + c];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x2 xx = as_bf16x2(xv[t]);
+        ag[m] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vg[t]), xx, ag[m], false);
+        au[m] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vu[t]), xx, au[m], false);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) {
+      ag[m] += __shfl_xor(ag[m], off, 32);
+      au[m] += __shfl_xor(au[m], off, 32);
+    }
+  }
+  if (hl == 0) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) h[(int64_t)m * N + col] = to_bf16(silu_f32(ag[m]) * au[m]);
+  }
+}
+
+template <int M>
+hipError_t launch_m(int N, int K, const void* x, const void* wg, const void* wu, void* h,
+                    hipStream_t s) {
+  const unsigned blocks = (unsigned)((N + kColsPerBlock - 1) / kColsPerBlock);
+  const size_t lds = (size_t)M * K * 2;
+  hipLaunchKernelGGL(gemv_kernel<M>, dim3(blocks), dim3(kThreads), lds, s,
+                     static_cast<const bf16*>(x), static_cast<const bf16*>(wg),
+                     static_cast<const bf16*>(wu), static_cast<bf16*>(h), N, K);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(int M, int N, int K, const void* x, const void* wg, const void* wu, void* h,
+                       hipStream_t s) {
+  switch (M) {
+    case 1: return launch_m<1>(N, K, x, wg, wu, h, s);
+    case 2: return launch_m<2>(N, K, x, wg, wu, h, s);
+    case 3: return launch_m<3>(N, K, x, wg, wu, h, s);
+    case 4: return launch_m<4>(N, K, x, wg, wu, h, s);
+    case 5: return launch_m<5>(N, K, x, wg, wu, h, s);
+    case 6: return launch_m<6>(N, K, x, wg, wu, h, s);
+    case 7: return launch_m<7>(N, K, x, wg, wu, h, s);
+    case 8: return launch_m<8>(N, K, x, wg, wu, h, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace swg

@@ -1,0 +1,144 @@
+// Host-side argument validation and workspace layout for the C ABI.
+// Pure C++ (no HIP), so it can be compiled and tested without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "swiglu.h"
+
+namespace swg {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+inline int elem_size(int dtype) { return dtype == SWIGLU_BF16 ? 2 : 4; }
+// Elements per 16-byte row chunk: rows must be whole chunks for 128-bit loads.
+inline int chunk_elems(int dtype) { return dtype == SWIGLU_BF16 ? 8 : 4; }
+
+inline int check_dtype(int dtype) {
+  return (dtype == SWIGLU_F32 || dtype == SWIGLU_BF16) ? SWIGLU_OK : SWIGLU_ERR_DTYPE;
+}
+
+inline int check_dims(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return SWIGLU_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SWIGLU_ERR_SHAPE;
+  return SWIGLU_OK;
+}
+
+// GEMM tiles are 128 x 128; the launch grid must stay below 2^31 workgroups.
+inline bool tiles_fit(int64_t m, int64_t n) {
+  return ((m + 127) / 128) * ((n + 127) / 128) < (int64_t(1) << 31);
+}
+
+inline int check_ptr(const void* p) {
+  if (p == nullptr) return SWIGLU_ERR_NULL;
+  if (!aligned(p, 16)) return SWIGLU_ERR_ALIGN;
+  return SWIGLU_OK;
+}
+
+// Backward workspace: four regions, each starting on a 256-byte boundary.
+//   D   [M, 2 Np]     dg in columns [0, Np), du in [Np, 2 Np), zero padded
+//   DT  [2 Np, Mp]    transpose of D, zero padded along M
+//   XT  [K, Mp]       transpose of x, zero padded along M
+//   WT  [K, 2 Np]     [Wg; Wu] transposed, zero padded along N
+// with Mp = round_up(M, 8), Np = round_up(N, 8).
+struct BwdLayout {
+  int64_t Mp, Np;
+  size_t off_d, off_dt, off_xt, off_wt, total;
+};
+
+inline BwdLayout bwd_layout(int dtype, int64_t M, int64_t N, int64_t K) {
+  BwdLayout L;
+  const size_t es = (size_t)elem_size(dtype);
+  L.Mp = round_up(M, 8);
+  L.Np = round_up(N, 8);
+  auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
+  size_t off = 0;
+  L.off_d = off;  off += a256((size_t)M * 2 * L.Np * es);
+  L.off_dt = off; off += a256((size_t)2 * L.Np * L.Mp * es);
+  L.off_xt = off; off += a256((size_t)K * L.Mp * es);
+  L.off_wt = off; off += a256((size_t)K * 2 * L.Np * es);
+  L.total = off;
+  return L;
+}
+
+inline int validate_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                        const void* wu, const void* h) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_dims(M, N, K))) return st;
+  if (K % chunk_elems(dtype) != 0) return SWIGLU_ERR_SHAPE;
+  if (!tiles_fit(M, N)) return SWIGLU_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return SWIGLU_OK;
+  if ((st = check_ptr(h))) return st;
+  if (K > 0) {
+    if ((st = check_ptr(x))) return st;
+    if ((st = check_ptr(wg))) return st;
+    if ((st = check_ptr(wu))) return st;
+  }
+  return SWIGLU_OK;
+}
+
+inline int validate_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                        const void* wu, const void* dh, const void* dx, const void* dwg,
+                        const void* dwu, const void* ws, size_t ws_bytes) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if ((st = check_dims(M, N, K))) return st;
+  if (K % chunk_elems(dtype) != 0) return SWIGLU_ERR_SHAPE;
+  const BwdLayout L = bwd_layout(dtype, M, N, K);
+  if (!tiles_fit(M, L.Np) || !tiles_fit(M, K) || !tiles_fit(2 * L.Np, K)) return SWIGLU_ERR_UNSUPPORTED;
+  if (K == 0) return SWIGLU_OK;                       // every output is empty
+  if (M > 0 && (st = check_ptr(dx))) return st;
+  if (N > 0 && (st = check_ptr(dwg))) return st;
+  if (N > 0 && (st = check_ptr(dwu))) return st;
+  if (M == 0 || N == 0) return SWIGLU_OK;             // outputs are zero-filled
+  if ((st = check_ptr(x))) return st;
+  if ((st = check_ptr(wg))) return st;
+  if ((st = check_ptr(wu))) return st;
+  if ((st = check_ptr(dh))) return st;
+  if (ws == nullptr) return SWIGLU_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return SWIGLU_ERR_ALIGN;
+  if (ws_bytes < L.total) return SWIGLU_ERR_WORKSPACE;
+  return SWIGLU_OK;
+}
+
+inline int validate_gemv(int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                         const void* wu, const void* h) {
+  if (M < 0 || M > 8) return SWIGLU_ERR_SHAPE;
+  int st = check_dims(M, N, K);
+  if (st) return st;
+  if (K % 8 != 0) return SWIGLU_ERR_SHAPE;
+  if (M * K * 2 > 65536) return SWIGLU_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return SWIGLU_OK;
+  if ((st = check_ptr(h))) return st;
+  if (K > 0) {
+    if ((st = check_ptr(x))) return st;
+    if ((st = check_ptr(wg))) return st;
+    if ((st = check_ptr(wu))) return st;
+  }
+  return SWIGLU_OK;
+}
+
+inline int validate_act_quant(int64_t rows, int64_t cols, const float* gate, const float* up,
+                              float L, const void* q, const void* scale, const void* count,
+                              const void* hout) {
+  if (rows < 0 || cols < 0) return SWIGLU_ERR_SHAPE;
+  if (cols % 32 != 0) return SWIGLU_ERR_SHAPE;
+  if (rows > 0 && cols > (int64_t(1) << 40) / rows) return SWIGLU_ERR_SHAPE;
+  if (!(L > 0.0f)) return SWIGLU_ERR_ARG;             // rejects NaN, zero and negatives
+  if (count != nullptr && !aligned(count, 8)) return SWIGLU_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return SWIGLU_OK;
+  int st;
+  if ((st = check_ptr(gate))) return st;
+  if ((st = check_ptr(up))) return st;
+  if ((st = check_ptr(q))) return st;
+  if ((st = check_ptr(scale))) return st;
+  if (hout != nullptr && !aligned(hout, 16)) return SWIGLU_ERR_ALIGN;
+  return SWIGLU_OK;
+}
+
+}  // namespace swg

@@ -1,0 +1,168 @@
+"""PyTorch-facing wrappers of libswiglu.
+
+Argument marshalling only: tensors are checked, made contiguous, outputs are
+allocated with torch.empty on the input's device, and the library is called
+on the current HIP stream.  Every step of the computation runs in the HIP
+kernels behind the C ABI.
+
+Inputs of rank >= 3 are viewed as [M, K] and the output restored to the
+leading shape ("VisualGen MLP: cublasLt GELU-tanh epilogue for the
+unquantized bf16 path", TensorRT-LLM PR 17693, section Change: rank >= 3
+inputs are flattened to [M, in] and restored afterward).
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._lib import SWIGLU_BF16, SWIGLU_F32, check, lib
+
+_DT = {torch.bfloat16: SWIGLU_BF16, torch.float32: SWIGLU_F32}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"libswiglu supports bfloat16 and float32, got {t.dtype}") from None
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _same(*ts):
+    d, dev = ts[0].dtype, ts[0].device
+    for t in ts[1:]:
+        if t.dtype != d:
+            raise TypeError(f"dtype mismatch: {t.dtype} vs {d}")
+        if t.device != dev:
+            raise ValueError(f"device mismatch: {t.device} vs {dev}")
+    if dev.type != "cuda":
+        raise ValueError("libswiglu operates on GPU tensors only")
+
+
+def _p(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """h = SiLU(x Wg^T) * (x Wu^T).  x [..., K], Wg/Wu [N, K] -> h [..., N]."""
+    _same(x, wg, wu)
+    lead, K = x.shape[:-1], x.shape[-1]
+    N = wg.shape[0]
+    if wg.shape != (N, K) or wu.shape != (N, K):
+        raise ValueError(f"weights must be [N, K] = [{N}, {K}], got {tuple(wg.shape)}, {tuple(wu.shape)}")
+    M = math.prod(lead)
+    x2 = x.reshape(M, K).contiguous()
+    wg, wu = wg.contiguous(), wu.contiguous()
+    h = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if out is not None and (out.shape != (M, N) or out.dtype != x.dtype or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous [M, N] tensor of the input dtype")
+    check("swiglu_fwd", lib().swiglu_fwd(_dtype_code(x), M, N, K, _p(x2), _p(wg), _p(wu), _p(h), _stream(x)))
+    return h.reshape(*lead, N)
+
+
+def bwd_workspace_bytes(dtype: torch.dtype, M: int, N: int, K: int) -> int:
+    return int(lib().swiglu_bwd_workspace_bytes(_DT[dtype], M, N, K))
+
+
+def bwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, dh: torch.Tensor,
+        workspace: torch.Tensor | None = None):
+    """(dx, dwg, dwu) of L = sum(dh * h).  Shapes as in fwd; dh [..., N]."""
+    _same(x, wg, wu, dh)
+    lead, K = x.shape[:-1], x.shape[-1]
+    N = wg.shape[0]
+    M = math.prod(lead)
+    if dh.shape != (*lead, N):
+        raise ValueError(f"dh must be {(*lead, N)}, got {tuple(dh.shape)}")
+    x2 = x.reshape(M, K).contiguous()
+    dh2 = dh.reshape(M, N).contiguous()
+    wg, wu = wg.contiguous(), wu.contiguous()
+    if dh2.shape[0] != M:
+        raise ValueError("dh must have the leading shape of x")
+    dt = _dtype_code(x)
+    need = int(lib().swiglu_bwd_workspace_bytes(dt, M, N, K))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    dx = torch.empty((M, K), dtype=x.dtype, device=x.device)
+    dwg = torch.empty((N, K), dtype=x.dtype, device=x.device)
+    dwu = torch.empty((N, K), dtype=x.dtype, device=x.device)
+    check("swiglu_bwd", lib().swiglu_bwd(dt, M, N, K, _p(x2), _p(wg), _p(wu), _p(dh2), _p(dx), _p(dwg),
+                                         _p(dwu), _p(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(x)))
+    return dx.reshape(*lead, K), dwg, dwu
+
+
+def gemv_fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode forward for M <= 8 tokens (bf16): same result as fwd."""
+    _same(x, wg, wu)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("gemv_fwd is bf16 only")
+    lead, K = x.shape[:-1], x.shape[-1]
+    N = wg.shape[0]
+    M = math.prod(lead)
+    x2 = x.reshape(M, K).contiguous()
+    wg, wu = wg.contiguous(), wu.contiguous()
+    h = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
+    check("swiglu_gemv_fwd", lib().swiglu_gemv_fwd(M, N, K, _p(x2), _p(wg), _p(wu), _p(h), _stream(x)))
+    return h.reshape(*lead, N)
+
+
+def act_quant(gate: torch.Tensor, up: torch.Tensor, clamp_limit: float = math.inf,
+              count: bool = True, h_out: bool = False, out=None):
+    """Elementwise SwiGLU + 1x32 UE8M0/E4M3 quantisation.
+
+    Returns (q uint8 [rows, cols], scale uint8 [rows, cols/32],
+    clamp_count int64 tensor [1] or None, h fp32 or None).
+    `out` may pass preallocated (q, scale, count, h) tensors.
+    """
+    _same(gate, up)
+    if gate.dtype != torch.float32:
+        raise TypeError("act_quant takes fp32 gate/up")
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    cols = gate.shape[-1]
+    rows = math.prod(gate.shape[:-1])
+    g2 = gate.reshape(rows, cols).contiguous()
+    u2 = up.reshape(rows, cols).contiguous()
+    dev = gate.device
+    if out is not None:
+        q, scale, cnt, h = out
+    else:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        scale = torch.empty((rows, cols // 32 if cols % 32 == 0 else 0), dtype=torch.uint8, device=dev)
+        cnt = torch.empty(1, dtype=torch.int64, device=dev) if count else None
+        h = torch.empty((rows, cols), dtype=torch.float32, device=dev) if h_out else None
+    check("swiglu_act_quant", lib().swiglu_act_quant(rows, cols, _p(g2), _p(u2), float(clamp_limit), _p(q),
+                                                     _p(scale), _p(cnt), _p(h), _stream(gate)))
+    return q, scale, cnt, h
+
+
+def probe_read2(a: torch.Tensor, b: torch.Tensor, sink: torch.Tensor) -> None:
+    """Pure read of two equally sized buffers (cold-read floor measurement)."""
+    nbytes = a.numel() * a.element_size()
+    if b.numel() * b.element_size() != nbytes:
+        raise ValueError("probe buffers must have equal size")
+    check("swiglu_probe_read2", lib().swiglu_probe_read2(_p(a), _p(b), nbytes, _p(sink), _stream(a)))
+
+
+class SwiGLUFunction(torch.autograd.Function):
+    """Autograd wrapper: forward = fwd, backward = bwd (g and u are recomputed)."""
+
+    @staticmethod
+    def forward(ctx, x, wg, wu):
+        ctx.save_for_backward(x, wg, wu)
+        return fwd(x, wg, wu)
+
+    @staticmethod
+    def backward(ctx, dh):
+        x, wg, wu = ctx.saved_tensors
+        dx, dwg, dwu = bwd(x, wg, wu, dh)
+        return dx, dwg, dwu
+
+
+def swiglu(x, wg, wu):
+    """Differentiable fused SwiGLU gate/up stage."""
+    return SwiGLUFunction.apply(x, wg, wu)

@@ -1,0 +1,96 @@
+"""Helpers shared by the GPU parity tests: host<->device transfer of the
+synthetic inputs, and the tolerance checks.
+
+Tolerances (written out here, derived in the design doc):
+  * the gates stated for the path: normwise relative error max|y-r|/max|r|
+    <= 1e-5 for fp32 and <= 2e-2 for bf16, cosine >= 0.9999 for bf16;
+  * an elementwise bound per output built from |A||B| products: with
+    u = 2^-24, fp32 accumulation of n exact products errs by at most
+    gamma_n * sum|a||b| (gamma_n = n u / (1 - n u)); a bf16 operand rounding
+    adds 2^-9 * sum|a||b|; the final rounding adds half an ulp of the output
+    type (2^-9 relative for bf16, 2^-24 for fp32).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+U32 = 2.0 ** -24
+BF16_HALF_ULP = 2.0 ** -9
+
+
+def gamma(n: int, u: float = U32) -> float:
+    return n * u / (1 - n * u)
+
+
+def dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def dev_f32(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return synth.bf16_bits_to_f32(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def f64_of(bits_or_f32: np.ndarray) -> np.ndarray:
+    if bits_or_f32.dtype == np.uint16:
+        return synth.bf16_bits_to_f32(bits_or_f32).astype(np.float64)
+    return bits_or_f32.astype(np.float64)
+
+
+def assert_gates(y, r, dtype: str, what: str):
+    """The stated gates: normwise relative error and (bf16) cosine."""
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    e = oracle.normwise_rel_err(y, r)
+    c = oracle.cosine(y, r)
+    if dtype == "f32":
+        assert e <= 1e-5, f"{what}: normwise rel err {e:.3e} > 1e-5"
+    else:
+        assert e <= 2e-2, f"{what}: normwise rel err {e:.3e} > 2e-2"
+        assert c >= 0.9999, f"{what}: cosine {c:.6f} < 0.9999"
+    return e, c
+
+
+def assert_within(y, r, bound, what: str):
+    """Elementwise |y - r| <= bound; reports the worst ratio."""
+    err = np.abs(y - r)
+    ratio = np.max(err / np.maximum(bound, 1e-300))
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (f"{what}: {len(bad)} elements exceed the bound; first {bad[:3].tolist()}, "
+                           f"worst ratio {ratio:.3g}")
+    return ratio
+
+
+def fwd_bound(x, wg, wu, dtype: str, rows=None):
+    """Elementwise error bound of the fused forward h = silu(g) u on the given rows.
+
+    g and u carry the fp32 accumulation error E = gamma_{K+1} sum|x||w| (the +1
+    covers the rounding of fp32 products on the fp32 path; bf16 products are
+    exact); it reaches h through |silu'(g)| |u| E_g + |silu(g)| E_u (|silu'| is
+    below 1.1).  The activation itself is good to a few fp32 ulps (8 u |h|
+    covers it) and the output rounding adds 2^-9 |h| (bf16) or u |h| (fp32).
+    """
+    xr = x if rows is None else x[rows]
+    K = x.shape[1]
+    g, u = oracle.gate_up(xr, wg, wu)
+    Sg = np.abs(xr) @ np.abs(wg).T
+    Su = np.abs(xr) @ np.abs(wu).T
+    G = gamma(K + 1)
+    h = oracle.silu(g) * u
+    prop = 1.1 * np.abs(u) * G * Sg + np.abs(oracle.silu(g)) * G * Su + G * Sg * G * Su
+    out = BF16_HALF_ULP if dtype == "bf16" else U32
+    return h, 2 * (prop + (8 * U32 + out) * np.abs(h)) + 1e-30
+
+
+def dsw_terms(x, wg, wu, dh):
+    g, u = oracle.gate_up(x, wg, wu)
+    dg, du = oracle.dswiglu(g, u, dh)
+    return g, u, dg, du

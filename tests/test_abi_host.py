@@ -1,0 +1,149 @@
+"""Host-side tests of the C-ABI library (no GPU): it loads, exports every
+symbol the header declares, and rejects invalid arguments before any launch.
+
+Every call here fails validation, so no kernel is enqueued and no HIP call is
+made (validation runs on the host before anything else).
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import swiglu_mlp_fwd_amd as S
+from swiglu_mlp_fwd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swiglu.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EARG, EUNSUP = 0, 1, 2, 3, 4, 5, 6, 7
+A = 0x10000  # a 16-byte-aligned fake device address; never dereferenced
+MIS = 0x10008
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from swiglu_mlp_fwd_amd import build
+        build.build()
+    return S.lib()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(swiglu_\w+)\s*\(", src, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = set(header_functions())
+    for n in ("swiglu_fwd", "swiglu_bwd", "swiglu_bwd_workspace_bytes", "swiglu_gemv_fwd",
+              "swiglu_act_quant", "swiglu_status_str", "swiglu_last_hip_error"):
+        assert n in names
+
+
+def test_library_exports_every_header_symbol(L):
+    names = header_functions()
+    assert names
+    for n in names:
+        assert hasattr(L, n), n
+    # ...and the binding's signature table covers exactly those symbols.
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_version_and_status_strings(L):
+    assert L.swiglu_version() >= 100
+    assert L.swiglu_status_str(0) == b"ok"
+    for s in range(1, 9):
+        assert L.swiglu_status_str(s) not in (b"ok", b"unknown status")
+    assert L.swiglu_status_str(99) == b"unknown status"
+    assert L.swiglu_last_hip_error() == 0
+
+
+def test_fwd_validation(L):
+    f = L.swiglu_fwd
+    assert f(2, 4, 4, 8, A, A, A, A, None) == EDTYPE
+    assert f(1, -1, 4, 8, A, A, A, A, None) == ESHAPE
+    assert f(1, 4, 4, 12, A, A, A, A, None) == ESHAPE          # bf16 needs K % 8 == 0
+    assert f(0, 4, 4, 6, A, A, A, A, None) == ESHAPE           # fp32 needs K % 4 == 0
+    assert f(1, 4, 4, 8, None, A, A, A, None) == ENULL
+    assert f(1, 4, 4, 8, A, A, A, None, None) == ENULL
+    assert f(1, 4, 4, 8, A, MIS, A, A, None) == EALIGN
+    assert f(1, 1 << 31, 4, 8, A, A, A, A, None) == ESHAPE
+    assert f(1, 0, 4, 8, None, None, None, None, None) == OK   # empty: nothing to do
+    assert f(1, 4, 0, 8, None, None, None, None, None) == OK
+
+
+def test_bwd_validation(L):
+    f = L.swiglu_bwd
+    need = L.swiglu_bwd_workspace_bytes(1, 100, 60, 64)
+    assert need > 0 and need % 256 == 0
+    assert L.swiglu_bwd_workspace_bytes(5, 1, 1, 8) == 0
+    assert L.swiglu_bwd_workspace_bytes(1, -1, 1, 8) == 0
+    args = [1, 100, 60, 64, A, A, A, A, A, A, A]
+    assert f(*args, A, need - 1, None) == EWS
+    assert f(*args, None, need, None) == EWS
+    assert f(*args, 0x10010, need, None) == EALIGN             # workspace needs 256-byte alignment
+    assert f(1, 100, 60, 64, A, A, A, None, A, A, A, A, need, None) == ENULL
+    assert f(1, 100, 60, 60, A, A, A, A, A, A, A, A, need, None) == ESHAPE
+    assert f(1, 100, 60, 64, A, A, A, A, A, MIS, A, A, need, None) == EALIGN
+    assert f(1, 100, 60, 0, None, None, None, None, None, None, None, None, 0, None) == OK
+
+
+def test_workspace_layout_formula(L):
+    # D [M, 2Np] + DT [2Np, Mp] + XT [K, Mp] + WT [K, 2Np], each 256-byte aligned.
+    def a256(v):
+        return (v + 255) // 256 * 256
+    for (dt, es) in ((0, 4), (1, 2)):
+        for (M, N, K) in ((100, 60, 64), (8192, 14336, 4096), (1, 1, 8)):
+            Mp, Np = -(-M // 8) * 8, -(-N // 8) * 8
+            want = a256(M * 2 * Np * es) + a256(2 * Np * Mp * es) + a256(K * Mp * es) + a256(K * 2 * Np * es)
+            assert L.swiglu_bwd_workspace_bytes(dt, M, N, K) == want
+
+
+def test_gemv_validation(L):
+    f = L.swiglu_gemv_fwd
+    assert f(9, 16, 64, A, A, A, A, None) == ESHAPE
+    assert f(-1, 16, 64, A, A, A, A, None) == ESHAPE
+    assert f(2, 16, 60, A, A, A, A, None) == ESHAPE
+    assert f(8, 16, 8192, A, A, A, A, None) == EUNSUP          # x does not fit the LDS stage
+    assert f(2, 16, 64, A, None, A, A, None) == ENULL
+    assert f(2, 16, 64, A, A, A, MIS, None) == EALIGN
+    assert f(0, 16, 64, None, None, None, None, None) == OK
+
+
+def test_act_quant_validation(L):
+    f = L.swiglu_act_quant
+    assert f(4, 48, A, A, 7.0, A, A, None, None, None) == ESHAPE   # cols % 32
+    assert f(-1, 64, A, A, 7.0, A, A, None, None, None) == ESHAPE
+    assert f(4, 64, A, A, 0.0, A, A, None, None, None) == EARG
+    assert f(4, 64, A, A, -1.0, A, A, None, None, None) == EARG
+    assert f(4, 64, A, A, math.nan, A, A, None, None, None) == EARG
+    assert f(4, 64, None, A, 7.0, A, A, None, None, None) == ENULL
+    assert f(4, 64, A, A, 7.0, A, None, None, None, None) == ENULL
+    assert f(4, 64, A, A, 7.0, A, A, 0x10004, None, None) == EALIGN  # count needs 8-byte alignment
+    assert f(4, 64, A, A, math.inf, MIS, A, None, None, None) == EALIGN
+
+
+def test_probe_validation(L):
+    assert L.swiglu_probe_read2(A, A, 17, A, None) == ESHAPE
+    assert L.swiglu_probe_read2(None, A, 32, A, None) == ENULL
+    assert L.swiglu_probe_read2(A, A, 0, A, None) == OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()
+
+
+def test_product_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "swiglu_mlp_fwd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in text and "from oracle" not in text, fn
+                assert "synth" not in text, fn
