@@ -27,8 +27,8 @@
 //   waves (64 x 128 per wave); both were the fastest of the tile shapes
 //   measured at the 8192 x 14336 x 4096 training shapes.  LDS holds two k-steps
 //   (double buffer); rows are stored as eight 16-byte chunks with the chunk
-//   index XOR-swizzled by (row & 7), so the 16-byte MFMA operand reads of 8
-//   consecutive rows hit 8 distinct bank groups.
+//   index XOR-swizzled (swz below) so the 16-byte MFMA operand reads are
+//   free of bank conflicts.
 // MFMA operand mapping: lane l supplies row (l & 31) of its 32-row operand
 // tile and the 16-byte chunk (2 kk + (l >> 5)) of the k-step; the same chunk
 // mapping for A and B makes the products pair up correctly whatever order
@@ -57,6 +57,19 @@ struct Tile {
 
 enum class Epi { kSwiGLU, kDSwiGLU, kStore };
 
+// Physical 16-byte chunk of logical chunk c in LDS row r.  gfx950 serves a
+// 128-bit LDS read for 16 lanes per cycle across 64 four-byte banks, i.e.
+// 16 distinct 16-byte bank groups (group = (8 r + chunk) mod 16 for 128-byte
+// rows).  The MFMA operand reads put 16 consecutive rows at one logical
+// chunk in a lane group; XOR-ing the chunk with (r >> 1) & 7 gives those 16
+// rows 16 distinct groups, and keeps the 16-byte stores of 2 full rows per
+// 16 lanes conflict-free.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// Largest row count a block tile of either operand has.
+template <int BM, int BN>
+__device__ __forceinline__ constexpr int r_cap() { return BM > BN ? BM : BN; }
+
 template <typename T> struct Mma;
 
 template <> struct Mma<bf16> {
@@ -84,124 +97,15 @@ template <typename T> __device__ __forceinline__ float load_in(const T* p);
 template <> __device__ __forceinline__ float load_in<bf16>(const bf16* p) { return from_bf16(*p); }
 template <> __device__ __forceinline__ float load_in<float>(const float* p) { return *p; }
 
+// Epilogue shared by both kernels.  32 x 32 accumulator layout: lane l,
+// element e holds row 8 (e >> 2) + 4 (l >> 5) + (e & 3), column l & 31.
 template <typename T, Epi E, int NB, class TL>
-__global__ __launch_bounds__(TL::kThreads) void gemm_kernel(GemmArgs p) {
-  constexpr int kBM = TL::kBM, kBN = TL::kBN, kThreads = TL::kThreads;
-  constexpr int kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
-  constexpr int kRows = kBM + NB * kBN;                 // LDS rows per k-step
-  constexpr int kUnits = kRows * kChunks / kThreads;    // 16-byte loads per thread
-  constexpr int kPer = Mma<T>::kPerChunk;
-  extern __shared__ u32x4 lds[];                        // [2][kRows * kChunks]
-
-  const int ntm = (p.m + kBM - 1) / kBM;
-  const int ntn = (p.n + kBN - 1) / kBN;
-  const int tile = xcd_remap(blockIdx.x, ntm * ntn);
-  const int group = kGroupM * ntn;
-  const int first_m = (tile / group) * kGroupM;
-  const int gm = min(ntm - first_m, kGroupM);
-  const int tm = first_m + (tile % group) % gm;
-  const int tn = (tile % group) / gm;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / TL::kWGN, wn = wave % TL::kWGN;
-
-  const T* A = static_cast<const T*>(p.a);
-  const T* B0 = static_cast<const T*>(p.b0);
-  const T* B1 = static_cast<const T*>(p.b1);
-  const int nchunk_r = p.r / kPer;                      // r % kPer == 0 (host-checked)
-  const int nk = (nchunk_r + kChunks - 1) / kChunks;
-
-  // Global -> register staging of one k-step.  Thread t moves the 16-byte
-  // chunk (t & 7) of rows (t >> 3) + (kThreads / 8) i of each operand tile.
-  constexpr int kRowsPerPass = kThreads / kChunks;
-  constexpr int kUA = kBM / kRowsPerPass;               // loads for A
-  constexpr int kUB = kBN / kRowsPerPass;               // loads per B
-  static_assert(kUnits == kUA + NB * kUB, "staging split");
-  const int trow = tid >> 3, tch = tid & 7;
-  u32x4 stage[kUnits];
-  auto gload = [&](int ks) {
-    const int kc = ks * kChunks + tch;
-    const bool kin = kc < nchunk_r;
-    const int64_t koff = (int64_t)kc * kPer;
-#pragma unroll
-    for (int i = 0; i < kUA; ++i) {
-      const int g = tm * kBM + trow + kRowsPerPass * i;
-      stage[i] = (kin && g < p.arows) ? *reinterpret_cast<const u32x4*>(A + (int64_t)g * p.lda + koff)
-                                      : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int w = 0; w < NB; ++w) {
-      const T* B = w == 0 ? B0 : B1;
-#pragma unroll
-      for (int i = 0; i < kUB; ++i) {
-        const int g = tn * kBN + trow + kRowsPerPass * i;
-        stage[kUA + w * kUB + i] =
-            (kin && g < p.brows) ? *reinterpret_cast<const u32x4*>(B + (int64_t)g * p.ldb + koff)
-                                 : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-    u32x4* L = lds + buf * (kRows * kChunks);
-#pragma unroll
-    for (int i = 0; i < kUnits; ++i) {
-      const int row = trow + kRowsPerPass * i;          // rows of A, then B0, then B1
-      L[row * kChunks + (tch ^ (row & 7))] = stage[i];
-    }
-  };
-
-  f32x16 acc[NB][kTM][kTN];
-#pragma unroll
-  for (int w = 0; w < NB; ++w)
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kTN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[w][i][j][e] = 0.0f;
-
-  if (nk > 0) {
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    if (nk > 1) gload(1);
-  }
+__device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[NB][TL::kTM][TL::kTN],
+                                           int tm, int tn, int wm, int wn, int lane) {
+  constexpr int kBM = TL::kBM, kBN = TL::kBN, kTM = TL::kTM, kTN = TL::kTN;
+  constexpr int kWM = TL::kWM, kWN = TL::kWN;
   const int r32 = lane & 31;
   const int half = lane >> 5;
-  for (int ks = 0; ks < nk; ++ks) {
-    const u32x4* L = lds + (ks & 1) * (kRows * kChunks);
-#pragma unroll
-    for (int kk = 0; kk < kChunks / 2; ++kk) {
-      const int ch = 2 * kk + half;
-      u32x4 av[kTM], bv[NB][kTN];
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        const int row = wm * kWM + i * 32 + r32;
-        av[i] = L[row * kChunks + (ch ^ (row & 7))];
-      }
-#pragma unroll
-      for (int w = 0; w < NB; ++w)
-#pragma unroll
-        for (int j = 0; j < kTN; ++j) {
-          const int row = kBM + w * kBN + wn * kWN + j * 32 + r32;
-          bv[w][j] = L[row * kChunks + (ch ^ (row & 7))];
-        }
-#pragma unroll
-      for (int w = 0; w < NB; ++w)
-#pragma unroll
-        for (int i = 0; i < kTM; ++i)
-#pragma unroll
-          for (int j = 0; j < kTN; ++j) Mma<T>::run(acc[w][i][j], av[i], bv[w][j]);
-    }
-    if (ks + 1 < nk) lstore((ks + 1) & 1);
-    if (ks + 2 < nk) gload(ks + 2);
-    __syncthreads();
-  }
-
-  // Epilogue.  32 x 32 accumulator layout: lane l, element e holds
-  // row 8 (e >> 2) + 4 (l >> 5) + (e & 3), column l & 31.
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
@@ -245,6 +149,542 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(GemmArgs p) {
 }
 
 template <typename T, Epi E, int NB, class TL>
+__global__ __launch_bounds__(TL::kThreads) void gemm_kernel(GemmArgs p) {
+  constexpr int kBM = TL::kBM, kBN = TL::kBN, kThreads = TL::kThreads;
+  constexpr int kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
+  constexpr int kRows = kBM + NB * kBN;                 // LDS rows per k-step
+  constexpr int kUnits = kRows * kChunks / kThreads;    // 16-byte loads per thread
+  constexpr int kPer = Mma<T>::kPerChunk;
+  extern __shared__ u32x4 lds[];                        // [2][kRows * kChunks]
+
+  const int ntm = (p.m + kBM - 1) / kBM;
+  const int ntn = (p.n + kBN - 1) / kBN;
+  const int tile = xcd_remap(blockIdx.x, ntm * ntn);
+  const int group = kGroupM * ntn;
+  const int first_m = (tile / group) * kGroupM;
+  const int gm = min(ntm - first_m, kGroupM);
+  const int tm = first_m + (tile % group) % gm;
+  const int tn = (tile % group) / gm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // Wave index through readfirstlane: the compiler then knows it is uniform,
+  // so LDS-DMA bases (M0) and buffer descriptors stay in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / TL::kWGN, wn = wave % TL::kWGN;
+
+  const T* A = static_cast<const T*>(p.a);
+  const T* B0 = static_cast<const T*>(p.b0);
+  const T* B1 = static_cast<const T*>(p.b1);
+  const int nchunk_r = p.r / kPer;                      // r % kPer == 0 (host-checked)
+  const int nk = (nchunk_r + kChunks - 1) / kChunks;
+
+  // Global -> register staging of one k-step.  Thread t moves the 16-byte
+  // chunk (t & 7) of rows (t >> 3) + (kThreads / 8) i of each operand tile.
+  constexpr int kRowsPerPass = kThreads / kChunks;
+  constexpr int kUA = kBM / kRowsPerPass;               // loads for A
+  constexpr int kUB = kBN / kRowsPerPass;               // loads per B
+  static_assert(kUnits == kUA + NB * kUB, "staging split");
+  const int trow = tid >> 3, tch = tid & 7;
+  u32x4 stage[kUnits];
+  auto gload = [&](int ks) {
+    const int kc = ks * kChunks + tch;
+    const bool kin = kc < nchunk_r;
+    const int64_t koff = (int64_t)kc * kPer;
+#pragma unroll
+    for (int i = 0; i < kUA; ++i) {
+      const int g = tm * kBM + trow + kRowsPerPass * i;
+      stage[i] = (kin && g < p.arows) ? *reinterpret_cast<const u32x4*>(A + (int64_t)g * p.lda + koff)
+                                      : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int w = 0; w < NB; ++w) {
+      const T* B = w == 0 ? B0 : B1;
+#pragma unroll
+      for (int i = 0; i < kUB; ++i) {
+        const int g = tn * kBN + trow + kRowsPerPass * i;
+        stage[kUA + w * kUB + i] =
+            (kin && g < p.brows) ? *reinterpret_cast<const u32x4*>(B + (int64_t)g * p.ldb + koff)
+                                 : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    u32x4* L = lds + buf * (kRows * kChunks);
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      const int row = trow + kRowsPerPass * i;          // rows of A, then B0, then B1
+      L[row * kChunks + swz(row, tch)] = stage[i];
+    }
+  };
+
+  f32x16 acc[NB][kTM][kTN];
+#pragma unroll
+  for (int w = 0; w < NB; ++w)
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[w][i][j][e] = 0.0f;
+
+  if (nk > 0) {
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    if (nk > 1) gload(1);
+  }
+  const int r32 = lane & 31;
+  const int half = lane >> 5;
+  for (int ks = 0; ks < nk; ++ks) {
+    const u32x4* L = lds + (ks & 1) * (kRows * kChunks);
+#pragma unroll
+    for (int kk = 0; kk < kChunks / 2; ++kk) {
+      const int ch = 2 * kk + half;
+      u32x4 av[kTM], bv[NB][kTN];
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) {
+        const int row = wm * kWM + i * 32 + r32;
+        av[i] = L[row * kChunks + swz(row, ch)];
+      }
+#pragma unroll
+      for (int w = 0; w < NB; ++w)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+          const int row = kBM + w * kBN + wn * kWN + j * 32 + r32;
+          bv[w][j] = L[row * kChunks + swz(row, ch)];
+        }
+#pragma unroll
+      for (int w = 0; w < NB; ++w)
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int j = 0; j < kTN; ++j) Mma<T>::run(acc[w][i][j], av[i], bv[w][j]);
+    }
+    if (ks + 1 < nk) lstore((ks + 1) & 1);
+    if (ks + 2 < nk) gload(ks + 2);
+    __syncthreads();
+  }
+
+  store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
+}
+
+// s_waitcnt that only bounds the vector-memory counter (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14]; expcnt [6:4] and lgkmcnt [11:8] left at
+// their maxima).  The LDS DMA loads below count as vector-memory operations.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Raw buffer descriptor over [base, base + bytes): reads past the end return
+// zero.  Every field goes through readfirstlane so the descriptor is known to
+// be wave-uniform and lives in scalar registers (a descriptor the compiler
+// thinks divergent turns each buffer access into a waterfall loop).
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const T* base, int64_t bytes) {
+  const uint64_t bp = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bp);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, n, 0x00020000);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which waits
+// for every outstanding vector-memory operation, i.e. would drain the DMA
+// ring).  Each wave has already waited for its own DMA of the step with
+// wait_vmcnt; the empty asm statements keep the compiler from moving LDS
+// accesses across the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Second GEMM kernel, used for bf16: the operand tiles go from global memory
+// straight into LDS (buffer_load_dwordx4 ... lds, the gfx950 16-byte LDS
+// DMA), through an S-stage ring of KC-chunk k-steps, with no register
+// staging.  Each wave moves a fixed slab of 64 rows of the stage (all in one
+// operand); a DMA instruction writes 1 KiB of LDS in lane order, so the
+// XOR swizzle is applied on the global side: the lane that lands in
+// physical chunk q of row r fetches logical chunk q ^ swizzle(r).  Buffer
+// descriptors bound each operand's block-tile rows, so rows past the end and
+// k-chunks past the reduction length (given an out-of-range offset) read as
+// zero with no branch.  Per k-step: wait for this wave's DMA of the step,
+// one barrier (every wave's data has landed, and every wave has finished the
+// step whose ring slot is refilled next), issue the DMA of step ks + S - 1,
+// then the MFMAs, with the operand fragments of the next half-step read from
+// LDS while the current ones are in the matrix cores.
+template <typename T, Epi E, int NB, class TL, int KC, int S, bool kPrio>
+__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(TL::kThreads / 256, TL::kThreads / 256)))
+void gemm_dma_kernel(GemmArgs p) {
+  constexpr int kBM = TL::kBM, kBN = TL::kBN, kThreads = TL::kThreads;
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
+  constexpr int kRows = kBM + NB * kBN;                 // LDS rows per k-step
+  constexpr int kRowBytes = KC * 16;
+  constexpr int kStageBytes = kRows * kRowBytes;
+  constexpr int kRowsPerDma = 64 / KC;                  // rows one DMA instruction covers
+  constexpr int kRowsPerWave = kRows / kWaves;
+  constexpr int kDma = kRowsPerWave / kRowsPerDma;      // DMA instructions per wave per k-step
+  constexpr int kSwzShift = (KC == 8) ? 1 : (KC == 4 ? 2 : 3);  // log2(16 / KC)
+  constexpr int kPer = Mma<T>::kPerChunk;
+  static_assert(KC == 4 || KC == 8, "chunks per row");
+  static_assert(kRows % (kWaves * kRowsPerDma) == 0, "DMA split");
+  static_assert(kBM % kRowsPerWave == 0 && kBN % kRowsPerWave == 0, "a wave's slab lies in one operand");
+  extern __shared__ u32x4 lds[];
+  char* const lds_bytes = reinterpret_cast<char*>(lds);
+
+  const int ntm = (p.m + kBM - 1) / kBM;
+  const int ntn = (p.n + kBN - 1) / kBN;
+  const int tile = xcd_remap(blockIdx.x, ntm * ntn);
+  const int group = kGroupM * ntn;
+  const int first_m = (tile / group) * kGroupM;
+  const int gm = min(ntm - first_m, kGroupM);
+  const int tm = first_m + (tile % group) % gm;
+  const int tn = (tile % group) / gm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // Wave index through readfirstlane: the compiler then knows it is uniform,
+  // so LDS-DMA bases (M0) and buffer descriptors stay in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / TL::kWGN, wn = wave % TL::kWGN;
+  const int nchunk_r = p.r / kPer;
+  const int nk = (nchunk_r + KC - 1) / KC;
+
+  // This wave's DMA slab and its operand.
+  const int row0 = wave * kRowsPerWave;
+  const T* base;
+  int64_t ld;
+  int valid;
+  int local0;
+  if (row0 < kBM) {
+    base = static_cast<const T*>(p.a) + (int64_t)tm * kBM * p.lda;
+    ld = p.lda;
+    valid = p.arows - tm * kBM;
+    local0 = row0;
+  } else {
+    const int r = row0 - kBM;
+    base = static_cast<const T*>(r < kBN ? p.b0 : p.b1) + (int64_t)tn * kBN * p.ldb;
+    ld = p.ldb;
+    valid = p.brows - tn * kBN;
+    local0 = r % kBN;
+  }
+  valid = valid < 0 ? 0 : (valid > (r_cap<kBM, kBN>()) ? r_cap<kBM, kBN>() : valid);
+  const __amdgpu_buffer_rsrc_t rsrc = uniform_rsrc(base, valid * ld * (int64_t)sizeof(T));
+  // Lane i of a DMA fills physical chunk (i % KC) of stage row rr = row0 +
+  // d * kRowsPerDma + i / KC; it fetches logical chunk (i % KC) ^ swz(rr).
+  uint32_t voff_row[kDma];
+  int lch[kDma];
+#pragma unroll
+  for (int d = 0; d < kDma; ++d) {
+    const int rr = row0 + d * kRowsPerDma + lane / KC;
+    lch[d] = (lane % KC) ^ ((rr >> kSwzShift) & (KC - 1));
+    voff_row[d] = (uint32_t)((int64_t)(local0 + d * kRowsPerDma + lane / KC) * ld * (int64_t)sizeof(T));
+  }
+  auto issue = [&](int ks) {
+    char* dst = lds_bytes + (ks % S) * kStageBytes + row0 * kRowBytes;
+#pragma unroll
+    for (int d = 0; d < kDma; ++d) {
+      const int kc = ks * KC + lch[d];
+      const uint32_t off = kc < nchunk_r ? voff_row[d] + (uint32_t)(kc * kPer * (int)sizeof(T)) : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + d * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[NB][kTM][kTN];
+#pragma unroll
+  for (int w = 0; w < NB; ++w)
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[w][i][j][e] = 0.0f;
+
+  const int r32 = lane & 31;
+  const int half = lane >> 5;
+  auto frag = [&](const char* L, int row, int ch) -> u32x4 {
+    const int pc = ch ^ ((row >> kSwzShift) & (KC - 1));
+    return *reinterpret_cast<const u32x4*>(L + row * kRowBytes + pc * 16);
+  };
+
+  // Operand fragments of one half-step (16 k), double-buffered in registers.
+  u32x4 av[2][kTM], bv[2][NB][kTN];
+  auto read_frags = [&](int buf, const char* L, int kk) {
+    const int ch = 2 * kk + half;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i) av[buf][i] = frag(L, wm * kWM + i * 32 + r32, ch);
+#pragma unroll
+    for (int w = 0; w < NB; ++w)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) bv[buf][w][j] = frag(L, kBM + w * kBN + wn * kWN + j * 32 + r32, ch);
+  };
+  auto mfmas = [&](int buf) {
+    if (kPrio) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int w = 0; w < NB; ++w)
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) Mma<T>::run(acc[w][i][j], av[buf][i], bv[buf][w][j]);
+    if (kPrio) __builtin_amdgcn_s_setprio(0);
+  };
+  // Wait until at most `later` of this wave's DMA steps are still in flight
+  // (DMA completes in issue order, so every earlier step has landed), and
+  // until its own LDS reads are done, so no slot it read is still being read
+  // when the barrier lets another wave's DMA refill it.
+  auto wait_dma = [&](int later) {
+    static_assert(S <= 4, "wait table");
+    if (later <= 0) wait_vmcnt<0>();
+    else if (later == 1) wait_vmcnt<kDma>();
+    else if (later == 2) wait_vmcnt<2 * kDma>();
+    else wait_vmcnt<3 * kDma>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0), other counters free
+  };
+
+  // Schedule.  The ring holds S steps; the prologue fills it.  The
+  // fragments of half-step kk + 1 are read before the MFMAs of half-step kk
+  // (scheduling fences keep the two register sets apart), and the step
+  // boundary sits inside the last half-step: wait for the next step's DMA,
+  // barrier, refill the slot of the step just consumed with step ks + S, and
+  // read the next step's first fragments before the last MFMAs of this
+  // step.  So no LDS read latency is exposed in the steady state.
+  constexpr int kKK = KC / 2;
+  static_assert(kKK % 2 == 0, "the next step's first fragments go to buffer 0");
+#pragma unroll
+  for (int s0 = 0; s0 < S; ++s0)
+    if (s0 < nk) issue(s0);
+  if (nk > 0) {
+    wait_dma(min(S - 1, nk - 1));
+    barrier_no_fence();
+    read_frags(0, lds_bytes, 0);
+  }
+  for (int ks = 0; ks < nk; ++ks) {
+    const char* L = lds_bytes + (ks % S) * kStageBytes;
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
+      if (kk + 1 < kKK) {
+        read_frags((kk + 1) & 1, L, kk + 1);
+      } else if (ks + 1 < nk) {
+        wait_dma(min(S - 2, nk - 2 - ks));   // step ks + 1 has landed
+        barrier_no_fence();                  // and every wave has read step ks
+        if (ks + S < nk) issue(ks + S);      // refills the slot of step ks
+        read_frags(0, lds_bytes + ((ks + 1) % S) * kStageBytes, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(kk & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
+}
+
+// Third GEMM kernel ("ping-pong"), for 8-wave tiles: the waves form two
+// groups of four, one wave of each group on every SIMD (wave w runs on SIMD
+// w % 4).  The groups alternate between a memory phase (read every operand
+// fragment of one k-step from LDS into registers; group 0 also issues the
+// LDS DMA of a later step) and a compute phase (only MFMAs, from registers),
+// offset by one barrier, so each SIMD's matrix core is fed by one group
+// while the other group waits on memory:
+//
+//   group 0: P B M0 B C0 B M1 B C1 B ... B C(n-1) B T
+//   group 1:   B    B M0 B C0 B M1 B ... B C(n-1) B
+//
+// (P: prologue DMA + wait, B: barrier, T: group 0's trailing barrier; both
+// groups execute 2 n + 2 barriers on every path.)  Group 0 moves all the
+// DMA; before the barrier that ends its compute phase of step t it waits
+// for its DMA of step t + 1, which every later reader of step t + 1 is
+// behind.  The DMA of step t + S - 1 is issued in group 0's memory phase of
+// step t into the ring slot of step t - 1, whose last reader (group 1's
+// memory phase of step t - 1) ended at the preceding barrier.
+template <typename T, Epi E, int NB, class TL, int KC, int S, bool kPrio>
+__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pp_kernel(GemmArgs p) {
+  constexpr int kBM = TL::kBM, kBN = TL::kBN, kThreads = TL::kThreads;
+  constexpr int kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
+  constexpr int kRows = kBM + NB * kBN;
+  constexpr int kRowBytes = KC * 16;
+  constexpr int kStageBytes = kRows * kRowBytes;
+  constexpr int kRowsPerDma = 64 / KC;
+  constexpr int kRowsPerWave = kRows / 4;               // group 0's four waves move the stage
+  constexpr int kDma = kRowsPerWave / kRowsPerDma;
+  constexpr int kSwzShift = (KC == 8) ? 1 : 2;
+  constexpr int kPer = Mma<T>::kPerChunk;
+  constexpr int kKK = KC / 2;
+  static_assert(kThreads == 512, "ping-pong needs 8 waves");
+  static_assert(KC == 4 || KC == 8, "chunks per row");
+  static_assert(S >= 2, "stages");
+  static_assert(kBM % kRowsPerWave == 0 && kBN % kRowsPerWave == 0, "a wave's slab lies in one operand");
+  extern __shared__ u32x4 lds[];
+  char* const lds_bytes = reinterpret_cast<char*>(lds);
+
+  const int ntm = (p.m + kBM - 1) / kBM;
+  const int ntn = (p.n + kBN - 1) / kBN;
+  const int tile = xcd_remap(blockIdx.x, ntm * ntn);
+  const int group = kGroupM * ntn;
+  const int first_m = (tile / group) * kGroupM;
+  const int gm = min(ntm - first_m, kGroupM);
+  const int tm = first_m + (tile % group) % gm;
+  const int tn = (tile % group) / gm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // Wave index through readfirstlane: the compiler then knows it is uniform,
+  // so LDS-DMA bases (M0) and buffer descriptors stay in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int wm = wave / TL::kWGN, wn = wave % TL::kWGN;
+  const int nchunk_r = p.r / kPer;
+  const int nk = (nchunk_r + KC - 1) / KC;
+
+  // DMA slab of a group-0 wave (group 1 computes the same things but never issues).
+  const int row0 = (wave & 3) * kRowsPerWave;
+  const T* base;
+  int64_t ld;
+  int valid;
+  int local0;
+  if (row0 < kBM) {
+    base = static_cast<const T*>(p.a) + (int64_t)tm * kBM * p.lda;
+    ld = p.lda;
+    valid = p.arows - tm * kBM;
+    local0 = row0;
+  } else {
+    const int r = row0 - kBM;
+    base = static_cast<const T*>(r < kBN ? p.b0 : p.b1) + (int64_t)tn * kBN * p.ldb;
+    ld = p.ldb;
+    valid = p.brows - tn * kBN;
+    local0 = r % kBN;
+  }
+  valid = valid < 0 ? 0 : (valid > (r_cap<kBM, kBN>()) ? r_cap<kBM, kBN>() : valid);
+  const __amdgpu_buffer_rsrc_t rsrc = uniform_rsrc(base, valid * ld * (int64_t)sizeof(T));
+  uint32_t voff_row[kDma];
+  int lch[kDma];
+#pragma unroll
+  for (int d = 0; d < kDma; ++d) {
+    const int rr = row0 + d * kRowsPerDma + lane / KC;
+    lch[d] = (lane % KC) ^ ((rr >> kSwzShift) & (KC - 1));
+    voff_row[d] = (uint32_t)((int64_t)(local0 + d * kRowsPerDma + lane / KC) * ld * (int64_t)sizeof(T));
+  }
+  auto issue = [&](int ks) {
+    char* dst = lds_bytes + (ks % S) * kStageBytes + row0 * kRowBytes;
+#pragma unroll
+    for (int d = 0; d < kDma; ++d) {
+      const int kc = ks * KC + lch[d];
+      const uint32_t off = kc < nchunk_r ? voff_row[d] + (uint32_t)(kc * kPer * (int)sizeof(T)) : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + d * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[NB][kTM][kTN];
+#pragma unroll
+  for (int w = 0; w < NB; ++w)
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[w][i][j][e] = 0.0f;
+
+  const int r32 = lane & 31;
+  const int half = lane >> 5;
+  auto frag = [&](const char* L, int row, int ch) -> u32x4 {
+    const int pc = ch ^ ((row >> kSwzShift) & (KC - 1));
+    return *reinterpret_cast<const u32x4*>(L + row * kRowBytes + pc * 16);
+  };
+
+  // Prologue.
+  if (grp == 0) {
+#pragma unroll
+    for (int s0 = 0; s0 < S - 1; ++s0)
+      if (s0 < nk) issue(s0);
+    if (S - 2 < nk) wait_vmcnt<(S - 2) * kDma>();  // step 0 has landed (later steps may fly)
+    else wait_vmcnt<0>();
+  }
+  barrier_no_fence();
+  if (grp == 1) barrier_no_fence();
+
+  u32x4 av[kKK][kTM], bv[kKK][NB][kTN];
+  for (int ks = 0; ks < nk; ++ks) {
+    // Memory phase.
+    const char* L = lds_bytes + (ks % S) * kStageBytes;
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
+      const int ch = 2 * kk + half;
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) av[kk][i] = frag(L, wm * kWM + i * 32 + r32, ch);
+#pragma unroll
+      for (int w = 0; w < NB; ++w)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) bv[kk][w][j] = frag(L, kBM + w * kBN + wn * kWN + j * 32 + r32, ch);
+    }
+    if (grp == 0 && ks + S - 1 < nk) issue(ks + S - 1);
+    barrier_no_fence();
+    // Compute phase.
+    if (kPrio) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk)
+#pragma unroll
+      for (int w = 0; w < NB; ++w)
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+          for (int j = 0; j < kTN; ++j) Mma<T>::run(acc[w][i][j], av[kk][i], bv[kk][w][j]);
+    if (kPrio) __builtin_amdgcn_s_setprio(0);
+    if (grp == 0 && ks + 1 < nk) {
+      if (ks + S - 1 < nk) wait_vmcnt<(S - 2) * kDma>();
+      else wait_vmcnt<0>();
+    }
+    barrier_no_fence();
+  }
+  if (grp == 0) barrier_no_fence();
+
+  store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
+}
+
+template <typename T, Epi E, int NB, class TL, int KC, int S, bool kPrio = false>
+hipError_t launch_pp(const GemmArgs& a, hipStream_t s) {
+  const int ntm = (a.m + TL::kBM - 1) / TL::kBM;
+  const int ntn = (a.n + TL::kBN - 1) / TL::kBN;
+  const int64_t tiles = (int64_t)ntm * ntn;
+  if (tiles == 0) return hipSuccess;
+  const size_t lds = (size_t)S * (TL::kBM + NB * TL::kBN) * KC * 16;
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [&] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pp_kernel<T, E, NB, TL, KC, S, kPrio>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  });
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gemm_pp_kernel<T, E, NB, TL, KC, S, kPrio>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, Epi E, int NB, class TL, int KC, int S, bool kPrio = false>
+hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
+  const int ntm = (a.m + TL::kBM - 1) / TL::kBM;
+  const int ntn = (a.n + TL::kBN - 1) / TL::kBN;
+  const int64_t tiles = (int64_t)ntm * ntn;
+  if (tiles == 0) return hipSuccess;
+  const size_t lds = (size_t)S * (TL::kBM + NB * TL::kBN) * KC * 16;
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [&] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<T, E, NB, TL, KC, S, kPrio>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  });
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gemm_dma_kernel<T, E, NB, TL, KC, S, kPrio>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, Epi E, int NB, class TL>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int ntm = (a.m + TL::kBM - 1) / TL::kBM;
   const int ntn = (a.n + TL::kBN - 1) / TL::kBN;
@@ -269,17 +709,17 @@ using TileSingle = Tile<256, 256, 4, 2>; // 8 waves, 64 x 128 per wave
 }  // namespace
 
 hipError_t launch_fwd_dual(Dt dt, const GemmArgs& a, hipStream_t s) {
-  return dt == Dt::kBF16 ? launch<bf16, Epi::kSwiGLU, 2, TileDual>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2, true>(a, s)
                          : launch<float, Epi::kSwiGLU, 2, TileDual>(a, s);
 }
 
 hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s) {
-  return dt == Dt::kBF16 ? launch<bf16, Epi::kDSwiGLU, 2, TileDual>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, true>(a, s)
                          : launch<float, Epi::kDSwiGLU, 2, TileDual>(a, s);
 }
 
 hipError_t launch_gemm_store(Dt dt, const GemmArgs& a, hipStream_t s) {
-  return dt == Dt::kBF16 ? launch<bf16, Epi::kStore, 1, TileSingle>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2>(a, s)
                          : launch<float, Epi::kStore, 1, TileSingle>(a, s);
 }
 
