@@ -377,22 +377,34 @@ void gemm_dma_kernel(GemmArgs p) {
   }
   valid = valid < 0 ? 0 : (valid > (r_cap<kBM, kBN>()) ? r_cap<kBM, kBN>() : valid);
   const __amdgpu_buffer_rsrc_t rsrc = uniform_rsrc(base, valid * ld * (int64_t)sizeof(T));
-  // Lane i of a DMA fills physical chunk (i % KC) of stage row rr = row0 +
-  // d * kRowsPerDma + i / KC; it fetches logical chunk (i % KC) ^ swz(rr).
-  uint32_t voff_row[kDma];
-  int lch[kDma];
+  // Lane i of DMA d fills physical chunk (i % KC) of stage row
+  // rr = row0 + d * kRowsPerDma + i / KC and fetches logical chunk
+  // (i % KC) ^ swz(rr).  row0 is a multiple of 64, so swz(rr) depends on d
+  // only through d's low bits: one chunk index per residue of d, and a row
+  // offset that is linear in d (kept in two registers per lane).
+  constexpr int kLchPeriod = (KC == 8) ? 2 : 1;
+  int lch[kLchPeriod];
 #pragma unroll
-  for (int d = 0; d < kDma; ++d) {
+  for (int d = 0; d < kLchPeriod; ++d) {
     const int rr = row0 + d * kRowsPerDma + lane / KC;
     lch[d] = (lane % KC) ^ ((rr >> kSwzShift) & (KC - 1));
-    voff_row[d] = (uint32_t)((int64_t)(local0 + d * kRowsPerDma + lane / KC) * ld * (int64_t)sizeof(T));
   }
+  const uint32_t voff0 = (uint32_t)((int64_t)(local0 + lane / KC) * ld * (int64_t)sizeof(T));
+  const uint32_t dstride = (uint32_t)((int64_t)kRowsPerDma * ld * (int64_t)sizeof(T));
   auto issue = [&](int ks) {
     char* dst = lds_bytes + (ks % S) * kStageBytes + row0 * kRowBytes;
+    uint32_t koff[kLchPeriod];
+    bool kin[kLchPeriod];
+#pragma unroll
+    for (int q = 0; q < kLchPeriod; ++q) {
+      const int kc = ks * KC + lch[q];
+      kin[q] = kc < nchunk_r;
+      koff[q] = voff0 + (uint32_t)(kc * kPer * (int)sizeof(T));
+    }
 #pragma unroll
     for (int d = 0; d < kDma; ++d) {
-      const int kc = ks * KC + lch[d];
-      const uint32_t off = kc < nchunk_r ? voff_row[d] + (uint32_t)(kc * kPer * (int)sizeof(T)) : 0x80000000u;
+      const int q = d % kLchPeriod;
+      const uint32_t off = kin[q] ? koff[q] + (uint32_t)d * dstride : 0x80000000u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + d * 1024), 16, off, 0, 0, 0);
     }
   };
@@ -709,12 +721,12 @@ using TileSingle = Tile<256, 256, 4, 2>; // 8 waves, 64 x 128 per wave
 }  // namespace
 
 hipError_t launch_fwd_dual(Dt dt, const GemmArgs& a, hipStream_t s) {
-  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2, true>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2>(a, s)
                          : launch<float, Epi::kSwiGLU, 2, TileDual>(a, s);
 }
 
 hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s) {
-  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, true>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2>(a, s)
                          : launch<float, Epi::kDSwiGLU, 2, TileDual>(a, s);
 }
 
