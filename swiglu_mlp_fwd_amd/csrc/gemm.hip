@@ -269,6 +269,147 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(GemmArgs p) {
   store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
 }
 
+// Epilogue through LDS for 16-bit outputs (used by the DMA kernel once its
+// LDS ring is idle).  The MFMA accumulator layout gives each lane one column
+// and runs of 4 rows, so direct stores are 2 bytes per lane.  Instead:
+//   - dSwiGLU only: the dh tile is staged in LDS with 16-byte coalesced
+//     loads and read back in accumulator layout with ds_read_b64_tr_b16
+//     (16 lanes addressing a 4-row x 16-column block receive one column each,
+//     4 rows deep -- exactly a lane's run of 4 accumulator rows);
+//   - results are written to LDS (2-byte writes, rows padded so the two
+//     half-waves hit different banks) and read back as 16-byte row chunks
+//     that are stored with coalesced 16-byte global stores.
+// Needs every output row pitch (and dh's) to be a multiple of 8 elements;
+// the caller uses store_tile otherwise.
+template <Epi E, class TL>
+struct EpiLds {
+  static constexpr int kCols = TL::kBN;                      // columns per output tile
+  static constexpr int kPitch = kCols * 2 + 32;              // bytes per staged row
+  static constexpr int kRegion = TL::kBM * kPitch;
+  static constexpr int kBytes = (E == Epi::kDSwiGLU ? 2 : 1) * kRegion;
+};
+
+typedef __attribute__((ext_vector_type(4))) short short4_t;
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+template <Epi E, int NB, class TL>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[NB][TL::kTM][TL::kTN],
+                                               int tm, int tn, int wm, int wn, int lane, int tid,
+                                               char* lds) {
+  constexpr int kBM = TL::kBM, kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
+  constexpr int kThreads = TL::kThreads;
+  constexpr int kCols = EpiLds<E, TL>::kCols;
+  constexpr int kPitch = EpiLds<E, TL>::kPitch;
+  constexpr int kRegion = EpiLds<E, TL>::kRegion;
+  constexpr int kCPR = kCols / 8;                           // 16-byte chunks per row
+  const int r32 = lane & 31, half = lane >> 5;
+  const int grow0 = tm * kBM, gcol0 = tn * kCols;
+
+  // Staged element (row, col) of region `reg`.
+  auto at = [&](int reg, int row, int col) -> char* { return lds + reg * kRegion + row * kPitch + col * 2; };
+
+  float dhv[kTM][kTN][16];
+  if constexpr (E == Epi::kDSwiGLU) {
+    const bf16* dh = static_cast<const bf16*>(p.dh);
+    for (int c = tid; c < kBM * kCPR; c += kThreads) {
+      const int r = c / kCPR, ch = c % kCPR;
+      const int grow = grow0 + r, gcol = gcol0 + ch * 8;
+      u32x4 v = {0, 0, 0, 0};
+      if (grow < p.m && gcol < p.ncols) {
+        const bf16* src = dh + (int64_t)grow * p.lddh + gcol;
+        if (gcol + 8 <= p.ncols) {
+          v = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          uint16_t tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+          for (int q = 0; q < p.ncols - gcol; ++q) tmp[q] = __builtin_bit_cast(uint16_t, src[q]);
+          v = __builtin_bit_cast(u32x4, tmp);
+        }
+      }
+      *reinterpret_cast<u32x4*>(at(0, r, ch * 8)) = v;
+    }
+    __syncthreads();
+    const int s16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
+#pragma unroll
+        for (int eq = 0; eq < 4; ++eq) {
+          const int row = wm * kWM + i * 32 + 8 * eq + 4 * half + (s16 >> 2);
+          const int col = wn * kWN + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+          const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_short4_t*)(lds_char_t*)(at(0, row, col)));
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dhv[i][j][4 * eq + q] = bits_f32((uint32_t)(uint16_t)v[q] << 16);
+        }
+    __syncthreads();
+  }
+
+  // Results into LDS.
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = wm * kWM + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+        const int col = wn * kWN + j * 32 + r32;
+        if constexpr (E == Epi::kSwiGLU) {
+          const float g = acc[0][i][j][e], u = acc[NB - 1][i][j][e];
+          *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(silu_f32(g) * u);
+        } else if constexpr (E == Epi::kDSwiGLU) {
+          const float g = acc[0][i][j][e], u = acc[NB - 1][i][j][e];
+          const float dh = dhv[i][j][e];
+          float sg, sl;
+          sigmoid_silu_f32(g, sg, sl);
+          *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(dh * u * (sg * (1.0f + g * (1.0f - sg))));
+          *reinterpret_cast<bf16*>(at(1, row, col)) = to_bf16(dh * sl);
+        } else {
+          *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(acc[0][i][j][e]);
+        }
+      }
+  __syncthreads();
+
+  // 16-byte chunks out.
+  auto put = [&](bf16* dst, const u32x4& v, int nvalid) {
+    if (nvalid >= 8) {
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      uint16_t tmp[8];
+      *reinterpret_cast<u32x4*>(tmp) = v;
+      for (int q = 0; q < nvalid; ++q) reinterpret_cast<uint16_t*>(dst)[q] = tmp[q];
+    }
+  };
+  for (int c = tid; c < kBM * kCPR; c += kThreads) {
+    const int r = c / kCPR, ch = c % kCPR;
+    const int grow = grow0 + r, gcol = gcol0 + ch * 8;
+    if (grow >= p.m || gcol >= p.n) continue;
+    if constexpr (E == Epi::kSwiGLU) {
+      if (gcol >= p.ncols) continue;
+      put(static_cast<bf16*>(p.out0) + (int64_t)grow * p.ldo + gcol,
+          *reinterpret_cast<const u32x4*>(at(0, r, ch * 8)), min(8, p.ncols - gcol));
+    } else if constexpr (E == Epi::kDSwiGLU) {
+      bf16* dst = static_cast<bf16*>(p.out0) + (int64_t)grow * p.ldo + gcol;
+      const int nv = min(8, p.n - gcol);
+      put(dst, *reinterpret_cast<const u32x4*>(at(0, r, ch * 8)), nv);
+      put(dst + p.du_off, *reinterpret_cast<const u32x4*>(at(1, r, ch * 8)), nv);
+    } else {
+      if (gcol >= p.ncols) continue;
+      bf16* dst;
+      if (grow < p.split) {
+        if (grow >= p.lim0) continue;
+        dst = static_cast<bf16*>(p.out0) + (int64_t)grow * p.ldo + gcol;
+      } else {
+        if (grow - p.split >= p.lim1) continue;
+        dst = static_cast<bf16*>(p.out1) + (int64_t)(grow - p.split) * p.ldo + gcol;
+      }
+      put(dst, *reinterpret_cast<const u32x4*>(at(0, r, ch * 8)), min(8, p.ncols - gcol));
+    }
+  }
+}
+
 // s_waitcnt that only bounds the vector-memory counter (gfx9 encoding:
 // vmcnt in bits [3:0] and [15:14]; expcnt [6:4] and lgkmcnt [11:8] left at
 // their maxima).  The LDS DMA loads below count as vector-memory operations.
@@ -495,187 +636,16 @@ void gemm_dma_kernel(GemmArgs p) {
     }
   }
 
+  if constexpr (sizeof(T) == 2) {
+    const bool vec = (p.ldo % 8 == 0) && (E != Epi::kDSwiGLU || (p.lddh % 8 == 0 && p.du_off % 8 == 0));
+    if (vec) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // own LDS reads done
+      barrier_no_fence();                   // every wave is done with the ring
+      store_tile_lds<E, NB, TL>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes);
+      return;
+    }
+  }
   store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
-}
-
-// Third GEMM kernel ("ping-pong"), for 8-wave tiles: the waves form two
-// groups of four, one wave of each group on every SIMD (wave w runs on SIMD
-// w % 4).  The groups alternate between a memory phase (read every operand
-// fragment of one k-step from LDS into registers; group 0 also issues the
-// LDS DMA of a later step) and a compute phase (only MFMAs, from registers),
-// offset by one barrier, so each SIMD's matrix core is fed by one group
-// while the other group waits on memory:
-//
-//   group 0: P B M0 B C0 B M1 B C1 B ... B C(n-1) B T
-//   group 1:   B    B M0 B C0 B M1 B ... B C(n-1) B
-//
-// (P: prologue DMA + wait, B: barrier, T: group 0's trailing barrier; both
-// groups execute 2 n + 2 barriers on every path.)  Group 0 moves all the
-// DMA; before the barrier that ends its compute phase of step t it waits
-// for its DMA of step t + 1, which every later reader of step t + 1 is
-// behind.  The DMA of step t + S - 1 is issued in group 0's memory phase of
-// step t into the ring slot of step t - 1, whose last reader (group 1's
-// memory phase of step t - 1) ended at the preceding barrier.
-template <typename T, Epi E, int NB, class TL, int KC, int S, bool kPrio>
-__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_pp_kernel(GemmArgs p) {
-  constexpr int kBM = TL::kBM, kBN = TL::kBN, kThreads = TL::kThreads;
-  constexpr int kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
-  constexpr int kRows = kBM + NB * kBN;
-  constexpr int kRowBytes = KC * 16;
-  constexpr int kStageBytes = kRows * kRowBytes;
-  constexpr int kRowsPerDma = 64 / KC;
-  constexpr int kRowsPerWave = kRows / 4;               // group 0's four waves move the stage
-  constexpr int kDma = kRowsPerWave / kRowsPerDma;
-  constexpr int kSwzShift = (KC == 8) ? 1 : 2;
-  constexpr int kPer = Mma<T>::kPerChunk;
-  constexpr int kKK = KC / 2;
-  static_assert(kThreads == 512, "ping-pong needs 8 waves");
-  static_assert(KC == 4 || KC == 8, "chunks per row");
-  static_assert(S >= 2, "stages");
-  static_assert(kBM % kRowsPerWave == 0 && kBN % kRowsPerWave == 0, "a wave's slab lies in one operand");
-  extern __shared__ u32x4 lds[];
-  char* const lds_bytes = reinterpret_cast<char*>(lds);
-
-  const int ntm = (p.m + kBM - 1) / kBM;
-  const int ntn = (p.n + kBN - 1) / kBN;
-  const int tile = xcd_remap(blockIdx.x, ntm * ntn);
-  const int group = kGroupM * ntn;
-  const int first_m = (tile / group) * kGroupM;
-  const int gm = min(ntm - first_m, kGroupM);
-  const int tm = first_m + (tile % group) % gm;
-  const int tn = (tile % group) / gm;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  // Wave index through readfirstlane: the compiler then knows it is uniform,
-  // so LDS-DMA bases (M0) and buffer descriptors stay in scalar registers.
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int wm = wave / TL::kWGN, wn = wave % TL::kWGN;
-  const int nchunk_r = p.r / kPer;
-  const int nk = (nchunk_r + KC - 1) / KC;
-
-  // DMA slab of a group-0 wave (group 1 computes the same things but never issues).
-  const int row0 = (wave & 3) * kRowsPerWave;
-  const T* base;
-  int64_t ld;
-  int valid;
-  int local0;
-  if (row0 < kBM) {
-    base = static_cast<const T*>(p.a) + (int64_t)tm * kBM * p.lda;
-    ld = p.lda;
-    valid = p.arows - tm * kBM;
-    local0 = row0;
-  } else {
-    const int r = row0 - kBM;
-    base = static_cast<const T*>(r < kBN ? p.b0 : p.b1) + (int64_t)tn * kBN * p.ldb;
-    ld = p.ldb;
-    valid = p.brows - tn * kBN;
-    local0 = r % kBN;
-  }
-  valid = valid < 0 ? 0 : (valid > (r_cap<kBM, kBN>()) ? r_cap<kBM, kBN>() : valid);
-  const __amdgpu_buffer_rsrc_t rsrc = uniform_rsrc(base, valid * ld * (int64_t)sizeof(T));
-  uint32_t voff_row[kDma];
-  int lch[kDma];
-#pragma unroll
-  for (int d = 0; d < kDma; ++d) {
-    const int rr = row0 + d * kRowsPerDma + lane / KC;
-    lch[d] = (lane % KC) ^ ((rr >> kSwzShift) & (KC - 1));
-    voff_row[d] = (uint32_t)((int64_t)(local0 + d * kRowsPerDma + lane / KC) * ld * (int64_t)sizeof(T));
-  }
-  auto issue = [&](int ks) {
-    char* dst = lds_bytes + (ks % S) * kStageBytes + row0 * kRowBytes;
-#pragma unroll
-    for (int d = 0; d < kDma; ++d) {
-      const int kc = ks * KC + lch[d];
-      const uint32_t off = kc < nchunk_r ? voff_row[d] + (uint32_t)(kc * kPer * (int)sizeof(T)) : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + d * 1024), 16, off, 0, 0, 0);
-    }
-  };
-
-  f32x16 acc[NB][kTM][kTN];
-#pragma unroll
-  for (int w = 0; w < NB; ++w)
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kTN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[w][i][j][e] = 0.0f;
-
-  const int r32 = lane & 31;
-  const int half = lane >> 5;
-  auto frag = [&](const char* L, int row, int ch) -> u32x4 {
-    const int pc = ch ^ ((row >> kSwzShift) & (KC - 1));
-    return *reinterpret_cast<const u32x4*>(L + row * kRowBytes + pc * 16);
-  };
-
-  // Prologue.
-  if (grp == 0) {
-#pragma unroll
-    for (int s0 = 0; s0 < S - 1; ++s0)
-      if (s0 < nk) issue(s0);
-    if (S - 2 < nk) wait_vmcnt<(S - 2) * kDma>();  // step 0 has landed (later steps may fly)
-    else wait_vmcnt<0>();
-  }
-  barrier_no_fence();
-  if (grp == 1) barrier_no_fence();
-
-  u32x4 av[kKK][kTM], bv[kKK][NB][kTN];
-  for (int ks = 0; ks < nk; ++ks) {
-    // Memory phase.
-    const char* L = lds_bytes + (ks % S) * kStageBytes;
-#pragma unroll
-    for (int kk = 0; kk < kKK; ++kk) {
-      const int ch = 2 * kk + half;
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) av[kk][i] = frag(L, wm * kWM + i * 32 + r32, ch);
-#pragma unroll
-      for (int w = 0; w < NB; ++w)
-#pragma unroll
-        for (int j = 0; j < kTN; ++j) bv[kk][w][j] = frag(L, kBM + w * kBN + wn * kWN + j * 32 + r32, ch);
-    }
-    if (grp == 0 && ks + S - 1 < nk) issue(ks + S - 1);
-    barrier_no_fence();
-    // Compute phase.
-    if (kPrio) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kk = 0; kk < kKK; ++kk)
-#pragma unroll
-      for (int w = 0; w < NB; ++w)
-#pragma unroll
-        for (int i = 0; i < kTM; ++i)
-#pragma unroll
-          for (int j = 0; j < kTN; ++j) Mma<T>::run(acc[w][i][j], av[kk][i], bv[kk][w][j]);
-    if (kPrio) __builtin_amdgcn_s_setprio(0);
-    if (grp == 0 && ks + 1 < nk) {
-      if (ks + S - 1 < nk) wait_vmcnt<(S - 2) * kDma>();
-      else wait_vmcnt<0>();
-    }
-    barrier_no_fence();
-  }
-  if (grp == 0) barrier_no_fence();
-
-  store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
-}
-
-template <typename T, Epi E, int NB, class TL, int KC, int S, bool kPrio = false>
-hipError_t launch_pp(const GemmArgs& a, hipStream_t s) {
-  const int ntm = (a.m + TL::kBM - 1) / TL::kBM;
-  const int ntn = (a.n + TL::kBN - 1) / TL::kBN;
-  const int64_t tiles = (int64_t)ntm * ntn;
-  if (tiles == 0) return hipSuccess;
-  const size_t lds = (size_t)S * (TL::kBM + NB * TL::kBN) * KC * 16;
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [&] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pp_kernel<T, E, NB, TL, KC, S, kPrio>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  });
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_pp_kernel<T, E, NB, TL, KC, S, kPrio>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
-  return hipGetLastError();
 }
 
 template <typename T, Epi E, int NB, class TL, int KC, int S, bool kPrio = false>
@@ -684,7 +654,9 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   const int ntn = (a.n + TL::kBN - 1) / TL::kBN;
   const int64_t tiles = (int64_t)ntm * ntn;
   if (tiles == 0) return hipSuccess;
-  const size_t lds = (size_t)S * (TL::kBM + NB * TL::kBN) * KC * 16;
+  const size_t ring = (size_t)S * (TL::kBM + NB * TL::kBN) * KC * 16;
+  const size_t epi = sizeof(T) == 2 ? (size_t)EpiLds<E, TL>::kBytes : 0;
+  const size_t lds = ring > epi ? ring : epi;
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [&] {
