@@ -446,6 +446,17 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
+// Loads the kernel arguments the epilogue uses into scalar registers before
+// the main loop.  Left to itself the compiler issues some of these scalar
+// loads just before the loop; a scalar load still in flight there shares the
+// LDS wait counter and completes out of order, which forces every LDS wait in
+// the loop down to zero and so exposes the latency of every fragment read.
+__device__ __forceinline__ void pin_epilogue_args(const GemmArgs& p) {
+  asm volatile("" ::"s"(p.out0), "s"(p.out1), "s"(p.ldo), "s"(p.dh), "s"(p.lddh));
+  asm volatile("" ::"s"(p.split), "s"(p.lim0), "s"(p.lim1), "s"(p.ncols), "s"(p.du_off), "s"(p.m),
+               "s"(p.n));
+}
+
 // Second GEMM kernel, used for bf16: the operand tiles go from global memory
 // straight into LDS (buffer_load_dwordx4 ... lds, the gfx950 16-byte LDS
 // DMA), through an S-stage ring of KC-chunk k-steps, with no register
@@ -497,6 +508,7 @@ void gemm_dma_kernel(GemmArgs p) {
   const int wm = wave / TL::kWGN, wn = wave % TL::kWGN;
   const int nchunk_r = p.r / kPer;
   const int nk = (nchunk_r + KC - 1) / KC;
+  pin_epilogue_args(p);
 
   // This wave's DMA slab and its operand.
   const int row0 = wave * kRowsPerWave;
@@ -618,13 +630,18 @@ void gemm_dma_kernel(GemmArgs p) {
     barrier_no_fence();
     read_frags(0, lds_bytes, 0);
   }
-  for (int ks = 0; ks < nk; ++ks) {
+  // One k-step; `more` (a constant after inlining) says whether a next step
+  // follows.  The last step is peeled off so the steady-state loop has no
+  // branch around the next step's fragment reads: at such a join the
+  // compiler's LDS wait counts would have to cover both paths, and the last
+  // MFMAs of every step would wait for the next step's reads.
+  auto kstep = [&](int ks, bool more) {
     const char* L = lds_bytes + (ks % S) * kStageBytes;
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk) {
       if (kk + 1 < kKK) {
         read_frags((kk + 1) & 1, L, kk + 1);
-      } else if (ks + 1 < nk) {
+      } else if (more) {
         wait_dma(min(S - 2, nk - 2 - ks));   // step ks + 1 has landed
         barrier_no_fence();                  // and every wave has read step ks
         if (ks + S < nk) issue(ks + S);      // refills the slot of step ks
@@ -634,7 +651,9 @@ void gemm_dma_kernel(GemmArgs p) {
       mfmas(kk & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  for (int ks = 0; ks + 1 < nk; ++ks) kstep(ks, true);
+  if (nk > 0) kstep(nk - 1, false);
 
   if constexpr (sizeof(T) == 2) {
     const bool vec = (p.ldo % 8 == 0) && (E != Epi::kDSwiGLU || (p.lddh % 8 == 0 && p.du_off % 8 == 0));
