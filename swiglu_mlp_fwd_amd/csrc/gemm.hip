@@ -471,7 +471,7 @@ __device__ __forceinline__ void pin_epilogue_args(const GemmArgs& p) {
 // step whose ring slot is refilled next), issue the DMA of step ks + S - 1,
 // then the MFMAs, with the operand fragments of the next half-step read from
 // LDS while the current ones are in the matrix cores.
-template <typename T, Epi E, int NB, class TL, int KC, int S, bool kPrio>
+template <typename T, Epi E, int NB, class TL, int KC, int S, bool kIL>
 __global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(TL::kThreads / 256, TL::kThreads / 256)))
 void gemm_dma_kernel(GemmArgs p) {
   constexpr int kBM = TL::kBM, kBN = TL::kBN, kThreads = TL::kThreads;
@@ -591,14 +591,12 @@ void gemm_dma_kernel(GemmArgs p) {
       for (int j = 0; j < kTN; ++j) bv[buf][w][j] = frag(L, kBM + w * kBN + wn * kWN + j * 32 + r32, ch);
   };
   auto mfmas = [&](int buf) {
-    if (kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int w = 0; w < NB; ++w)
 #pragma unroll
       for (int i = 0; i < kTM; ++i)
 #pragma unroll
         for (int j = 0; j < kTN; ++j) Mma<T>::run(acc[w][i][j], av[buf][i], bv[buf][w][j]);
-    if (kPrio) __builtin_amdgcn_s_setprio(0);
   };
   // Wait until at most `later` of this wave's DMA steps are still in flight
   // (DMA completes in issue order, so every earlier step has landed), and
@@ -642,10 +640,34 @@ void gemm_dma_kernel(GemmArgs p) {
       if (kk + 1 < kKK) {
         read_frags((kk + 1) & 1, L, kk + 1);
       } else if (more) {
-        wait_dma(min(S - 2, nk - 2 - ks));   // step ks + 1 has landed
-        barrier_no_fence();                  // and every wave has read step ks
-        if (ks + S < nk) issue(ks + S);      // refills the slot of step ks
-        read_frags(0, lds_bytes + ((ks + 1) % S) * kStageBytes, 0);
+        if constexpr (kIL) {
+          // The refill is issued for every step (steps past the end read
+          // nothing: their offsets are out of range and land zeros in a dead
+          // slot), so the wait is always for the newest step in flight.
+          wait_dma(S - 2);
+          barrier_no_fence();
+          read_frags(0, lds_bytes + ((ks + 1) % S) * kStageBytes, 0);
+          // The DMA instructions of the refill go one by one between the
+          // MFMAs of this half-step instead of stalling the matrix core.
+          __builtin_amdgcn_sched_barrier(0);
+          issue(ks + S);
+          mfmas(kk & 1);
+          constexpr int kMf = NB * kTM * kTN;
+          constexpr int kPerDma = kMf / kDma > 0 ? kMf / kDma : 1;
+#pragma unroll
+          for (int t = 0; t < kDma; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, kPerDma, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          continue;
+        } else {
+          wait_dma(min(S - 2, nk - 2 - ks));   // step ks + 1 has landed
+          barrier_no_fence();                  // and every wave has read step ks
+          if (ks + S < nk) issue(ks + S);      // refills the slot of step ks
+          read_frags(0, lds_bytes + ((ks + 1) % S) * kStageBytes, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       mfmas(kk & 1);
@@ -658,6 +680,7 @@ void gemm_dma_kernel(GemmArgs p) {
   if constexpr (sizeof(T) == 2) {
     const bool vec = (p.ldo % 8 == 0) && (E != Epi::kDSwiGLU || (p.lddh % 8 == 0 && p.du_off % 8 == 0));
     if (vec) {
+      wait_vmcnt<0>();                      // no DMA still landing in the ring
       __builtin_amdgcn_s_waitcnt(0xC07F);   // own LDS reads done
       barrier_no_fence();                   // every wave is done with the ring
       store_tile_lds<E, NB, TL>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes);
@@ -667,7 +690,7 @@ void gemm_dma_kernel(GemmArgs p) {
   store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
 }
 
-template <typename T, Epi E, int NB, class TL, int KC, int S, bool kPrio = false>
+template <typename T, Epi E, int NB, class TL, int KC, int S, bool kIL = false>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   const int ntm = (a.m + TL::kBM - 1) / TL::kBM;
   const int ntn = (a.n + TL::kBN - 1) / TL::kBN;
@@ -679,11 +702,11 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [&] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<T, E, NB, TL, KC, S, kPrio>),
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<T, E, NB, TL, KC, S, kIL>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   });
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_dma_kernel<T, E, NB, TL, KC, S, kPrio>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
+  hipLaunchKernelGGL((gemm_dma_kernel<T, E, NB, TL, KC, S, kIL>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -712,17 +735,17 @@ using TileSingle = Tile<256, 256, 4, 2>; // 8 waves, 64 x 128 per wave
 }  // namespace
 
 hipError_t launch_fwd_dual(Dt dt, const GemmArgs& a, hipStream_t s) {
-  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2, true>(a, s)
                          : launch<float, Epi::kSwiGLU, 2, TileDual>(a, s);
 }
 
 hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s) {
-  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, true>(a, s)
                          : launch<float, Epi::kDSwiGLU, 2, TileDual>(a, s);
 }
 
 hipError_t launch_gemm_store(Dt dt, const GemmArgs& a, hipStream_t s) {
-  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, true>(a, s)
                          : launch<float, Epi::kStore, 1, TileSingle>(a, s);
 }
 
