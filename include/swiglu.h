@@ -64,15 +64,17 @@ enum swiglu_dtype { SWIGLU_F32 = 0, SWIGLU_BF16 = 1 };
  *
  *   x  [M, K], wg [N, K], wu [N, K]  (inputs, dtype)
  *   h  [M, N]                        (output, dtype)
- * Layout rule: K % 8 == 0 for bf16 and K % 4 == 0 for fp32 (16-byte rows).
+ * Layout rule: K % 8 == 0 for bf16 and K % 4 == 0 for fp32 (16-byte rows);
+ * bf16 also needs K <= 2^22 - 64 (else SWIGLU_ERR_UNSUPPORTED).
  * K == 0 gives h = 0. */
 int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K,
                const void* x, const void* wg, const void* wu, void* h,
                void* stream);
 
 /* Bytes of device workspace swiglu_bwd needs for these sizes (0 on invalid
- * sizes).  The workspace holds dg and du, their transposes, x^T and the
- * transposed weight pair. */
+ * sizes).  bf16: the workspace holds dg and du, 2 * M * round_up(N, 64)
+ * elements.  fp32: dg and du, their transposes, x^T and the transposed
+ * weight pair. */
 size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K);
 
 /* Backward of the fused stage ("Fused SwiGLU/dSwiGLU", Liger-Kernel issue
@@ -82,16 +84,17 @@ size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K);
  *   dx = dg Wg + du Wu,   dwg = dg^T x,   dwu = du^T x
  * dg and du are rounded to `dtype` once (they are matrix-core operands);
  * every contraction accumulates in fp32 and rounds its output once.
- * Five kernels run in order on `stream`: the recompute dual GEMM with the
- * dSwiGLU epilogue, transposes of x, the weights and [dg | du], then the dX
- * GEMM and the stacked dW GEMM.
+ * Kernels run in order on `stream`: the recompute dual GEMM with the
+ * dSwiGLU epilogue, then the dX GEMM and the stacked dW GEMM; bf16 reads
+ * the weights, x and [dg | du] in place, fp32 first transposes them.
  *
  *   x [M, K], wg/wu [N, K], dh [M, N]         (inputs, dtype)
  *   dx [M, K], dwg [N, K], dwu [N, K]         (outputs, dtype; overwritten)
  *   workspace: device buffer of at least swiglu_bwd_workspace_bytes(...)
  *              bytes, 256-byte aligned; contents are scratch.
  * Layout rule: K % 8 == 0 for bf16, K % 4 == 0 for fp32; M and N are free
- * (the transposed operands are zero-padded to 16-byte rows). */
+ * (padded operands are zero-filled).  bf16 also needs K and
+ * 2 * round_up(N, 64) at most 2^22 - 64 (else SWIGLU_ERR_UNSUPPORTED). */
 int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K,
                const void* x, const void* wg, const void* wu, const void* dh,
                void* dx, void* dwg, void* dwu,

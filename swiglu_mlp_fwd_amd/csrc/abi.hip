@@ -70,9 +70,6 @@ int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const 
   const swg::BwdLayout L = swg::bwd_layout(dtype, M, N, K);
   char* ws = static_cast<char*>(workspace);
   void* D = ws + L.off_d;
-  void* DT = ws + L.off_dt;
-  void* XT = ws + L.off_xt;
-  void* WT = ws + L.off_wt;
   const int Mi = (int)M, Ni = (int)N, Ki = (int)K, Mp = (int)L.Mp, Np = (int)L.Np;
   hipError_t e;
 
@@ -83,6 +80,28 @@ int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const 
   b1.out0 = D; b1.ldo = 2 * (int64_t)Np; b1.ncols = Ni;
   b1.dh = dh; b1.lddh = N; b1.du_off = Np;
   if ((e = swg::launch_bwd_dswiglu(dt, b1, s)) != hipSuccess) return hip_status(e);
+
+  if (dt == swg::Dt::kBF16) {
+    // 2. dX [M, K] = D [M, 2 Np] . [Wg; Wu] [2 Np, K]: the weights are read
+    //    in place as a reduction-major operand (reduction rows < Np from Wg,
+    //    the rest from Wu; rows N..Np-1 of each read as zero).
+    swg::GemmArgs b2{};
+    b2.a = D; b2.b0 = wg; b2.b1 = wu; b2.lda = 2 * (int64_t)Np; b2.ldb = K;
+    b2.arows = Mi; b2.brows = Ni; b2.m = Mi; b2.n = Ki; b2.r = 2 * Np; b2.rsplit = Np;
+    b2.out0 = dx; b2.ldo = K; b2.split = Mi; b2.lim0 = Mi; b2.lim1 = 0; b2.ncols = Ki;
+    if ((e = swg::launch_gemm_store_t(false, true, b2, s)) != hipSuccess) return hip_status(e);
+    // 3. [dWg; dWu] [2 Np, K] = D^T . x: both operands reduction-major
+    //    (reduction over the M rows of D and x).
+    swg::GemmArgs b3{};
+    b3.a = D; b3.b0 = x; b3.lda = 2 * (int64_t)Np; b3.ldb = K;
+    b3.arows = Mi; b3.brows = Mi; b3.m = 2 * Np; b3.n = Ki; b3.r = Mi; b3.rsplit = 0x7fffffc0;
+    b3.out0 = dwg; b3.out1 = dwu; b3.ldo = K; b3.split = Np; b3.lim0 = Ni; b3.lim1 = Ni;
+    b3.ncols = Ki;
+    return hip_status(swg::launch_gemm_store_t(true, true, b3, s));
+  }
+  void* DT = ws + L.off_dt;
+  void* XT = ws + L.off_xt;
+  void* WT = ws + L.off_wt;
 
   // 2. Transposes: x -> XT [K, Mp]; Wg, Wu -> WT [K, 2 Np]; D -> DT [2 Np, Mp].
   if ((e = swg::launch_transpose(dt, x, K, Mi, Ki, XT, Mp, 0, Mp, s)) != hipSuccess) return hip_status(e);

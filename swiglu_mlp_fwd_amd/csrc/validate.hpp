@@ -39,8 +39,11 @@ inline int check_ptr(const void* p) {
   return SWIGLU_OK;
 }
 
-// Backward workspace: four regions, each starting on a 256-byte boundary.
+// Backward workspace, regions starting on 256-byte boundaries.
 //   D   [M, 2 Np]     dg in columns [0, Np), du in [Np, 2 Np), zero padded
+// bf16 needs only D, with Np = round_up(N, 64): its matrix-core GEMMs read
+// D, x and the weights in place (reduction-major tiles where needed), and a
+// 64-row reduction step never straddles the dg / du halves.  fp32 also has
 //   DT  [2 Np, Mp]    transpose of D, zero padded along M
 //   XT  [K, Mp]       transpose of x, zero padded along M
 //   WT  [K, 2 Np]     [Wg; Wu] transposed, zero padded along N
@@ -53,17 +56,21 @@ struct BwdLayout {
 inline BwdLayout bwd_layout(int dtype, int64_t M, int64_t N, int64_t K) {
   BwdLayout L;
   const size_t es = (size_t)elem_size(dtype);
+  const bool bf16 = dtype == SWIGLU_BF16;
   L.Mp = round_up(M, 8);
-  L.Np = round_up(N, 8);
+  L.Np = round_up(N, bf16 ? 64 : 8);
   auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
   size_t off = 0;
   L.off_d = off;  off += a256((size_t)M * 2 * L.Np * es);
-  L.off_dt = off; off += a256((size_t)2 * L.Np * L.Mp * es);
-  L.off_xt = off; off += a256((size_t)K * L.Mp * es);
-  L.off_wt = off; off += a256((size_t)K * 2 * L.Np * es);
+  L.off_dt = off; if (!bf16) off += a256((size_t)2 * L.Np * L.Mp * es);
+  L.off_xt = off; if (!bf16) off += a256((size_t)K * L.Mp * es);
+  L.off_wt = off; if (!bf16) off += a256((size_t)K * 2 * L.Np * es);
   L.total = off;
   return L;
 }
+
+// The bf16 kernels address a 256-row operand tile with 32-bit byte offsets.
+constexpr int64_t kMaxLdBf16 = (int64_t(1) << 22) - 64;
 
 inline int validate_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
                         const void* wu, const void* h) {
@@ -72,6 +79,7 @@ inline int validate_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* 
   if ((st = check_dims(M, N, K))) return st;
   if (K % chunk_elems(dtype) != 0) return SWIGLU_ERR_SHAPE;
   if (!tiles_fit(M, N)) return SWIGLU_ERR_UNSUPPORTED;
+  if (dtype == SWIGLU_BF16 && K > kMaxLdBf16) return SWIGLU_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return SWIGLU_OK;
   if ((st = check_ptr(h))) return st;
   if (K > 0) {
@@ -91,6 +99,7 @@ inline int validate_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* 
   if (K % chunk_elems(dtype) != 0) return SWIGLU_ERR_SHAPE;
   const BwdLayout L = bwd_layout(dtype, M, N, K);
   if (!tiles_fit(M, L.Np) || !tiles_fit(M, K) || !tiles_fit(2 * L.Np, K)) return SWIGLU_ERR_UNSUPPORTED;
+  if (dtype == SWIGLU_BF16 && (K > kMaxLdBf16 || 2 * L.Np > kMaxLdBf16)) return SWIGLU_ERR_UNSUPPORTED;
   if (K == 0) return SWIGLU_OK;                       // every output is empty
   if (M > 0 && (st = check_ptr(dx))) return st;
   if (N > 0 && (st = check_ptr(dwg))) return st;

@@ -92,14 +92,25 @@ def test_bwd_validation(L):
 
 
 def test_workspace_layout_formula(L):
-    # D [M, 2Np] + DT [2Np, Mp] + XT [K, Mp] + WT [K, 2Np], each 256-byte aligned.
+    # fp32: D [M, 2Np] + DT [2Np, Mp] + XT [K, Mp] + WT [K, 2Np], each 256-byte
+    # aligned, Np = round_up(N, 8).  bf16: D alone, Np = round_up(N, 64).
     def a256(v):
         return (v + 255) // 256 * 256
-    for (dt, es) in ((0, 4), (1, 2)):
-        for (M, N, K) in ((100, 60, 64), (8192, 14336, 4096), (1, 1, 8)):
-            Mp, Np = -(-M // 8) * 8, -(-N // 8) * 8
-            want = a256(M * 2 * Np * es) + a256(2 * Np * Mp * es) + a256(K * Mp * es) + a256(K * 2 * Np * es)
-            assert L.swiglu_bwd_workspace_bytes(dt, M, N, K) == want
+    for (M, N, K) in ((100, 60, 64), (8192, 14336, 4096), (1, 1, 8)):
+        Mp, Np = -(-M // 8) * 8, -(-N // 8) * 8
+        want = a256(M * 2 * Np * 4) + a256(2 * Np * Mp * 4) + a256(K * Mp * 4) + a256(K * 2 * Np * 4)
+        assert L.swiglu_bwd_workspace_bytes(0, M, N, K) == want
+        Np = -(-N // 64) * 64
+        assert L.swiglu_bwd_workspace_bytes(1, M, N, K) == a256(M * 2 * Np * 2)
+
+
+def test_bf16_leading_dimension_limit(L):
+    EUNSUP = 7
+    lim = (1 << 22) - 64
+    assert L.swiglu_fwd(1, 4, 4, lim + 64, A, A, A, A, None) == EUNSUP
+    assert L.swiglu_bwd_workspace_bytes(1, 4, lim // 2, 8) > 0
+    need = L.swiglu_bwd_workspace_bytes(1, 4, lim // 2 + 64, 8)
+    assert L.swiglu_bwd(1, 4, lim // 2 + 64, 8, A, A, A, A, A, A, A, A, need, None) == EUNSUP
 
 
 def test_gemv_validation(L):

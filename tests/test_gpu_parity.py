@@ -182,7 +182,8 @@ def test_bwd_tiny_fp32():
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("shape", [(300, 520, 264), (1, 1, 8), (33, 17, 40), (129, 300, 136)])
+@pytest.mark.parametrize("shape", [(300, 520, 264), (1, 1, 8), (33, 17, 40), (129, 300, 136),
+                                   (520, 700, 328), (257, 640, 520)])
 def test_bwd_ragged(dt, shape):
     M, N, K = shape
     if dt == "bf16":
