@@ -33,6 +33,10 @@
 // tile and the 16-byte chunk (2 kk + (l >> 5)) of the k-step; the same chunk
 // mapping for A and B makes the products pair up correctly whatever order
 // the matrix core uses within a chunk.
+// Reduction-major operands (stored [r, rows], as x, the weights and [dg|du]
+// are for the backward's dW and dX products) are staged as they lie in
+// memory and their fragments are gathered with transposing LDS reads, so
+// the backward never materialises a transposed copy.
 #include <mutex>
 
 #include "common.hpp"
@@ -876,6 +880,9 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 
 using TileDual = Tile<256, 128, 4, 2>;   // 8 waves, 64 x 64 per wave per weight
 using TileSingle = Tile<256, 256, 4, 2>; // 8 waves, 64 x 128 per wave
+// 8 waves, 128 x 64 per wave: with a reduction-major B operand (two
+// transposing reads per fragment) the B side gets the fewer fragments.
+using TileSingleT = Tile<256, 256, 2, 4>;
 
 }  // namespace
 
@@ -890,8 +897,8 @@ hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm_store_t(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
-  if (ta && tb) return launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 1, true, true>(a, s);
-  if (tb) return launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 1, false, true>(a, s);
+  if (ta && tb) return launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 2, true, true>(a, s);
+  if (tb) return launch_dma<bf16, Epi::kStore, 1, TileSingleT, 8, 2, 2, false, true>(a, s);
   if (ta) return hipErrorInvalidValue;
   return launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 1>(a, s);
 }
