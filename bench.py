@@ -54,9 +54,59 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target host time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the decode / act_quant / fp32 legs")
-    p.add_argument("--only", choices=["step", "fwd", "decode", "act_quant", "fp32"], default=None,
-                   help="profiling aid: run one leg only (no JSON contract)")
+    p.add_argument("--only", choices=["step", "fwd", "decode", "act_quant", "fp32", "traffic"], default=None,
+                   help="profiling aid: run one leg only (no JSON contract); 'traffic' runs the headline "
+                        "forward and a 1 GiB copy (the counter calibration) for the --pmc runs")
+    p.add_argument("--digest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                   help="read the counter_collection.csv files of two rocprofv3 --pmc runs of "
+                        "'--only traffic' (FETCH_SIZE, then WRITE_SIZE) and write profiles/traffic.json")
     return p.parse_args()
+
+
+COPY_BYTES = 1 << 30            # calibration copy: reads and writes this many bytes per launch
+FWD_KERNEL_TAG = "gemm_dma_kernelIDF16bLNS0_3EpiE0E"   # mangled-name fragment of the bf16 fused forward
+COPY_KERNEL_TAG = "copy"
+
+
+def digest_traffic(fetch_csv: str, write_csv: str) -> None:
+    """HBM bytes per launch of the fused forward from two --pmc runs: the
+    FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the forward kernel,
+    each scaled by (known bytes / counter reading) of a plain 1 GiB copy
+    measured in the same run."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            tag = "fwd" if FWD_KERNEL_TAG in name else ("copy" if COPY_KERNEL_TAG in name else None)
+            if tag is None:
+                continue
+            vals.setdefault(tag, {}).setdefault(r["Dispatch_Id"], 0.0)
+            vals[tag][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: sum(v.values()) / len(v) for k, v in vals.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    sf = COPY_BYTES / (f["copy"] * 1024.0)
+    sw = COPY_BYTES / (w["copy"] * 1024.0)
+    fetch_b = f["fwd"] * 1024.0 * sf
+    write_b = w["fwd"] * 1024.0 * sw
+    out = {"fwd_dual_gemm_bf16_8192x14336x4096": {
+        "source_hash": kernel_source_hash(),
+        "bytes_per_launch": round(fetch_b + write_b),
+        "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+        "fetch_kib_raw": round(f["fwd"], 1), "write_kib_raw": round(w["fwd"], 1),
+        "copy_fetch_kib_raw": round(f["copy"], 1), "copy_write_kib_raw": round(w["copy"], 1),
+        "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
+        "algorithmic_bytes": (M4 * K4 + 2 * N4 * K4 + M4 * N4) * 2}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
 
 
 def kernel_source_hash() -> str:
@@ -124,6 +174,9 @@ def graph_time_per_call(torch, calls, reps=5):
 
 def main():
     args = parse()
+    if args.digest_traffic:
+        digest_traffic(*args.digest_traffic)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the library runs on one GPU and has no "
@@ -159,13 +212,29 @@ def main():
         S.fwd(x, wg, wu, out=h)
         return S.bwd(x, wg, wu, dh, workspace=ws)
 
-    if args.only in ("step", "fwd"):
+    if args.only in ("step", "fwd", "traffic"):
         for _ in range(args.warmup + args.steps):
-            if args.only == "fwd":
-                S.fwd(x, wg, wu, out=h)
-            else:
+            if args.only == "step":
                 step()
+            else:
+                S.fwd(x, wg, wu, out=h)
+        if args.only == "traffic":
+            del ws
+            torch.cuda.empty_cache()
+            src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+            dst = torch.empty_like(src)
+            for _ in range(args.steps):
+                dst.copy_(src)
         torch.cuda.synchronize()
+        log("done")
+        return
+    if args.only in ("decode", "act_quant", "fp32"):
+        del x, wg, wu, dh, ws, h
+        torch.cuda.empty_cache()
+        leg = {"decode": lambda: decode_leg(torch, S, synth, np, dev, to_dev_bf16),
+               "act_quant": lambda: act_quant_leg(torch, S, synth, np, dev),
+               "fp32": lambda: fp32_leg(torch, S, synth, np, dev)}[args.only]
+        leg()
         log("done")
         return
 

@@ -887,12 +887,12 @@ using TileSingleT = Tile<256, 256, 2, 4>;
 }  // namespace
 
 hipError_t launch_fwd_dual(Dt dt, const GemmArgs& a, hipStream_t s) {
-  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2, 1>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2, 2>(a, s)
                          : launch<float, Epi::kSwiGLU, 2, TileDual>(a, s);
 }
 
 hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s) {
-  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, 1>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, 2>(a, s)
                          : launch<float, Epi::kDSwiGLU, 2, TileDual>(a, s);
 }
 
@@ -900,11 +900,11 @@ hipError_t launch_gemm_store_t(bool ta, bool tb, const GemmArgs& a, hipStream_t 
   if (ta && tb) return launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 2, true, true>(a, s);
   if (tb) return launch_dma<bf16, Epi::kStore, 1, TileSingleT, 8, 2, 2, false, true>(a, s);
   if (ta) return hipErrorInvalidValue;
-  return launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 1>(a, s);
+  return launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 2>(a, s);
 }
 
 hipError_t launch_gemm_store(Dt dt, const GemmArgs& a, hipStream_t s) {
-  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 1>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 2>(a, s)
                          : launch<float, Epi::kStore, 1, TileSingle>(a, s);
 }
 
