@@ -23,6 +23,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxBlocks = 1024;   // 4 workgroups per CU, grid-stride beyond
+constexpr int kUnroll = 4;         // chunks per lane per loop iteration
 
 // UE8M0 exponent of a block: smallest E with amax <= 448 * 2^E, clamped to
 // [-127, 127]; E = 128 when amax is +inf.  amax is finite-or-inf, >= 0.
@@ -90,11 +91,27 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float* __rest
                                                              int64_t nchunks) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   uint32_t cnt = 0;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += stride) {
-    const f32x4* gp = reinterpret_cast<const f32x4*>(gate) + 2 * c;
-    const f32x4* up4 = reinterpret_cast<const f32x4*>(up) + 2 * c;
-    const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
-    const f32x4 u0 = __builtin_nontemporal_load(up4), u1 = __builtin_nontemporal_load(up4 + 1);
+  // kUnroll chunks per lane per iteration (grid-stride apart): all their
+  // loads are issued before any is used, for more bytes in flight.
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < nchunks; c0 += kUnroll * stride) {
+    f32x4 G0[kUnroll], G1[kUnroll], U0[kUnroll], U1[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t c = c0 + j * stride;
+      if (c < nchunks) {
+        const f32x4* gp = reinterpret_cast<const f32x4*>(gate) + 2 * c;
+        const f32x4* up4 = reinterpret_cast<const f32x4*>(up) + 2 * c;
+        G0[j] = __builtin_nontemporal_load(gp);
+        G1[j] = __builtin_nontemporal_load(gp + 1);
+        U0[j] = __builtin_nontemporal_load(up4);
+        U1[j] = __builtin_nontemporal_load(up4 + 1);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+    const int64_t c = c0 + j * stride;
+    if (c >= nchunks) break;
+    const f32x4 g0 = G0[j], g1 = G1[j], u0 = U0[j], u1 = U1[j];
     float h[8];
     float amax = 0.0f;
 #pragma unroll
@@ -123,6 +140,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float* __rest
       f32x4* hp = reinterpret_cast<f32x4*>(hout) + 2 * c;
       hp[0] = f32x4{h[0], h[1], h[2], h[3]};
       hp[1] = f32x4{h[4], h[5], h[6], h[7]};
+    }
     }
   }
   if (kCount) {

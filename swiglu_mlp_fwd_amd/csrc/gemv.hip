@@ -20,8 +20,10 @@ namespace swg {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kColsPerBlock = 8;  // 4 waves x 2 half-waves
+// 8 waves: x is staged once per 16 columns, and at M = 8 (64 KiB of x at
+// K = 4096) two workgroups per CU still give 16 waves of loads in flight.
+constexpr int kThreads = 512;
+constexpr int kColsPerBlock = 16;  // 8 waves x 2 half-waves
 
 template <int M>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__ x,
