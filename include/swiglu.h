@@ -72,9 +72,8 @@ int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K,
                void* stream);
 
 /* Bytes of device workspace swiglu_bwd needs for these sizes (0 on invalid
- * sizes).  bf16: the workspace holds dg and du, 2 * M * round_up(N, 64)
- * elements.  fp32: dg and du, their transposes, x^T and the transposed
- * weight pair. */
+ * sizes).  It holds [dg | du], its transpose and x^T; fp32 also the
+ * transposed weight pair. */
 size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K);
 
 /* Backward of the fused stage ("Fused SwiGLU/dSwiGLU", Liger-Kernel issue
@@ -85,16 +84,17 @@ size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K);
  * dg and du are rounded to `dtype` once (they are matrix-core operands);
  * every contraction accumulates in fp32 and rounds its output once.
  * Kernels run in order on `stream`: the recompute dual GEMM with the
- * dSwiGLU epilogue, then the dX GEMM and the stacked dW GEMM; bf16 reads
- * the weights, x and [dg | du] in place, fp32 first transposes them.
+ * dSwiGLU epilogue (bf16: it also writes [dg | du] transposed), the dX GEMM
+ * (bf16 reads the weights in place; fp32 transposes them first) and the
+ * stacked dW GEMM over the transposes of [dg | du] and x.
  *
  *   x [M, K], wg/wu [N, K], dh [M, N]         (inputs, dtype)
  *   dx [M, K], dwg [N, K], dwu [N, K]         (outputs, dtype; overwritten)
  *   workspace: device buffer of at least swiglu_bwd_workspace_bytes(...)
  *              bytes, 256-byte aligned; contents are scratch.
  * Layout rule: K % 8 == 0 for bf16, K % 4 == 0 for fp32; M and N are free
- * (padded operands are zero-filled).  bf16 also needs K and
- * 2 * round_up(N, 64) at most 2^22 - 64 (else SWIGLU_ERR_UNSUPPORTED). */
+ * (padded operands are zero-filled).  bf16 also needs K, 2 * round_up(N, 64)
+ * and round_up(M, 8) at most 2^22 - 64 (else SWIGLU_ERR_UNSUPPORTED). */
 int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K,
                const void* x, const void* wg, const void* wu, const void* dh,
                void* dx, void* dwg, void* dwu,

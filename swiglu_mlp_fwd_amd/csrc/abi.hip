@@ -79,28 +79,36 @@ int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const 
   b1.arows = Mi; b1.brows = Ni; b1.m = Mi; b1.n = Np; b1.r = Ki;
   b1.out0 = D; b1.ldo = 2 * (int64_t)Np; b1.ncols = Ni;
   b1.dh = dh; b1.lddh = N; b1.du_off = Np;
+  void* DT = ws + L.off_dt;
+  void* XT = ws + L.off_xt;
+  if (dt == swg::Dt::kBF16) {
+    b1.out1 = DT;            // the epilogue also writes D^T [2 Np, Mp]
+    b1.ldt = Mp;
+  }
   if ((e = swg::launch_bwd_dswiglu(dt, b1, s)) != hipSuccess) return hip_status(e);
 
   if (dt == swg::Dt::kBF16) {
-    // 2. dX [M, K] = D [M, 2 Np] . [Wg; Wu] [2 Np, K]: the weights are read
-    //    in place as a reduction-major operand (reduction rows < Np from Wg,
-    //    the rest from Wu; rows N..Np-1 of each read as zero).
+    // 2. dX [M, K] = D [M, 2 Np] . ([Wg; Wu]^T [K, 2 Np])^T, reducing over
+    //    the stacked N (the transposes are zero padded from N to Np).
+    void* WTb = ws + L.off_wt;
+    if ((e = swg::launch_transpose(dt, wg, K, Ni, Ki, WTb, 2 * (int64_t)Np, 0, Np, s)) != hipSuccess) return hip_status(e);
+    if ((e = swg::launch_transpose(dt, wu, K, Ni, Ki, WTb, 2 * (int64_t)Np, Np, Np, s)) != hipSuccess) return hip_status(e);
     swg::GemmArgs b2{};
-    b2.a = D; b2.b0 = wg; b2.b1 = wu; b2.lda = 2 * (int64_t)Np; b2.ldb = K;
-    b2.arows = Mi; b2.brows = Ni; b2.m = Mi; b2.n = Ki; b2.r = 2 * Np; b2.rsplit = Np;
+    b2.a = D; b2.b0 = WTb; b2.lda = 2 * (int64_t)Np; b2.ldb = 2 * (int64_t)Np;
+    b2.arows = Mi; b2.brows = Ki; b2.m = Mi; b2.n = Ki; b2.r = 2 * Np;
     b2.out0 = dx; b2.ldo = K; b2.split = Mi; b2.lim0 = Mi; b2.lim1 = 0; b2.ncols = Ki;
-    if ((e = swg::launch_gemm_store_t(false, true, b2, s)) != hipSuccess) return hip_status(e);
-    // 3. [dWg; dWu] [2 Np, K] = D^T . x: both operands reduction-major
-    //    (reduction over the M rows of D and x).
+    if ((e = swg::launch_gemm_store_t(false, false, b2, s)) != hipSuccess) return hip_status(e);
+    // 3. [dWg; dWu] [2 Np, K] = D^T [2 Np, Mp] . (x^T [K, Mp])^T, reducing
+    //    over M: D^T came from the recompute's epilogue, x^T from a
+    //    transpose (zero padded to Mp).
+    if ((e = swg::launch_transpose(dt, x, K, Mi, Ki, XT, Mp, 0, Mp, s)) != hipSuccess) return hip_status(e);
     swg::GemmArgs b3{};
-    b3.a = D; b3.b0 = x; b3.lda = 2 * (int64_t)Np; b3.ldb = K;
-    b3.arows = Mi; b3.brows = Mi; b3.m = 2 * Np; b3.n = Ki; b3.r = Mi; b3.rsplit = 0x7fffffc0;
+    b3.a = DT; b3.b0 = XT; b3.lda = Mp; b3.ldb = Mp;
+    b3.arows = 2 * Np; b3.brows = Ki; b3.m = 2 * Np; b3.n = Ki; b3.r = Mp;
     b3.out0 = dwg; b3.out1 = dwu; b3.ldo = K; b3.split = Np; b3.lim0 = Ni; b3.lim1 = Ni;
     b3.ncols = Ki;
-    return hip_status(swg::launch_gemm_store_t(true, true, b3, s));
+    return hip_status(swg::launch_gemm_store_t(false, false, b3, s));
   }
-  void* DT = ws + L.off_dt;
-  void* XT = ws + L.off_xt;
   void* WT = ws + L.off_wt;
 
   // 2. Transposes: x -> XT [K, Mp]; Wg, Wu -> WT [K, 2 Np]; D -> DT [2 Np, Mp].

@@ -51,9 +51,10 @@ constexpr int kGroupM = 8;          // tile raster: groups of 8 row-tiles
 
 // Block tile kBM x kBN (rows of A x rows of each B), waves in a kWGM x kWGN
 // grid, each wave owning (kBM / kWGM) x (kBN / kWGN) of every B operand.
-template <int BM_, int BN_, int WGM_, int WGN_>
+template <int BM_, int BN_, int WGM_, int WGN_, int OCC_ = 1>
 struct Tile {
   static constexpr int kBM = BM_, kBN = BN_, kWGM = WGM_, kWGN = WGN_;
+  static constexpr int kOcc = OCC_;                          // workgroups per CU aimed for
   static constexpr int kThreads = 64 * WGM_ * WGN_;
   static constexpr int kWM = BM_ / WGM_, kWN = BN_ / WGN_;   // wave tile
   static constexpr int kTM = kWM / 32, kTN = kWN / 32;       // 32x32 MFMA tiles per wave
@@ -322,11 +323,12 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
       u32x4 v = {0, 0, 0, 0};
       if (grow < p.m && gcol < p.ncols) {
         const bf16* src = dh + (int64_t)grow * p.lddh + gcol;
-        if (gcol + 8 <= p.ncols) {
+        if (gcol + 8 <= p.ncols && p.lddh % 8 == 0) {
           v = *reinterpret_cast<const u32x4*>(src);
         } else {
           uint16_t tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-          for (int q = 0; q < p.ncols - gcol; ++q) tmp[q] = __builtin_bit_cast(uint16_t, src[q]);
+          const int nq = min(8, p.ncols - gcol);
+          for (int q = 0; q < nq; ++q) tmp[q] = __builtin_bit_cast(uint16_t, src[q]);
           v = __builtin_bit_cast(u32x4, tmp);
         }
       }
@@ -362,12 +364,14 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
         const int col = wn * kWN + j * 32 + r32;
         if constexpr (E == Epi::kSwiGLU) {
           const float g = acc[0][i][j][e], u = acc[NB - 1][i][j][e];
-          *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(silu_f32(g) * u);
+          float sg, sl;
+          sigmoid_silu_bf16out(g, sg, sl);
+          *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(sl * u);
         } else if constexpr (E == Epi::kDSwiGLU) {
           const float g = acc[0][i][j][e], u = acc[NB - 1][i][j][e];
           const float dh = dhv[i][j][e];
           float sg, sl;
-          sigmoid_silu_f32(g, sg, sl);
+          sigmoid_silu_bf16out(g, sg, sl);
           *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(dh * u * (sg * (1.0f + g * (1.0f - sg))));
           *reinterpret_cast<bf16*>(at(1, row, col)) = to_bf16(dh * sl);
         } else {
@@ -410,6 +414,39 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
         dst = static_cast<bf16*>(p.out1) + (int64_t)(grow - p.split) * p.ldo + gcol;
       }
       put(dst, *reinterpret_cast<const u32x4*>(at(0, r, ch * 8)), min(8, p.ncols - gcol));
+    }
+  }
+
+  // dSwiGLU: [dg | du] transposed into out1 (row n of dg, row du_off + n of
+  // du, columns m), for the dW product that reduces over m.  A 16-byte chunk
+  // there is 8 consecutive rows m of one column n of the staged tile: two
+  // transposing reads (rows +0..3, +4..7) give each lane of a 16-lane group
+  // one column.  In a wave the 4 groups take 4 consecutive chunks of the
+  // same 16 columns (64 contiguous bytes per output row); the two groups
+  // served together read opposite row halves first (rows 0..3 and 4..7 of
+  // their chunks sit in disjoint bank halves with the 288-byte pitch), and
+  // swap halves on the second read.  Rows m in [p.m, ldt) of the tile hold
+  // zeros (zero x rows and dh), so out1's padding columns are written zero.
+  if constexpr (E == Epi::kDSwiGLU) {
+    if (p.out1 != nullptr) {
+      bf16* dt = static_cast<bf16*>(p.out1);
+      constexpr int kNB = kCols / 16, kMQ = kBM / 32;       // 16-column blocks, 32-row groups
+      const int g = lane >> 4, s16 = lane & 15, hsel = g & 1;
+      for (int t = tid >> 6; t < 2 * kNB * kMQ; t += kThreads / 64) {
+        const int reg = t / (kNB * kMQ);
+        const int nb = (t / kMQ) % kNB, mq = t % kMQ;
+        const int m0 = (mq * 4 + g) * 8;
+        const int c = nb * 16 + 4 * (s16 & 3);
+        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4_t*)(lds_char_t*)(at(reg, m0 + 4 * hsel + (s16 >> 2), c)));
+        const short4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4_t*)(lds_char_t*)(at(reg, m0 + 4 * (1 - hsel) + (s16 >> 2), c)));
+        const u32x2 a = __builtin_bit_cast(u32x2, hsel ? v2 : v1);   // rows m0 .. m0 + 3
+        const u32x2 b = __builtin_bit_cast(u32x2, hsel ? v1 : v2);   // rows m0 + 4 .. m0 + 7
+        const int n = gcol0 + nb * 16 + s16, m = grow0 + m0;
+        if (n < p.n && m < p.ldt)
+          *reinterpret_cast<u32x4*>(dt + ((int64_t)reg * p.du_off + n) * p.ldt + m) = u32x4{a[0], a[1], b[0], b[1]};
+      }
     }
   }
 }
@@ -476,7 +513,7 @@ __device__ __forceinline__ void pin_epilogue_args(const GemmArgs& p) {
 // then the MFMAs, with the operand fragments of the next half-step read from
 // LDS while the current ones are in the matrix cores.
 template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL, bool TA, bool TB>
-__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(TL::kThreads / 256, TL::kThreads / 256)))
+__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(TL::kThreads * TL::kOcc / 256, TL::kThreads * TL::kOcc / 256)))
 void gemm_dma_kernel(GemmArgs p) {
   constexpr int kBM = TL::kBM, kBN = TL::kBN, kThreads = TL::kThreads;
   constexpr int kWaves = kThreads / 64;
@@ -827,7 +864,7 @@ void gemm_dma_kernel(GemmArgs p) {
   if (nk > 0) kstep(nk - 1, false);
 
   if constexpr (sizeof(T) == 2) {
-    const bool vec = (p.ldo % 8 == 0) && (E != Epi::kDSwiGLU || (p.lddh % 8 == 0 && p.du_off % 8 == 0));
+    const bool vec = (p.ldo % 8 == 0) && (E != Epi::kDSwiGLU || p.du_off % 8 == 0);
     if (vec) {
       wait_vmcnt<0>();                      // no DMA still landing in the ring
       __builtin_amdgcn_s_waitcnt(0xC07F);   // own LDS reads done

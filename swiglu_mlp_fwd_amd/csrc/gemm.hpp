@@ -28,6 +28,8 @@ struct GemmArgs {
   int du_off;          // dswiglu: du is written at column du_off + n of out0
   int rsplit;          // reduction-major B: reduction rows < rsplit come from b0,
                        // rows >= rsplit from b1 (at row - rsplit); a multiple of 64
+  int64_t ldt;         // dswiglu with out1 != null: out1 receives out0 transposed,
+                       // [2 du_off, ldt] with rows m in [arows, ldt) zero (bf16 only)
 };
 
 enum class Dt { kF32 = 0, kBF16 = 1 };

@@ -41,13 +41,12 @@ inline int check_ptr(const void* p) {
 
 // Backward workspace, regions starting on 256-byte boundaries.
 //   D   [M, 2 Np]     dg in columns [0, Np), du in [Np, 2 Np), zero padded
-// bf16 needs only D, with Np = round_up(N, 64): its matrix-core GEMMs read
-// D, x and the weights in place (reduction-major tiles where needed), and a
-// 64-row reduction step never straddles the dg / du halves.  fp32 also has
 //   DT  [2 Np, Mp]    transpose of D, zero padded along M
 //   XT  [K, Mp]       transpose of x, zero padded along M
-//   WT  [K, 2 Np]     [Wg; Wu] transposed, zero padded along N
-// with Mp = round_up(M, 8), Np = round_up(N, 8).
+//   WT  [K, 2 Np]     [Wg; Wu] transposed, zero padded along N (fp32 only)
+// with Mp = round_up(M, 8).  bf16 uses Np = round_up(N, 64) (a 64-row
+// reduction step of the dX product, which reads the weights in place, never
+// straddles the dg / du halves) and has no WT; fp32 uses Np = round_up(N, 8).
 struct BwdLayout {
   int64_t Mp, Np;
   size_t off_d, off_dt, off_xt, off_wt, total;
@@ -62,9 +61,9 @@ inline BwdLayout bwd_layout(int dtype, int64_t M, int64_t N, int64_t K) {
   auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
   size_t off = 0;
   L.off_d = off;  off += a256((size_t)M * 2 * L.Np * es);
-  L.off_dt = off; if (!bf16) off += a256((size_t)2 * L.Np * L.Mp * es);
-  L.off_xt = off; if (!bf16) off += a256((size_t)K * L.Mp * es);
-  L.off_wt = off; if (!bf16) off += a256((size_t)K * 2 * L.Np * es);
+  L.off_dt = off; off += a256((size_t)2 * L.Np * L.Mp * es);
+  L.off_xt = off; off += a256((size_t)K * L.Mp * es);
+  L.off_wt = off; off += a256((size_t)K * 2 * L.Np * es);
   L.total = off;
   return L;
 }
@@ -99,7 +98,8 @@ inline int validate_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* 
   if (K % chunk_elems(dtype) != 0) return SWIGLU_ERR_SHAPE;
   const BwdLayout L = bwd_layout(dtype, M, N, K);
   if (!tiles_fit(M, L.Np) || !tiles_fit(M, K) || !tiles_fit(2 * L.Np, K)) return SWIGLU_ERR_UNSUPPORTED;
-  if (dtype == SWIGLU_BF16 && (K > kMaxLdBf16 || 2 * L.Np > kMaxLdBf16)) return SWIGLU_ERR_UNSUPPORTED;
+  if (dtype == SWIGLU_BF16 && (K > kMaxLdBf16 || 2 * L.Np > kMaxLdBf16 || L.Mp > kMaxLdBf16))
+    return SWIGLU_ERR_UNSUPPORTED;
   if (K == 0) return SWIGLU_OK;                       // every output is empty
   if (M > 0 && (st = check_ptr(dx))) return st;
   if (N > 0 && (st = check_ptr(dwg))) return st;
