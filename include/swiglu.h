@@ -72,8 +72,8 @@ int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K,
                void* stream);
 
 /* Bytes of device workspace swiglu_bwd needs for these sizes (0 on invalid
- * sizes).  It holds [dg | du], its transpose and x^T; fp32 also the
- * transposed weight pair. */
+ * sizes).  It holds [dg | du], its transpose, x^T and the transposed weight
+ * pair. */
 size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K);
 
 /* Backward of the fused stage ("Fused SwiGLU/dSwiGLU", Liger-Kernel issue
@@ -84,9 +84,9 @@ size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K);
  * dg and du are rounded to `dtype` once (they are matrix-core operands);
  * every contraction accumulates in fp32 and rounds its output once.
  * Kernels run in order on `stream`: the recompute dual GEMM with the
- * dSwiGLU epilogue (bf16: it also writes [dg | du] transposed), the dX GEMM
- * (bf16 reads the weights in place; fp32 transposes them first) and the
- * stacked dW GEMM over the transposes of [dg | du] and x.
+ * dSwiGLU epilogue (bf16: it also writes [dg | du] transposed; fp32 uses a
+ * transpose kernel), transposes of x and the weights, the dX GEMM and the
+ * stacked dW GEMM.
  *
  *   x [M, K], wg/wu [N, K], dh [M, N]         (inputs, dtype)
  *   dx [M, K], dwg [N, K], dwu [N, K]         (outputs, dtype; overwritten)

@@ -43,10 +43,10 @@ inline int check_ptr(const void* p) {
 //   D   [M, 2 Np]     dg in columns [0, Np), du in [Np, 2 Np), zero padded
 //   DT  [2 Np, Mp]    transpose of D, zero padded along M
 //   XT  [K, Mp]       transpose of x, zero padded along M
-//   WT  [K, 2 Np]     [Wg; Wu] transposed, zero padded along N (fp32 only)
-// with Mp = round_up(M, 8).  bf16 uses Np = round_up(N, 64) (a 64-row
-// reduction step of the dX product, which reads the weights in place, never
-// straddles the dg / du halves) and has no WT; fp32 uses Np = round_up(N, 8).
+//   WT  [K, 2 Np]     [Wg; Wu] transposed, zero padded along N
+// with Mp = round_up(M, 8); Np = round_up(N, 64) for bf16 (its tiles and
+// 64-element reduction steps then never straddle the dg / du halves) and
+// round_up(N, 8) for fp32.
 struct BwdLayout {
   int64_t Mp, Np;
   size_t off_d, off_dt, off_xt, off_wt, total;

@@ -92,8 +92,8 @@ def test_bwd_validation(L):
 
 
 def test_workspace_layout_formula(L):
-    # fp32: D [M, 2Np] + DT [2Np, Mp] + XT [K, Mp] + WT [K, 2Np], each 256-byte
-    # aligned, Np = round_up(N, 8).  bf16: no WT, Np = round_up(N, 64).
+    # D [M, 2Np] + DT [2Np, Mp] + XT [K, Mp] + WT [K, 2Np], each 256-byte
+    # aligned; Np = round_up(N, 8) for fp32 and round_up(N, 64) for bf16.
     def a256(v):
         return (v + 255) // 256 * 256
     for (M, N, K) in ((100, 60, 64), (8192, 14336, 4096), (1, 1, 8)):
@@ -101,7 +101,7 @@ def test_workspace_layout_formula(L):
         want = a256(M * 2 * Np * 4) + a256(2 * Np * Mp * 4) + a256(K * Mp * 4) + a256(K * 2 * Np * 4)
         assert L.swiglu_bwd_workspace_bytes(0, M, N, K) == want
         Np = -(-N // 64) * 64
-        want = a256(M * 2 * Np * 2) + a256(2 * Np * Mp * 2) + a256(K * Mp * 2)
+        want = a256(M * 2 * Np * 2) + a256(2 * Np * Mp * 2) + a256(K * Mp * 2) + a256(K * 2 * Np * 2)
         assert L.swiglu_bwd_workspace_bytes(1, M, N, K) == want
 
 
