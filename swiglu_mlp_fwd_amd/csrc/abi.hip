@@ -97,7 +97,7 @@ int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const 
     b2.a = D; b2.b0 = WTb; b2.lda = 2 * (int64_t)Np; b2.ldb = 2 * (int64_t)Np;
     b2.arows = Mi; b2.brows = Ki; b2.m = Mi; b2.n = Ki; b2.r = 2 * Np;
     b2.out0 = dx; b2.ldo = K; b2.split = Mi; b2.lim0 = Mi; b2.lim1 = 0; b2.ncols = Ki;
-    if ((e = swg::launch_gemm_store_t(false, false, b2, s)) != hipSuccess) return hip_status(e);
+    if ((e = swg::launch_gemm_store(dt, b2, s)) != hipSuccess) return hip_status(e);
     // 3. [dWg; dWu] [2 Np, K] = D^T [2 Np, Mp] . (x^T [K, Mp])^T, reducing
     //    over M: D^T came from the recompute's epilogue, x^T from a
     //    transpose (zero padded to Mp).
@@ -107,7 +107,7 @@ int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const 
     b3.arows = 2 * Np; b3.brows = Ki; b3.m = 2 * Np; b3.n = Ki; b3.r = Mp;
     b3.out0 = dwg; b3.out1 = dwu; b3.ldo = K; b3.split = Np; b3.lim0 = Ni; b3.lim1 = Ni;
     b3.ncols = Ki;
-    return hip_status(swg::launch_gemm_store_t(false, false, b3, s));
+    return hip_status(swg::launch_gemm_store(dt, b3, s));
   }
   void* WT = ws + L.off_wt;
 

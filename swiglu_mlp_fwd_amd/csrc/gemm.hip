@@ -33,10 +33,6 @@
 // tile and the 16-byte chunk (2 kk + (l >> 5)) of the k-step; the same chunk
 // mapping for A and B makes the products pair up correctly whatever order
 // the matrix core uses within a chunk.
-// Reduction-major operands (stored [r, rows], as x, the weights and [dg|du]
-// are for the backward's dW and dX products) are staged as they lie in
-// memory and their fragments are gathered with transposing LDS reads, so
-// the backward never materialises a transposed copy.
 #include <mutex>
 
 #include "common.hpp"
@@ -51,10 +47,9 @@ constexpr int kGroupM = 8;          // tile raster: groups of 8 row-tiles
 
 // Block tile kBM x kBN (rows of A x rows of each B), waves in a kWGM x kWGN
 // grid, each wave owning (kBM / kWGM) x (kBN / kWGN) of every B operand.
-template <int BM_, int BN_, int WGM_, int WGN_, int OCC_ = 1>
+template <int BM_, int BN_, int WGM_, int WGN_>
 struct Tile {
   static constexpr int kBM = BM_, kBN = BN_, kWGM = WGM_, kWGN = WGN_;
-  static constexpr int kOcc = OCC_;                          // workgroups per CU aimed for
   static constexpr int kThreads = 64 * WGM_ * WGN_;
   static constexpr int kWM = BM_ / WGM_, kWN = BN_ / WGN_;   // wave tile
   static constexpr int kTM = kWM / 32, kTN = kWN / 32;       // 32x32 MFMA tiles per wave
@@ -512,8 +507,8 @@ __device__ __forceinline__ void pin_epilogue_args(const GemmArgs& p) {
 // step whose ring slot is refilled next), issue the DMA of step ks + S - 1,
 // then the MFMAs, with the operand fragments of the next half-step read from
 // LDS while the current ones are in the matrix cores.
-template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL, bool TA, bool TB>
-__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(TL::kThreads * TL::kOcc / 256, TL::kThreads * TL::kOcc / 256)))
+template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL>
+__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(TL::kThreads / 256, TL::kThreads / 256)))
 void gemm_dma_kernel(GemmArgs p) {
   constexpr int kBM = TL::kBM, kBN = TL::kBN, kThreads = TL::kThreads;
   constexpr int kWaves = kThreads / 64;
@@ -529,12 +524,6 @@ void gemm_dma_kernel(GemmArgs p) {
   static_assert(KC == 4 || KC == 8, "chunks per row");
   static_assert(kRows % (kWaves * kRowsPerDma) == 0, "DMA split");
   static_assert(kBM % kRowsPerWave == 0 && kBN % kRowsPerWave == 0, "a wave's slab lies in one operand");
-  // Reduction-major operands: 64 reduction rows of 256 operand rows per
-  // stage (512-byte LDS rows), one B operand, 16-bit elements.
-  static_assert(!TA || (kBM == 256 && KC == 8 && sizeof(T) == 2), "reduction-major A tile");
-  static_assert(!TB || (kBN == 256 && KC == 8 && NB == 1 && sizeof(T) == 2), "reduction-major B tile");
-  static_assert(!(TA || TB) || kRowsPerWave % 4 == 0, "whole reduction rows per wave");
-  constexpr int kTRow = 512;                            // bytes per reduction row of such a tile
   extern __shared__ u32x4 lds[];
   char* const lds_bytes = reinterpret_cast<char*>(lds);
 
@@ -553,21 +542,17 @@ void gemm_dma_kernel(GemmArgs p) {
   // so LDS-DMA bases (M0) and buffer descriptors stay in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / TL::kWGN, wn = wave % TL::kWGN;
-  const int nchunk_r = p.r / kPer;                      // reduction-contiguous: r % kPer == 0
-  const int nk = (p.r + KC * kPer - 1) / (KC * kPer);   // reduction-major r is any length
+  const int nchunk_r = p.r / kPer;                      // r % kPer == 0 (host-checked)
+  const int nk = (nchunk_r + KC - 1) / KC;
   pin_epilogue_args(p);
 
   // This wave's DMA slab and its operand.
   const int row0 = wave * kRowsPerWave;
-  const bool in_a = row0 < kBM;
-  // Whether the slab belongs to a reduction-major operand (a compile-time
-  // constant unless exactly one operand is).
-  const bool slab_t = (TA == TB) ? TA : (in_a ? TA : TB);
   const T* base;
   int64_t ld;
   int valid;
   int local0;
-  if (in_a) {
+  if (row0 < kBM) {
     base = static_cast<const T*>(p.a) + (int64_t)tm * kBM * p.lda;
     ld = p.lda;
     valid = p.arows - tm * kBM;
@@ -581,62 +566,6 @@ void gemm_dma_kernel(GemmArgs p) {
   }
   valid = valid < 0 ? 0 : (valid > (r_cap<kBM, kBN>()) ? r_cap<kBM, kBN>() : valid);
   const __amdgpu_buffer_rsrc_t rsrc = uniform_rsrc(base, valid * ld * (int64_t)sizeof(T));
-  // Reduction-major slab: 16 reduction rows (512 bytes each) per 64 stage
-  // rows; a DMA instruction fills two of them.  The descriptor is rebuilt
-  // per k-step over the step's 64 reduction rows from operand column col0
-  // to the end of the last existing row, so rows past the end read as zero;
-  // a row's columns past the operand's width read whatever follows (or zero
-  // past the buffer) and only reach outputs that are never stored.
-  // The values it needs are made wave-uniform registers here (readfirstlane),
-  // so the compiler keeps them instead of reloading kernel arguments inside
-  // the main loop (a scalar load there would stall every LDS wait).
-  const int col0 = in_a ? tm * kBM : tn * kBN;
-  const int kr0 = (in_a ? row0 : row0 - kBM) / 4;
-  auto rfl_ptr = [](const void* q) -> uint64_t {
-    const uint64_t v = reinterpret_cast<uint64_t>(q);
-    // readfirstlane returns int: go through uint32_t so the low word is
-    // zero-extended, not sign-extended into the high word.
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
-    return ((uint64_t)hi << 32) | lo;
-  };
-  const uint64_t t_base0 = rfl_ptr(static_cast<const T*>(in_a ? p.a : p.b0) + col0);
-  const uint64_t t_base1 = rfl_ptr(static_cast<const T*>(in_a ? p.a : p.b1) + col0);
-  const int t_split = __builtin_amdgcn_readfirstlane(in_a ? 0x7fffffc0 : p.rsplit);
-  const int t_rows = __builtin_amdgcn_readfirstlane(in_a ? p.arows : p.brows);
-  const int t_ldb = (int)ld * (int)sizeof(T);     // 64 * ld * sizeof(T) < 2^31 (host-checked)
-  const uint64_t n_addr = rfl_ptr(base);
-  const int n_bytes = __builtin_amdgcn_readfirstlane((int)(valid * ld * (int64_t)sizeof(T)));
-  // Descriptor of k-step ks for this wave's slab, one formula for both
-  // layouts (plain arithmetic and selects, so no branch splits the refill
-  // that is interleaved with the MFMAs).  With srow the step's first
-  // reduction row in its source:
-  //   address = base[srow past split] + srow * ldb,
-  //   bytes   = max(0, clamp(rows - srow, 0, 64) * ldb - c).
-  // A reduction-contiguous slab uses ldb = 0, rows = "unbounded" and
-  // c = -(its fixed size).
-  const bool sl_t = (TA || TB) && slab_t;
-  const uint64_t s_base0 = sl_t ? t_base0 : n_addr;
-  const uint64_t s_base1 = sl_t ? t_base1 : n_addr;
-  const int s_split = sl_t ? t_split : 0x7fffffc0;
-  const int s_rows = sl_t ? t_rows : 0x7fffffc0;
-  const int s_ldb = sl_t ? t_ldb : 0;
-  const int s_c = sl_t ? col0 * (int)sizeof(T) : -n_bytes;
-  auto step_rsrc = [&](int ks) {
-    if constexpr (!TA && !TB) {
-      return rsrc;
-    } else {
-      const bool second = ks * 64 >= s_split;
-      const int srow = ks * 64 - (second ? s_split : 0);
-      int rem = s_rows - srow;
-      rem = rem < 64 ? rem : 64;
-      rem = rem > 0 ? rem : 0;
-      int bytes = rem * s_ldb - s_c;
-      bytes = bytes > 0 ? bytes : 0;
-      const uint64_t addr = (second ? s_base1 : s_base0) + (uint64_t)((int64_t)srow * s_ldb);
-      return uniform_rsrc(reinterpret_cast<const T*>(addr), bytes);
-    }
-  };
   // Lane i of DMA d fills physical chunk (i % KC) of stage row
   // rr = row0 + d * kRowsPerDma + i / KC and fetches logical chunk
   // (i % KC) ^ swz(rr).  row0 is a multiple of 64, so swz(rr) depends on d
@@ -650,39 +579,22 @@ void gemm_dma_kernel(GemmArgs p) {
     lch[d] = (lane % KC) ^ ((rr >> kSwzShift) & (KC - 1));
   }
   const uint32_t voff0 = (uint32_t)((int64_t)(local0 + lane / KC) * ld * (int64_t)sizeof(T));
-  // Per-lane offset of DMA d = kb[d % period] + d * dstride (+ the k-step's
-  // chunk offset for a reduction-contiguous slab).  Reduction-major slab:
-  // lane i of DMA d fills physical chunk (i & 31) of reduction row
-  // kr0 + 2 d + (i >> 5) and fetches logical chunk (i & 31) ^ tswz(row),
-  // tswz(row) = 4 (row & 3) (fragment reads below explain the choice).
-  uint32_t kb[kLchPeriod];
-#pragma unroll
-  for (int q = 0; q < kLchPeriod; ++q) {
-    kb[q] = voff0 + (uint32_t)(lch[q] * kPer * (int)sizeof(T));
-    if constexpr (TA || TB) {
-      const int lct = (lane & 31) ^ (4 * ((2 * q + (lane >> 5)) & 3));
-      const uint32_t kt = (uint32_t)(((int64_t)(kr0 + (lane >> 5)) * ld + 8 * lct) * (int64_t)sizeof(T));
-      kb[q] = slab_t ? kt : kb[q];
-    }
-  }
-  const uint32_t dstride = (uint32_t)((int64_t)(slab_t ? 2 : kRowsPerDma) * ld * (int64_t)sizeof(T));
-  const uint32_t kstep_bytes = slab_t ? 0u : (uint32_t)(KC * kPer * (int)sizeof(T));
-  const int klim = slab_t ? 0x7fffffff : nchunk_r;
+  const uint32_t dstride = (uint32_t)((int64_t)kRowsPerDma * ld * (int64_t)sizeof(T));
   auto issue = [&](int ks) {
     char* dst = lds_bytes + (ks % S) * kStageBytes + row0 * kRowBytes;
-    const __amdgpu_buffer_rsrc_t rs = step_rsrc(ks);
     uint32_t koff[kLchPeriod];
     bool kin[kLchPeriod];
 #pragma unroll
     for (int q = 0; q < kLchPeriod; ++q) {
-      kin[q] = ks * KC + lch[q] < klim;
-      koff[q] = kb[q] + (uint32_t)ks * kstep_bytes;
+      const int kc = ks * KC + lch[q];
+      kin[q] = kc < nchunk_r;
+      koff[q] = voff0 + (uint32_t)(kc * kPer * (int)sizeof(T));
     }
 #pragma unroll
     for (int d = 0; d < kDma; ++d) {
       const int q = d % kLchPeriod;
       const uint32_t off = kin[q] ? koff[q] + (uint32_t)d * dstride : 0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + d * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + d * 1024), 16, off, 0, 0, 0);
     }
   };
 
@@ -703,46 +615,16 @@ void gemm_dma_kernel(GemmArgs p) {
     return *reinterpret_cast<const u32x4*>(L + row * kRowBytes + pc * 16);
   };
 
-  // MFMA operand fragment of a reduction-major tile R (512-byte rows) for
-  // operand rows c0 .. c0 + 31 and reductions 16 kk .. 16 kk + 15: lane l
-  // needs 8 consecutive reductions 16 kk + 8 (l >> 5) + [0, 8) of operand
-  // row c0 + (l & 31), i.e. a column of the stored tile.  ds_read_b64_tr_b16
-  // gives each lane of a 16-lane group one column, 4 rows deep, of the
-  // 4 x 16 block the group addresses (source lane s addressing row s >> 2,
-  // columns 4 (s & 3) .. + 3), so two such reads (rows +0..3, +4..7) form the
-  // fragment.  The 32 lanes served together read 4 rows x 64 bytes; the
-  // chunk swizzle 4 (row & 3) puts those 4 rows in distinct bank groups.
-  auto frag_t = [&](const char* R, int c0, int kk) -> u32x4 {
-    const int g = lane >> 4, sl = lane & 15;
-    const int k = 16 * kk + 8 * (g >> 1) + (sl >> 2);
-    const int c = c0 + 16 * (g & 1) + 4 * (sl & 3);
-    const char* a = R + k * kTRow + ((((c >> 3) ^ (4 * (sl >> 2)))) << 4) + (c & 7) * 2;
-    typedef __attribute__((ext_vector_type(4))) short s4_t;
-    typedef __attribute__((address_space(3))) s4_t lds_s4_t;
-    const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s4_t*)(__attribute__((address_space(3))) char*)(a));
-    const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s4_t*)(__attribute__((address_space(3))) char*)(a + 4 * kTRow));
-    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-    return u32x4{l2[0], l2[1], h2[0], h2[1]};
-  };
-
   // Operand fragments of one half-step (16 k), double-buffered in registers.
   u32x4 av[2][kTM], bv[2][NB][kTN];
   auto read_frags = [&](int buf, const char* L, int kk) {
     const int ch = 2 * kk + half;
 #pragma unroll
-    for (int i = 0; i < kTM; ++i) {
-      if constexpr (TA) av[buf][i] = frag_t(L, wm * kWM + i * 32, kk);
-      else av[buf][i] = frag(L, wm * kWM + i * 32 + r32, ch);
-    }
+    for (int i = 0; i < kTM; ++i) av[buf][i] = frag(L, wm * kWM + i * 32 + r32, ch);
 #pragma unroll
     for (int w = 0; w < NB; ++w)
 #pragma unroll
-      for (int j = 0; j < kTN; ++j) {
-        if constexpr (TB) bv[buf][w][j] = frag_t(L + kBM * kRowBytes, wn * kWN + j * 32, kk);
-        else bv[buf][w][j] = frag(L, kBM + w * kBN + wn * kWN + j * 32 + r32, ch);
-      }
+      for (int j = 0; j < kTN; ++j) bv[buf][w][j] = frag(L, kBM + w * kBN + wn * kWN + j * 32 + r32, ch);
   };
   auto mfmas = [&](int buf) {
 #pragma unroll
@@ -792,7 +674,7 @@ void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk) {
       constexpr int kMf = NB * kTM * kTN;
-      constexpr int kRd = (TA ? 2 : 1) * kTM + (TB ? 2 : 1) * NB * kTN;
+      constexpr int kRd = kTM + NB * kTN;
       if (kk + 1 < kKK) {
         if constexpr (kIL >= 2) {
           // Fragment reads of the next half-step spread between the MFMAs.
@@ -876,7 +758,7 @@ void gemm_dma_kernel(GemmArgs p) {
   store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
 }
 
-template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL = 0, bool TA = false, bool TB = false>
+template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL = 0>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   const int ntm = (a.m + TL::kBM - 1) / TL::kBM;
   const int ntn = (a.n + TL::kBN - 1) / TL::kBN;
@@ -888,11 +770,11 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [&] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<T, E, NB, TL, KC, S, kIL, TA, TB>),
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<T, E, NB, TL, KC, S, kIL>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   });
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_dma_kernel<T, E, NB, TL, KC, S, kIL, TA, TB>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
+  hipLaunchKernelGGL((gemm_dma_kernel<T, E, NB, TL, KC, S, kIL>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -917,9 +799,6 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
 
 using TileDual = Tile<256, 128, 4, 2>;   // 8 waves, 64 x 64 per wave per weight
 using TileSingle = Tile<256, 256, 4, 2>; // 8 waves, 64 x 128 per wave
-// 8 waves, 128 x 64 per wave: with a reduction-major B operand (two
-// transposing reads per fragment) the B side gets the fewer fragments.
-using TileSingleT = Tile<256, 256, 2, 4>;
 
 }  // namespace
 
@@ -931,13 +810,6 @@ hipError_t launch_fwd_dual(Dt dt, const GemmArgs& a, hipStream_t s) {
 hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s) {
   return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, 2>(a, s)
                          : launch<float, Epi::kDSwiGLU, 2, TileDual>(a, s);
-}
-
-hipError_t launch_gemm_store_t(bool ta, bool tb, const GemmArgs& a, hipStream_t s) {
-  if (ta && tb) return launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 2, true, true>(a, s);
-  if (tb) return launch_dma<bf16, Epi::kStore, 1, TileSingleT, 8, 2, 2, false, true>(a, s);
-  if (ta) return hipErrorInvalidValue;
-  return launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 2>(a, s);
 }
 
 hipError_t launch_gemm_store(Dt dt, const GemmArgs& a, hipStream_t s) {

@@ -26,8 +26,6 @@ struct GemmArgs {
   const void* dh;      // dswiglu: upstream gradient [arows, ncols], row stride lddh
   int64_t lddh;
   int du_off;          // dswiglu: du is written at column du_off + n of out0
-  int rsplit;          // reduction-major B: reduction rows < rsplit come from b0,
-                       // rows >= rsplit from b1 (at row - rsplit); a multiple of 64
   int64_t ldt;         // dswiglu with out1 != null: out1 receives out0 transposed,
                        // [2 du_off, ldt] with rows m in [arows, ldt) zero (bf16 only)
 };
@@ -37,10 +35,6 @@ enum class Dt { kF32 = 0, kBF16 = 1 };
 hipError_t launch_fwd_dual(Dt dt, const GemmArgs& a, hipStream_t s);      // h = silu(g) * u
 hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s);   // D = [dg | du]
 hipError_t launch_gemm_store(Dt dt, const GemmArgs& a, hipStream_t s);    // C = A B^T
-// bf16 C = A B^T with reduction-major operands: ta (tb) says A (B) is stored
-// [r, rows] (row stride lda / ldb) rather than [rows, r].  arows / brows then
-// count the stored reduction rows; only 256 x 256 tiles with the plain store.
-hipError_t launch_gemm_store_t(bool ta, bool tb, const GemmArgs& a, hipStream_t s);
 
 // out[c, col_off + r] = in[r, c] for r < rows, 0 for rows <= r < rows_pad.
 hipError_t launch_transpose(Dt dt, const void* in, int64_t ld_in, int rows, int cols,
