@@ -17,7 +17,10 @@
 //            unquantized bf16 path", TensorRT-LLM PR 17693);
 //   kDSwiGLU du = dh * SiLU(g), dg = dh * u * s * (1 + g (1 - s)), s = sigma(g)
 //            (the backward of the same stage, Liger-Kernel issue 1383);
+//            bf16 can also write [dg | du] transposed for the dW product;
 //   kStore   C itself, routed to one of two outputs by row.
+// sigma is the accurate fp32 form for fp32 outputs and the short hardware
+// exp2 / reciprocal form (common.hpp) where the result is rounded to bf16.
 //
 // Tiling: a workgroup owns a BM x BN block tile (rows of A x rows of each
 //   B), k-steps of 128 bytes per row (64 bf16 or 32 fp32), and its waves form
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(GemmArgs p) {
 //   - results are written to LDS (2-byte writes, rows padded so the two
 //     half-waves hit different banks) and read back as 16-byte row chunks
 //     that are stored with coalesced 16-byte global stores.
-// Needs every output row pitch (and dh's) to be a multiple of 8 elements;
+// Needs every output row pitch (and du_off) to be a multiple of 8 elements;
 // the caller uses store_tile otherwise.
 template <Epi E, class TL>
 struct EpiLds {
