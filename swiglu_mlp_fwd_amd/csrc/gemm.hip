@@ -296,10 +296,42 @@ typedef __attribute__((ext_vector_type(4))) short short4_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
+// dSwiGLU: the 16-byte chunks of the dh tile a thread stages (chunk
+// c = tid + k * threads, row c / (BN / 8), column chunk c % (BN / 8)).  Whole
+// chunks inside the matrix are loaded into registers by dh_prefetch, issued
+// before the last k-step so the HBM latency hides behind its MFMAs; the
+// epilogue then only has to write them to LDS.  Other chunks (past the last
+// row, or straddling the last column) are handled in the epilogue.
+template <class TL>
+struct DhPre {
+  static constexpr int kCPR = TL::kBN / 8;
+  static constexpr int kPer = TL::kBM * kCPR / TL::kThreads;
+  u32x4 v[kPer];
+};
+
+template <class TL>
+__device__ __forceinline__ bool dh_whole(const GemmArgs& p, int grow, int gcol) {
+  return grow < p.m && gcol + 8 <= p.ncols && p.lddh % 8 == 0;
+}
+
+template <class TL>
+__device__ __forceinline__ void dh_prefetch(const GemmArgs& p, int tm, int tn, int tid, DhPre<TL>& pre) {
+  constexpr int kCPR = DhPre<TL>::kCPR;
+  const bf16* dh = static_cast<const bf16*>(p.dh);
+#pragma unroll
+  for (int k = 0; k < DhPre<TL>::kPer; ++k) {
+    const int c = tid + k * TL::kThreads;
+    const int grow = tm * TL::kBM + c / kCPR, gcol = tn * TL::kBN + (c % kCPR) * 8;
+    pre.v[k] = u32x4{0, 0, 0, 0};
+    if (dh_whole<TL>(p, grow, gcol))
+      pre.v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dh + (int64_t)grow * p.lddh + gcol));
+  }
+}
+
 template <Epi E, int NB, class TL>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[NB][TL::kTM][TL::kTN],
                                                int tm, int tn, int wm, int wn, int lane, int tid,
-                                               char* lds) {
+                                               char* lds, const DhPre<TL>& pre) {
   constexpr int kBM = TL::kBM, kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
   constexpr int kThreads = TL::kThreads;
   constexpr int kCols = EpiLds<E, TL>::kCols;
@@ -314,21 +346,20 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
 
   float dhv[kTM][kTN][16];
   if constexpr (E == Epi::kDSwiGLU) {
+    static_assert(DhPre<TL>::kCPR == kCPR && DhPre<TL>::kPer * kThreads == kBM * kCPR, "dh chunk mapping");
     const bf16* dh = static_cast<const bf16*>(p.dh);
-    for (int c = tid; c < kBM * kCPR; c += kThreads) {
+#pragma unroll
+    for (int k = 0; k < DhPre<TL>::kPer; ++k) {
+      const int c = tid + k * kThreads;
       const int r = c / kCPR, ch = c % kCPR;
       const int grow = grow0 + r, gcol = gcol0 + ch * 8;
-      u32x4 v = {0, 0, 0, 0};
-      if (grow < p.m && gcol < p.ncols) {
+      u32x4 v = pre.v[k];
+      if (!dh_whole<TL>(p, grow, gcol) && grow < p.m && gcol < p.ncols) {
         const bf16* src = dh + (int64_t)grow * p.lddh + gcol;
-        if (gcol + 8 <= p.ncols && p.lddh % 8 == 0) {
-          v = *reinterpret_cast<const u32x4*>(src);
-        } else {
-          uint16_t tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-          const int nq = min(8, p.ncols - gcol);
-          for (int q = 0; q < nq; ++q) tmp[q] = __builtin_bit_cast(uint16_t, src[q]);
-          v = __builtin_bit_cast(u32x4, tmp);
-        }
+        uint16_t tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        const int nq = min(8, p.ncols - gcol);
+        for (int q = 0; q < nq; ++q) tmp[q] = __builtin_bit_cast(uint16_t, src[q]);
+        v = __builtin_bit_cast(u32x4, tmp);
       }
       *reinterpret_cast<u32x4*>(at(0, r, ch * 8)) = v;
     }
@@ -420,8 +451,8 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
   // there is 8 consecutive rows m of one column n of the staged tile: two
   // transposing reads (rows +0..3, +4..7) give each lane of a 16-lane group
   // one column.  In a wave the 4 groups take 4 consecutive chunks of the
-  // same 16 columns (64 contiguous bytes per output row); the two groups
-  // served together read opposite row halves first (rows 0..3 and 4..7 of
+  // same 16 columns (64 contiguous bytes per output row and instruction);
+  // the two groups served together read opposite row halves first (rows 0..3 and 4..7 of
   // their chunks sit in disjoint bank halves with the 288-byte pitch), and
   // swap halves on the second read.  Rows m in [p.m, ldt) of the tile hold
   // zeros (zero x rows and dh), so out1's padding columns are written zero.
@@ -430,7 +461,14 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
       bf16* dt = static_cast<bf16*>(p.out1);
       constexpr int kNB = kCols / 16, kMQ = kBM / 32;       // 16-column blocks, 32-row groups
       const int g = lane >> 4, s16 = lane & 15, hsel = g & 1;
-      for (int t = tid >> 6; t < 2 * kNB * kMQ; t += kThreads / 64) {
+      // A wave takes consecutive tasks: all 32-row groups of one 16-column
+      // block in turn, so each output row it touches gets 512 contiguous
+      // bytes over its iterations.
+      constexpr int kTasks = 2 * kNB * kMQ, kPerWave = kTasks / (kThreads / 64);
+      static_assert(kTasks % (kThreads / 64) == 0, "D^T tasks per wave");
+#pragma unroll 4
+      for (int it = 0; it < kPerWave; ++it) {
+        const int t = (tid >> 6) * kPerWave + it;
         const int reg = t / (kNB * kMQ);
         const int nb = (t / kMQ) % kNB, mq = t % kMQ;
         const int m0 = (mq * 4 + g) * 8;
@@ -745,7 +783,9 @@ void gemm_dma_kernel(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  DhPre<TL> dpre;
   for (int ks = 0; ks + 1 < nk; ++ks) kstep(ks, true);
+  if constexpr (E == Epi::kDSwiGLU && sizeof(T) == 2) dh_prefetch<TL>(p, tm, tn, tid, dpre);
   if (nk > 0) kstep(nk - 1, false);
 
   if constexpr (sizeof(T) == 2) {
@@ -754,7 +794,7 @@ void gemm_dma_kernel(GemmArgs p) {
       wait_vmcnt<0>();                      // no DMA still landing in the ring
       __builtin_amdgcn_s_waitcnt(0xC07F);   // own LDS reads done
       barrier_no_fence();                   // every wave is done with the ring
-      store_tile_lds<E, NB, TL>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes);
+      store_tile_lds<E, NB, TL>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes, dpre);
       return;
     }
   }
