@@ -91,6 +91,9 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float* __rest
                                                              int64_t nchunks) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   uint32_t cnt = 0;
+  // Without counting, a given counter just receives 0 (one store, no
+  // separate zeroing launch).
+  if (!kCount && count != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *count = 0ull;
   // kUnroll chunks per lane per iteration (grid-stride apart): all their
   // loads are issued before any is used, for more bytes in flight.
   for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < nchunks; c0 += kUnroll * stride) {
@@ -176,7 +179,8 @@ hipError_t launch_act_quant(int64_t rows, int64_t cols, const float* gate, const
                             float limit, bool clamp, uint8_t* q, uint8_t* scale, uint64_t* count,
                             float* hout, hipStream_t s) {
   const bool counting = clamp && count != nullptr;
-  if (count != nullptr) {
+  const int64_t nchunks0 = rows * cols / 8;
+  if (counting || (count != nullptr && nchunks0 == 0)) {
     hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s,
                        reinterpret_cast<unsigned long long*>(count));
   }
@@ -190,11 +194,11 @@ hipError_t launch_act_quant(int64_t rows, int64_t cols, const float* gate, const
       if (hout) launch_aq<true, true, true>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
       else launch_aq<true, true, false>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
     } else if (clamp) {
-      if (hout) launch_aq<true, false, true>(grid, gate, up, limit, q, scale, nullptr, hout, nchunks, s);
-      else launch_aq<true, false, false>(grid, gate, up, limit, q, scale, nullptr, hout, nchunks, s);
+      if (hout) launch_aq<true, false, true>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
+      else launch_aq<true, false, false>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
     } else {
-      if (hout) launch_aq<false, false, true>(grid, gate, up, limit, q, scale, nullptr, hout, nchunks, s);
-      else launch_aq<false, false, false>(grid, gate, up, limit, q, scale, nullptr, hout, nchunks, s);
+      if (hout) launch_aq<false, false, true>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
+      else launch_aq<false, false, false>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
     }
   }
   return hipGetLastError();
