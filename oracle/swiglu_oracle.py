@@ -285,6 +285,39 @@ def quantize_1x32(h32):
 
 
 # ---------------------------------------------------------------------------
+# Elementwise SwiGLU backward on materialised gate/up.  [PTO-20] performance
+# section (the backward table: gate/up given, optional clamp, optional
+# routing weights with recompute) and implementation notes (weight_grad is a
+# reassociated reduction, accepted at 1e-4).  Reading: the forward is
+#   y[r, c] = w[r] * SiLU(clamp(g[r, c])) * clamp(u[r, c])
+# (w = 1 without weights); the backward takes dy and returns dg, du and
+# weight_grad[r] = dL/dw[r] = sum_c dy[r, c] * SiLU(clamp(g)) * clamp(u).
+# The clamp passes the gradient where |v| <= L (or v is NaN) and stops it
+# where it clamped (|v| > L), the same test as the clamp count.
+# ---------------------------------------------------------------------------
+
+def act_bwd(gate, up, dy, clamp_limit=np.inf, weights=None):
+    """Returns (dgate, dup, weight_grad) in float64; weight_grad[r] is
+    sum_c dy * h with h the (unweighted) activation, also without weights."""
+    gate = np.asarray(gate, np.float64)
+    up = np.asarray(up, np.float64)
+    dy = np.asarray(dy, np.float64)
+    assert up.shape == gate.shape == dy.shape
+    L = float(clamp_limit)
+    g = clamp_nan_preserving(gate, L)
+    u = clamp_nan_preserving(up, L)
+    pass_g = ~(np.abs(gate) > L)          # NaN compares false: passes
+    pass_u = ~(np.abs(up) > L)
+    w = np.ones(gate.shape[0]) if weights is None else np.asarray(weights, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        dh = w[:, None] * dy
+        dgate = np.where(pass_g, dh * u * silu_grad(g), 0.0)
+        dup = np.where(pass_u, dh * silu(g), 0.0)
+        weight_grad = np.sum(dy * (silu(g) * u), axis=1)
+    return dgate, dup, weight_grad
+
+
+# ---------------------------------------------------------------------------
 # Comparison metrics (test infrastructure, float64).
 # ---------------------------------------------------------------------------
 

@@ -140,6 +140,75 @@ def test_backward_matches_finite_differences_everywhere():
     assert worst < 1e-7
 
 
+def test_act_bwd_matches_finite_differences():
+    """Elementwise backward: central differences of
+    L = sum(dy * w * SiLU(clamp(g)) * clamp(u)) w.r.t. every g, u and w,
+    with the clamp on (values kept at least 1e-3 away from +-L, where the
+    clamp has its kinks) and off.  weight_grad is dL/dw."""
+    rs = np.random.default_rng(11)
+    rows, cols = 6, 40
+    for L in (np.inf, 1.3):
+        g = rs.normal(0.0, 2.0, (rows, cols))
+        u = rs.normal(0.0, 2.0, (rows, cols))
+        if np.isfinite(L):
+            for a in (g, u):
+                near = np.abs(np.abs(a) - L) < 1e-3
+                a[near] += 3e-3
+        dy = rs.normal(0.0, 1.0, (rows, cols))
+        w = rs.uniform(0.1, 1.0, rows)
+
+        def loss(g_, u_, w_):
+            gc = np.clip(g_, -L, L)
+            uc = np.clip(u_, -L, L)
+            return float(np.sum(dy * w_[:, None] * (gc / (1.0 + np.exp(-gc))) * uc))
+
+        dg, du, wgrad = oracle.act_bwd(g, u, dy, L, w)
+        eps = 1e-6
+        for name, grad in (("g", dg), ("u", du), ("w", wgrad)):
+            args = {"g": g.copy(), "u": u.copy(), "w": w.copy()}
+            t = args[name]
+            fd = np.empty_like(t)
+            for idx in np.ndindex(t.shape):
+                v = t[idx]
+                t[idx] = v + eps
+                lp = loss(args["g"], args["u"], args["w"])
+                t[idx] = v - eps
+                lm = loss(args["g"], args["u"], args["w"])
+                t[idx] = v
+                fd[idx] = (lp - lm) / (2 * eps)
+            err = np.max(np.abs(fd - grad) / np.maximum(1.0, np.abs(grad)))
+            assert err < 1e-7, (L, name, err)
+        if np.isfinite(L):
+            # Clamped positions carry exactly zero gradient.
+            assert np.all(dg[np.abs(g) > L] == 0.0) and np.all(du[np.abs(u) > L] == 0.0)
+            assert np.count_nonzero(np.abs(g) > L) > 10
+
+
+def test_act_bwd_special_cases():
+    # Without weights the result is that of unit weights.
+    rs = np.random.default_rng(12)
+    g, u, dy = (rs.normal(0, 1.5, (3, 8)) for _ in range(3))
+    a = oracle.act_bwd(g, u, dy)
+    b = oracle.act_bwd(g, u, dy, np.inf, np.ones(3))
+    for x_, y_ in zip(a, b):
+        np.testing.assert_array_equal(x_, y_)
+    # g = 0: SiLU(0) = 0 and SiLU'(0) = 1/2, so du = 0, dg = dy * u / 2, weight_grad = 0.
+    z = np.zeros((2, 4))
+    dg, du, wgrad = oracle.act_bwd(z, u[:2, :4], dy[:2, :4])
+    np.testing.assert_array_equal(du, 0.0)
+    np.testing.assert_allclose(dg, dy[:2, :4] * u[:2, :4] / 2, rtol=1e-15)
+    np.testing.assert_array_equal(wgrad, 0.0)
+    # A NaN gate passes the clamp (not clamped) and gives NaN gradients in its
+    # element only; an infinite up value is clamped and stops its gradient.
+    g2 = np.array([[np.nan, 0.5], [0.25, 1.0]])
+    u2 = np.array([[1.0, np.inf], [2.0, -3.0]])
+    dy2 = np.ones((2, 2))
+    dg, du, wgrad = oracle.act_bwd(g2, u2, dy2, 2.0)
+    assert np.isnan(dg[0, 0]) and np.isnan(du[0, 0]) and np.isnan(wgrad[0])
+    assert du[0, 1] == 0.0 and dg[0, 1] > 0 and du[1, 1] == 0.0
+    assert math.isclose(du[1, 0], 0.25 / (1 + math.exp(-0.25)), rel_tol=1e-15)
+
+
 def test_dswiglu_reduces_to_product_rule_at_zero_gate():
     # At g = 0: silu(0) = 0 and silu'(0) = 1/2, so du = 0 and dg = dh * u / 2.
     g = np.zeros(4)
