@@ -18,6 +18,9 @@ The same run also measures, after the timed region and outside `value`:
            the same buffers (the cold-read floor);
   act_quant the elementwise SwiGLU + FP8 block quantisation of [4001, 3584]
            fp32 inputs (4 rotated copies), in GB/s;
+  act_bwd  the elementwise SwiGLU backward on [4001, 3584] fp32 gate/up/dy
+           (4 rotated copies): clamp 0.5 without weights, and per-row weights
+           with the weight gradient and no clamp, in GB/s;
   fp32     the IEEE-fp32 fused forward at M=4001, K=2048, N=3584, in TFLOP/s;
   cpu_baseline  the fp64 oracle on a row sample of the headline workload,
            timed on the host cores.
@@ -54,7 +57,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target host time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the decode / act_quant / fp32 legs")
-    p.add_argument("--only", choices=["step", "fwd", "decode", "act_quant", "fp32", "traffic"], default=None,
+    p.add_argument("--only", choices=["step", "fwd", "decode", "act_quant", "act_bwd", "fp32", "traffic"], default=None,
                    help="profiling aid: run one leg only (no JSON contract); 'traffic' runs the headline "
                         "forward and a 1 GiB copy (the counter calibration) for the --pmc runs")
     p.add_argument("--digest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
@@ -228,11 +231,12 @@ def main():
         torch.cuda.synchronize()
         log("done")
         return
-    if args.only in ("decode", "act_quant", "fp32"):
+    if args.only in ("decode", "act_quant", "act_bwd", "fp32"):
         del x, wg, wu, dh, ws, h
         torch.cuda.empty_cache()
         leg = {"decode": lambda: decode_leg(torch, S, synth, np, dev, to_dev_bf16),
                "act_quant": lambda: act_quant_leg(torch, S, synth, np, dev),
+               "act_bwd": lambda: act_bwd_leg(torch, S, synth, np, dev),
                "fp32": lambda: fp32_leg(torch, S, synth, np, dev)}[args.only]
         leg()
         log("done")
@@ -302,6 +306,7 @@ def main():
     if not args.no_extra:
         result["decode"] = decode_leg(torch, S, synth, np, dev, to_dev_bf16)
         result["act_quant"] = act_quant_leg(torch, S, synth, np, dev)
+        result["act_bwd"] = act_bwd_leg(torch, S, synth, np, dev)
         result["fp32"] = fp32_leg(torch, S, synth, np, dev)
 
     # ------------------------------------------------------------ cpu baseline
@@ -363,6 +368,29 @@ def act_quant_leg(torch, S, synth, np, dev):
         res[key] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
         log(f"act_quant {R}x{C} {key}: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
     del G, U, outs
+    torch.cuda.empty_cache()
+    return res
+
+
+def act_bwd_leg(torch, S, synth, np, dev):
+    R, C = 4001, 3584
+    d = synth.act_bwd_f32(R, C, seed=0)
+    copies = 4
+    ins = [tuple(torch.from_numpy(d[k]).to(dev) for k in ("gate", "up", "dy", "weights")) for _ in range(copies)]
+    outs = [(torch.empty((R, C), dtype=torch.float32, device=dev), torch.empty((R, C), dtype=torch.float32, device=dev),
+             torch.empty(R, dtype=torch.float32, device=dev)) for _ in range(copies)]
+    res = {"rows": R, "cols": C, "copies": copies, "unit": "GB/s"}
+    for key, L, use_w in (("clamp_0.5", 0.5, False), ("weights_wgrad", math.inf, True)):
+        nbytes = 5 * R * C * 4 + (2 * R * 4 if use_w else 0)
+        calls = [(lambda i=i: S.act_bwd(ins[i][0], ins[i][1], ins[i][2], L, weights=ins[i][3] if use_w else None,
+                                        out=(outs[i][0], outs[i][1], outs[i][2] if use_w else None)))
+                 for _ in range(4) for i in range(copies)]
+        t, _ = graph_time_per_call(torch, calls)
+        gbs = nbytes / t / 1e9
+        res[key] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "bytes_per_call": nbytes,
+                    "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"act_bwd {R}x{C} {key}: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
+    del ins, outs
     torch.cuda.empty_cache()
     return res
 

@@ -139,6 +139,30 @@ int swiglu_act_quant(int64_t rows, int64_t cols,
                      uint8_t* q, uint8_t* scale, uint64_t* clamp_count,
                      float* h_out, void* stream);
 
+/* Elementwise SwiGLU backward on materialised gate/up ("quant: add SwiGLU
+ * forward/backward VMI kernels", TileKernels-PTO PR 20: the performance
+ * section's backward table -- gate/up given, optional clamp, optional routing
+ * weights with recompute -- and the implementation notes on weight_grad, a
+ * reassociated per-row reduction).  For the forward
+ *   y[r, c] = w[r] * SiLU(g') * u',   g' = clamp(gate, -L, L), u' = clamp(up, -L, L)
+ * (w = 1 when weights is NULL; NaN passes the clamp), given dy:
+ *   dgate = w dy u' s (1 + g' (1 - s)), s = sigmoid(g'), where |gate| <= L
+ *           (or NaN), 0 where the clamp acted;
+ *   dup   = w dy SiLU(g') where |up| <= L (or NaN), 0 where the clamp acted;
+ *   weight_grad[r] = sum_c dy[r, c] * SiLU(g') * u'   (dL/dw[r]).
+ *
+ *   gate, up, dy   [rows, cols] fp32 inputs
+ *   weights        NULL, or [rows] fp32
+ *   clamp_limit    L > 0, or +INFINITY for no clamp (NaN or L <= 0: error)
+ *   dgate, dup     [rows, cols] fp32 outputs
+ *   weight_grad    NULL, or [rows] fp32 output
+ * Products and the row sum are formed in fp64, each output rounded once.
+ * Layout rule: cols % 4 == 0 (16-byte rows). */
+int swiglu_act_bwd(int64_t rows, int64_t cols,
+                   const float* gate, const float* up, const float* dy,
+                   const float* weights, float clamp_limit,
+                   float* dgate, float* dup, float* weight_grad, void* stream);
+
 /* Measurement aid: a pure streaming read of two device buffers of `bytes`
  * bytes each (16-byte multiples), the cold-read floor against which the
  * decode kernel is judged ("Fused SwiGLU benchmark", section HBM

@@ -150,6 +150,17 @@ int swiglu_act_quant(int64_t rows, int64_t cols, const float* gate, const float*
                                           clamp_count, h_out, as_stream(stream)));
 }
 
+int swiglu_act_bwd(int64_t rows, int64_t cols, const float* gate, const float* up, const float* dy,
+                   const float* weights, float clamp_limit, float* dgate, float* dup,
+                   float* weight_grad, void* stream) {
+  int st = swg::validate_act_bwd(rows, cols, gate, up, dy, weights, clamp_limit, dgate, dup,
+                                 weight_grad);
+  if (st != SWIGLU_OK || rows == 0) return st;
+  const bool clamp = !isinf(clamp_limit);
+  return hip_status(swg::launch_act_bwd(rows, cols, gate, up, dy, weights, clamp_limit, clamp,
+                                        dgate, dup, weight_grad, as_stream(stream)));
+}
+
 int swiglu_probe_read2(const void* a, const void* b, size_t bytes, uint32_t* sink, void* stream) {
   if (bytes % 16 != 0) return SWIGLU_ERR_SHAPE;
   if (bytes == 0) return SWIGLU_OK;

@@ -71,6 +71,25 @@ __device__ __forceinline__ void sigmoid_silu_f32(float z, float& s, float& silu)
   silu = z * s;
 }
 
+// sigma(z) and 1 - sigma(z), both to a few ulps (the complement is not
+// formed by subtracting, which would lose it for large z):
+//   z >= 0: sigma = 1 / (1 + e),  1 - sigma = e / (1 + e),  e = exp(-|z|),
+//   z < 0 : the two swap.  NaN gives NaN for both.
+__device__ __forceinline__ void sigmoid_pair_f32(float z, float& s, float& c) {
+#pragma clang fp contract(off)
+  float p;
+  int n;
+  exp_neg_split(fminf(fabsf(z), 128.0f), p, n);
+  const float e = ldexpf(p, n);
+  const float d = 1.0f + e;
+  float r = __builtin_amdgcn_rcpf(d);
+  r = __builtin_fmaf(r, __builtin_fmaf(-d, r, 1.0f), r);
+  const float er = e * r;
+  s = (z >= 0.0f) ? r : er;
+  c = (z >= 0.0f) ? er : r;
+  if (z != z) s = c = z;
+}
+
 // sigma(z) and SiLU(z) for results that are rounded to bf16 right after:
 // sigma = 1 / (1 + 2^(-z log2 e)) with the hardware exp2 and reciprocal
 // (about 13 VALU slots instead of about 25).  The product z log2 e is

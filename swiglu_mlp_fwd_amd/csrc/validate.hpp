@@ -150,4 +150,25 @@ inline int validate_act_quant(int64_t rows, int64_t cols, const float* gate, con
   return SWIGLU_OK;
 }
 
+inline int validate_act_bwd(int64_t rows, int64_t cols, const float* gate, const float* up,
+                            const float* dy, const float* weights, float L, const float* dgate,
+                            const float* dup, const float* wgrad) {
+  if (rows < 0 || cols < 0) return SWIGLU_ERR_SHAPE;
+  if (cols % 4 != 0) return SWIGLU_ERR_SHAPE;
+  if (rows > 0 && cols > (int64_t(1) << 40) / rows) return SWIGLU_ERR_SHAPE;
+  if (!(L > 0.0f)) return SWIGLU_ERR_ARG;             // rejects NaN, zero and negatives
+  if (weights != nullptr && !aligned(weights, 4)) return SWIGLU_ERR_ALIGN;
+  if (wgrad != nullptr && !aligned(wgrad, 4)) return SWIGLU_ERR_ALIGN;
+  if (rows == 0) return SWIGLU_OK;
+  if (cols > 0) {
+    int st;
+    if ((st = check_ptr(gate))) return st;
+    if ((st = check_ptr(up))) return st;
+    if ((st = check_ptr(dy))) return st;
+    if ((st = check_ptr(dgate))) return st;
+    if ((st = check_ptr(dup))) return st;
+  }
+  return SWIGLU_OK;
+}
+
 }  // namespace swg

@@ -140,6 +140,41 @@ def act_quant(gate: torch.Tensor, up: torch.Tensor, clamp_limit: float = math.in
     return q, scale, cnt, h
 
 
+def act_bwd(gate: torch.Tensor, up: torch.Tensor, dy: torch.Tensor, clamp_limit: float = math.inf,
+            weights: torch.Tensor | None = None, weight_grad: bool = False, out=None):
+    """Elementwise SwiGLU backward (fp32) of y = w * SiLU(clamp(gate)) * clamp(up).
+
+    Returns (dgate, dup, weight_grad or None); weights is [rows] or None.
+    `out` may pass preallocated (dgate, dup, weight_grad) tensors.
+    """
+    _same(gate, up, dy)
+    if gate.dtype != torch.float32:
+        raise TypeError("act_bwd takes fp32 gate/up/dy")
+    if gate.shape != up.shape or gate.shape != dy.shape:
+        raise ValueError("gate, up and dy must have the same shape")
+    cols = gate.shape[-1]
+    rows = math.prod(gate.shape[:-1])
+    g2 = gate.reshape(rows, cols).contiguous()
+    u2 = up.reshape(rows, cols).contiguous()
+    d2 = dy.reshape(rows, cols).contiguous()
+    w = None
+    if weights is not None:
+        _same(gate, weights)
+        if weights.numel() != rows:
+            raise ValueError(f"weights must have {rows} elements")
+        w = weights.reshape(rows).contiguous()
+    dev = gate.device
+    if out is not None:
+        dg, du, wg = out
+    else:
+        dg = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+        du = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+        wg = torch.empty(rows, dtype=torch.float32, device=dev) if weight_grad else None
+    check("swiglu_act_bwd", lib().swiglu_act_bwd(rows, cols, _p(g2), _p(u2), _p(d2), _p(w), float(clamp_limit),
+                                                 _p(dg), _p(du), _p(wg), _stream(gate)))
+    return dg.reshape(gate.shape), du.reshape(gate.shape), wg
+
+
 def probe_read2(a: torch.Tensor, b: torch.Tensor, sink: torch.Tensor) -> None:
     """Pure read of two equally sized buffers (cold-read floor measurement)."""
     nbytes = a.numel() * a.element_size()

@@ -17,6 +17,7 @@ import numpy as np
 
 STREAM_X, STREAM_WG, STREAM_WU, STREAM_DH = 1, 2, 3, 4
 STREAM_GATE, STREAM_UP, STREAM_SPECIALS = 5, 6, 7
+STREAM_DY, STREAM_ROWW = 8, 9
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -138,3 +139,13 @@ def act_quant_f32(rows: int, cols: int, seed: int = 0, specials: bool = True) ->
         inject_specials(gate, seed, STREAM_SPECIALS)
         inject_specials(up, seed, STREAM_SPECIALS + 100)
     return dict(gate=gate, up=up)
+
+
+def act_bwd_f32(rows: int, cols: int, seed: int = 0, specials: bool = False) -> dict:
+    """Elementwise backward case: gate, up ~ N(0, 2) and dy ~ N(0, 1) fp32,
+    per-row weights ~ U(0, 1); optional specials in gate and up as in
+    act_quant_f32."""
+    d = act_quant_f32(rows, cols, seed, specials)
+    d["dy"] = normal_f32((rows, cols), 1.0, seed, STREAM_DY)
+    d["weights"] = rng(seed, STREAM_ROWW).uniform(0.0, 1.0, rows).astype(np.float32)
+    return d

@@ -138,6 +138,19 @@ def test_act_quant_validation(L):
     assert f(4, 64, A, A, math.inf, MIS, A, None, None, None) == EALIGN
 
 
+def test_act_bwd_validation(L):
+    f = L.swiglu_act_bwd
+    assert f(4, 62, A, A, A, None, 7.0, A, A, None, None) == ESHAPE    # cols % 4
+    assert f(-1, 64, A, A, A, None, 7.0, A, A, None, None) == ESHAPE
+    assert f(4, 64, A, A, A, None, 0.0, A, A, None, None) == EARG
+    assert f(4, 64, A, A, A, None, math.nan, A, A, None, None) == EARG
+    assert f(4, 64, A, None, A, None, 7.0, A, A, None, None) == ENULL
+    assert f(4, 64, A, A, A, None, 7.0, A, None, None, None) == ENULL
+    assert f(4, 64, A, A, MIS, None, math.inf, A, A, None, None) == EALIGN
+    assert f(4, 64, A, A, A, 0x10002, math.inf, A, A, None, None) == EALIGN   # weights: 4-byte aligned
+    assert f(0, 64, None, None, None, None, 7.0, None, None, None, None) == OK
+
+
 def test_probe_validation(L):
     assert L.swiglu_probe_read2(A, A, 17, A, None) == ESHAPE
     assert L.swiglu_probe_read2(None, A, 32, A, None) == ENULL

@@ -417,3 +417,79 @@ def test_probe_read2_runs():
     sink = torch.zeros(4096, dtype=torch.int32, device=DEV)
     S.probe_read2(a, b, sink)
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------- act_bwd (next f1)
+
+ULP32 = 2.0 ** -24
+TINY32 = 2.0 ** -149
+
+
+def check_act_bwd(d, L, use_w, what):
+    g, u, dy = d["gate"], d["up"], d["dy"]
+    w = d["weights"] if use_w else None
+    dg, du, wg = S.act_bwd(dev_f32(g), dev_f32(u), dev_f32(dy), L,
+                           weights=None if w is None else dev_f32(w), weight_grad=True)
+    torch.cuda.synchronize()
+    dg, du, wg = dg.cpu().numpy().astype(np.float64), du.cpu().numpy().astype(np.float64), wg.cpu().numpy().astype(np.float64)
+    rg, ru, rw = oracle.act_bwd(g.astype(np.float64), u.astype(np.float64), dy.astype(np.float64), L,
+                                None if w is None else w.astype(np.float64))
+    # Term magnitudes the device error is bounded by (8 ulps of each, plus
+    # the final rounding): |w dy u'| s (1 + |g'| (1 - s)) for dg, |w dy g' s| for du.
+    gc = oracle.clamp_nan_preserving(g.astype(np.float64), L)
+    uc = oracle.clamp_nan_preserving(u.astype(np.float64), L)
+    wv = np.ones(g.shape[0]) if w is None else w.astype(np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        s = oracle.sigmoid(gc)
+        tg = np.abs(wv[:, None] * dy) * np.abs(uc) * s * (1.0 + np.abs(gc) * (1.0 - s))
+        tu = np.abs(wv[:, None] * dy * gc * s)
+        tw = np.sum(np.abs(dy * gc * s * uc), axis=1)
+    for name, y, r, t in (("dgate", dg, rg, tg), ("dup", du, ru, tu), ("weight_grad", wg, rw, tw)):
+        nan_y, nan_r = np.isnan(y), np.isnan(r)
+        assert np.array_equal(nan_y, nan_r), f"{what} {name}: NaN pattern differs ({np.count_nonzero(nan_y != nan_r)})"
+        inf_r = np.isinf(r)
+        assert np.array_equal(y[inf_r], r[inf_r]) and not np.any(np.isinf(y[~inf_r & ~nan_r])), f"{what} {name}: inf"
+        fin = ~nan_r & ~inf_r
+        if not fin.any():
+            continue
+        with np.errstate(invalid="ignore"):
+            # A term that is NaN (e.g. a NaN up value beside a clamped gate,
+            # whose gradient is exactly 0 on both sides) bounds nothing.
+            bound = np.nan_to_num(8 * ULP32 * t[fin], nan=np.inf) + ULP32 * np.abs(r[fin]) + TINY32
+        ratio = np.where(y[fin] == r[fin], 0.0, np.abs(y[fin] - r[fin]) / bound)
+        assert ratio.max() <= 1.0, f"{what} {name}: worst error {ratio.max():.3f} of the bound"
+        log(f"{what} {name}: worst error {ratio.max():.4f} of the bound")
+    # Clamped positions carry exactly zero gradient.
+    if np.isfinite(L):
+        assert np.all(dg[np.abs(g) > L] == 0.0) and np.all(du[np.abs(u) > L] == 0.0)
+
+
+@pytest.mark.parametrize("L,use_w", [(math.inf, True), (0.5, False), (7.0, True)])
+def test_act_bwd_full_4001x3584(L, use_w):
+    d = synth.act_bwd_f32(4001, 3584, seed=0)
+    check_act_bwd(d, L, use_w, f"act_bwd 4001x3584 L={L} weights={use_w}")
+
+
+@pytest.mark.parametrize("shape", [(1, 4), (3, 12), (7, 2052), (65, 260), (5, 0)])
+def test_act_bwd_ragged_and_specials(shape):
+    rows, cols = shape
+    d = synth.act_bwd_f32(rows, cols, seed=3, specials=True)
+    for L in (math.inf, 1.5):
+        check_act_bwd(d, L, True, f"act_bwd {shape} L={L} specials")
+
+
+def test_act_bwd_without_weight_grad_and_empty():
+    d = synth.act_bwd_f32(8, 64, seed=4)
+    dg, du, wg = S.act_bwd(dev_f32(d["gate"]), dev_f32(d["up"]), dev_f32(d["dy"]), 7.0)
+    torch.cuda.synchronize()
+    assert wg is None
+    rg, ru, _ = oracle.act_bwd(d["gate"].astype(np.float64), d["up"].astype(np.float64),
+                               d["dy"].astype(np.float64), 7.0)
+    # (elementwise error bounds are checked in check_act_bwd; here the
+    # normwise error shows the outputs are right without a weight_grad)
+    assert oracle.normwise_rel_err(dg.cpu().numpy(), rg) < 1e-6
+    assert oracle.normwise_rel_err(du.cpu().numpy(), ru) < 1e-6
+    e = torch.empty((0, 16), dtype=torch.float32, device=DEV)
+    dg, du, wg = S.act_bwd(e, e, e, math.inf, weight_grad=True)
+    torch.cuda.synchronize()
+    assert dg.shape == (0, 16) and wg.shape == (0,)
