@@ -32,6 +32,8 @@ Readings taken where the pages are silent (each is also listed in the design doc):
   * silu(z) = z * sigmoid(z) evaluated by IEEE rules: silu(+inf)=+inf,
     silu(-inf)=NaN (-inf * 0), silu(NaN)=NaN;
   * the derivative of silu is the closed form s * (1 + z * (1 - s)), s = sigmoid(z);
+  * the GeGLU variant replaces SiLU by the tanh GELU,
+    z / 2 * (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)));
   * the clamp is symmetric [-L, L] on both gate and up, applied before the
     activation, NaN passing through; the clamp count is the number of gate and
     up values with |v| > L (NaN not counted);
@@ -44,6 +46,8 @@ Readings taken where the pages are silent (each is also listed in the design doc):
     rounds past 448 becomes NaN.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -76,6 +80,29 @@ def silu_grad(z):
         return s * (1.0 + z * (1.0 - s))
 
 
+# GELU with the tanh approximation, the activation of the GeGLU variant:
+# [Liger-937] feature pitch (the Liger MLP modules fuse swiglu and geglu) and
+# [TRT-17693] (the cublasLt epilogue implements tanh-approximated GELU,
+# gelu_tanh).  Reading: the standard tanh form
+#   gelu_tanh(z) = z / 2 * (1 + tanh(sqrt(2 / pi) * (z + 0.044715 z^3))),
+# and the gated form h = gelu_tanh(g) * u, in place of SiLU.
+GELU_C = math.sqrt(2.0 / math.pi)
+GELU_A = 0.044715
+
+
+def gelu_tanh(z):
+    """z / 2 * (1 + tanh(y)), y = sqrt(2/pi) (z + 0.044715 z^3), evaluated as
+    z * sigma(2 y): the identity (1 + tanh y) / 2 = 1 / (1 + e^-2y) is exact,
+    and this form keeps full relative precision in the negative tail, where
+    1 + tanh(y) cancels."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        return z * sigmoid(2.0 * GELU_C * (z + GELU_A * z * z * z))
+
+
+ACTIVATIONS = {"silu": silu, "gelu_tanh": gelu_tanh}
+
+
 # ---------------------------------------------------------------------------
 # Forward.  [Liger-1383] Background and [Liger-937] TL;DR approach 3:
 # h = SiLU(x Wg^T) * (x Wu^T), weights in nn.Linear [N, K] layout
@@ -88,6 +115,17 @@ def gate_up(x, wg, wu):
     wg = np.asarray(wg, np.float64)
     wu = np.asarray(wu, np.float64)
     return x @ wg.T, x @ wu.T
+
+
+def glu_fwd(x, wg, wu, act="silu"):
+    """h = act(x Wg^T) * (x Wu^T) with act in ACTIVATIONS."""
+    g, u = gate_up(x, wg, wu)
+    return ACTIVATIONS[act](g) * u
+
+
+def glu_fwd_rows(x, wg, wu, rows, act="silu"):
+    """Rows `rows` of glu_fwd, computed one row at a time."""
+    return glu_fwd(np.asarray(x, np.float64)[rows], wg, wu, act)
 
 
 def swiglu_fwd(x, wg, wu):

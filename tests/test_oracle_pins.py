@@ -57,6 +57,60 @@ def test_silu_special_values():
     assert np.isnan(oracle.silu(np.nan))
 
 
+# ------------------------------------------------------------- GELU (tanh)
+
+def test_gelu_tanh_matches_torch_library_routine():
+    """torch's gelu(approximate='tanh') in float64 (a library routine) on a grid
+    that spans the saturated tails."""
+    z = np.concatenate([np.linspace(-40, 40, 40001), [0.0, -0.0, 1e-300, -1e-300, 5e5, -5e5]])
+    ref = torch.nn.functional.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    got = oracle.gelu_tanh(z)
+    # torch evaluates 1 + tanh(y), which cancels in the negative tail, so the
+    # comparison is absolute there (relative to |z|) and relative elsewhere.
+    np.testing.assert_array_less(np.abs(got - ref), 1e-15 * np.maximum(1.0, np.abs(z)) + 1e-300)
+    big = np.abs(ref) > 1e-3
+    np.testing.assert_allclose(got[big], ref[big], rtol=1e-13)
+
+
+def test_gelu_tanh_negative_tail_relative_accuracy():
+    # In the tail the value is z * e^(2y) / (1 + e^(2y)); with log-space
+    # arithmetic: log|h| = log|z| + 2y - log1p(e^(2y)).
+    z = np.linspace(-30.0, -4.0, 261)
+    y = oracle.GELU_C * (z + oracle.GELU_A * z ** 3)
+    logh = np.log(-z) + 2 * y - np.log1p(np.exp(2 * y))
+    got = oracle.gelu_tanh(z)
+    ok = logh > -700
+    np.testing.assert_allclose(np.log(-got[ok]), logh[ok], rtol=1e-13, atol=1e-13)
+
+
+def test_gelu_tanh_identity_limits_and_erf_distance():
+    z = np.linspace(-20, 20, 4001)
+    # gelu(z) - gelu(-z) = z (tanh is odd), as for SiLU.
+    np.testing.assert_allclose(oracle.gelu_tanh(z) - oracle.gelu_tanh(-z), z, rtol=1e-14, atol=1e-14)
+    # The tanh form stays within 5e-4 of the erf GELU z * Phi(z) everywhere.
+    from scipy.special import erf
+    exact = 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+    assert np.max(np.abs(oracle.gelu_tanh(z) - exact)) < 5e-4
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+    v = oracle.gelu_tanh(np.array([np.inf, -np.inf, np.nan]))
+    assert v[0] == np.inf and np.isnan(v[1]) and np.isnan(v[2])
+
+
+def test_geglu_forward_orientation_with_selection_weights():
+    """The gated forward with GELU: g and u pick known x columns."""
+    M, N, K = 4, 6, 9
+    rs = np.random.default_rng(5)
+    x = rs.standard_normal((M, K)) * 2
+    pg = rs.integers(0, K, N)
+    pu = rs.integers(0, K, N)
+    wg = np.zeros((N, K)); wg[np.arange(N), pg] = 1.0
+    wu = np.zeros((N, K)); wu[np.arange(N), pu] = 1.0
+    h = oracle.glu_fwd(x, wg, wu, "gelu_tanh")
+    ref = torch.nn.functional.gelu(torch.from_numpy(x[:, pg]), approximate="tanh").numpy() * x[:, pu]
+    np.testing.assert_allclose(h, ref, rtol=1e-14, atol=0)
+    np.testing.assert_array_equal(oracle.glu_fwd(x, wg, wu, "silu"), oracle.swiglu_fwd(x, wg, wu))
+
+
 # ------------------------------------------------------------------- forward
 
 def test_forward_orientation_with_selection_weights():
