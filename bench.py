@@ -22,6 +22,7 @@ The same run also measures, after the timed region and outside `value`:
            (4 rotated copies): clamp 0.5 without weights, and per-row weights
            with the weight gradient and no clamp, in GB/s;
   fp32     the IEEE-fp32 fused forward at M=4001, K=2048, N=3584, in TFLOP/s;
+  geglu    the GeGLU forward (GELU-tanh gate) at the headline shape, in TFLOP/s;
   cpu_baseline  the fp64 oracle on a row sample of the headline workload,
            timed on the host cores.
 """
@@ -297,6 +298,8 @@ def main():
         "bwd_ms": round((t_step - t_fwd) * 1e3, 4),
         "bwd_tflops_8MNK": round(8.0 * M4 * N4 * K4 / (t_step - t_fwd) / 1e12, 2),
     }
+    if not args.no_extra:
+        result["geglu"] = geglu_leg(torch, S, x, wg, wu, h)
     del h
     sample_inputs = {k: d4[k] for k in ("x", "wg", "wu", "dh")}
     del x, wg, wu, dh, ws
@@ -370,6 +373,25 @@ def act_quant_leg(torch, S, synth, np, dev):
     del G, U, outs
     torch.cuda.empty_cache()
     return res
+
+
+def geglu_leg(torch, S, x, wg, wu, h):
+    """GeGLU forward (GELU-tanh gate) on the headline inputs."""
+    for _ in range(3):
+        S.fwd(x, wg, wu, out=h, act="gelu_tanh")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    e0.record()
+    for _ in range(n):
+        S.fwd(x, wg, wu, out=h, act="gelu_tanh")
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / n
+    tf = 4.0 * M4 * N4 * K4 / t / 1e12
+    log(f"geglu fwd {M4}x{N4}x{K4}: {t * 1e3:.3f} ms, {tf:.1f} TFLOP/s")
+    return {"M": M4, "N": N4, "K": K4, "ms": round(t * 1e3, 4), "TFLOPs": round(tf, 2),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def act_bwd_leg(torch, S, synth, np, dev):

@@ -71,6 +71,25 @@ int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K,
                const void* x, const void* wg, const void* wu, void* h,
                void* stream);
 
+/* Gate activations of the gated forward. */
+enum swiglu_act {
+  SWIGLU_ACT_SILU = 0,       /* SwiGLU: SiLU(z) = z * sigmoid(z)                    */
+  SWIGLU_ACT_GELU_TANH = 1   /* GeGLU: z / 2 * (1 + tanh(sqrt(2/pi)(z + 0.044715 z^3))) */
+};
+
+/* The gated forward with a choice of gate activation:
+ *   h = act(x Wg^T) * (x Wu^T)
+ * act = SWIGLU_ACT_SILU is swiglu_fwd; SWIGLU_ACT_GELU_TANH is the GeGLU
+ * variant ("Another MLP implementation along with multiplier support",
+ * Liger-Kernel issue 937, feature pitch: the MLP modules fuse swiglu and
+ * geglu; "VisualGen MLP: cublasLt GELU-tanh epilogue for the unquantized
+ * bf16 path", TensorRT-LLM PR 17693: the tanh-approximated GELU applied to
+ * the fp32 accumulator).  Arguments, layouts and errors as swiglu_fwd; an
+ * unknown act gives SWIGLU_ERR_ARG. */
+int swiglu_fwd_act(int act, int dtype, int64_t M, int64_t N, int64_t K,
+                   const void* x, const void* wg, const void* wu, void* h,
+                   void* stream);
+
 /* Bytes of device workspace swiglu_bwd needs for these sizes (0 on invalid
  * sizes).  It holds [dg | du], its transpose, x^T and the transposed weight
  * pair. */
@@ -113,6 +132,11 @@ int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K,
 int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K,
                     const void* x, const void* wg, const void* wu, void* h,
                     void* stream);
+
+/* swiglu_gemv_fwd with a choice of gate activation (see swiglu_fwd_act). */
+int swiglu_gemv_fwd_act(int act, int64_t M, int64_t N, int64_t K,
+                        const void* x, const void* wg, const void* wu, void* h,
+                        void* stream);
 
 /* Elementwise SwiGLU with FP8 block quantisation, one pass ("quant: add
  * SwiGLU forward/backward VMI kernels", TileKernels-PTO PR 20, sections

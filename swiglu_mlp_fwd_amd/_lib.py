@@ -13,6 +13,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswiglu.s
 
 SWIGLU_F32 = 0
 SWIGLU_BF16 = 1
+SWIGLU_ACT_SILU = 0
+SWIGLU_ACT_GELU_TANH = 1
 
 _c_i64 = ctypes.c_int64
 _c_ptr = ctypes.c_void_p
@@ -20,10 +22,14 @@ _c_ptr = ctypes.c_void_p
 # name -> (restype, argtypes), in the order of include/swiglu.h
 SIGNATURES = {
     "swiglu_fwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+    "swiglu_fwd_act": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr,
+                                      _c_ptr, _c_ptr]),
     "swiglu_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _c_i64, _c_i64, _c_i64]),
     "swiglu_bwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                   _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr]),
     "swiglu_gemv_fwd": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+    "swiglu_gemv_fwd_act": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                           _c_ptr]),
     "swiglu_act_quant": (ctypes.c_int, [_c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr,
                                         _c_ptr, _c_ptr, _c_ptr]),
     "swiglu_act_bwd": (ctypes.c_int, [_c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_float,

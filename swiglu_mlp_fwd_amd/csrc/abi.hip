@@ -33,8 +33,9 @@ hipError_t fill_zero(int dtype, void* p, int64_t rows, int64_t cols, hipStream_t
 
 extern "C" {
 
-int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
-               const void* wu, void* h, void* stream) {
+int swiglu_fwd_act(int act, int dtype, int64_t M, int64_t N, int64_t K, const void* x,
+                   const void* wg, const void* wu, void* h, void* stream) {
+  if (act != SWIGLU_ACT_SILU && act != SWIGLU_ACT_GELU_TANH) return SWIGLU_ERR_ARG;
   int st = swg::validate_fwd(dtype, M, N, K, x, wg, wu, h);
   if (st != SWIGLU_OK || M == 0 || N == 0) return st;
   swg::GemmArgs a{};
@@ -43,7 +44,12 @@ int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const 
   a.arows = (int)M; a.brows = (int)N;
   a.m = (int)M; a.n = (int)N; a.r = (int)K;
   a.out0 = h; a.ldo = N; a.ncols = (int)N;
-  return hip_status(swg::launch_fwd_dual(as_dt(dtype), a, as_stream(stream)));
+  return hip_status(swg::launch_fwd_dual(as_dt(dtype), static_cast<swg::Act>(act), a, as_stream(stream)));
+}
+
+int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+               const void* wu, void* h, void* stream) {
+  return swiglu_fwd_act(SWIGLU_ACT_SILU, dtype, M, N, K, x, wg, wu, h, stream);
 }
 
 size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K) {
@@ -133,11 +139,18 @@ int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const 
   return hip_status(swg::launch_gemm_store(dt, b3, s));
 }
 
-int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
-                    const void* wu, void* h, void* stream) {
+int swiglu_gemv_fwd_act(int act, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                        const void* wu, void* h, void* stream) {
+  if (act != SWIGLU_ACT_SILU && act != SWIGLU_ACT_GELU_TANH) return SWIGLU_ERR_ARG;
   int st = swg::validate_gemv(M, N, K, x, wg, wu, h);
   if (st != SWIGLU_OK || M == 0 || N == 0) return st;
-  return hip_status(swg::launch_gemv((int)M, (int)N, (int)K, x, wg, wu, h, as_stream(stream)));
+  return hip_status(swg::launch_gemv(static_cast<swg::Act>(act), (int)M, (int)N, (int)K, x, wg, wu,
+                                     h, as_stream(stream)));
+}
+
+int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                    const void* wu, void* h, void* stream) {
+  return swiglu_gemv_fwd_act(SWIGLU_ACT_SILU, M, N, K, x, wg, wu, h, stream);
 }
 
 int swiglu_act_quant(int64_t rows, int64_t cols, const float* gate, const float* up,

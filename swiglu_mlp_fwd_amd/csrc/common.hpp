@@ -106,6 +106,29 @@ __device__ __forceinline__ void sigmoid_silu_bf16out(float z, float& s, float& s
   silu = z * s;
 }
 
+// GELU with the tanh approximation, as z * sigma(2 y) with
+// y = sqrt(2/pi) (z + 0.044715 z^3), i.e. 2 y = z (c1 + c3 z^2): the identity
+// (1 + tanh y) / 2 = sigma(2 y) is exact and avoids the cancellation of
+// 1 + tanh(y) for negative z.  Infinities and NaN follow IEEE as for SiLU.
+constexpr float kGeluC1 = 1.5957691216057308f;      // 2 sqrt(2 / pi)
+constexpr float kGeluC3 = 0.07135481627260025f;     // 2 sqrt(2 / pi) * 0.044715
+
+// Accurate form (fp32 outputs).
+__device__ __forceinline__ float gelu_tanh_f32(float z) {
+  const float t = z * __builtin_fmaf(kGeluC3, z * z, kGeluC1);
+  float s, c;
+  sigmoid_pair_f32(t, s, c);
+  return z * s;
+}
+
+// Short form for results rounded to bf16 right after (hardware exp2 and
+// reciprocal, as sigmoid_silu_bf16out).
+__device__ __forceinline__ float gelu_tanh_bf16out(float z) {
+  const float t = z * __builtin_fmaf(kGeluC3, z * z, kGeluC1);
+  constexpr float kL2e = 1.44269504088896340736f;
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t * kL2e));
+}
+
 __device__ __forceinline__ float silu_f32(float z) {
   float s, silu;
   sigmoid_silu_f32(z, s, silu);

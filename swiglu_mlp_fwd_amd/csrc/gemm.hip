@@ -11,6 +11,7 @@
 // and SwiGLU in one kernel so g and u never reach memory).
 //
 // Epilogues:
+//   kGeGLU   the same with GELU (tanh form) in place of SiLU;
 //   kSwiGLU  h = SiLU(g) * u, one rounding to the output type (the activation
 //            is applied to the fp32 accumulator, as in the numerics follow-up
 //            of "VisualGen MLP: cublasLt GELU-tanh epilogue for the
@@ -58,7 +59,27 @@ struct Tile {
   static constexpr int kTM = kWM / 32, kTN = kWN / 32;       // 32x32 MFMA tiles per wave
 };
 
-enum class Epi { kSwiGLU, kDSwiGLU, kStore };
+enum class Epi { kSwiGLU, kGeGLU, kDSwiGLU, kStore };
+
+// Gated forward epilogues: h = act(g) * u.
+constexpr bool gated_fwd(Epi e) { return e == Epi::kSwiGLU || e == Epi::kGeGLU; }
+
+template <Epi E>
+__device__ __forceinline__ float act_accurate(float g) {
+  if constexpr (E == Epi::kGeGLU) return gelu_tanh_f32(g);
+  else return silu_f32(g);
+}
+
+template <Epi E>
+__device__ __forceinline__ float act_bf16out(float g) {
+  if constexpr (E == Epi::kGeGLU) {
+    return gelu_tanh_bf16out(g);
+  } else {
+    float s, sl;
+    sigmoid_silu_bf16out(g, s, sl);
+    return sl;
+  }
+}
 
 // Physical 16-byte chunk of logical chunk c in LDS row r.  gfx950 serves a
 // 128-bit LDS read for 16 lanes per cycle across 64 four-byte banks, i.e.
@@ -118,12 +139,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[NB][
         const int row = tm * kBM + wm * kWM + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
         const int col = tn * kBN + wn * kWN + j * 32 + r32;
         if (row >= p.m || col >= p.n) continue;
-        if constexpr (E == Epi::kSwiGLU) {
+        if constexpr (gated_fwd(E)) {
           if (col >= p.ncols) continue;
           const float g = acc[0][i][j][e];
           const float u = acc[NB - 1][i][j][e];
           T* out = static_cast<T*>(p.out0);
-          out[(int64_t)row * p.ldo + col] = cvt_out<T>(silu_f32(g) * u);
+          out[(int64_t)row * p.ldo + col] = cvt_out<T>(act_accurate<E>(g) * u);
         } else if constexpr (E == Epi::kDSwiGLU) {
           const float g = acc[0][i][j][e];
           const float u = acc[NB - 1][i][j][e];
@@ -391,11 +412,9 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
       for (int e = 0; e < 16; ++e) {
         const int row = wm * kWM + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
         const int col = wn * kWN + j * 32 + r32;
-        if constexpr (E == Epi::kSwiGLU) {
+        if constexpr (gated_fwd(E)) {
           const float g = acc[0][i][j][e], u = acc[NB - 1][i][j][e];
-          float sg, sl;
-          sigmoid_silu_bf16out(g, sg, sl);
-          *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(sl * u);
+          *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(act_bf16out<E>(g) * u);
         } else if constexpr (E == Epi::kDSwiGLU) {
           const float g = acc[0][i][j][e], u = acc[NB - 1][i][j][e];
           const float dh = dhv[i][j][e];
@@ -423,7 +442,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
     const int r = c / kCPR, ch = c % kCPR;
     const int grow = grow0 + r, gcol = gcol0 + ch * 8;
     if (grow >= p.m || gcol >= p.n) continue;
-    if constexpr (E == Epi::kSwiGLU) {
+    if constexpr (gated_fwd(E)) {
       if (gcol >= p.ncols) continue;
       put(static_cast<bf16*>(p.out0) + (int64_t)grow * p.ldo + gcol,
           *reinterpret_cast<const u32x4*>(at(0, r, ch * 8)), min(8, p.ncols - gcol));
@@ -845,7 +864,10 @@ using TileSingle = Tile<256, 256, 4, 2>; // 8 waves, 64 x 128 per wave
 
 }  // namespace
 
-hipError_t launch_fwd_dual(Dt dt, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_fwd_dual(Dt dt, Act act, const GemmArgs& a, hipStream_t s) {
+  if (act == Act::kGeluTanh)
+    return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kGeGLU, 2, TileDual, 8, 2, 2>(a, s)
+                           : launch<float, Epi::kGeGLU, 2, TileDual>(a, s);
   return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2, 2>(a, s)
                          : launch<float, Epi::kSwiGLU, 2, TileDual>(a, s);
 }

@@ -31,8 +31,9 @@ struct GemmArgs {
 };
 
 enum class Dt { kF32 = 0, kBF16 = 1 };
+enum class Act { kSilu = 0, kGeluTanh = 1 };   // the gate activation of the gated forward
 
-hipError_t launch_fwd_dual(Dt dt, const GemmArgs& a, hipStream_t s);      // h = silu(g) * u
+hipError_t launch_fwd_dual(Dt dt, Act act, const GemmArgs& a, hipStream_t s);  // h = act(g) * u
 hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s);   // D = [dg | du]
 hipError_t launch_gemm_store(Dt dt, const GemmArgs& a, hipStream_t s);    // C = A B^T
 
@@ -41,7 +42,7 @@ hipError_t launch_transpose(Dt dt, const void* in, int64_t ld_in, int rows, int 
                             void* out, int64_t ld_out, int col_off, int rows_pad,
                             hipStream_t s);
 
-hipError_t launch_gemv(int M, int N, int K, const void* x, const void* wg, const void* wu,
+hipError_t launch_gemv(Act act, int M, int N, int K, const void* x, const void* wg, const void* wu,
                        void* h, hipStream_t s);
 
 hipError_t launch_act_bwd(int64_t rows, int64_t cols, const float* gate, const float* up,

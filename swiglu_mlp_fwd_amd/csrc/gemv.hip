@@ -25,7 +25,7 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kColsPerBlock = 16;  // 8 waves x 2 half-waves
 
-template <int M>
+template <int M, Act A>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__ x,
                                                         const bf16* __restrict__ wg,
                                                         const bf16* __restrict__ wu,
@@ -73,36 +73,46 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__
   }
   if (hl == 0) {
 #pragma unroll
-    for (int m = 0; m < M; ++m) h[(int64_t)m * N + col] = to_bf16(silu_f32(ag[m]) * au[m]);
+    for (int m = 0; m < M; ++m) {
+      const float a = (A == Act::kGeluTanh) ? gelu_tanh_f32(ag[m]) : silu_f32(ag[m]);
+      h[(int64_t)m * N + col] = to_bf16(a * au[m]);
+    }
   }
 }
 
-template <int M>
+template <int M, Act A>
 hipError_t launch_m(int N, int K, const void* x, const void* wg, const void* wu, void* h,
                     hipStream_t s) {
   const unsigned blocks = (unsigned)((N + kColsPerBlock - 1) / kColsPerBlock);
   const size_t lds = (size_t)M * K * 2;
-  hipLaunchKernelGGL(gemv_kernel<M>, dim3(blocks), dim3(kThreads), lds, s,
+  hipLaunchKernelGGL((gemv_kernel<M, A>), dim3(blocks), dim3(kThreads), lds, s,
                      static_cast<const bf16*>(x), static_cast<const bf16*>(wg),
                      static_cast<const bf16*>(wu), static_cast<bf16*>(h), N, K);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemv(int M, int N, int K, const void* x, const void* wg, const void* wu, void* h,
-                       hipStream_t s) {
+template <Act A>
+hipError_t launch_act(int M, int N, int K, const void* x, const void* wg, const void* wu, void* h,
+                      hipStream_t s) {
   switch (M) {
-    case 1: return launch_m<1>(N, K, x, wg, wu, h, s);
-    case 2: return launch_m<2>(N, K, x, wg, wu, h, s);
-    case 3: return launch_m<3>(N, K, x, wg, wu, h, s);
-    case 4: return launch_m<4>(N, K, x, wg, wu, h, s);
-    case 5: return launch_m<5>(N, K, x, wg, wu, h, s);
-    case 6: return launch_m<6>(N, K, x, wg, wu, h, s);
-    case 7: return launch_m<7>(N, K, x, wg, wu, h, s);
-    case 8: return launch_m<8>(N, K, x, wg, wu, h, s);
+    case 1: return launch_m<1, A>(N, K, x, wg, wu, h, s);
+    case 2: return launch_m<2, A>(N, K, x, wg, wu, h, s);
+    case 3: return launch_m<3, A>(N, K, x, wg, wu, h, s);
+    case 4: return launch_m<4, A>(N, K, x, wg, wu, h, s);
+    case 5: return launch_m<5, A>(N, K, x, wg, wu, h, s);
+    case 6: return launch_m<6, A>(N, K, x, wg, wu, h, s);
+    case 7: return launch_m<7, A>(N, K, x, wg, wu, h, s);
+    case 8: return launch_m<8, A>(N, K, x, wg, wu, h, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+}  // namespace
+
+hipError_t launch_gemv(Act act, int M, int N, int K, const void* x, const void* wg, const void* wu,
+                       void* h, hipStream_t s) {
+  return act == Act::kGeluTanh ? launch_act<Act::kGeluTanh>(M, N, K, x, wg, wu, h, s)
+                               : launch_act<Act::kSilu>(M, N, K, x, wg, wu, h, s);
 }
 
 }  // namespace swg

@@ -16,9 +16,17 @@ import math
 
 import torch
 
-from ._lib import SWIGLU_BF16, SWIGLU_F32, check, lib
+from ._lib import SWIGLU_ACT_GELU_TANH, SWIGLU_ACT_SILU, SWIGLU_BF16, SWIGLU_F32, check, lib
 
 _DT = {torch.bfloat16: SWIGLU_BF16, torch.float32: SWIGLU_F32}
+_ACT = {"silu": SWIGLU_ACT_SILU, "gelu_tanh": SWIGLU_ACT_GELU_TANH}
+
+
+def _act_code(act: str) -> int:
+    try:
+        return _ACT[act]
+    except KeyError:
+        raise ValueError(f"act must be one of {sorted(_ACT)}, got {act!r}") from None
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -47,8 +55,10 @@ def _p(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """h = SiLU(x Wg^T) * (x Wu^T).  x [..., K], Wg/Wu [N, K] -> h [..., N]."""
+def fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor | None = None,
+        act: str = "silu") -> torch.Tensor:
+    """h = act(x Wg^T) * (x Wu^T), act "silu" (SwiGLU) or "gelu_tanh" (GeGLU).
+    x [..., K], Wg/Wu [N, K] -> h [..., N]."""
     _same(x, wg, wu)
     lead, K = x.shape[:-1], x.shape[-1]
     N = wg.shape[0]
@@ -60,7 +70,8 @@ def fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor |
     h = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
     if out is not None and (out.shape != (M, N) or out.dtype != x.dtype or not out.is_contiguous()):
         raise ValueError("out must be a contiguous [M, N] tensor of the input dtype")
-    check("swiglu_fwd", lib().swiglu_fwd(_dtype_code(x), M, N, K, _p(x2), _p(wg), _p(wu), _p(h), _stream(x)))
+    check("swiglu_fwd_act", lib().swiglu_fwd_act(_act_code(act), _dtype_code(x), M, N, K, _p(x2), _p(wg), _p(wu),
+                                                 _p(h), _stream(x)))
     return h.reshape(*lead, N)
 
 
@@ -95,7 +106,8 @@ def bwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, dh: torch.Tensor,
     return dx.reshape(*lead, K), dwg, dwu
 
 
-def gemv_fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+def gemv_fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor | None = None,
+             act: str = "silu") -> torch.Tensor:
     """Decode forward for M <= 8 tokens (bf16): same result as fwd."""
     _same(x, wg, wu)
     if x.dtype != torch.bfloat16:
@@ -106,7 +118,8 @@ def gemv_fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Ten
     x2 = x.reshape(M, K).contiguous()
     wg, wu = wg.contiguous(), wu.contiguous()
     h = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
-    check("swiglu_gemv_fwd", lib().swiglu_gemv_fwd(M, N, K, _p(x2), _p(wg), _p(wu), _p(h), _stream(x)))
+    check("swiglu_gemv_fwd_act", lib().swiglu_gemv_fwd_act(_act_code(act), M, N, K, _p(x2), _p(wg), _p(wu), _p(h),
+                                                           _stream(x)))
     return h.reshape(*lead, N)
 
 

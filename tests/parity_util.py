@@ -69,14 +69,15 @@ def assert_within(y, r, bound, what: str):
     return ratio
 
 
-def fwd_bound(x, wg, wu, dtype: str, rows=None):
-    """Elementwise error bound of the fused forward h = silu(g) u on the given rows.
+def fwd_bound(x, wg, wu, dtype: str, rows=None, act: str = "silu"):
+    """Elementwise error bound of the fused forward h = act(g) u on the given rows.
 
     g and u carry the fp32 accumulation error E = gamma_{K+1} sum|x||w| (the +1
     covers the rounding of fp32 products on the fp32 path; bf16 products are
-    exact); it reaches h through |silu'(g)| |u| E_g + |silu(g)| E_u (|silu'| is
-    below 1.1).  The activation itself is good to a few fp32 ulps (8 u |h|
-    covers it) and the output rounding adds 2^-9 |h| (bf16) or u |h| (fp32).
+    exact); it reaches h through |act'(g)| |u| E_g + |act(g)| E_u (|silu'| is
+    below 1.1, |gelu_tanh'| below 1.13).  The activation itself is good to a
+    few fp32 ulps (8 u |h| covers it) and the output rounding adds 2^-9 |h|
+    (bf16) or u |h| (fp32).
     """
     xr = x if rows is None else x[rows]
     K = x.shape[1]
@@ -84,8 +85,9 @@ def fwd_bound(x, wg, wu, dtype: str, rows=None):
     Sg = np.abs(xr) @ np.abs(wg).T
     Su = np.abs(xr) @ np.abs(wu).T
     G = gamma(K + 1)
-    h = oracle.silu(g) * u
-    prop = 1.1 * np.abs(u) * G * Sg + np.abs(oracle.silu(g)) * G * Su + G * Sg * G * Su
+    a = oracle.ACTIVATIONS[act](g)
+    h = a * u
+    prop = 1.2 * np.abs(u) * G * Sg + np.abs(a) * G * Su + G * Sg * G * Su
     out = BF16_HALF_ULP if dtype == "bf16" else U32
     return h, 2 * (prop + (8 * U32 + out) * np.abs(h)) + 1e-30
 

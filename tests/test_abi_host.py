@@ -138,6 +138,17 @@ def test_act_quant_validation(L):
     assert f(4, 64, A, A, math.inf, MIS, A, None, None, None) == EALIGN
 
 
+def test_activation_choice_validation(L):
+    # An unknown activation is rejected before anything else.
+    assert L.swiglu_fwd_act(2, 1, 4, 4, 8, A, A, A, A, None) == EARG
+    assert L.swiglu_fwd_act(-1, 1, 4, 4, 8, A, A, A, A, None) == EARG
+    assert L.swiglu_gemv_fwd_act(7, 1, 4, 8, A, A, A, A, None) == EARG
+    # Known activations reach the usual validation.
+    assert L.swiglu_fwd_act(1, 1, 4, 4, 12, A, A, A, A, None) == ESHAPE     # K % 8
+    assert L.swiglu_gemv_fwd_act(1, 9, 4, 8, A, A, A, A, None) == ESHAPE    # M <= 8
+    assert L.swiglu_fwd_act(1, 1, 0, 4, 8, None, None, None, None, None) == OK
+
+
 def test_act_bwd_validation(L):
     f = L.swiglu_act_bwd
     assert f(4, 62, A, A, A, None, 7.0, A, A, None, None) == ESHAPE    # cols % 4

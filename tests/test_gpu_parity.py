@@ -44,13 +44,16 @@ def to_f64(d: dict) -> dict:
 
 # ----------------------------------------------------------------- forward
 
-def check_fwd(d, dtype, rows=None, what="fwd", via="dual"):
+def check_fwd(d, dtype, rows=None, what="fwd", via="dual", act="silu"):
     t = to_dev(d)
     f = to_f64(d)
-    h = S.fwd(t["x"], t["wg"], t["wu"]) if via == "dual" else S.gemv_fwd(t["x"], t["wg"], t["wu"])
+    if via == "dual":
+        h = S.fwd(t["x"], t["wg"], t["wu"], act=act)
+    else:
+        h = S.gemv_fwd(t["x"], t["wg"], t["wu"], act=act)
     torch.cuda.synchronize()
     y = host_f64(h if rows is None else h[torch.as_tensor(rows, device=DEV)])
-    ref, bound = fwd_bound(f["x"], f["wg"], f["wu"], dtype, rows)
+    ref, bound = fwd_bound(f["x"], f["wg"], f["wu"], dtype, rows, act)
     e, c = assert_gates(y, ref, dtype, what)
     ratio = assert_within(y, ref, bound, what)
     log(f"{what}: normwise {e:.3e} cosine {c:.7f} bound-ratio {ratio:.3f}")
@@ -493,3 +496,34 @@ def test_act_bwd_without_weight_grad_and_empty():
     dg, du, wg = S.act_bwd(e, e, e, math.inf, weight_grad=True)
     torch.cuda.synchronize()
     assert dg.shape == (0, 16) and wg.shape == (0,)
+
+
+# ------------------------------------------------------ GeGLU (next f2)
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(300, 520, 264), (1, 1, 8), (129, 127, 72)])
+def test_geglu_fwd_ragged(dt, shape):
+    M, N, K = shape
+    d = synth.train_bf16(M, N, K, seed=6, with_dh=False) if dt == "bf16" else synth.gemm_fp32(M, N, K, seed=6)
+    check_fwd(d, dt, what=f"geglu fwd {dt} {shape}", act="gelu_tanh")
+
+
+def test_geglu_fwd_fp32_full_4001x3584x2048():
+    d = synth.gemm_fp32(4001, 3584, 2048, seed=0)
+    check_fwd(d, "f32", what="geglu fwd fp32 4001x3584x2048", act="gelu_tanh")
+
+
+def test_geglu_fwd_bf16_full_8192x14336x4096_sampled():
+    M, N, K = 8192, 14336, 4096
+    d = synth.train_bf16(M, N, K, seed=0, with_dh=False)
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(2).integers(0, M, 62)]))
+    check_fwd(d, "bf16", rows=rows, what="geglu fwd bf16 8192x14336x4096 (sampled rows)", act="gelu_tanh")
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("NK", [(6912, 1536), (257, 520)])
+def test_geglu_gemv(M, NK):
+    N, K = NK
+    d = synth.decode_bf16(M, N, K, seed=7)
+    check_fwd(d, "bf16", what=f"geglu gemv M={M} N={N} K={K}", via="gemv", act="gelu_tanh")
