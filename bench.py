@@ -58,7 +58,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target host time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the decode / act_quant / fp32 legs")
-    p.add_argument("--only", choices=["step", "fwd", "decode", "act_quant", "act_bwd", "fp32", "traffic"], default=None,
+    p.add_argument("--only", choices=["step", "fwd", "decode", "act_quant", "act_bwd", "fp32", "fwd_fp8", "traffic"], default=None,
                    help="profiling aid: run one leg only (no JSON contract); 'traffic' runs the headline "
                         "forward and a 1 GiB copy (the counter calibration) for the --pmc runs")
     p.add_argument("--digest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
@@ -232,6 +232,10 @@ def main():
         torch.cuda.synchronize()
         log("done")
         return
+    if args.only == "fwd_fp8":
+        fwd_fp8_leg(torch, S, x, wg, wu)
+        log("done")
+        return
     if args.only in ("decode", "act_quant", "act_bwd", "fp32"):
         del x, wg, wu, dh, ws, h
         torch.cuda.empty_cache()
@@ -300,6 +304,7 @@ def main():
     }
     if not args.no_extra:
         result["geglu"] = geglu_leg(torch, S, x, wg, wu, h)
+        result["fwd_fp8"] = fwd_fp8_leg(torch, S, x, wg, wu)
     del h
     sample_inputs = {k: d4[k] for k in ("x", "wg", "wu", "dh")}
     del x, wg, wu, dh, ws
@@ -392,6 +397,33 @@ def geglu_leg(torch, S, x, wg, wu, h):
     log(f"geglu fwd {M4}x{N4}x{K4}: {t * 1e3:.3f} ms, {tf:.1f} TFLOP/s")
     return {"M": M4, "N": N4, "K": K4, "ms": round(t * 1e3, 4), "TFLOPs": round(tf, 2),
             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def fwd_fp8_leg(torch, S, x, wg, wu):
+    """Forward with the 1x32 E4M3 quantisation of h fused into the epilogue,
+    on the headline inputs (no h_out): h leaves as 1-byte codes + scales."""
+    dev = x.device
+    q = torch.empty((M4, N4), dtype=torch.uint8, device=dev)
+    sc = torch.empty((M4, N4 // 32), dtype=torch.uint8, device=dev)
+    res = {"M": M4, "N": N4, "K": K4}
+    for act in ("silu", "gelu_tanh"):
+        for _ in range(3):
+            S.fwd_fp8(x, wg, wu, act=act, out=(q, sc, None))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 10
+        e0.record()
+        for _ in range(n):
+            S.fwd_fp8(x, wg, wu, act=act, out=(q, sc, None))
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / n
+        tf = 4.0 * M4 * N4 * K4 / t / 1e12
+        log(f"fwd_fp8 {act} {M4}x{N4}x{K4}: {t * 1e3:.3f} ms, {tf:.1f} TFLOP/s")
+        res[act] = {"ms": round(t * 1e3, 4), "TFLOPs": round(tf, 2),
+                    "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del q, sc
+    return res
 
 
 def act_bwd_leg(torch, S, synth, np, dev):

@@ -138,6 +138,28 @@ int swiglu_gemv_fwd_act(int act, int64_t M, int64_t N, int64_t K,
                         const void* x, const void* wg, const void* wu, void* h,
                         void* stream);
 
+/* Gated forward with the FP8 block quantisation fused into the dual GEMM's
+ * epilogue, so h leaves the kernel as the down projection's FP8 operand
+ * (the quantisation of swiglu_act_quant below applied to the h of
+ * swiglu_fwd_act; "quant: add SwiGLU forward/backward VMI kernels",
+ * TileKernels-PTO PR 20, implementation notes, for the 1x32 UE8M0 / E4M3
+ * format):
+ *   h = act(x Wg^T) * (x Wu^T), fp32 accumulation; act(g) to a few fp32
+ *       ulps, then the fp32 product;
+ *   per row and 1x32 block of N: amax, E, scale byte and E4M3FN codes
+ *   exactly as in swiglu_act_quant (no clamp).
+ *
+ *   act        SWIGLU_ACT_SILU or SWIGLU_ACT_GELU_TANH
+ *   x, wg, wu  bf16 [M, K], [N, K], [N, K] (16-byte aligned)
+ *   q          [M, N] uint8 E4M3FN codes (output, 16-byte aligned)
+ *   scale      [M, N / 32] uint8 UE8M0 bytes (output)
+ *   h_out      NULL, or [M, N] fp32 receiving the h that was quantised
+ * Layout rules: bf16 only, K % 8 == 0, N % 32 == 0, K <= 2^22 - 64.
+ * Returns SWIGLU_ERR_SHAPE / _ALIGN / _NULL / _UNSUPPORTED as swiglu_fwd. */
+int swiglu_fwd_fp8(int act, int64_t M, int64_t N, int64_t K,
+                   const void* x, const void* wg, const void* wu,
+                   uint8_t* q, uint8_t* scale, float* h_out, void* stream);
+
 /* Elementwise SwiGLU with FP8 block quantisation, one pass ("quant: add
  * SwiGLU forward/backward VMI kernels", TileKernels-PTO PR 20, sections
  * overview and implementation notes):

@@ -52,6 +52,21 @@ int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const 
   return swiglu_fwd_act(SWIGLU_ACT_SILU, dtype, M, N, K, x, wg, wu, h, stream);
 }
 
+int swiglu_fwd_fp8(int act, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                   const void* wu, uint8_t* q, uint8_t* scale, float* h_out, void* stream) {
+  if (act != SWIGLU_ACT_SILU && act != SWIGLU_ACT_GELU_TANH) return SWIGLU_ERR_ARG;
+  int st = swg::validate_fwd_fp8(M, N, K, x, wg, wu, q, scale, h_out);
+  if (st != SWIGLU_OK || M == 0 || N == 0) return st;
+  swg::GemmArgs a{};
+  a.a = x; a.b0 = wg; a.b1 = wu;
+  a.lda = K; a.ldb = K;
+  a.arows = (int)M; a.brows = (int)N;
+  a.m = (int)M; a.n = (int)N; a.r = (int)K;
+  a.out0 = q; a.ldo = N; a.ncols = (int)N;
+  a.q_scale = scale; a.q_h = h_out;
+  return hip_status(swg::launch_fwd_dual_fp8(static_cast<swg::Act>(act), a, as_stream(stream)));
+}
+
 size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K) {
   if (swg::check_dtype(dtype) != SWIGLU_OK || swg::check_dims(M, N, K) != SWIGLU_OK) return 0;
   return swg::bwd_layout(dtype, M, N, K).total;

@@ -40,6 +40,7 @@
 #include <mutex>
 
 #include "common.hpp"
+#include "fp8.hpp"
 #include "gemm.hpp"
 
 namespace swg {
@@ -59,10 +60,12 @@ struct Tile {
   static constexpr int kTM = kWM / 32, kTN = kWN / 32;       // 32x32 MFMA tiles per wave
 };
 
-enum class Epi { kSwiGLU, kGeGLU, kDSwiGLU, kStore };
+enum class Epi { kSwiGLU, kGeGLU, kDSwiGLU, kStore, kSwiGLUq, kGeGLUq };
 
 // Gated forward epilogues: h = act(g) * u.
 constexpr bool gated_fwd(Epi e) { return e == Epi::kSwiGLU || e == Epi::kGeGLU; }
+// ... with h quantised to E4M3 per 1x32 block (UE8M0 scales).
+constexpr bool gated_q(Epi e) { return e == Epi::kSwiGLUq || e == Epi::kGeGLUq; }
 
 template <Epi E>
 __device__ __forceinline__ float act_accurate(float g) {
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(GemmArgs p) {
 template <Epi E, class TL>
 struct EpiLds {
   static constexpr int kCols = TL::kBN;                      // columns per output tile
-  static constexpr int kPitch = kCols * 2 + 32;              // bytes per staged row
+  static constexpr int kPitch = kCols * (gated_q(E) ? 4 : 2) + 32;   // bytes per staged row
   static constexpr int kRegion = TL::kBM * kPitch;
   static constexpr int kBytes = (E == Epi::kDSwiGLU ? 2 : 1) * kRegion;
 };
@@ -502,6 +505,74 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
         if (n < p.n && m < p.ldt)
           *reinterpret_cast<u32x4*>(dt + ((int64_t)reg * p.du_off + n) * p.ldt + m) = u32x4{a[0], a[1], b[0], b[1]};
       }
+    }
+  }
+}
+
+// FP8-output epilogue of the gated forward ("quant: add SwiGLU
+// forward/backward VMI kernels", TileKernels-PTO PR 20, implementation
+// notes: 1x32 blocks along the hidden dimension, packed UE8M0 scale, E4M3
+// without saturation): h = act(g) * u from the fp32 accumulators (the
+// activation to a few fp32 ulps, then the fp32 product) is staged in LDS
+// as fp32; each thread then takes whole 1x32 blocks of a row, forms the
+// block amax (NaN ignored), the UE8M0 exponent and the 32 codes, and writes
+// 32 code bytes, one scale byte and optionally the fp32 h.  Needs n % 32 == 0
+// (whole blocks), row strides that keep 16-byte alignment.
+template <Epi E, int NB, class TL>
+__device__ __forceinline__ void store_tile_fp8(const GemmArgs& p, f32x16 (&acc)[NB][TL::kTM][TL::kTN],
+                                               int tm, int tn, int wm, int wn, int lane, int tid,
+                                               char* lds) {
+  constexpr int kBM = TL::kBM, kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
+  constexpr int kThreads = TL::kThreads;
+  constexpr int kCols = EpiLds<E, TL>::kCols;
+  constexpr int kPitch = EpiLds<E, TL>::kPitch;
+  const int r32 = lane & 31, half = lane >> 5;
+  const int grow0 = tm * kBM, gcol0 = tn * kCols;
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = wm * kWM + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+        const int col = wn * kWN + j * 32 + r32;
+        const float g = acc[0][i][j][e], u = acc[NB - 1][i][j][e];
+        const float h = (E == Epi::kGeGLUq ? gelu_tanh_f32(g) : silu_f32(g)) * u;
+        *reinterpret_cast<float*>(lds + row * kPitch + col * 4) = h;
+      }
+  __syncthreads();
+  // Block q: row q % kBM, 32-column block q / kBM, so 16 lanes read 16 rows
+  // at one column offset.
+  constexpr int kBlocks = kBM * (kCols / 32);
+  uint8_t* codes = static_cast<uint8_t*>(p.out0);
+  uint8_t* scale = static_cast<uint8_t*>(p.q_scale);
+  const int64_t lds_ = p.n / 32;
+  for (int qb = tid; qb < kBlocks; qb += kThreads) {
+    const int r = qb % kBM, b = qb / kBM;
+    const int grow = grow0 + r, gcol = gcol0 + b * 32;
+    if (grow >= p.m || gcol >= p.n) continue;
+    f32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const f32x4*>(lds + r * kPitch + b * 128 + k * 16);
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) amax = fmaxf(amax, fabsf(v[k][t]));   // maxNum: NaN ignored
+    const int ex = block_exponent(amax);
+    const float sc = ldexpf(1.0f, -ex);
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w[k] = e4m3_pair(v[k][0], v[k][1], sc) | (e4m3_pair(v[k][2], v[k][3], sc) << 16);
+    u32x4* dst = reinterpret_cast<u32x4*>(codes + (int64_t)grow * p.ldo + gcol);
+    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    scale[(int64_t)grow * lds_ + gcol / 32] = (uint8_t)(ex + 127);
+    if (p.q_h != nullptr) {
+      f32x4* hd = reinterpret_cast<f32x4*>(p.q_h + (int64_t)grow * p.ldo + gcol);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) hd[k] = v[k];
     }
   }
 }
@@ -807,17 +878,24 @@ void gemm_dma_kernel(GemmArgs p) {
   if constexpr (E == Epi::kDSwiGLU && sizeof(T) == 2) dh_prefetch<TL>(p, tm, tn, tid, dpre);
   if (nk > 0) kstep(nk - 1, false);
 
-  if constexpr (sizeof(T) == 2) {
-    const bool vec = (p.ldo % 8 == 0) && (E != Epi::kDSwiGLU || p.du_off % 8 == 0);
-    if (vec) {
-      wait_vmcnt<0>();                      // no DMA still landing in the ring
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // own LDS reads done
-      barrier_no_fence();                   // every wave is done with the ring
-      store_tile_lds<E, NB, TL>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes, dpre);
-      return;
+  if constexpr (gated_q(E)) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    barrier_no_fence();
+    store_tile_fp8<E, NB, TL>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes);
+  } else {
+    if constexpr (sizeof(T) == 2) {
+      const bool vec = (p.ldo % 8 == 0) && (E != Epi::kDSwiGLU || p.du_off % 8 == 0);
+      if (vec) {
+        wait_vmcnt<0>();                      // no DMA still landing in the ring
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // own LDS reads done
+        barrier_no_fence();                   // every wave is done with the ring
+        store_tile_lds<E, NB, TL>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes, dpre);
+        return;
+      }
     }
+    store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
   }
-  store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
 }
 
 template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL = 0>
@@ -870,6 +948,11 @@ hipError_t launch_fwd_dual(Dt dt, Act act, const GemmArgs& a, hipStream_t s) {
                            : launch<float, Epi::kGeGLU, 2, TileDual>(a, s);
   return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2, 2>(a, s)
                          : launch<float, Epi::kSwiGLU, 2, TileDual>(a, s);
+}
+
+hipError_t launch_fwd_dual_fp8(Act act, const GemmArgs& a, hipStream_t s) {
+  return act == Act::kGeluTanh ? launch_dma<bf16, Epi::kGeGLUq, 2, TileDual, 8, 2, 2>(a, s)
+                               : launch_dma<bf16, Epi::kSwiGLUq, 2, TileDual, 8, 2, 2>(a, s);
 }
 
 hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s) {

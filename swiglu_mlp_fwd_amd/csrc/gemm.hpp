@@ -28,12 +28,18 @@ struct GemmArgs {
   int du_off;          // dswiglu: du is written at column du_off + n of out0
   int64_t ldt;         // dswiglu with out1 != null: out1 receives out0 transposed,
                        // [2 du_off, ldt] with rows m in [arows, ldt) zero (bf16 only)
+  // FP8-output forward: E4M3 codes in out0 (row stride ldo bytes), UE8M0
+  // scale bytes in q_scale (row stride n / 32), optional fp32 h in q_h (ldo).
+  void* q_scale;
+  float* q_h;
 };
 
 enum class Dt { kF32 = 0, kBF16 = 1 };
 enum class Act { kSilu = 0, kGeluTanh = 1 };   // the gate activation of the gated forward
 
 hipError_t launch_fwd_dual(Dt dt, Act act, const GemmArgs& a, hipStream_t s);  // h = act(g) * u
+// bf16 inputs, h = act(g) * u quantised per 1x32 block (n % 32 == 0).
+hipError_t launch_fwd_dual_fp8(Act act, const GemmArgs& a, hipStream_t s);
 hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s);   // D = [dg | du]
 hipError_t launch_gemm_store(Dt dt, const GemmArgs& a, hipStream_t s);    // C = A B^T
 

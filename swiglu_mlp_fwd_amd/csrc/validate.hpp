@@ -132,6 +132,25 @@ inline int validate_gemv(int64_t M, int64_t N, int64_t K, const void* x, const v
   return SWIGLU_OK;
 }
 
+inline int validate_fwd_fp8(int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                            const void* wu, const void* q, const void* scale, const void* h_out) {
+  int st;
+  if ((st = check_dims(M, N, K))) return st;
+  if (K % chunk_elems(SWIGLU_BF16) != 0 || N % 32 != 0) return SWIGLU_ERR_SHAPE;
+  if (!tiles_fit(M, N)) return SWIGLU_ERR_UNSUPPORTED;
+  if (K > kMaxLdBf16) return SWIGLU_ERR_UNSUPPORTED;
+  if (h_out != nullptr && !aligned(h_out, 16)) return SWIGLU_ERR_ALIGN;
+  if (M == 0 || N == 0) return SWIGLU_OK;
+  if ((st = check_ptr(q))) return st;
+  if (scale == nullptr) return SWIGLU_ERR_NULL;
+  if (K > 0) {
+    if ((st = check_ptr(x))) return st;
+    if ((st = check_ptr(wg))) return st;
+    if ((st = check_ptr(wu))) return st;
+  }
+  return SWIGLU_OK;
+}
+
 inline int validate_act_quant(int64_t rows, int64_t cols, const float* gate, const float* up,
                               float L, const void* q, const void* scale, const void* count,
                               const void* hout) {

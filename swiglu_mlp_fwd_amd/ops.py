@@ -75,6 +75,35 @@ def fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor |
     return h.reshape(*lead, N)
 
 
+def fwd_fp8(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, act: str = "silu", h_out: bool = False,
+            out=None):
+    """Gated forward with h quantised in the GEMM epilogue (bf16 inputs).
+
+    Returns (q uint8 [M, N] E4M3FN codes, scale uint8 [M, N/32] UE8M0 bytes,
+    h fp32 [M, N] or None); `out` may pass preallocated (q, scale, h).
+    """
+    _same(x, wg, wu)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("fwd_fp8 takes bf16 inputs")
+    lead, K = x.shape[:-1], x.shape[-1]
+    N = wg.shape[0]
+    if wg.shape != (N, K) or wu.shape != (N, K):
+        raise ValueError(f"weights must be [N, K] = [{N}, {K}], got {tuple(wg.shape)}, {tuple(wu.shape)}")
+    M = math.prod(lead)
+    x2 = x.reshape(M, K).contiguous()
+    wg, wu = wg.contiguous(), wu.contiguous()
+    dev = x.device
+    if out is not None:
+        q, scale, h = out
+    else:
+        q = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        scale = torch.empty((M, N // 32 if N % 32 == 0 else 0), dtype=torch.uint8, device=dev)
+        h = torch.empty((M, N), dtype=torch.float32, device=dev) if h_out else None
+    check("swiglu_fwd_fp8", lib().swiglu_fwd_fp8(_act_code(act), M, N, K, _p(x2), _p(wg), _p(wu), _p(q), _p(scale),
+                                                 _p(h), _stream(x)))
+    return q, scale, h
+
+
 def bwd_workspace_bytes(dtype: torch.dtype, M: int, N: int, K: int) -> int:
     return int(lib().swiglu_bwd_workspace_bytes(_DT[dtype], M, N, K))
 

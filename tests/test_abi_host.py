@@ -149,6 +149,22 @@ def test_activation_choice_validation(L):
     assert L.swiglu_fwd_act(1, 1, 0, 4, 8, None, None, None, None, None) == OK
 
 
+def test_fwd_fp8_validation(L):
+    f = L.swiglu_fwd_fp8
+    assert f(2, 4, 64, 8, A, A, A, A, A, None, None) == EARG           # unknown activation
+    assert f(0, 4, 48, 8, A, A, A, A, A, None, None) == ESHAPE         # N % 32
+    assert f(0, 4, 64, 12, A, A, A, A, A, None, None) == ESHAPE        # bf16: K % 8
+    assert f(0, -1, 64, 8, A, A, A, A, A, None, None) == ESHAPE
+    assert f(0, 4, 64, (1 << 22), A, A, A, A, A, None, None) == EUNSUP
+    assert f(1, 4, 64, 8, A, A, A, None, A, None, None) == ENULL       # q
+    assert f(1, 4, 64, 8, A, A, A, A, None, None, None) == ENULL       # scale
+    assert f(1, 4, 64, 8, A, A, A, MIS, A, None, None) == EALIGN       # q: 16-byte rows
+    assert f(1, 4, 64, 8, A, A, A, A, A, MIS, None) == EALIGN          # h_out
+    assert f(0, 4, 64, 8, A, MIS, A, A, A, None, None) == EALIGN
+    assert f(0, 0, 64, 8, None, None, None, None, None, None, None) == OK
+    assert f(0, 4, 0, 8, None, None, None, None, None, None, None) == OK
+
+
 def test_act_bwd_validation(L):
     f = L.swiglu_act_bwd
     assert f(4, 62, A, A, A, None, 7.0, A, A, None, None) == ESHAPE    # cols % 4

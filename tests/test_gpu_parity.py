@@ -527,3 +527,88 @@ def test_geglu_gemv(M, NK):
     N, K = NK
     d = synth.decode_bf16(M, N, K, seed=7)
     check_fwd(d, "bf16", what=f"geglu gemv M={M} N={N} K={K}", via="gemv", act="gelu_tanh")
+
+
+# ---------------------------------------- FP8-output forward (next f4)
+
+def check_fwd_fp8(d, rows=None, act="silu", what="fwd_fp8"):
+    """q, scale from the fused epilogue against the oracle.
+
+    1. h (fp32, returned beside q) is within the forward's bound of the exact
+       act(g) u;
+    2. same precision: the oracle's 1x32 quantiser applied to that h gives
+       exactly the device's scale bytes and codes;
+    3. from the inputs: each scale byte lies between the UE8M0 bytes of the
+       smallest and largest block amax that h's bound allows, and each code,
+       at the device's scale, between the codes of h - bound and h + bound
+       (encoding is monotone in the value, so this is the whole set of codes
+       that some h within the bound would produce).
+    """
+    t = to_dev(d)
+    f = to_f64(d)
+    q, sc, h = S.fwd_fp8(t["x"], t["wg"], t["wu"], act=act, h_out=True)
+    q2, sc2, none = S.fwd_fp8(t["x"], t["wg"], t["wu"], act=act, h_out=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(q, q2) and torch.equal(sc, sc2), f"{what}: output differs without h_out"
+    sel = slice(None) if rows is None else torch.as_tensor(rows, device=DEV)
+    q, sc, h = q[sel].cpu().numpy(), sc[sel].cpu().numpy(), h[sel].cpu().numpy()
+    ref, bound = fwd_bound(f["x"], f["wg"], f["wu"], "f32", rows, act)
+    e, c = assert_gates(h.astype(np.float64), ref, "f32", what)
+    ratio = assert_within(h.astype(np.float64), ref, bound, what + " h")
+    # 2. same precision
+    oq, os_ = oracle.quantize_1x32(h)
+    assert np.array_equal(sc, os_), f"{what}: scales differ from oracle(quantise(device h))"
+    assert np.array_equal(q, oq), f"{what}: codes differ from oracle(quantise(device h))"
+    # 3. from the inputs
+    R, N = ref.shape
+    lo_mag = np.maximum(np.abs(ref) - bound, 0.0).reshape(R, N // 32, 32).max(axis=2)
+    hi_mag = (np.abs(ref) + bound).reshape(R, N // 32, 32).max(axis=2)
+    E_lo, E_hi = oracle.ue8m0_exponent(lo_mag), oracle.ue8m0_exponent(hi_mag)
+    E = sc.astype(np.int64) - 127
+    assert np.all((E_lo <= E) & (E <= E_hi)), f"{what}: a scale byte no h within the bound gives"
+    Ee = np.repeat(E, 32, axis=1)
+    o_lo = oracle.e4m3_ordinal(oracle.e4m3_encode(np.ldexp(ref - bound, -Ee)))
+    o_hi = oracle.e4m3_ordinal(oracle.e4m3_encode(np.ldexp(ref + bound, -Ee)))
+    o = oracle.e4m3_ordinal(q)
+    bad = (o < o_lo) | (o > o_hi)
+    assert not bad.any(), f"{what}: {int(bad.sum())} codes outside the bound's interval"
+    exact_q, exact_s = oracle.quantize_1x32(ref.astype(np.float32))
+    log(f"{what}: h normwise {e:.3e} cosine {c:.7f} bound-ratio {ratio:.3f}; vs exact h: "
+        f"scale diffs {int((sc != exact_s).sum())}, code diffs {int((q != exact_q).sum())} of {q.size}")
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
+@pytest.mark.parametrize("shape", [(300, 544, 264), (1, 32, 8), (129, 96, 72), (37, 1056, 1032)])
+def test_fwd_fp8_ragged(act, shape):
+    M, N, K = shape
+    d = synth.train_bf16(M, N, K, seed=8, with_dh=False)
+    check_fwd_fp8(d, act=act, what=f"fwd_fp8 {act} {shape}")
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
+def test_fwd_fp8_full_8192x14336x4096_sampled(act):
+    M, N, K = 8192, 14336, 4096
+    d = synth.train_bf16(M, N, K, seed=0, with_dh=False)
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(4).integers(0, M, 30)]))
+    check_fwd_fp8(d, rows=rows, act=act, what=f"fwd_fp8 {act} 8192x14336x4096 (sampled rows)")
+    torch.cuda.empty_cache()
+
+
+def test_fwd_fp8_k_zero_and_empty():
+    x = torch.empty((5, 0), dtype=torch.bfloat16, device=DEV)
+    w = torch.empty((64, 0), dtype=torch.bfloat16, device=DEV)
+    q = torch.full((5, 64), 0x55, dtype=torch.uint8, device=DEV)
+    s = torch.full((5, 2), 0x55, dtype=torch.uint8, device=DEV)
+    h = torch.full((5, 64), 3.0, dtype=torch.float32, device=DEV)
+    S.fwd_fp8(x, w, w, out=(q, s, h))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(q).item() == 0          # E4M3 +0
+    assert torch.count_nonzero(s).item() == 0          # amax 0 -> E = -127 -> byte 0
+    assert torch.count_nonzero(h).item() == 0
+    e = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    w = torch.empty((64, 64), dtype=torch.bfloat16, device=DEV)
+    qq, ss, hh = S.fwd_fp8(e, w, w, h_out=True)
+    torch.cuda.synchronize()
+    assert qq.shape == (0, 64) and ss.shape == (0, 2) and hh.shape == (0, 64)
+
