@@ -368,11 +368,11 @@ def act_quant_leg(torch, S, synth, np, dev):
              torch.empty(1, dtype=torch.int64, device=dev), None) for _ in range(copies)]
     nbytes = 2 * R * C * 4 + R * C + R * C // 32
     res = {"rows": R, "cols": C, "copies": copies, "bytes_per_call": nbytes, "unit": "GB/s"}
-    for L in (math.inf, 7.0):
-        calls = [(lambda i=i: S.act_quant(G[i], U[i], L, out=outs[i])) for _ in range(4) for i in range(copies)]
+    for act, L in (("silu", math.inf), ("silu", 7.0), ("gelu_tanh", math.inf)):
+        calls = [(lambda i=i: S.act_quant(G[i], U[i], L, out=outs[i], act=act)) for _ in range(4) for i in range(copies)]
         t, _ = graph_time_per_call(torch, calls)
         gbs = nbytes / t / 1e9
-        key = "no_clamp" if math.isinf(L) else "clamp_7"
+        key = ("no_clamp" if math.isinf(L) else "clamp_7") + ("" if act == "silu" else "_geglu")
         res[key] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
         log(f"act_quant {R}x{C} {key}: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
     del G, U, outs

@@ -185,6 +185,15 @@ int swiglu_act_quant(int64_t rows, int64_t cols,
                      uint8_t* q, uint8_t* scale, uint64_t* clamp_count,
                      float* h_out, void* stream);
 
+/* swiglu_act_quant with a choice of gate activation: SWIGLU_ACT_SILU, or
+ * SWIGLU_ACT_GELU_TANH for h = GELU_tanh(g') * u' (the GeGLU variant; see
+ * swiglu_fwd_act).  Either way h is formed from the fp32 inputs and rounded
+ * to fp32 once before the quantisation; unknown act: SWIGLU_ERR_ARG. */
+int swiglu_act_quant_act(int act, int64_t rows, int64_t cols,
+                         const float* gate, const float* up, float clamp_limit,
+                         uint8_t* q, uint8_t* scale, uint64_t* clamp_count,
+                         float* h_out, void* stream);
+
 /* Elementwise SwiGLU backward on materialised gate/up ("quant: add SwiGLU
  * forward/backward VMI kernels", TileKernels-PTO PR 20: the performance
  * section's backward table -- gate/up given, optional clamp, optional routing

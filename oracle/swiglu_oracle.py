@@ -283,12 +283,13 @@ def clamp_nan_preserving(v, limit):
     return np.where(v > limit, limit, np.where(v < -limit, -limit, v))
 
 
-def act_quant(gate, up, clamp_limit=np.inf):
+def act_quant(gate, up, clamp_limit=np.inf, act="silu"):
     """Returns (q [rows, cols] uint8 E4M3 codes, scale [rows, cols/32] uint8,
     clamp_count int, h32 [rows, cols] float32).
 
     h32 is the activation rounded to fp32, the precision in which both sides
-    take the scale and code decisions.
+    take the scale and code decisions.  act selects the gate activation
+    (ACTIVATIONS: "silu", or "gelu_tanh" for the GeGLU variant).
     """
     gate = np.asarray(gate, np.float64)
     up = np.asarray(up, np.float64)
@@ -300,7 +301,7 @@ def act_quant(gate, up, clamp_limit=np.inf):
     g = clamp_nan_preserving(gate, L)
     u = clamp_nan_preserving(up, L)
     with np.errstate(over="ignore", invalid="ignore"):
-        h64 = silu(g) * u
+        h64 = ACTIVATIONS[act](g) * u
         h32 = h64.astype(np.float32)
     q, scale = quantize_1x32(h32)
     return q, scale, count, h32

@@ -168,14 +168,22 @@ int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K, const void* x, const void* 
   return swiglu_gemv_fwd_act(SWIGLU_ACT_SILU, M, N, K, x, wg, wu, h, stream);
 }
 
-int swiglu_act_quant(int64_t rows, int64_t cols, const float* gate, const float* up,
-                     float clamp_limit, uint8_t* q, uint8_t* scale, uint64_t* clamp_count,
-                     float* h_out, void* stream) {
+int swiglu_act_quant_act(int act, int64_t rows, int64_t cols, const float* gate, const float* up,
+                         float clamp_limit, uint8_t* q, uint8_t* scale, uint64_t* clamp_count,
+                         float* h_out, void* stream) {
+  if (act != SWIGLU_ACT_SILU && act != SWIGLU_ACT_GELU_TANH) return SWIGLU_ERR_ARG;
   int st = swg::validate_act_quant(rows, cols, gate, up, clamp_limit, q, scale, clamp_count, h_out);
   if (st != SWIGLU_OK) return st;
   const bool clamp = !isinf(clamp_limit);
-  return hip_status(swg::launch_act_quant(rows, cols, gate, up, clamp_limit, clamp, q, scale,
-                                          clamp_count, h_out, as_stream(stream)));
+  return hip_status(swg::launch_act_quant(static_cast<swg::Act>(act), rows, cols, gate, up, clamp_limit,
+                                          clamp, q, scale, clamp_count, h_out, as_stream(stream)));
+}
+
+int swiglu_act_quant(int64_t rows, int64_t cols, const float* gate, const float* up,
+                     float clamp_limit, uint8_t* q, uint8_t* scale, uint64_t* clamp_count,
+                     float* h_out, void* stream) {
+  return swiglu_act_quant_act(SWIGLU_ACT_SILU, rows, cols, gate, up, clamp_limit, q, scale,
+                              clamp_count, h_out, stream);
 }
 
 int swiglu_act_bwd(int64_t rows, int64_t cols, const float* gate, const float* up, const float* dy,

@@ -1,4 +1,5 @@
-// Elementwise SwiGLU with FP8 (E4M3FN) 1x32 block quantisation, one pass.
+// Elementwise SwiGLU (or GeGLU) with FP8 (E4M3FN) 1x32 block quantisation,
+// one pass.
 //
 // "quant: add SwiGLU forward/backward VMI kernels" (TileKernels-PTO PR 20),
 // overview and implementation notes: an optional clamp with a count of the
@@ -26,7 +27,7 @@ constexpr int kThreads = 256;
 constexpr int kMaxBlocks = 1024;   // 4 workgroups per CU, grid-stride beyond
 constexpr int kUnroll = 4;         // chunks per lane per loop iteration
 
-template <bool kClamp, bool kCount, bool kHout>
+template <Act A, bool kClamp, bool kCount, bool kHout>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float* __restrict__ gate,
                                                              const float* __restrict__ up, float L,
                                                              uint8_t* __restrict__ q,
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float* __rest
         g = cg ? copysignf(L, g) : g;
         u = cu ? copysignf(L, u) : u;
       }
-      h[e] = swiglu_value(g, u);
+      h[e] = A == Act::kGeluTanh ? gelu_value(g, u) : swiglu_value(g, u);
       amax = fmaxf(amax, fabsf(h[e]));  // maxNum: NaN operands are ignored
     }
     amax = fmaxf(amax, __shfl_xor(amax, 1));
@@ -110,17 +111,35 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float* __rest
 
 __global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
 
-template <bool kClamp, bool kCount, bool kHout>
+template <Act A, bool kClamp, bool kCount, bool kHout>
 void launch_aq(unsigned grid, const float* gate, const float* up, float L, uint8_t* q,
                uint8_t* scale, uint64_t* count, float* hout, int64_t nchunks, hipStream_t s) {
-  hipLaunchKernelGGL((act_quant_kernel<kClamp, kCount, kHout>), dim3(grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((act_quant_kernel<A, kClamp, kCount, kHout>), dim3(grid), dim3(kThreads), 0, s,
                      gate, up, L, q, scale, reinterpret_cast<unsigned long long*>(count), hout,
                      nchunks);
 }
 
+template <Act A>
+void launch_aq_variant(bool counting, bool clamp, unsigned grid, const float* gate, const float* up,
+                       float limit, uint8_t* q, uint8_t* scale, uint64_t* count, float* hout,
+                       int64_t nchunks, hipStream_t s) {
+  // The count is only accumulated when a counter is given and the clamp is
+  // on; with the clamp off no value can exceed the limit.
+  if (counting) {
+    if (hout) launch_aq<A, true, true, true>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
+    else launch_aq<A, true, true, false>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
+  } else if (clamp) {
+    if (hout) launch_aq<A, true, false, true>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
+    else launch_aq<A, true, false, false>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
+  } else {
+    if (hout) launch_aq<A, false, false, true>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
+    else launch_aq<A, false, false, false>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_act_quant(int64_t rows, int64_t cols, const float* gate, const float* up,
+hipError_t launch_act_quant(Act act, int64_t rows, int64_t cols, const float* gate, const float* up,
                             float limit, bool clamp, uint8_t* q, uint8_t* scale, uint64_t* count,
                             float* hout, hipStream_t s) {
   const bool counting = clamp && count != nullptr;
@@ -133,18 +152,10 @@ hipError_t launch_act_quant(int64_t rows, int64_t cols, const float* gate, const
   if (nchunks > 0) {
     int64_t want = (nchunks + kThreads - 1) / kThreads;
     const unsigned grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);
-    // The count is only accumulated when a counter is given and the clamp is
-    // on; with the clamp off no value can exceed the limit.
-    if (counting) {
-      if (hout) launch_aq<true, true, true>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
-      else launch_aq<true, true, false>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
-    } else if (clamp) {
-      if (hout) launch_aq<true, false, true>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
-      else launch_aq<true, false, false>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
-    } else {
-      if (hout) launch_aq<false, false, true>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
-      else launch_aq<false, false, false>(grid, gate, up, limit, q, scale, count, hout, nchunks, s);
-    }
+    if (act == Act::kGeluTanh)
+      launch_aq_variant<Act::kGeluTanh>(counting, clamp, grid, gate, up, limit, q, scale, count, hout, nchunks, s);
+    else
+      launch_aq_variant<Act::kSilu>(counting, clamp, grid, gate, up, limit, q, scale, count, hout, nchunks, s);
   }
   return hipGetLastError();
 }

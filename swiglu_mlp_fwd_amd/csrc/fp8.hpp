@@ -64,4 +64,35 @@ __device__ __forceinline__ float swiglu_value(float g, float u) {
   return (float)(((double)g * (double)u) * sig);
 }
 
+// h = GELU_tanh(g) * u rounded once to fp32, GELU_tanh(z) = z sigma(t) with
+// t = 2 sqrt(2/pi) (z + 0.044715 z^3) ("VisualGen MLP: cublasLt GELU-tanh
+// epilogue for the unquantized bf16 path", TensorRT-LLM PR 17693, the GELU
+// tanh activation; (1 + tanh y) / 2 = sigma(2 y)).
+//
+// The argument t is formed in fp64: in fp32 its rounding error would be
+// multiplied by |t| in sigma's tail (sigma(-a) ~ e^-a), hundreds of ulps at
+// |t| ~ 100.  |t| (capped at 1024, where e^-|t| is 0 even in fp64) is split
+// as ah + al with ah = fp32(|t|), |al| <= 2^-14; e^-|t| = p 2^n (1 - al)
+// to well under an ulp, and the rest is as in swiglu_value.
+__device__ __forceinline__ float gelu_value(float g, float u) {
+#pragma clang fp contract(off)
+  constexpr double kC1 = 1.5957691216057308;      // 2 sqrt(2 / pi)
+  constexpr double kC3 = 0.071354816272600254;    // 2 sqrt(2 / pi) * 0.044715
+  const double z = g;
+  const double t = z * (kC1 + kC3 * (z * z));
+  const double a = fmin(fabs(t), 1024.0);         // fmin drops NaN: g = NaN propagates below
+  const float ah = (float)a;
+  const float al = (float)(a - (double)ah);
+  float p;
+  int n;
+  exp_neg_split(ah, p, n);
+  p = p - p * al;
+  const float d = 1.0f + ldexpf(p, n);
+  float r = __builtin_amdgcn_rcpf(d);
+  r = __builtin_fmaf(r, __builtin_fmaf(-d, r, 1.0f), r);
+  const bool pos = t >= 0.0;
+  const double sig = ldexp((double)(pos ? r : p * r), pos ? 0 : n);
+  return (float)((z * (double)u) * sig);
+}
+
 }  // namespace swg

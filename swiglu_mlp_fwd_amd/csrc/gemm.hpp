@@ -55,7 +55,7 @@ hipError_t launch_act_bwd(int64_t rows, int64_t cols, const float* gate, const f
                           const float* dy, const float* weights, float limit, bool clamp,
                           float* dgate, float* dup, float* wgrad, hipStream_t s);
 
-hipError_t launch_act_quant(int64_t rows, int64_t cols, const float* gate, const float* up,
+hipError_t launch_act_quant(Act act, int64_t rows, int64_t cols, const float* gate, const float* up,
                             float limit, bool clamp, uint8_t* q, uint8_t* scale,
                             uint64_t* count, float* hout, hipStream_t s);
 

@@ -153,8 +153,9 @@ def gemv_fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Ten
 
 
 def act_quant(gate: torch.Tensor, up: torch.Tensor, clamp_limit: float = math.inf,
-              count: bool = True, h_out: bool = False, out=None):
-    """Elementwise SwiGLU + 1x32 UE8M0/E4M3 quantisation.
+              count: bool = True, h_out: bool = False, out=None, act: str = "silu"):
+    """Elementwise SwiGLU (act "silu") or GeGLU ("gelu_tanh") + 1x32 UE8M0/E4M3
+    quantisation.
 
     Returns (q uint8 [rows, cols], scale uint8 [rows, cols/32],
     clamp_count int64 tensor [1] or None, h fp32 or None).
@@ -177,8 +178,9 @@ def act_quant(gate: torch.Tensor, up: torch.Tensor, clamp_limit: float = math.in
         scale = torch.empty((rows, cols // 32 if cols % 32 == 0 else 0), dtype=torch.uint8, device=dev)
         cnt = torch.empty(1, dtype=torch.int64, device=dev) if count else None
         h = torch.empty((rows, cols), dtype=torch.float32, device=dev) if h_out else None
-    check("swiglu_act_quant", lib().swiglu_act_quant(rows, cols, _p(g2), _p(u2), float(clamp_limit), _p(q),
-                                                     _p(scale), _p(cnt), _p(h), _stream(gate)))
+    check("swiglu_act_quant_act", lib().swiglu_act_quant_act(_act_code(act), rows, cols, _p(g2), _p(u2),
+                                                             float(clamp_limit), _p(q), _p(scale), _p(cnt), _p(h),
+                                                             _stream(gate)))
     return q, scale, cnt, h
 
 

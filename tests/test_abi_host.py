@@ -149,6 +149,13 @@ def test_activation_choice_validation(L):
     assert L.swiglu_fwd_act(1, 1, 0, 4, 8, None, None, None, None, None) == OK
 
 
+def test_act_quant_activation_validation(L):
+    f = L.swiglu_act_quant_act
+    assert f(2, 4, 64, A, A, 7.0, A, A, None, None, None) == EARG
+    assert f(1, 4, 48, A, A, 7.0, A, A, None, None, None) == ESHAPE
+    assert f(1, 4, 64, A, A, 0.0, A, A, None, None, None) == EARG
+
+
 def test_fwd_fp8_validation(L):
     f = L.swiglu_fwd_fp8
     assert f(2, 4, 64, 8, A, A, A, A, A, None, None) == EARG           # unknown activation

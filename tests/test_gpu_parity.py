@@ -282,12 +282,12 @@ def f32_ulp_distance(a, b):
 H_ULP_MAX = 8   # the device activation is within this many fp32 ulps of the rounded exact value
 
 
-def check_act_quant(gate, up, L, what):
+def check_act_quant(gate, up, L, what, act="silu"):
     rows, cols = gate.shape
-    q, sc, cnt, h = S.act_quant(dev_f32(gate), dev_f32(up), L, count=True, h_out=True)
+    q, sc, cnt, h = S.act_quant(dev_f32(gate), dev_f32(up), L, count=True, h_out=True, act=act)
     torch.cuda.synchronize()
     q, sc, h = q.cpu().numpy(), sc.cpu().numpy(), h.cpu().numpy()
-    rq, rs, rc, rh = oracle.act_quant(gate.astype(np.float64), up.astype(np.float64), L)
+    rq, rs, rc, rh = oracle.act_quant(gate.astype(np.float64), up.astype(np.float64), L, act=act)
     # 1. clamp count: exact.
     assert int(cnt.item()) == rc, f"{what}: clamp count {int(cnt.item())} != {rc}"
     # 2. the activation h: same NaN/inf pattern, finite values within H_ULP_MAX ulps.
@@ -519,6 +519,35 @@ def test_geglu_fwd_bf16_full_8192x14336x4096_sampled():
     rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(2).integers(0, M, 62)]))
     check_fwd(d, "bf16", rows=rows, what="geglu fwd bf16 8192x14336x4096 (sampled rows)", act="gelu_tanh")
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("L", [math.inf, 7.0])
+def test_geglu_act_quant_full_4001x3584(L):
+    d = synth.act_quant_f32(4001, 3584, seed=0)
+    check_act_quant(d["gate"], d["up"], L, f"geglu act_quant 4001x3584 L={L}", act="gelu_tanh")
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (3, 384), (7, 2048)])
+def test_geglu_act_quant_ragged(shape):
+    d = synth.act_quant_f32(*shape, seed=6)
+    check_act_quant(d["gate"], d["up"], 7.0, f"geglu act_quant {shape}", act="gelu_tanh")
+
+
+def test_geglu_act_quant_tails_subnormal_and_huge():
+    """The GELU tail (sigma of t ~ -100: the argument's rounding would cost
+    hundreds of ulps in fp32), subnormal gates with huge up, tiny products."""
+    rs = np.random.default_rng(10)
+    rows, cols = 64, 256
+    gate = rs.uniform(-13.0, 13.0, (rows, cols)).astype(np.float32)
+    up = (rs.standard_normal((rows, cols)) * np.exp2(rs.integers(0, 120, (rows, cols)))).astype(np.float32)
+    check_act_quant(gate, up, math.inf, "geglu act_quant tail", act="gelu_tanh")
+    mant = rs.integers(1, 1 << 23, rows * cols, dtype=np.uint32)
+    sub = (mant | (rs.integers(0, 2, rows * cols, dtype=np.uint32) << 31)).view(np.float32).reshape(rows, cols)
+    big = (rs.standard_normal((rows, cols)) * np.exp2(rs.integers(-20, 100, (rows, cols)))).astype(np.float32)
+    check_act_quant(sub.copy(), big, math.inf, "geglu act_quant subnormal gate, huge up", act="gelu_tanh")
+    g2 = rs.uniform(-30, 30, (rows, cols)).astype(np.float32)
+    u2 = rs.uniform(-1e-30, 1e-30, (rows, cols)).astype(np.float32)
+    check_act_quant(g2, u2, math.inf, "geglu act_quant tiny products", act="gelu_tanh")
 
 
 @pytest.mark.parametrize("M", [1, 3, 8])

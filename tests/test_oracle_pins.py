@@ -446,6 +446,31 @@ def test_act_quant_random_blocks_vs_bruteforce():
     assert count == int(np.sum(np.abs(g) > 3.0) + np.sum(np.abs(u) > 3.0))
 
 
+def test_act_quant_geglu_variant_against_torch_gelu():
+    """act="gelu_tanh": h is torch's tanh-form GELU (a library routine) of the
+    clamped gate times the clamped up, then the same 1x32 quantiser."""
+    d = synth.act_quant_f32(8, 64, seed=4)
+    g, u = d["gate"].astype(np.float64), d["up"].astype(np.float64)
+    L = 3.0
+    q, scale, count, h32 = oracle.act_quant(g, u, L, act="gelu_tanh")
+    gt = torch.clamp(torch.from_numpy(g), -L, L)
+    ut = torch.clamp(torch.from_numpy(u), -L, L)
+    ref = (torch.nn.functional.gelu(gt, approximate="tanh") * ut).numpy()
+    # torch's float64 GELU and the oracle's sigma form agree to a few float64
+    # ulps; rounded to fp32 they may differ only at a rounding boundary.
+    # The inputs carry the specials (NaN, +-inf, subnormals): NaN must match.
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(h32), nan) and nan.any()
+    diff = np.abs(h32[~nan].astype(np.float64) - ref[~nan])
+    assert np.all(diff <= np.spacing(np.abs(ref[~nan]).astype(np.float32)).astype(np.float64))
+    q2, s2 = oracle.quantize_1x32(h32)
+    np.testing.assert_array_equal(q, q2)
+    np.testing.assert_array_equal(scale, s2)
+    assert count == int(np.sum(np.abs(g) > L) + np.sum(np.abs(u) > L))
+    _, _, _, h_silu = oracle.act_quant(g, u, L)
+    assert not np.array_equal(h32, h_silu)
+
+
 # ------------------------------------------------------------------- metrics
 
 def test_metrics():
