@@ -95,7 +95,7 @@ __device__ __forceinline__ void sigmoid_pair_f32(float z, float& s, float& c) {
 // (about 13 VALU slots instead of about 25).  The product z log2 e is
 // rounded once, so sigma carries a relative error of at most
 // |z| * 2^-24 * ln 2 plus a few ulps: below 1e-5 for |z| < 100, far under
-// the 2^-9 of the bf16 rounding that follows.  Limits follow IEEE:
+// the 2^-8 of the bf16 rounding that follows.  Limits follow IEEE:
 // z -> -inf gives sigma = 0 (2^+inf = inf, 1 / inf = 0), so SiLU(-inf) =
 // -inf * 0 = NaN as in the accurate form; z = +inf gives sigma = 1; NaN
 // propagates.

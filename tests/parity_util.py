@@ -7,8 +7,9 @@ Tolerances (written out here, derived in the design doc):
   * an elementwise bound per output built from |A||B| products: with
     u = 2^-24, fp32 accumulation of n exact products errs by at most
     gamma_n * sum|a||b| (gamma_n = n u / (1 - n u)); a bf16 operand rounding
-    adds 2^-9 * sum|a||b|; the final rounding adds half an ulp of the output
-    type (2^-9 relative for bf16, 2^-24 for fp32).
+    adds 2^-8 * sum|a||b|; the final rounding adds half an ulp of the output
+    type (2^-8 relative for bf16, which keeps 8 significant bits; 2^-24 for
+    fp32).
 """
 from __future__ import annotations
 
@@ -19,7 +20,7 @@ import oracle
 import synth
 
 U32 = 2.0 ** -24
-BF16_HALF_ULP = 2.0 ** -9
+BF16_HALF_ULP = 2.0 ** -8   # unit roundoff of bf16 (8 significant bits)
 
 
 def gamma(n: int, u: float = U32) -> float:
@@ -76,7 +77,7 @@ def fwd_bound(x, wg, wu, dtype: str, rows=None, act: str = "silu"):
     covers the rounding of fp32 products on the fp32 path; bf16 products are
     exact); it reaches h through |act'(g)| |u| E_g + |act(g)| E_u (|silu'| is
     below 1.1, |gelu_tanh'| below 1.13).  The activation itself is good to a
-    few fp32 ulps (8 u |h| covers it) and the output rounding adds 2^-9 |h|
+    few fp32 ulps (8 u |h| covers it) and the output rounding adds 2^-8 |h|
     (bf16) or u |h| (fp32).
     """
     xr = x if rows is None else x[rows]

@@ -120,7 +120,7 @@ def bwd_bounds(f, dtype, rows=None, cols=None):
 
     dg and du carry: the recompute error of g, u (gamma_{K+1} sum|x||w|)
     propagated through the dSwiGLU formula, a few fp32 ulps of the
-    activation, and their rounding to the operand type (2^-9 for bf16).  The
+    activation, and their rounding to the operand type (2^-8 for bf16).  The
     contractions add gamma_n of the absolute products and the output
     rounding.  A factor 2 of headroom is applied.
     """
