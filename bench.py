@@ -236,7 +236,7 @@ def main():
         fwd_fp8_leg(torch, S, x, wg, wu)
         log("done")
         return
-    if args.only in ("decode", "act_quant", "act_bwd", "fp32"):
+    if args.only in ("decode", "act_quant", "act_bwd", "fp32"):  # noqa: SIM102
         del x, wg, wu, dh, ws, h
         torch.cuda.empty_cache()
         leg = {"decode": lambda: decode_leg(torch, S, synth, np, dev, to_dev_bf16),
@@ -444,6 +444,20 @@ def act_bwd_leg(torch, S, synth, np, dev):
         res[key] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "bytes_per_call": nbytes,
                     "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
         log(f"act_bwd {R}x{C} {key}: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
+    del ins, outs
+    # bf16 tensors (weights and weight_grad fp32).
+    ins = [tuple(t.to(torch.bfloat16) for t in (torch.from_numpy(d[k]).to(dev) for k in ("gate", "up", "dy")))
+           for _ in range(copies)]
+    outs = [(torch.empty((R, C), dtype=torch.bfloat16, device=dev), torch.empty((R, C), dtype=torch.bfloat16, device=dev))
+            for _ in range(copies)]
+    nbytes = 5 * R * C * 2
+    calls = [(lambda i=i: S.act_bwd(ins[i][0], ins[i][1], ins[i][2], 0.5, out=(outs[i][0], outs[i][1], None)))
+             for _ in range(4) for i in range(copies)]
+    t, _ = graph_time_per_call(torch, calls)
+    gbs = nbytes / t / 1e9
+    res["bf16_clamp_0.5"] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "bytes_per_call": nbytes,
+                             "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
+    log(f"act_bwd {R}x{C} bf16_clamp_0.5: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
     del ins, outs
     torch.cuda.empty_cache()
     return res

@@ -218,6 +218,17 @@ int swiglu_act_bwd(int64_t rows, int64_t cols,
                    const float* weights, float clamp_limit,
                    float* dgate, float* dup, float* weight_grad, void* stream);
 
+/* swiglu_act_bwd with a choice of tensor format (the backward table's fmt
+ * column, read as the type of gate, up, dy, dgate and dup): SWIGLU_F32, or
+ * SWIGLU_BF16 with bf16 tensors, fp32 arithmetic as above and each output
+ * rounded once (to nearest even) to bf16.  weights and weight_grad stay
+ * fp32.  Layout rule: rows are whole 16-byte chunks (cols % 4 == 0 for fp32,
+ * cols % 8 == 0 for bf16); unknown dtype: SWIGLU_ERR_DTYPE. */
+int swiglu_act_bwd_dt(int dtype, int64_t rows, int64_t cols,
+                      const void* gate, const void* up, const void* dy,
+                      const float* weights, float clamp_limit,
+                      void* dgate, void* dup, float* weight_grad, void* stream);
+
 /* Measurement aid: a pure streaming read of two device buffers of `bytes`
  * bytes each (16-byte multiples), the cold-read floor against which the
  * decode kernel is judged ("Fused SwiGLU benchmark", section HBM

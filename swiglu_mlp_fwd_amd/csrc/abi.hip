@@ -186,15 +186,22 @@ int swiglu_act_quant(int64_t rows, int64_t cols, const float* gate, const float*
                               clamp_count, h_out, stream);
 }
 
-int swiglu_act_bwd(int64_t rows, int64_t cols, const float* gate, const float* up, const float* dy,
-                   const float* weights, float clamp_limit, float* dgate, float* dup,
-                   float* weight_grad, void* stream) {
-  int st = swg::validate_act_bwd(rows, cols, gate, up, dy, weights, clamp_limit, dgate, dup,
+int swiglu_act_bwd_dt(int dtype, int64_t rows, int64_t cols, const void* gate, const void* up,
+                      const void* dy, const float* weights, float clamp_limit, void* dgate, void* dup,
+                      float* weight_grad, void* stream) {
+  int st = swg::validate_act_bwd(dtype, rows, cols, gate, up, dy, weights, clamp_limit, dgate, dup,
                                  weight_grad);
   if (st != SWIGLU_OK || rows == 0) return st;
   const bool clamp = !isinf(clamp_limit);
-  return hip_status(swg::launch_act_bwd(rows, cols, gate, up, dy, weights, clamp_limit, clamp,
-                                        dgate, dup, weight_grad, as_stream(stream)));
+  return hip_status(swg::launch_act_bwd(as_dt(dtype), rows, cols, gate, up, dy, weights, clamp_limit,
+                                        clamp, dgate, dup, weight_grad, as_stream(stream)));
+}
+
+int swiglu_act_bwd(int64_t rows, int64_t cols, const float* gate, const float* up, const float* dy,
+                   const float* weights, float clamp_limit, float* dgate, float* dup,
+                   float* weight_grad, void* stream) {
+  return swiglu_act_bwd_dt(SWIGLU_F32, rows, cols, gate, up, dy, weights, clamp_limit, dgate, dup,
+                           weight_grad, stream);
 }
 
 int swiglu_probe_read2(const void* a, const void* b, size_t bytes, uint32_t* sink, void* stream) {

@@ -12,12 +12,14 @@
 //   weight_grad[r] = sum_c dy SiLU(g') u'
 // with s = sigma(g').  sigma and 1 - sigma come from the accurate fp32 form
 // (each to a few ulps, the complement without cancellation); the products
-// and the row sum are formed in fp64 and the outputs rounded to fp32 once.
+// and the row sum are formed in fp64 and each output is rounded once to its
+// type.  gate, up, dy, dgate and dup are all fp32 or all bf16 (the table's
+// fp32 and bf16 formats); weights and weight_grad are fp32.
 //
 // Mapping: one wave per row (grid-stride over rows); lane l handles the
-// 16-byte chunks l, l + 64, ... of the row, kUnroll chunks' loads issued
-// before any is used; the row sum is reduced across the wave with xor
-// shuffles and written by lane 0.
+// 16-byte chunks l, l + 64, ... of the row (4 fp32 or 8 bf16 elements),
+// kUnroll chunks' loads issued before any is used; the row sum is reduced
+// across the wave with xor shuffles and written by lane 0.
 #include "common.hpp"
 #include "gemm.hpp"
 
@@ -30,8 +32,8 @@ constexpr int kMaxBlocks = 4096;
 constexpr int kUnroll = 4;
 
 template <bool kClamp>
-__device__ __forceinline__ void bwd_elem(float g, float u, float dy, double w, float L, float& dg,
-                                         float& du, double& acc) {
+__device__ __forceinline__ void bwd_elem(float g, float u, float dy, double w, float L, double& dg,
+                                         double& du, double& acc) {
   bool pg = true, pu = true;
   if (kClamp) {
     pg = !(fabsf(g) > L);
@@ -44,33 +46,76 @@ __device__ __forceinline__ void bwd_elem(float g, float u, float dy, double w, f
   const double silu = (double)g * (double)s;
   const double dh = w * (double)dy;
   const double t = (double)s * (1.0 + (double)g * (double)c);
-  dg = pg ? (float)(dh * (double)u * t) : 0.0f;
-  du = pu ? (float)(dh * silu) : 0.0f;
+  dg = pg ? dh * (double)u * t : 0.0;
+  du = pu ? dh * silu : 0.0;
   acc += (double)dy * (silu * (double)u);
 }
 
-template <bool kClamp, bool kWeights, bool kGrad>
-__global__ __launch_bounds__(kThreads) void act_bwd_kernel(const float* __restrict__ gate,
-                                                           const float* __restrict__ up,
-                                                           const float* __restrict__ dy,
+// fp64 -> bf16 with one rounding (to nearest even): round to fp32 by
+// round-to-odd, then to bf16 by RNE.  Round-to-odd keeps the information
+// the second rounding needs (fp32 has 16 more bits than bf16), so the pair
+// equals a direct RNE of d.
+__device__ __forceinline__ uint32_t bf16_bits_rne(double d) {
+  const float f = (float)d;
+  uint32_t b = f32_bits(f);
+  if ((double)f != d && (b & 1u) == 0u && f == f) {
+    // Inexact with an even last bit: the odd neighbour lies toward d.
+    b += (fabs((double)f) > fabs(d)) ? -1 : 1;
+  }
+  return __builtin_bit_cast(uint16_t, to_bf16(bits_f32(b)));
+}
+
+template <typename T> struct Chunk;
+template <> struct Chunk<float> {
+  static constexpr int kN = 4;
+  __device__ static void unpack(const u32x4& w, float (&v)[kN]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = bits_f32(w[i]);
+  }
+  __device__ static u32x4 pack(const double (&v)[kN]) {
+    return u32x4{f32_bits((float)v[0]), f32_bits((float)v[1]), f32_bits((float)v[2]), f32_bits((float)v[3])};
+  }
+};
+template <> struct Chunk<bf16> {
+  static constexpr int kN = 8;
+  __device__ static void unpack(const u32x4& w, float (&v)[kN]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bits_f32(w[i] << 16);
+      v[2 * i + 1] = bits_f32(w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ static u32x4 pack(const double (&v)[kN]) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = bf16_bits_rne(v[2 * i]) | (bf16_bits_rne(v[2 * i + 1]) << 16);
+    return w;
+  }
+};
+
+template <typename T, bool kClamp, bool kWeights, bool kGrad>
+__global__ __launch_bounds__(kThreads) void act_bwd_kernel(const T* __restrict__ gate,
+                                                           const T* __restrict__ up,
+                                                           const T* __restrict__ dy,
                                                            const float* __restrict__ weights, float L,
-                                                           float* __restrict__ dgate,
-                                                           float* __restrict__ dup,
+                                                           T* __restrict__ dgate,
+                                                           T* __restrict__ dup,
                                                            float* __restrict__ wgrad, int64_t rows,
                                                            int64_t cols) {
+  constexpr int kN = Chunk<T>::kN;
   const int lane = threadIdx.x & 63;
-  const int64_t nch = cols / 4;
+  const int64_t nch = cols / kN;
   for (int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < rows;
        r += (int64_t)gridDim.x * (kThreads / 64)) {
     const double w = kWeights ? (double)weights[r] : 1.0;
-    const f32x4* g4 = reinterpret_cast<const f32x4*>(gate + r * cols);
-    const f32x4* u4 = reinterpret_cast<const f32x4*>(up + r * cols);
-    const f32x4* d4 = reinterpret_cast<const f32x4*>(dy + r * cols);
-    f32x4* og = reinterpret_cast<f32x4*>(dgate + r * cols);
-    f32x4* ou = reinterpret_cast<f32x4*>(dup + r * cols);
+    const u32x4* g4 = reinterpret_cast<const u32x4*>(gate + r * cols);
+    const u32x4* u4 = reinterpret_cast<const u32x4*>(up + r * cols);
+    const u32x4* d4 = reinterpret_cast<const u32x4*>(dy + r * cols);
+    u32x4* og = reinterpret_cast<u32x4*>(dgate + r * cols);
+    u32x4* ou = reinterpret_cast<u32x4*>(dup + r * cols);
     double acc = 0.0;
     for (int64_t c0 = lane; c0 < nch; c0 += 64 * kUnroll) {
-      f32x4 G[kUnroll], U[kUnroll], D[kUnroll];
+      u32x4 G[kUnroll], U[kUnroll], D[kUnroll];
 #pragma unroll
       for (int j = 0; j < kUnroll; ++j) {
         const int64_t c = c0 + 64 * j;
@@ -84,11 +129,15 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(const float* __restri
       for (int j = 0; j < kUnroll; ++j) {
         const int64_t c = c0 + 64 * j;
         if (c >= nch) break;
-        float a[4], b[4];
+        float gv[kN], uv[kN], dv[kN];
+        Chunk<T>::unpack(G[j], gv);
+        Chunk<T>::unpack(U[j], uv);
+        Chunk<T>::unpack(D[j], dv);
+        double a[kN], b[kN];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bwd_elem<kClamp>(G[j][e], U[j][e], D[j][e], w, L, a[e], b[e], acc);
-        __builtin_nontemporal_store(f32x4{a[0], a[1], a[2], a[3]}, og + c);
-        __builtin_nontemporal_store(f32x4{b[0], b[1], b[2], b[3]}, ou + c);
+        for (int e = 0; e < kN; ++e) bwd_elem<kClamp>(gv[e], uv[e], dv[e], w, L, a[e], b[e], acc);
+        __builtin_nontemporal_store(Chunk<T>::pack(a), og + c);
+        __builtin_nontemporal_store(Chunk<T>::pack(b), ou + c);
       }
     }
     if (kGrad) {
@@ -99,23 +148,20 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(const float* __restri
   }
 }
 
-template <bool kClamp, bool kWeights, bool kGrad>
-void launch_ab(unsigned grid, const float* gate, const float* up, const float* dy, const float* w,
-               float L, float* dg, float* du, float* wgrad, int64_t rows, int64_t cols, hipStream_t s) {
-  hipLaunchKernelGGL((act_bwd_kernel<kClamp, kWeights, kGrad>), dim3(grid), dim3(kThreads), 0, s,
-                     gate, up, dy, w, L, dg, du, wgrad, rows, cols);
+template <typename T, bool kClamp, bool kWeights, bool kGrad>
+void launch_ab(unsigned grid, const void* gate, const void* up, const void* dy, const float* w,
+               float L, void* dg, void* du, float* wgrad, int64_t rows, int64_t cols, hipStream_t s) {
+  hipLaunchKernelGGL((act_bwd_kernel<T, kClamp, kWeights, kGrad>), dim3(grid), dim3(kThreads), 0, s,
+                     static_cast<const T*>(gate), static_cast<const T*>(up), static_cast<const T*>(dy), w, L,
+                     static_cast<T*>(dg), static_cast<T*>(du), wgrad, rows, cols);
 }
 
-}  // namespace
-
-hipError_t launch_act_bwd(int64_t rows, int64_t cols, const float* gate, const float* up,
-                          const float* dy, const float* weights, float limit, bool clamp,
-                          float* dgate, float* dup, float* wgrad, hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  const int64_t want = (rows + kThreads / 64 - 1) / (kThreads / 64);
-  const unsigned grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);
+template <typename T>
+void launch_typed(unsigned grid, bool clamp, const void* gate, const void* up, const void* dy,
+                  const float* weights, float limit, void* dgate, void* dup, float* wgrad, int64_t rows,
+                  int64_t cols, hipStream_t s) {
   const bool w = weights != nullptr, g = wgrad != nullptr;
-#define SWG_AB(C, W, G) launch_ab<C, W, G>(grid, gate, up, dy, weights, limit, dgate, dup, wgrad, rows, cols, s)
+#define SWG_AB(C, W, G) launch_ab<T, C, W, G>(grid, gate, up, dy, weights, limit, dgate, dup, wgrad, rows, cols, s)
   if (clamp) {
     if (w) { if (g) SWG_AB(true, true, true); else SWG_AB(true, true, false); }
     else { if (g) SWG_AB(true, false, true); else SWG_AB(true, false, false); }
@@ -124,6 +170,20 @@ hipError_t launch_act_bwd(int64_t rows, int64_t cols, const float* gate, const f
     else { if (g) SWG_AB(false, false, true); else SWG_AB(false, false, false); }
   }
 #undef SWG_AB
+}
+
+}  // namespace
+
+hipError_t launch_act_bwd(Dt dt, int64_t rows, int64_t cols, const void* gate, const void* up,
+                          const void* dy, const float* weights, float limit, bool clamp,
+                          void* dgate, void* dup, float* wgrad, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int64_t want = (rows + kThreads / 64 - 1) / (kThreads / 64);
+  const unsigned grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);
+  if (dt == Dt::kBF16)
+    launch_typed<bf16>(grid, clamp, gate, up, dy, weights, limit, dgate, dup, wgrad, rows, cols, s);
+  else
+    launch_typed<float>(grid, clamp, gate, up, dy, weights, limit, dgate, dup, wgrad, rows, cols, s);
   return hipGetLastError();
 }
 

@@ -51,9 +51,9 @@ hipError_t launch_transpose(Dt dt, const void* in, int64_t ld_in, int rows, int 
 hipError_t launch_gemv(Act act, int M, int N, int K, const void* x, const void* wg, const void* wu,
                        void* h, hipStream_t s);
 
-hipError_t launch_act_bwd(int64_t rows, int64_t cols, const float* gate, const float* up,
-                          const float* dy, const float* weights, float limit, bool clamp,
-                          float* dgate, float* dup, float* wgrad, hipStream_t s);
+hipError_t launch_act_bwd(Dt dt, int64_t rows, int64_t cols, const void* gate, const void* up,
+                          const void* dy, const float* weights, float limit, bool clamp,
+                          void* dgate, void* dup, float* wgrad, hipStream_t s);
 
 hipError_t launch_act_quant(Act act, int64_t rows, int64_t cols, const float* gate, const float* up,
                             float limit, bool clamp, uint8_t* q, uint8_t* scale,

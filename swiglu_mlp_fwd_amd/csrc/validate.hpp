@@ -169,11 +169,13 @@ inline int validate_act_quant(int64_t rows, int64_t cols, const float* gate, con
   return SWIGLU_OK;
 }
 
-inline int validate_act_bwd(int64_t rows, int64_t cols, const float* gate, const float* up,
-                            const float* dy, const float* weights, float L, const float* dgate,
-                            const float* dup, const float* wgrad) {
+inline int validate_act_bwd(int dtype, int64_t rows, int64_t cols, const void* gate, const void* up,
+                            const void* dy, const float* weights, float L, const void* dgate,
+                            const void* dup, const float* wgrad) {
+  int st0 = check_dtype(dtype);
+  if (st0) return st0;
   if (rows < 0 || cols < 0) return SWIGLU_ERR_SHAPE;
-  if (cols % 4 != 0) return SWIGLU_ERR_SHAPE;
+  if (cols % chunk_elems(dtype) != 0) return SWIGLU_ERR_SHAPE;   // 16-byte rows
   if (rows > 0 && cols > (int64_t(1) << 40) / rows) return SWIGLU_ERR_SHAPE;
   if (!(L > 0.0f)) return SWIGLU_ERR_ARG;             // rejects NaN, zero and negatives
   if (weights != nullptr && !aligned(weights, 4)) return SWIGLU_ERR_ALIGN;

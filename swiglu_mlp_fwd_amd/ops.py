@@ -186,14 +186,16 @@ def act_quant(gate: torch.Tensor, up: torch.Tensor, clamp_limit: float = math.in
 
 def act_bwd(gate: torch.Tensor, up: torch.Tensor, dy: torch.Tensor, clamp_limit: float = math.inf,
             weights: torch.Tensor | None = None, weight_grad: bool = False, out=None):
-    """Elementwise SwiGLU backward (fp32) of y = w * SiLU(clamp(gate)) * clamp(up).
+    """Elementwise SwiGLU backward of y = w * SiLU(clamp(gate)) * clamp(up).
 
-    Returns (dgate, dup, weight_grad or None); weights is [rows] or None.
-    `out` may pass preallocated (dgate, dup, weight_grad) tensors.
+    gate, up, dy are fp32 or bf16 (dgate, dup come out in the same type);
+    weights ([rows] or None) and weight_grad are fp32.
+    Returns (dgate, dup, weight_grad or None); `out` may pass preallocated
+    (dgate, dup, weight_grad) tensors.
     """
     _same(gate, up, dy)
-    if gate.dtype != torch.float32:
-        raise TypeError("act_bwd takes fp32 gate/up/dy")
+    if gate.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("act_bwd takes fp32 or bf16 gate/up/dy")
     if gate.shape != up.shape or gate.shape != dy.shape:
         raise ValueError("gate, up and dy must have the same shape")
     cols = gate.shape[-1]
@@ -203,7 +205,8 @@ def act_bwd(gate: torch.Tensor, up: torch.Tensor, dy: torch.Tensor, clamp_limit:
     d2 = dy.reshape(rows, cols).contiguous()
     w = None
     if weights is not None:
-        _same(gate, weights)
+        if weights.dtype != torch.float32 or weights.device != gate.device:
+            raise TypeError("weights must be an fp32 tensor on the device of gate")
         if weights.numel() != rows:
             raise ValueError(f"weights must have {rows} elements")
         w = weights.reshape(rows).contiguous()
@@ -211,11 +214,11 @@ def act_bwd(gate: torch.Tensor, up: torch.Tensor, dy: torch.Tensor, clamp_limit:
     if out is not None:
         dg, du, wg = out
     else:
-        dg = torch.empty((rows, cols), dtype=torch.float32, device=dev)
-        du = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+        dg = torch.empty((rows, cols), dtype=gate.dtype, device=dev)
+        du = torch.empty((rows, cols), dtype=gate.dtype, device=dev)
         wg = torch.empty(rows, dtype=torch.float32, device=dev) if weight_grad else None
-    check("swiglu_act_bwd", lib().swiglu_act_bwd(rows, cols, _p(g2), _p(u2), _p(d2), _p(w), float(clamp_limit),
-                                                 _p(dg), _p(du), _p(wg), _stream(gate)))
+    check("swiglu_act_bwd_dt", lib().swiglu_act_bwd_dt(_dtype_code(gate), rows, cols, _p(g2), _p(u2), _p(d2), _p(w),
+                                                       float(clamp_limit), _p(dg), _p(du), _p(wg), _stream(gate)))
     return dg.reshape(gate.shape), du.reshape(gate.shape), wg
 
 

@@ -149,3 +149,12 @@ def act_bwd_f32(rows: int, cols: int, seed: int = 0, specials: bool = False) -> 
     d["dy"] = normal_f32((rows, cols), 1.0, seed, STREAM_DY)
     d["weights"] = rng(seed, STREAM_ROWW).uniform(0.0, 1.0, rows).astype(np.float32)
     return d
+
+
+def act_bwd_bf16(rows: int, cols: int, seed: int = 0, specials: bool = False) -> dict:
+    """act_bwd_f32's values with gate, up and dy rounded (RNE) to bf16 bits;
+    weights stay fp32."""
+    d = act_bwd_f32(rows, cols, seed, specials)
+    for k in ("gate", "up", "dy"):
+        d[k] = f32_to_bf16_bits(d[k])
+    return d

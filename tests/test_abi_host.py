@@ -185,6 +185,15 @@ def test_act_bwd_validation(L):
     assert f(0, 64, None, None, None, None, 7.0, None, None, None, None) == OK
 
 
+def test_act_bwd_format_validation(L):
+    f = L.swiglu_act_bwd_dt
+    assert f(5, 4, 64, A, A, A, None, 7.0, A, A, None, None) == EDTYPE
+    assert f(1, 4, 60, A, A, A, None, 7.0, A, A, None, None) == ESHAPE     # bf16: cols % 8
+    assert f(0, 4, 60, A, A, A, None, 7.0, A, None, None, None) == ENULL   # fp32: cols % 4 suffices
+    assert f(1, 4, 64, A, A, MIS, None, 7.0, A, A, None, None) == EALIGN
+    assert f(1, 4, 64, A, A, A, None, 7.0, A, None, None, None) == ENULL
+
+
 def test_probe_validation(L):
     assert L.swiglu_probe_read2(A, A, 17, A, None) == ESHAPE
     assert L.swiglu_probe_read2(None, A, 32, A, None) == ENULL

@@ -428,15 +428,30 @@ ULP32 = 2.0 ** -24
 TINY32 = 2.0 ** -149
 
 
+def bf16_rne_f64(r):
+    """Round float64 values to bf16 (nearest, ties to even) and return
+    (rounded, spacing at that value): 8 significant bits, subnormal spacing
+    2^-133 below 2^-126."""
+    a = np.abs(r)
+    _, e = np.frexp(np.where(np.isfinite(a), a, 1.0))
+    sp = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    return np.copysign(np.rint(a / sp) * sp, r), sp
+
+
 def check_act_bwd(d, L, use_w, what):
+    """fp32 or bf16 (d["gate"] holds bf16 bits) elementwise backward."""
     g, u, dy = d["gate"], d["up"], d["dy"]
+    bf = g.dtype == np.uint16
     w = d["weights"] if use_w else None
-    dg, du, wg = S.act_bwd(dev_f32(g), dev_f32(u), dev_f32(dy), L,
+    dev = dev_bf16 if bf else dev_f32
+    dg, du, wg = S.act_bwd(dev(g), dev(u), dev(dy), L,
                            weights=None if w is None else dev_f32(w), weight_grad=True)
     torch.cuda.synchronize()
-    dg, du, wg = dg.cpu().numpy().astype(np.float64), du.cpu().numpy().astype(np.float64), wg.cpu().numpy().astype(np.float64)
-    rg, ru, rw = oracle.act_bwd(g.astype(np.float64), u.astype(np.float64), dy.astype(np.float64), L,
-                                None if w is None else w.astype(np.float64))
+    assert dg.dtype == (torch.bfloat16 if bf else torch.float32)
+    dg, du = dg.float().cpu().numpy().astype(np.float64), du.float().cpu().numpy().astype(np.float64)
+    wg = wg.cpu().numpy().astype(np.float64)
+    g, u, dy = f64_of(g), f64_of(u), f64_of(dy)
+    rg, ru, rw = oracle.act_bwd(g, u, dy, L, None if w is None else w.astype(np.float64))
     # Term magnitudes the device error is bounded by (8 ulps of each, plus
     # the final rounding): |w dy u'| s (1 + |g'| (1 - s)) for dg, |w dy g' s| for du.
     gc = oracle.clamp_nan_preserving(g.astype(np.float64), L)
@@ -458,10 +473,23 @@ def check_act_bwd(d, L, use_w, what):
         with np.errstate(invalid="ignore"):
             # A term that is NaN (e.g. a NaN up value beside a clamped gate,
             # whose gradient is exactly 0 on both sides) bounds nothing.
-            bound = np.nan_to_num(8 * ULP32 * t[fin], nan=np.inf) + ULP32 * np.abs(r[fin]) + TINY32
+            arith = np.nan_to_num(8 * ULP32 * t[fin], nan=np.inf) + TINY32
+        out_u = BF16_HALF_ULP if (bf and name != "weight_grad") else ULP32
+        bound = arith + out_u * np.abs(r[fin]) + (2.0 ** -133 if bf else 0.0)
         ratio = np.where(y[fin] == r[fin], 0.0, np.abs(y[fin] - r[fin]) / bound)
         assert ratio.max() <= 1.0, f"{what} {name}: worst error {ratio.max():.3f} of the bound"
-        log(f"{what} {name}: worst error {ratio.max():.4f} of the bound")
+        msg = f"{what} {name}: worst error {ratio.max():.4f} of the bound"
+        if bf and name != "weight_grad":
+            # One rounding: wherever the fp64 value is farther from a bf16
+            # rounding midpoint than the arithmetic error, the output is the
+            # round-to-nearest-even of the exact value.
+            q, sp = bf16_rne_f64(r[fin])
+            frac = np.abs(r[fin]) / sp
+            to_mid = np.abs(frac - np.floor(frac) - 0.5) * sp
+            safe = to_mid > arith
+            assert np.array_equal(y[fin][safe], q[safe]), f"{what} {name}: not the single rounding of the exact value"
+            msg += f", RNE-exact on {int(safe.sum())} of {safe.size}"
+        log(msg)
     # Clamped positions carry exactly zero gradient.
     if np.isfinite(L):
         assert np.all(dg[np.abs(g) > L] == 0.0) and np.all(du[np.abs(u) > L] == 0.0)
@@ -479,6 +507,20 @@ def test_act_bwd_ragged_and_specials(shape):
     d = synth.act_bwd_f32(rows, cols, seed=3, specials=True)
     for L in (math.inf, 1.5):
         check_act_bwd(d, L, True, f"act_bwd {shape} L={L} specials")
+
+
+@pytest.mark.parametrize("L,use_w", [(math.inf, True), (0.5, False)])
+def test_act_bwd_bf16_full_4001x3584(L, use_w):
+    d = synth.act_bwd_bf16(4001, 3584, seed=0)
+    check_act_bwd(d, L, use_w, f"act_bwd bf16 4001x3584 L={L} weights={use_w}")
+
+
+@pytest.mark.parametrize("shape", [(1, 8), (3, 24), (7, 2056), (65, 264), (5, 0)])
+def test_act_bwd_bf16_ragged_and_specials(shape):
+    rows, cols = shape
+    d = synth.act_bwd_bf16(rows, cols, seed=3, specials=True)
+    for L in (math.inf, 1.5):
+        check_act_bwd(d, L, True, f"act_bwd bf16 {shape} L={L} specials")
 
 
 def test_act_bwd_without_weight_grad_and_empty():
