@@ -24,7 +24,8 @@ namespace swg {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxBlocks = 1024;   // 4 workgroups per CU, grid-stride beyond
+constexpr int kMaxBlocks = 1024;       // with the count: 4 workgroups per CU (one atomic each)
+constexpr int kMaxBlocksFree = 4096;   // without it
 constexpr int kUnroll = 4;         // chunks per lane per loop iteration
 
 template <Act A, bool kClamp, bool kCount, bool kHout>
@@ -151,7 +152,8 @@ hipError_t launch_act_quant(Act act, int64_t rows, int64_t cols, const float* ga
   const int64_t nchunks = rows * cols / 8;
   if (nchunks > 0) {
     int64_t want = (nchunks + kThreads - 1) / kThreads;
-    const unsigned grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);
+    const int64_t cap = counting ? kMaxBlocks : kMaxBlocksFree;
+    const unsigned grid = (unsigned)(want < cap ? want : cap);
     if (act == Act::kGeluTanh)
       launch_aq_variant<Act::kGeluTanh>(counting, clamp, grid, gate, up, limit, q, scale, count, hout, nchunks, s);
     else
