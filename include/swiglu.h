@@ -90,6 +90,20 @@ int swiglu_fwd_act(int act, int dtype, int64_t M, int64_t N, int64_t K,
                    const void* x, const void* wg, const void* wu, void* h,
                    void* stream);
 
+/* The gated forward with scalar multipliers on the two projections
+ * ("Another MLP implementation along with multiplier support", Liger-Kernel
+ * issue 937: the dual GEMM with activation takes a gate multiplier, and the
+ * Falcon-H1 MLP has gate and up multipliers):
+ *   h = act(gate_mult * (x Wg^T)) * (up_mult * (x Wu^T))
+ * The pages do not place the multipliers; this form scales each projection's
+ * fp32 accumulator before the activation and the product, which is the same
+ * as scaling Wg and Wu and, for up_mult, as a multiplier after the
+ * activation.  Multipliers of 1 give swiglu_fwd_act exactly.  Non-finite
+ * multipliers: SWIGLU_ERR_ARG; the rest as swiglu_fwd_act. */
+int swiglu_fwd_mult(int act, int dtype, int64_t M, int64_t N, int64_t K,
+                    const void* x, const void* wg, const void* wu,
+                    float gate_mult, float up_mult, void* h, void* stream);
+
 /* Bytes of device workspace swiglu_bwd needs for these sizes (0 on invalid
  * sizes).  It holds [dg | du], its transpose, x^T and the transposed weight
  * pair. */
@@ -119,6 +133,18 @@ int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K,
                void* dx, void* dwg, void* dwu,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward of swiglu_fwd_mult with act = SiLU: with G = gate_mult * g,
+ * U = up_mult * u and S = sigmoid(G),
+ *   dg = gate_mult * dh * U * S * (1 + G * (1 - S)),   du = up_mult * dh * G * S,
+ * then dx, dwg, dwu from dg, du as in swiglu_bwd (same workspace, layouts
+ * and errors; non-finite multipliers: SWIGLU_ERR_ARG).  Multipliers of 1
+ * give swiglu_bwd exactly. */
+int swiglu_bwd_mult(int dtype, int64_t M, int64_t N, int64_t K,
+                    const void* x, const void* wg, const void* wu, const void* dh,
+                    float gate_mult, float up_mult,
+                    void* dx, void* dwg, void* dwu,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Decode forward for 1 <= M <= 8 tokens, bf16 only: the same h as
  * swiglu_fwd, computed by a weight-streaming kernel that reads each row of
  * Wg and Wu from HBM once for all M tokens and reduces on the vector units
@@ -137,6 +163,12 @@ int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K,
 int swiglu_gemv_fwd_act(int act, int64_t M, int64_t N, int64_t K,
                         const void* x, const void* wg, const void* wu, void* h,
                         void* stream);
+
+/* swiglu_gemv_fwd with an activation choice and the projection multipliers
+ * of swiglu_fwd_mult. */
+int swiglu_gemv_fwd_mult(int act, int64_t M, int64_t N, int64_t K,
+                         const void* x, const void* wg, const void* wu,
+                         float gate_mult, float up_mult, void* h, void* stream);
 
 /* Gated forward with the FP8 block quantisation fused into the dual GEMM's
  * epilogue, so h leaves the kernel as the down projection's FP8 operand

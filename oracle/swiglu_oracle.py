@@ -117,15 +117,21 @@ def gate_up(x, wg, wu):
     return x @ wg.T, x @ wu.T
 
 
-def glu_fwd(x, wg, wu, act="silu"):
-    """h = act(x Wg^T) * (x Wu^T) with act in ACTIVATIONS."""
+def glu_fwd(x, wg, wu, act="silu", gate_mult=1.0, up_mult=1.0):
+    """h = act(gate_mult * x Wg^T) * (up_mult * x Wu^T) with act in ACTIVATIONS.
+
+    The multipliers ([Liger-937] TL;DR: a gate multiplier passed to the dual
+    GEMM with activation; the Falcon-H1 MLP's gate and up multipliers) scale
+    each projection's output before the activation and the product.  Reading:
+    the pages do not place them; this is the same as scaling Wg and Wu.
+    """
     g, u = gate_up(x, wg, wu)
-    return ACTIVATIONS[act](g) * u
+    return ACTIVATIONS[act](gate_mult * g) * (up_mult * u)
 
 
-def glu_fwd_rows(x, wg, wu, rows, act="silu"):
+def glu_fwd_rows(x, wg, wu, rows, act="silu", gate_mult=1.0, up_mult=1.0):
     """Rows `rows` of glu_fwd, computed one row at a time."""
-    return glu_fwd(np.asarray(x, np.float64)[rows], wg, wu, act)
+    return glu_fwd(np.asarray(x, np.float64)[rows], wg, wu, act, gate_mult, up_mult)
 
 
 def swiglu_fwd(x, wg, wu):
@@ -163,36 +169,44 @@ def dswiglu(g, u, dh):
     return dg, du
 
 
-def swiglu_bwd(x, wg, wu, dh):
-    """(dx [M,K], dwg [N,K], dwu [N,K]) in float64."""
+def dswiglu_mult(g, u, dh, gate_mult=1.0, up_mult=1.0):
+    """(dg, du) of h = SiLU(gate_mult g) (up_mult u): the chain rule through
+    the scaled projections G = gate_mult g, U = up_mult u."""
+    dG, dU = dswiglu(gate_mult * np.asarray(g, np.float64), up_mult * np.asarray(u, np.float64), dh)
+    return gate_mult * dG, up_mult * dU
+
+
+def swiglu_bwd(x, wg, wu, dh, gate_mult=1.0, up_mult=1.0):
+    """(dx [M,K], dwg [N,K], dwu [N,K]) in float64, for the forward
+    glu_fwd(x, wg, wu, "silu", gate_mult, up_mult)."""
     x = np.asarray(x, np.float64)
     wg = np.asarray(wg, np.float64)
     wu = np.asarray(wu, np.float64)
     g, u = gate_up(x, wg, wu)
-    dg, du = dswiglu(g, u, dh)
+    dg, du = dswiglu_mult(g, u, dh, gate_mult, up_mult)
     dx = dg @ wg + du @ wu
     dwg = dg.T @ x
     dwu = du.T @ x
     return dx, dwg, dwu
 
 
-def swiglu_bwd_dx_rows(x, wg, wu, dh, rows):
+def swiglu_bwd_dx_rows(x, wg, wu, dh, rows, gate_mult=1.0, up_mult=1.0):
     """Selected rows of dX (row m of dX needs only row m of x and dh)."""
     rows = np.asarray(rows)
     x = np.asarray(x, np.float64)[rows]
     wg = np.asarray(wg, np.float64)
     wu = np.asarray(wu, np.float64)
     g, u = gate_up(x, wg, wu)
-    dg, du = dswiglu(g, u, np.asarray(dh)[rows])
+    dg, du = dswiglu_mult(g, u, np.asarray(dh)[rows], gate_mult, up_mult)
     return dg @ wg + du @ wu
 
 
-def swiglu_bwd_dw_rows(x, wg, wu, dh, cols):
+def swiglu_bwd_dw_rows(x, wg, wu, dh, cols, gate_mult=1.0, up_mult=1.0):
     """Selected rows n of dWg and dWu (they need column n of g, u and dh)."""
     cols = np.asarray(cols)
     x = np.asarray(x, np.float64)
     g, u = gate_up(x, np.asarray(wg)[cols], np.asarray(wu)[cols])
-    dg, du = dswiglu(g, u, np.asarray(dh, np.float64)[:, cols])
+    dg, du = dswiglu_mult(g, u, np.asarray(dh, np.float64)[:, cols], gate_mult, up_mult)
     return dg.T @ x, du.T @ x
 
 

@@ -26,12 +26,19 @@ SIGNATURES = {
                                       _c_ptr, _c_ptr]),
     "swiglu_fwd_fp8": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                       _c_ptr, _c_ptr, _c_ptr]),
+    "swiglu_fwd_mult": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr,
+                                       ctypes.c_float, ctypes.c_float, _c_ptr, _c_ptr]),
     "swiglu_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int, _c_i64, _c_i64, _c_i64]),
     "swiglu_bwd": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                   _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr]),
+    "swiglu_bwd_mult": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                       ctypes.c_float, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t,
+                                       _c_ptr]),
     "swiglu_gemv_fwd": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "swiglu_gemv_fwd_act": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                            _c_ptr]),
+    "swiglu_gemv_fwd_mult": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr,
+                                            ctypes.c_float, ctypes.c_float, _c_ptr, _c_ptr]),
     "swiglu_act_quant": (ctypes.c_int, [_c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr,
                                         _c_ptr, _c_ptr, _c_ptr]),
     "swiglu_act_quant_act": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.c_float, _c_ptr,

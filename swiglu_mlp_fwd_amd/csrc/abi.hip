@@ -33,9 +33,15 @@ hipError_t fill_zero(int dtype, void* p, int64_t rows, int64_t cols, hipStream_t
 
 extern "C" {
 
-int swiglu_fwd_act(int act, int dtype, int64_t M, int64_t N, int64_t K, const void* x,
-                   const void* wg, const void* wu, void* h, void* stream) {
+namespace {
+bool finite_mult(float m) { return isfinite(m); }
+}  // namespace
+
+int swiglu_fwd_mult(int act, int dtype, int64_t M, int64_t N, int64_t K, const void* x,
+                    const void* wg, const void* wu, float gate_mult, float up_mult, void* h,
+                    void* stream) {
   if (act != SWIGLU_ACT_SILU && act != SWIGLU_ACT_GELU_TANH) return SWIGLU_ERR_ARG;
+  if (!finite_mult(gate_mult) || !finite_mult(up_mult)) return SWIGLU_ERR_ARG;
   int st = swg::validate_fwd(dtype, M, N, K, x, wg, wu, h);
   if (st != SWIGLU_OK || M == 0 || N == 0) return st;
   swg::GemmArgs a{};
@@ -44,7 +50,13 @@ int swiglu_fwd_act(int act, int dtype, int64_t M, int64_t N, int64_t K, const vo
   a.arows = (int)M; a.brows = (int)N;
   a.m = (int)M; a.n = (int)N; a.r = (int)K;
   a.out0 = h; a.ldo = N; a.ncols = (int)N;
+  a.gmul = gate_mult; a.umul = up_mult;
   return hip_status(swg::launch_fwd_dual(as_dt(dtype), static_cast<swg::Act>(act), a, as_stream(stream)));
+}
+
+int swiglu_fwd_act(int act, int dtype, int64_t M, int64_t N, int64_t K, const void* x,
+                   const void* wg, const void* wu, void* h, void* stream) {
+  return swiglu_fwd_mult(act, dtype, M, N, K, x, wg, wu, 1.0f, 1.0f, h, stream);
 }
 
 int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
@@ -72,9 +84,10 @@ size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K) {
   return swg::bwd_layout(dtype, M, N, K).total;
 }
 
-int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
-               const void* wu, const void* dh, void* dx, void* dwg, void* dwu, void* workspace,
-               size_t workspace_bytes, void* stream) {
+int swiglu_bwd_mult(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                    const void* wu, const void* dh, float gate_mult, float up_mult, void* dx, void* dwg,
+                    void* dwu, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!finite_mult(gate_mult) || !finite_mult(up_mult)) return SWIGLU_ERR_ARG;
   int st = swg::validate_bwd(dtype, M, N, K, x, wg, wu, dh, dx, dwg, dwu, workspace,
                              workspace_bytes);
   if (st != SWIGLU_OK || K == 0) return st;
@@ -100,6 +113,7 @@ int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const 
   b1.arows = Mi; b1.brows = Ni; b1.m = Mi; b1.n = Np; b1.r = Ki;
   b1.out0 = D; b1.ldo = 2 * (int64_t)Np; b1.ncols = Ni;
   b1.dh = dh; b1.lddh = N; b1.du_off = Np;
+  b1.gmul = gate_mult; b1.umul = up_mult;
   void* DT = ws + L.off_dt;
   void* XT = ws + L.off_xt;
   if (dt == swg::Dt::kBF16) {
@@ -154,13 +168,26 @@ int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const 
   return hip_status(swg::launch_gemm_store(dt, b3, s));
 }
 
-int swiglu_gemv_fwd_act(int act, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
-                        const void* wu, void* h, void* stream) {
+int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+               const void* wu, const void* dh, void* dx, void* dwg, void* dwu, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return swiglu_bwd_mult(dtype, M, N, K, x, wg, wu, dh, 1.0f, 1.0f, dx, dwg, dwu, workspace,
+                         workspace_bytes, stream);
+}
+
+int swiglu_gemv_fwd_mult(int act, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                         const void* wu, float gate_mult, float up_mult, void* h, void* stream) {
   if (act != SWIGLU_ACT_SILU && act != SWIGLU_ACT_GELU_TANH) return SWIGLU_ERR_ARG;
+  if (!finite_mult(gate_mult) || !finite_mult(up_mult)) return SWIGLU_ERR_ARG;
   int st = swg::validate_gemv(M, N, K, x, wg, wu, h);
   if (st != SWIGLU_OK || M == 0 || N == 0) return st;
   return hip_status(swg::launch_gemv(static_cast<swg::Act>(act), (int)M, (int)N, (int)K, x, wg, wu,
-                                     h, as_stream(stream)));
+                                     h, gate_mult, up_mult, as_stream(stream)));
+}
+
+int swiglu_gemv_fwd_act(int act, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                        const void* wu, void* h, void* stream) {
+  return swiglu_gemv_fwd_mult(act, M, N, K, x, wg, wu, 1.0f, 1.0f, h, stream);
 }
 
 int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K, const void* x, const void* wg,

@@ -144,19 +144,19 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[NB][
         if (row >= p.m || col >= p.n) continue;
         if constexpr (gated_fwd(E)) {
           if (col >= p.ncols) continue;
-          const float g = acc[0][i][j][e];
-          const float u = acc[NB - 1][i][j][e];
+          const float g = p.gmul * acc[0][i][j][e];
+          const float u = p.umul * acc[NB - 1][i][j][e];
           T* out = static_cast<T*>(p.out0);
           out[(int64_t)row * p.ldo + col] = cvt_out<T>(act_accurate<E>(g) * u);
         } else if constexpr (E == Epi::kDSwiGLU) {
-          const float g = acc[0][i][j][e];
-          const float u = acc[NB - 1][i][j][e];
+          const float g = p.gmul * acc[0][i][j][e];
+          const float u = p.umul * acc[NB - 1][i][j][e];
           float dh = 0.0f;
           if (col < p.ncols) dh = load_in<T>(static_cast<const T*>(p.dh) + (int64_t)row * p.lddh + col);
           float s, sg;
           sigmoid_silu_f32(g, s, sg);
-          const float du = dh * sg;
-          const float dg = dh * u * (s * (1.0f + g * (1.0f - s)));
+          const float du = (dh * sg) * p.umul;
+          const float dg = (dh * u * (s * (1.0f + g * (1.0f - s)))) * p.gmul;
           T* out = static_cast<T*>(p.out0) + (int64_t)row * p.ldo;
           out[col] = cvt_out<T>(dg);
           out[p.du_off + col] = cvt_out<T>(du);
@@ -416,15 +416,16 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
         const int row = wm * kWM + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
         const int col = wn * kWN + j * 32 + r32;
         if constexpr (gated_fwd(E)) {
-          const float g = acc[0][i][j][e], u = acc[NB - 1][i][j][e];
+          const float g = p.gmul * acc[0][i][j][e], u = p.umul * acc[NB - 1][i][j][e];
           *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(act_bf16out<E>(g) * u);
         } else if constexpr (E == Epi::kDSwiGLU) {
-          const float g = acc[0][i][j][e], u = acc[NB - 1][i][j][e];
+          const float g = p.gmul * acc[0][i][j][e], u = p.umul * acc[NB - 1][i][j][e];
           const float dh = dhv[i][j][e];
           float sg, sl;
           sigmoid_silu_bf16out(g, sg, sl);
-          *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(dh * u * (sg * (1.0f + g * (1.0f - sg))));
-          *reinterpret_cast<bf16*>(at(1, row, col)) = to_bf16(dh * sl);
+          *reinterpret_cast<bf16*>(at(0, row, col)) =
+              to_bf16((dh * u * (sg * (1.0f + g * (1.0f - sg)))) * p.gmul);
+          *reinterpret_cast<bf16*>(at(1, row, col)) = to_bf16((dh * sl) * p.umul);
         } else {
           *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(acc[0][i][j][e]);
         }
@@ -536,7 +537,7 @@ __device__ __forceinline__ void store_tile_fp8(const GemmArgs& p, f32x16 (&acc)[
       for (int e = 0; e < 16; ++e) {
         const int row = wm * kWM + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
         const int col = wn * kWN + j * 32 + r32;
-        const float g = acc[0][i][j][e], u = acc[NB - 1][i][j][e];
+        const float g = p.gmul * acc[0][i][j][e], u = p.umul * acc[NB - 1][i][j][e];
         const float h = (E == Epi::kGeGLUq ? gelu_tanh_f32(g) : silu_f32(g)) * u;
         *reinterpret_cast<float*>(lds + row * kPitch + col * 4) = h;
       }
@@ -622,6 +623,7 @@ __device__ __forceinline__ void pin_epilogue_args(const GemmArgs& p) {
   asm volatile("" ::"s"(p.out0), "s"(p.out1), "s"(p.ldo), "s"(p.dh), "s"(p.lddh));
   asm volatile("" ::"s"(p.split), "s"(p.lim0), "s"(p.lim1), "s"(p.ncols), "s"(p.du_off), "s"(p.m),
                "s"(p.n));
+  asm volatile("" ::"s"(p.ldt), "s"(p.q_scale), "s"(p.q_h), "s"(p.gmul), "s"(p.umul));
 }
 
 // Second GEMM kernel, used for bf16: the operand tiles go from global memory

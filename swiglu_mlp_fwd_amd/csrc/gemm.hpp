@@ -32,6 +32,9 @@ struct GemmArgs {
   // scale bytes in q_scale (row stride n / 32), optional fp32 h in q_h (ldo).
   void* q_scale;
   float* q_h;
+  // Gated epilogues (forward, FP8 forward, dswiglu): the projections are
+  // scaled before use, g <- gmul * g and u <- umul * u (1 leaves them exact).
+  float gmul = 1.0f, umul = 1.0f;
 };
 
 enum class Dt { kF32 = 0, kBF16 = 1 };
@@ -49,7 +52,7 @@ hipError_t launch_transpose(Dt dt, const void* in, int64_t ld_in, int rows, int 
                             hipStream_t s);
 
 hipError_t launch_gemv(Act act, int M, int N, int K, const void* x, const void* wg, const void* wu,
-                       void* h, hipStream_t s);
+                       void* h, float gmul, float umul, hipStream_t s);
 
 hipError_t launch_act_bwd(Dt dt, int64_t rows, int64_t cols, const void* gate, const void* up,
                           const void* dy, const float* weights, float limit, bool clamp,

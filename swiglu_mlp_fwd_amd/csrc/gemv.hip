@@ -29,7 +29,8 @@ template <int M, Act A>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__ x,
                                                         const bf16* __restrict__ wg,
                                                         const bf16* __restrict__ wu,
-                                                        bf16* __restrict__ h, int N, int K) {
+                                                        bf16* __restrict__ h, int N, int K,
+                                                        float gmul, float umul) {
   extern __shared__ u32x4 xs[];  // [M][K / 8]
   const int nch = K >> 3;
   const int tid = threadIdx.x;
@@ -74,35 +75,36 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__
   if (hl == 0) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float a = (A == Act::kGeluTanh) ? gelu_tanh_f32(ag[m]) : silu_f32(ag[m]);
-      h[(int64_t)m * N + col] = to_bf16(a * au[m]);
+      const float g = gmul * ag[m], u = umul * au[m];
+      const float a = (A == Act::kGeluTanh) ? gelu_tanh_f32(g) : silu_f32(g);
+      h[(int64_t)m * N + col] = to_bf16(a * u);
     }
   }
 }
 
 template <int M, Act A>
 hipError_t launch_m(int N, int K, const void* x, const void* wg, const void* wu, void* h,
-                    hipStream_t s) {
+                    float gm, float um, hipStream_t s) {
   const unsigned blocks = (unsigned)((N + kColsPerBlock - 1) / kColsPerBlock);
   const size_t lds = (size_t)M * K * 2;
   hipLaunchKernelGGL((gemv_kernel<M, A>), dim3(blocks), dim3(kThreads), lds, s,
                      static_cast<const bf16*>(x), static_cast<const bf16*>(wg),
-                     static_cast<const bf16*>(wu), static_cast<bf16*>(h), N, K);
+                     static_cast<const bf16*>(wu), static_cast<bf16*>(h), N, K, gm, um);
   return hipGetLastError();
 }
 
 template <Act A>
 hipError_t launch_act(int M, int N, int K, const void* x, const void* wg, const void* wu, void* h,
-                      hipStream_t s) {
+                      float gm, float um, hipStream_t s) {
   switch (M) {
-    case 1: return launch_m<1, A>(N, K, x, wg, wu, h, s);
-    case 2: return launch_m<2, A>(N, K, x, wg, wu, h, s);
-    case 3: return launch_m<3, A>(N, K, x, wg, wu, h, s);
-    case 4: return launch_m<4, A>(N, K, x, wg, wu, h, s);
-    case 5: return launch_m<5, A>(N, K, x, wg, wu, h, s);
-    case 6: return launch_m<6, A>(N, K, x, wg, wu, h, s);
-    case 7: return launch_m<7, A>(N, K, x, wg, wu, h, s);
-    case 8: return launch_m<8, A>(N, K, x, wg, wu, h, s);
+    case 1: return launch_m<1, A>(N, K, x, wg, wu, h, gm, um, s);
+    case 2: return launch_m<2, A>(N, K, x, wg, wu, h, gm, um, s);
+    case 3: return launch_m<3, A>(N, K, x, wg, wu, h, gm, um, s);
+    case 4: return launch_m<4, A>(N, K, x, wg, wu, h, gm, um, s);
+    case 5: return launch_m<5, A>(N, K, x, wg, wu, h, gm, um, s);
+    case 6: return launch_m<6, A>(N, K, x, wg, wu, h, gm, um, s);
+    case 7: return launch_m<7, A>(N, K, x, wg, wu, h, gm, um, s);
+    case 8: return launch_m<8, A>(N, K, x, wg, wu, h, gm, um, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -110,9 +112,9 @@ hipError_t launch_act(int M, int N, int K, const void* x, const void* wg, const 
 }  // namespace
 
 hipError_t launch_gemv(Act act, int M, int N, int K, const void* x, const void* wg, const void* wu,
-                       void* h, hipStream_t s) {
-  return act == Act::kGeluTanh ? launch_act<Act::kGeluTanh>(M, N, K, x, wg, wu, h, s)
-                               : launch_act<Act::kSilu>(M, N, K, x, wg, wu, h, s);
+                       void* h, float gmul, float umul, hipStream_t s) {
+  return act == Act::kGeluTanh ? launch_act<Act::kGeluTanh>(M, N, K, x, wg, wu, h, gmul, umul, s)
+                               : launch_act<Act::kSilu>(M, N, K, x, wg, wu, h, gmul, umul, s);
 }
 
 }  // namespace swg

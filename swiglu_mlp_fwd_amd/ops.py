@@ -56,9 +56,9 @@ def _p(t: torch.Tensor | None) -> int | None:
 
 
 def fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor | None = None,
-        act: str = "silu") -> torch.Tensor:
-    """h = act(x Wg^T) * (x Wu^T), act "silu" (SwiGLU) or "gelu_tanh" (GeGLU).
-    x [..., K], Wg/Wu [N, K] -> h [..., N]."""
+        act: str = "silu", gate_mult: float = 1.0, up_mult: float = 1.0) -> torch.Tensor:
+    """h = act(gate_mult * x Wg^T) * (up_mult * x Wu^T), act "silu" (SwiGLU) or
+    "gelu_tanh" (GeGLU).  x [..., K], Wg/Wu [N, K] -> h [..., N]."""
     _same(x, wg, wu)
     lead, K = x.shape[:-1], x.shape[-1]
     N = wg.shape[0]
@@ -70,8 +70,8 @@ def fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor |
     h = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
     if out is not None and (out.shape != (M, N) or out.dtype != x.dtype or not out.is_contiguous()):
         raise ValueError("out must be a contiguous [M, N] tensor of the input dtype")
-    check("swiglu_fwd_act", lib().swiglu_fwd_act(_act_code(act), _dtype_code(x), M, N, K, _p(x2), _p(wg), _p(wu),
-                                                 _p(h), _stream(x)))
+    check("swiglu_fwd_mult", lib().swiglu_fwd_mult(_act_code(act), _dtype_code(x), M, N, K, _p(x2), _p(wg), _p(wu),
+                                                   float(gate_mult), float(up_mult), _p(h), _stream(x)))
     return h.reshape(*lead, N)
 
 
@@ -109,8 +109,9 @@ def bwd_workspace_bytes(dtype: torch.dtype, M: int, N: int, K: int) -> int:
 
 
 def bwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, dh: torch.Tensor,
-        workspace: torch.Tensor | None = None):
-    """(dx, dwg, dwu) of L = sum(dh * h).  Shapes as in fwd; dh [..., N]."""
+        workspace: torch.Tensor | None = None, gate_mult: float = 1.0, up_mult: float = 1.0):
+    """(dx, dwg, dwu) of L = sum(dh * h), h = SiLU(gate_mult x Wg^T) * (up_mult x Wu^T).
+    Shapes as in fwd; dh [..., N]."""
     _same(x, wg, wu, dh)
     lead, K = x.shape[:-1], x.shape[-1]
     N = wg.shape[0]
@@ -129,14 +130,14 @@ def bwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, dh: torch.Tensor,
     dx = torch.empty((M, K), dtype=x.dtype, device=x.device)
     dwg = torch.empty((N, K), dtype=x.dtype, device=x.device)
     dwu = torch.empty((N, K), dtype=x.dtype, device=x.device)
-    check("swiglu_bwd", lib().swiglu_bwd(dt, M, N, K, _p(x2), _p(wg), _p(wu), _p(dh2), _p(dx), _p(dwg),
-                                         _p(dwu), _p(workspace), workspace.numel() * workspace.element_size(),
-                                         _stream(x)))
+    check("swiglu_bwd_mult", lib().swiglu_bwd_mult(dt, M, N, K, _p(x2), _p(wg), _p(wu), _p(dh2), float(gate_mult),
+                                                   float(up_mult), _p(dx), _p(dwg), _p(dwu), _p(workspace),
+                                                   workspace.numel() * workspace.element_size(), _stream(x)))
     return dx.reshape(*lead, K), dwg, dwu
 
 
 def gemv_fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor | None = None,
-             act: str = "silu") -> torch.Tensor:
+             act: str = "silu", gate_mult: float = 1.0, up_mult: float = 1.0) -> torch.Tensor:
     """Decode forward for M <= 8 tokens (bf16): same result as fwd."""
     _same(x, wg, wu)
     if x.dtype != torch.bfloat16:
@@ -147,8 +148,8 @@ def gemv_fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Ten
     x2 = x.reshape(M, K).contiguous()
     wg, wu = wg.contiguous(), wu.contiguous()
     h = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
-    check("swiglu_gemv_fwd_act", lib().swiglu_gemv_fwd_act(_act_code(act), M, N, K, _p(x2), _p(wg), _p(wu), _p(h),
-                                                           _stream(x)))
+    check("swiglu_gemv_fwd_mult", lib().swiglu_gemv_fwd_mult(_act_code(act), M, N, K, _p(x2), _p(wg), _p(wu),
+                                                             float(gate_mult), float(up_mult), _p(h), _stream(x)))
     return h.reshape(*lead, N)
 
 
@@ -234,17 +235,19 @@ class SwiGLUFunction(torch.autograd.Function):
     """Autograd wrapper: forward = fwd, backward = bwd (g and u are recomputed)."""
 
     @staticmethod
-    def forward(ctx, x, wg, wu):
+    def forward(ctx, x, wg, wu, gate_mult=1.0, up_mult=1.0):
         ctx.save_for_backward(x, wg, wu)
-        return fwd(x, wg, wu)
+        ctx.mult = (gate_mult, up_mult)
+        return fwd(x, wg, wu, gate_mult=gate_mult, up_mult=up_mult)
 
     @staticmethod
     def backward(ctx, dh):
         x, wg, wu = ctx.saved_tensors
-        dx, dwg, dwu = bwd(x, wg, wu, dh)
-        return dx, dwg, dwu
+        dx, dwg, dwu = bwd(x, wg, wu, dh, gate_mult=ctx.mult[0], up_mult=ctx.mult[1])
+        return dx, dwg, dwu, None, None
 
 
-def swiglu(x, wg, wu):
-    """Differentiable fused SwiGLU gate/up stage."""
-    return SwiGLUFunction.apply(x, wg, wu)
+def swiglu(x, wg, wu, gate_mult: float = 1.0, up_mult: float = 1.0):
+    """Differentiable fused SwiGLU gate/up stage (scalar projection multipliers
+    are constants, not trained)."""
+    return SwiGLUFunction.apply(x, wg, wu, gate_mult, up_mult)

@@ -70,7 +70,7 @@ def assert_within(y, r, bound, what: str):
     return ratio
 
 
-def fwd_bound(x, wg, wu, dtype: str, rows=None, act: str = "silu"):
+def fwd_bound(x, wg, wu, dtype: str, rows=None, act: str = "silu", gate_mult: float = 1.0, up_mult: float = 1.0):
     """Elementwise error bound of the fused forward h = act(g) u on the given rows.
 
     g and u carry the fp32 accumulation error E = gamma_{K+1} sum|x||w| (the +1
@@ -82,12 +82,16 @@ def fwd_bound(x, wg, wu, dtype: str, rows=None, act: str = "silu"):
     """
     xr = x if rows is None else x[rows]
     K = x.shape[1]
-    g, u = oracle.gate_up(xr, wg, wu)
-    Sg = np.abs(xr) @ np.abs(wg).T
-    Su = np.abs(xr) @ np.abs(wu).T
+    # With multipliers the device forms fl(m * acc): the accumulation error
+    # scales with |m| (so does sum|x||w|), and the extra rounding, u |m g|, is
+    # below gamma_{K+1} sum|x||m w|, which the propagation term already holds.
+    h = oracle.glu_fwd(xr, wg, wu, act, gate_mult, up_mult)
+    ws, us = gate_mult * np.asarray(wg, np.float64), up_mult * np.asarray(wu, np.float64)
+    g, u = oracle.gate_up(xr, ws, us)
+    Sg = np.abs(xr) @ np.abs(ws).T
+    Su = np.abs(xr) @ np.abs(us).T
     G = gamma(K + 1)
     a = oracle.ACTIVATIONS[act](g)
-    h = a * u
     prop = 1.2 * np.abs(u) * G * Sg + np.abs(a) * G * Su + G * Sg * G * Su
     out = BF16_HALF_ULP if dtype == "bf16" else U32
     return h, 2 * (prop + (8 * U32 + out) * np.abs(h)) + 1e-30

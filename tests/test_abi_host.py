@@ -156,6 +156,19 @@ def test_act_quant_activation_validation(L):
     assert f(1, 4, 64, A, A, 0.0, A, A, None, None, None) == EARG
 
 
+def test_multiplier_validation(L):
+    inf, nan = math.inf, math.nan
+    assert L.swiglu_fwd_mult(0, 1, 4, 4, 8, A, A, A, inf, 1.0, A, None) == EARG
+    assert L.swiglu_fwd_mult(0, 1, 4, 4, 8, A, A, A, 1.0, nan, A, None) == EARG
+    assert L.swiglu_fwd_mult(2, 1, 4, 4, 8, A, A, A, 1.0, 1.0, A, None) == EARG
+    assert L.swiglu_fwd_mult(0, 1, 4, 4, 12, A, A, A, 0.5, 2.0, A, None) == ESHAPE
+    assert L.swiglu_gemv_fwd_mult(0, 2, 16, 64, A, A, A, -inf, 1.0, A, None) == EARG
+    assert L.swiglu_gemv_fwd_mult(0, 9, 16, 64, A, A, A, 0.5, 1.0, A, None) == ESHAPE
+    need = L.swiglu_bwd_workspace_bytes(1, 100, 60, 64)
+    assert L.swiglu_bwd_mult(1, 100, 60, 64, A, A, A, A, nan, 1.0, A, A, A, A, need, None) == EARG
+    assert L.swiglu_bwd_mult(1, 100, 60, 64, A, A, A, A, 0.5, 1.0, A, A, A, A, need - 1, None) == EWS
+
+
 def test_fwd_fp8_validation(L):
     f = L.swiglu_fwd_fp8
     assert f(2, 4, 64, 8, A, A, A, A, A, None, None) == EARG           # unknown activation

@@ -44,16 +44,16 @@ def to_f64(d: dict) -> dict:
 
 # ----------------------------------------------------------------- forward
 
-def check_fwd(d, dtype, rows=None, what="fwd", via="dual", act="silu"):
+def check_fwd(d, dtype, rows=None, what="fwd", via="dual", act="silu", mult=(1.0, 1.0)):
     t = to_dev(d)
     f = to_f64(d)
     if via == "dual":
-        h = S.fwd(t["x"], t["wg"], t["wu"], act=act)
+        h = S.fwd(t["x"], t["wg"], t["wu"], act=act, gate_mult=mult[0], up_mult=mult[1])
     else:
-        h = S.gemv_fwd(t["x"], t["wg"], t["wu"], act=act)
+        h = S.gemv_fwd(t["x"], t["wg"], t["wu"], act=act, gate_mult=mult[0], up_mult=mult[1])
     torch.cuda.synchronize()
     y = host_f64(h if rows is None else h[torch.as_tensor(rows, device=DEV)])
-    ref, bound = fwd_bound(f["x"], f["wg"], f["wu"], dtype, rows, act)
+    ref, bound = fwd_bound(f["x"], f["wg"], f["wu"], dtype, rows, act, mult[0], mult[1])
     e, c = assert_gates(y, ref, dtype, what)
     ratio = assert_within(y, ref, bound, what)
     log(f"{what}: normwise {e:.3e} cosine {c:.7f} bound-ratio {ratio:.3f}")
@@ -115,7 +115,7 @@ def test_fwd_rank3_flatten_restore():
 
 # ---------------------------------------------------------------- backward
 
-def bwd_bounds(f, dtype, rows=None, cols=None):
+def bwd_bounds(f, dtype, rows=None, cols=None, mult=(1.0, 1.0)):
     """Elementwise bounds for dX (rows) and dWg/dWu (cols) from |.| products.
 
     dg and du carry: the recompute error of g, u (gamma_{K+1} sum|x||w|)
@@ -123,8 +123,16 @@ def bwd_bounds(f, dtype, rows=None, cols=None):
     activation, and their rounding to the operand type (2^-8 for bf16).  The
     contractions add gamma_n of the absolute products and the output
     rounding.  A factor 2 of headroom is applied.
+
+    With multipliers (mg, mu) the terms are those of the problem with weights
+    mg Wg and mu Wu (the scaled projections are what the epilogue sees); dX is
+    the same, dWg and dWu, and their bounds, carry the factor mg or mu.  The
+    two extra roundings of the scaled dg, du sit inside the 16 ulps of the
+    activation term.
     """
-    x, wg, wu, dh = f["x"], f["wg"], f["wu"], f["dh"]
+    mg, mu = mult
+    x, dh = f["x"], f["dh"]
+    wg, wu = mg * f["wg"], mu * f["wu"]
     M, K = x.shape
     N = wg.shape[0]
     op = BF16_HALF_ULP if dtype == "bf16" else 0.0
@@ -154,21 +162,25 @@ def bwd_bounds(f, dtype, rows=None, cols=None):
         dwg, dwu = dg.T @ x, du.T @ x
         bg = ddg.T @ np.abs(x) + gamma(M + 1) * (np.abs(dg).T @ np.abs(x)) * (1 + op) + out * np.abs(dwg)
         bu = ddu.T @ np.abs(x) + gamma(M + 1) * (np.abs(du).T @ np.abs(x)) * (1 + op) + out * np.abs(dwu)
-        res["dwg"] = (dwg, 2 * bg + 1e-30)
-        res["dwu"] = (dwu, 2 * bu + 1e-30)
+        res["dwg"] = (mg * dwg, 2 * abs(mg) * bg + 1e-30)
+        res["dwu"] = (mu * dwu, 2 * abs(mu) * bu + 1e-30)
+    # The oracle's own multiplier backward gives the same references.
+    if rows is not None:
+        r = oracle.swiglu_bwd_dx_rows(f["x"], f["wg"], f["wu"], dh, rows, mg, mu)
+        assert oracle.normwise_rel_err(r, res["dx"][0]) < 1e-12   # fp64 association only
     return res
 
 
-def check_bwd(d, dtype, rows=None, cols=None, what="bwd"):
+def check_bwd(d, dtype, rows=None, cols=None, what="bwd", mult=(1.0, 1.0)):
     M = d["x"].shape[0]
     N = d["wg"].shape[0]
     rows = np.arange(M) if rows is None else rows
     cols = np.arange(N) if cols is None else cols
     t = to_dev(d)
     f = to_f64(d)
-    dx, dwg, dwu = S.bwd(t["x"], t["wg"], t["wu"], t["dh"])
+    dx, dwg, dwu = S.bwd(t["x"], t["wg"], t["wu"], t["dh"], gate_mult=mult[0], up_mult=mult[1])
     torch.cuda.synchronize()
-    ref = bwd_bounds(f, dtype, rows, cols)
+    ref = bwd_bounds(f, dtype, rows, cols, mult)
     ri = torch.as_tensor(rows, device=DEV)
     ci = torch.as_tensor(cols, device=DEV)
     got = {"dx": host_f64(dx[ri]), "dwg": host_f64(dwg[ci]), "dwu": host_f64(dwu[ci])}
@@ -683,3 +695,84 @@ def test_fwd_fp8_k_zero_and_empty():
     torch.cuda.synchronize()
     assert qq.shape == (0, 64) and ss.shape == (0, 2) and hh.shape == (0, 64)
 
+
+
+# ----------------------------------------------------- multipliers (next f3)
+
+MULTS = [(0.7, 1.3), (-2.5, 0.125)]
+
+
+@pytest.mark.parametrize("mult", MULTS)
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
+def test_mult_fwd_ragged(mult, dt, act):
+    M, N, K = 300, 520, 264
+    d = synth.train_bf16(M, N, K, seed=11, with_dh=False) if dt == "bf16" else synth.gemm_fp32(M, N, K, seed=11)
+    check_fwd(d, dt, what=f"fwd {act} {dt} mult={mult}", act=act, mult=mult)
+
+
+def test_mult_one_is_exactly_the_plain_forward_and_backward():
+    d = synth.train_bf16(260, 384, 136, seed=12)
+    t = to_dev(d)
+    h0 = S.fwd(t["x"], t["wg"], t["wu"])
+    h1 = S.fwd(t["x"], t["wg"], t["wu"], gate_mult=1.0, up_mult=1.0)
+    b0 = S.bwd(t["x"], t["wg"], t["wu"], t["dh"])
+    b1 = S.bwd(t["x"], t["wg"], t["wu"], t["dh"], gate_mult=1.0, up_mult=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
+    for a, b in zip(b0, b1):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_mult_fwd_bf16_full_8192x14336x4096_sampled():
+    M, N, K = 8192, 14336, 4096
+    d = synth.train_bf16(M, N, K, seed=0, with_dh=False)
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(5).integers(0, M, 30)]))
+    check_fwd(d, "bf16", rows=rows, what="fwd bf16 8192x14336x4096 mult=(0.7, 1.3) (sampled rows)",
+              mult=(0.7, 1.3))
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mult", MULTS)
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_mult_bwd_ragged(mult, dt):
+    M, N, K = 257, 640, 520
+    if dt == "bf16":
+        d = synth.train_bf16(M, N, K, seed=13)
+    else:
+        d = synth.gemm_fp32(M, N, K, seed=13)
+        d["dh"] = synth.normal_f32((M, N), 1.0, 13, synth.STREAM_DH)
+    check_bwd(d, dt, what=f"bwd {dt} mult={mult}", mult=mult)
+
+
+def test_mult_bwd_bf16_full_8192x14336x4096_sampled():
+    M, N, K = 8192, 14336, 4096
+    d = synth.train_bf16(M, N, K, seed=0)
+    rs = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, M - 1], rs.integers(0, M, 20)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rs.integers(0, N, 20)]))
+    check_bwd(d, "bf16", rows=rows, cols=cols, what="bwd bf16 8192x14336x4096 mult=(-2.5, 0.125) (sampled)",
+              mult=(-2.5, 0.125))
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_mult_gemv(M):
+    d = synth.decode_bf16(M, 6912, 1536, seed=14)
+    for act in ("silu", "gelu_tanh"):
+        check_fwd(d, "bf16", what=f"gemv {act} M={M} mult=(0.7, 1.3)", via="gemv", act=act, mult=(0.7, 1.3))
+
+
+def test_mult_autograd():
+    d = synth.train_bf16(24, 48, 64, seed=15)
+    t = to_dev(d)
+    x = t["x"].clone().requires_grad_(True)
+    wg = t["wg"].clone().requires_grad_(True)
+    wu = t["wu"].clone().requires_grad_(True)
+    h = S.swiglu(x, wg, wu, 0.7, 1.3)
+    h.backward(t["dh"])
+    dx, dwg, dwu = S.bwd(t["x"], t["wg"], t["wu"], t["dh"], gate_mult=0.7, up_mult=1.3)
+    torch.cuda.synchronize()
+    assert torch.equal(x.grad.view(torch.int16), dx.view(torch.int16))
+    assert torch.equal(wg.grad.view(torch.int16), dwg.view(torch.int16))
+    assert torch.equal(wu.grad.view(torch.int16), dwu.view(torch.int16))

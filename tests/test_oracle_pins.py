@@ -194,6 +194,58 @@ def test_backward_matches_finite_differences_everywhere():
     assert worst < 1e-7
 
 
+def test_multiplier_forward_is_weight_scaling():
+    """The multipliers scale the projections: glu_fwd with (mg, mu) equals the
+    plain (pinned) forward on mg * Wg and mu * Wu, for both activations."""
+    d = synth.tiny_fp32(seed=5, M=5, N=12, K=16)
+    x, wg, wu = (d[k].astype(np.float64) for k in ("x", "wg", "wu"))
+    for act in ("silu", "gelu_tanh"):
+        for mg, mu in ((0.7, 1.3), (-2.5, 0.125), (1.0, 1.0)):
+            h = oracle.glu_fwd(x, wg, wu, act, mg, mu)
+            ref = oracle.glu_fwd(x, mg * wg, mu * wu, act)
+            np.testing.assert_allclose(h, ref, rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(oracle.glu_fwd(x, wg, wu, "silu", 1.0, 1.0), oracle.swiglu_fwd(x, wg, wu))
+
+
+def test_multiplier_backward_matches_finite_differences():
+    """Central differences of L = sum(dh * SiLU(mg x Wg^T) * (mu x Wu^T)) w.r.t.
+    every element of x, Wg and Wu against swiglu_bwd with the multipliers;
+    multipliers of 1 give the plain backward exactly; the row helpers agree."""
+    d = synth.tiny_fp32(seed=6, M=3, N=10, K=12)
+    x, wg, wu, dh = (d[k].astype(np.float64) for k in ("x", "wg", "wu", "dh"))
+    mg, mu = 0.7, -1.3
+    dx, dwg, dwu = oracle.swiglu_bwd(x, wg, wu, dh, mg, mu)
+
+    def loss(x_, wg_, wu_):
+        g = mg * (x_ @ wg_.T)
+        u = mu * (x_ @ wu_.T)
+        return float(np.sum(dh * (g / (1.0 + np.exp(-g))) * u))
+
+    eps = 1e-6
+    for name, grad in (("x", dx), ("wg", dwg), ("wu", dwu)):
+        args = {"x": x.copy(), "wg": wg.copy(), "wu": wu.copy()}
+        t = args[name]
+        fd = np.empty_like(t)
+        for idx in np.ndindex(t.shape):
+            v = t[idx]
+            t[idx] = v + eps
+            lp = loss(args["x"], args["wg"], args["wu"])
+            t[idx] = v - eps
+            lm = loss(args["x"], args["wg"], args["wu"])
+            t[idx] = v
+            fd[idx] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(fd - grad) / np.maximum(1.0, np.abs(grad)))
+        assert err < 1e-7, (name, err)
+    for a, b in zip(oracle.swiglu_bwd(x, wg, wu, dh, 1.0, 1.0), oracle.swiglu_bwd(x, wg, wu, dh)):
+        np.testing.assert_array_equal(a, b)
+    rows, cols = np.array([0, 2]), np.array([1, 7, 9])
+    np.testing.assert_allclose(oracle.swiglu_bwd_dx_rows(x, wg, wu, dh, rows, mg, mu), dx[rows], rtol=1e-14,
+                               atol=1e-15)
+    a, b = oracle.swiglu_bwd_dw_rows(x, wg, wu, dh, cols, mg, mu)
+    np.testing.assert_allclose(a, dwg[cols], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(b, dwu[cols], rtol=1e-14, atol=1e-15)
+
+
 def test_act_bwd_matches_finite_differences():
     """Elementwise backward: central differences of
     L = sum(dy * w * SiLU(clamp(g)) * clamp(u)) w.r.t. every g, u and w,
