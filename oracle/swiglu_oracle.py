@@ -27,7 +27,7 @@ Sources (page title, then section):
                 scales, clamp with clamp counting, NOSAT FP8 cast keeping NaN),
                 validation (amax=inf packed UE8M0, subnormals, non-finite inputs).
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
   * weights are [N, K] row-major and g = x @ Wg^T (nn.Linear layout);
   * silu(z) = z * sigmoid(z) evaluated by IEEE rules: silu(+inf)=+inf,
     silu(-inf)=NaN (-inf * 0), silu(NaN)=NaN;

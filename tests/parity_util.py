@@ -1,7 +1,7 @@
 """Helpers shared by the GPU parity tests: host<->device transfer of the
 synthetic inputs, and the tolerance checks.
 
-Tolerances (written out here, derived in the design doc):
+Tolerances, with their derivation:
   * the gates stated for the path: normwise relative error max|y-r|/max|r|
     <= 1e-5 for fp32 and <= 2e-2 for bf16, cosine >= 0.9999 for bf16;
   * an elementwise bound per output built from |A||B| products: with
