@@ -33,6 +33,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -114,11 +115,17 @@ def digest_traffic(fetch_csv: str, write_csv: str) -> None:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank space removed, so
+    that a counter measurement stays valid across comment-only edits."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "swiglu_mlp_fwd_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, fn), "rb") as f:
-            h.update(fn.encode() + f.read())
+        with open(os.path.join(csrc, fn), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(fn.encode() + text.encode())
     return h.hexdigest()[:16]
 
 

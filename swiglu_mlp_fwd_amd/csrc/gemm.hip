@@ -11,17 +11,24 @@
 // and SwiGLU in one kernel so g and u never reach memory).
 //
 // Epilogues:
-//   kGeGLU   the same with GELU (tanh form) in place of SiLU;
 //   kSwiGLU  h = SiLU(g) * u, one rounding to the output type (the activation
 //            is applied to the fp32 accumulator, as in the numerics follow-up
 //            of "VisualGen MLP: cublasLt GELU-tanh epilogue for the
 //            unquantized bf16 path", TensorRT-LLM PR 17693);
+//   kGeGLU   the same with GELU (tanh form) in place of SiLU;
+//   kSwiGLUq, kGeGLUq  the same h quantised per 1x32 block (UE8M0 scale
+//            byte, E4M3 codes), so it leaves as the down projection's FP8
+//            operand;
 //   kDSwiGLU du = dh * SiLU(g), dg = dh * u * s * (1 + g (1 - s)), s = sigma(g)
 //            (the backward of the same stage, Liger-Kernel issue 1383);
 //            bf16 can also write [dg | du] transposed for the dW product;
 //   kStore   C itself, routed to one of two outputs by row.
-// sigma is the accurate fp32 form for fp32 outputs and the short hardware
-// exp2 / reciprocal form (common.hpp) where the result is rounded to bf16.
+// The gated epilogues first scale the accumulators by the projection
+// multipliers (g <- gmul g, u <- umul u; exact when they are 1), and the
+// dSwiGLU epilogue applies the chain rule through them.
+// sigma is the accurate fp32 form for fp32 and FP8 outputs and the short
+// hardware exp2 / reciprocal form (common.hpp) where the result is rounded
+// to bf16.
 //
 // Tiling: a workgroup owns a BM x BN block tile (rows of A x rows of each
 //   B), k-steps of 128 bytes per row (64 bf16 or 32 fp32), and its waves form
