@@ -702,13 +702,14 @@ def test_fwd_fp8_k_zero_and_empty():
 MULTS = [(0.7, 1.3), (-2.5, 0.125)]
 
 
+@pytest.mark.parametrize("shape", [(300, 520, 264), (129, 300, 72)])   # N % 8 != 0: scalar-store epilogue
 @pytest.mark.parametrize("mult", MULTS)
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
-def test_mult_fwd_ragged(mult, dt, act):
-    M, N, K = 300, 520, 264
+def test_mult_fwd_ragged(shape, mult, dt, act):
+    M, N, K = shape
     d = synth.train_bf16(M, N, K, seed=11, with_dh=False) if dt == "bf16" else synth.gemm_fp32(M, N, K, seed=11)
-    check_fwd(d, dt, what=f"fwd {act} {dt} mult={mult}", act=act, mult=mult)
+    check_fwd(d, dt, what=f"fwd {act} {dt} {shape} mult={mult}", act=act, mult=mult)
 
 
 def test_mult_one_is_exactly_the_plain_forward_and_backward():
