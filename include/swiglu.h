@@ -16,13 +16,16 @@
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is ordered on
  *     it; the call returns before the work is done.
  *   - The caller owns every buffer.  Outputs must not alias inputs or each
- *     other.  Every pointer must be 16-byte aligned (the kernels use 128-bit
- *     loads and stores).
+ *     other.  Tensor pointers must be 16-byte aligned (the kernels use
+ *     128-bit loads and stores) unless an entry point states otherwise.
+ *   - Devices: calls run on the current HIP device; buffers and `stream` must
+ *     belong to it.
  *   - Return value: SWIGLU_OK or an error code.  On an error nothing has been
  *     enqueued and no output has been written.  Sizes of zero are valid and
  *     enqueue only what is needed to give the outputs their defined values.
- *   - Calls are thread-safe: the library holds no mutable global state apart
- *     from a thread-local record of the last HIP error.
+ *   - Calls are thread-safe: the library's only global state is a
+ *     thread-local record of the last HIP error and a once-per-device kernel
+ *     attribute (the larger dynamic LDS size), set under call_once.
  */
 #ifndef SWIGLU_H_
 #define SWIGLU_H_

@@ -907,6 +907,26 @@ void gemm_dma_kernel(GemmArgs p) {
   }
 }
 
+// Allows `Kernel` more than the default 64 KiB of dynamic LDS.  The
+// attribute belongs to the kernel on the current device, so it is set once
+// per (kernel, device); concurrent first calls are serialised by call_once.
+template <auto Kernel>
+hipError_t allow_lds(size_t lds) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static hipError_t result[kMaxDevices];
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  auto set = [&] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds);
+  };
+  if (dev < 0 || dev >= kMaxDevices) return set();
+  std::call_once(once[dev], [&] { result[dev] = set(); });
+  return result[dev];
+}
+
 template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL = 0>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   const int ntm = (a.m + TL::kBM - 1) / TL::kBM;
@@ -916,12 +936,7 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   const size_t ring = (size_t)S * (TL::kBM + NB * TL::kBN) * KC * 16;
   const size_t epi = sizeof(T) == 2 ? (size_t)EpiLds<E, TL>::kBytes : 0;
   const size_t lds = ring > epi ? ring : epi;
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [&] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dma_kernel<T, E, NB, TL, KC, S, kIL>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  });
+  const hipError_t attr = allow_lds<&gemm_dma_kernel<T, E, NB, TL, KC, S, kIL>>(lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((gemm_dma_kernel<T, E, NB, TL, KC, S, kIL>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
   return hipGetLastError();
@@ -934,13 +949,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = (int64_t)ntm * ntn;
   if (tiles == 0) return hipSuccess;
   const size_t lds = 2u * (TL::kBM + NB * TL::kBN) * kChunks * sizeof(u32x4);
-  // Allow more than the default 64 KiB of dynamic LDS (idempotent; done once).
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [&] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<T, E, NB, TL>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  });
+  const hipError_t attr = allow_lds<&gemm_kernel<T, E, NB, TL>>(lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((gemm_kernel<T, E, NB, TL>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
   return hipGetLastError();
