@@ -100,7 +100,20 @@ def gelu_tanh(z):
         return z * sigmoid(2.0 * GELU_C * (z + GELU_A * z * z * z))
 
 
+def gelu_tanh_grad(z):
+    """d/dz gelu_tanh(z) = s + z s (1 - s) t'(z), with t = 2 y the argument of
+    sigma above, s = sigma(t) and t'(z) = 2 sqrt(2/pi) (1 + 3 * 0.044715 z^2)
+    (product and chain rule on z * sigma(t(z)), sigma' = sigma (1 - sigma))."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        t = 2.0 * GELU_C * (z + GELU_A * z * z * z)
+        s = sigmoid(t)
+        dt = 2.0 * GELU_C * (1.0 + 3.0 * GELU_A * z * z)
+        return s + z * s * (1.0 - s) * dt
+
+
 ACTIVATIONS = {"silu": silu, "gelu_tanh": gelu_tanh}
+ACTIVATION_GRADS = {"silu": silu_grad, "gelu_tanh": gelu_tanh_grad}
 
 
 # ---------------------------------------------------------------------------
@@ -169,44 +182,54 @@ def dswiglu(g, u, dh):
     return dg, du
 
 
-def dswiglu_mult(g, u, dh, gate_mult=1.0, up_mult=1.0):
-    """(dg, du) of h = SiLU(gate_mult g) (up_mult u): the chain rule through
+def dglu(g, u, dh, act="silu"):
+    """(dg, du) of h = act(g) u: dg = dh u act'(g), du = dh act(g)."""
+    g = np.asarray(g, np.float64)
+    u = np.asarray(u, np.float64)
+    dh = np.asarray(dh, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        return dh * u * ACTIVATION_GRADS[act](g), dh * ACTIVATIONS[act](g)
+
+
+def dswiglu_mult(g, u, dh, gate_mult=1.0, up_mult=1.0, act="silu"):
+    """(dg, du) of h = act(gate_mult g) (up_mult u): the chain rule through
     the scaled projections G = gate_mult g, U = up_mult u."""
-    dG, dU = dswiglu(gate_mult * np.asarray(g, np.float64), up_mult * np.asarray(u, np.float64), dh)
+    G, U = gate_mult * np.asarray(g, np.float64), up_mult * np.asarray(u, np.float64)
+    dG, dU = dswiglu(G, U, dh) if act == "silu" else dglu(G, U, dh, act)
     return gate_mult * dG, up_mult * dU
 
 
-def swiglu_bwd(x, wg, wu, dh, gate_mult=1.0, up_mult=1.0):
+def swiglu_bwd(x, wg, wu, dh, gate_mult=1.0, up_mult=1.0, act="silu"):
     """(dx [M,K], dwg [N,K], dwu [N,K]) in float64, for the forward
-    glu_fwd(x, wg, wu, "silu", gate_mult, up_mult)."""
+    glu_fwd(x, wg, wu, act, gate_mult, up_mult)."""
     x = np.asarray(x, np.float64)
     wg = np.asarray(wg, np.float64)
     wu = np.asarray(wu, np.float64)
     g, u = gate_up(x, wg, wu)
-    dg, du = dswiglu_mult(g, u, dh, gate_mult, up_mult)
+    dg, du = dswiglu_mult(g, u, dh, gate_mult, up_mult, act)
     dx = dg @ wg + du @ wu
     dwg = dg.T @ x
     dwu = du.T @ x
     return dx, dwg, dwu
 
 
-def swiglu_bwd_dx_rows(x, wg, wu, dh, rows, gate_mult=1.0, up_mult=1.0):
+def swiglu_bwd_dx_rows(x, wg, wu, dh, rows, gate_mult=1.0, up_mult=1.0, act="silu"):
     """Selected rows of dX (row m of dX needs only row m of x and dh)."""
     rows = np.asarray(rows)
     x = np.asarray(x, np.float64)[rows]
     wg = np.asarray(wg, np.float64)
     wu = np.asarray(wu, np.float64)
     g, u = gate_up(x, wg, wu)
-    dg, du = dswiglu_mult(g, u, np.asarray(dh)[rows], gate_mult, up_mult)
+    dg, du = dswiglu_mult(g, u, np.asarray(dh)[rows], gate_mult, up_mult, act)
     return dg @ wg + du @ wu
 
 
-def swiglu_bwd_dw_rows(x, wg, wu, dh, cols, gate_mult=1.0, up_mult=1.0):
+def swiglu_bwd_dw_rows(x, wg, wu, dh, cols, gate_mult=1.0, up_mult=1.0, act="silu"):
     """Selected rows n of dWg and dWu (they need column n of g, u and dh)."""
     cols = np.asarray(cols)
     x = np.asarray(x, np.float64)
     g, u = gate_up(x, np.asarray(wg)[cols], np.asarray(wu)[cols])
-    dg, du = dswiglu_mult(g, u, np.asarray(dh, np.float64)[:, cols], gate_mult, up_mult)
+    dg, du = dswiglu_mult(g, u, np.asarray(dh, np.float64)[:, cols], gate_mult, up_mult, act)
     return dg.T @ x, du.T @ x
 
 

@@ -96,6 +96,48 @@ def test_gelu_tanh_identity_limits_and_erf_distance():
     assert v[0] == np.inf and np.isnan(v[1]) and np.isnan(v[2])
 
 
+def test_gelu_tanh_grad_against_torch_autograd_and_differences():
+    """The GELU-tanh derivative: torch's autograd of gelu(approximate="tanh")
+    in float64 (a library routine), and central differences of the oracle's
+    own gelu_tanh."""
+    z = np.linspace(-12.0, 12.0, 24001)
+    zt = torch.from_numpy(z.copy()).requires_grad_(True)
+    torch.nn.functional.gelu(zt, approximate="tanh").sum().backward()
+    np.testing.assert_allclose(oracle.gelu_tanh_grad(z), zt.grad.numpy(), rtol=1e-12, atol=1e-14)
+    h = 1e-6
+    fd = (oracle.gelu_tanh(z + h) - oracle.gelu_tanh(z - h)) / (2 * h)
+    np.testing.assert_allclose(oracle.gelu_tanh_grad(z), fd, rtol=0, atol=2e-9)
+    assert oracle.gelu_tanh_grad(np.array([0.0]))[0] == 0.5          # sigma(0) = 1/2
+
+
+def test_geglu_backward_matches_finite_differences():
+    """Central differences of L = sum(dh * GELU(mg x Wg^T) * (mu x Wu^T)) w.r.t.
+    every element of x, Wg, Wu against swiglu_bwd(act="gelu_tanh")."""
+    d = synth.tiny_fp32(seed=7, M=3, N=10, K=12)
+    x, wg, wu, dh = (d[k].astype(np.float64) for k in ("x", "wg", "wu", "dh"))
+    for mg, mu in ((1.0, 1.0), (0.7, -1.3)):
+        dx, dwg, dwu = oracle.swiglu_bwd(x, wg, wu, dh, mg, mu, act="gelu_tanh")
+
+        def loss(x_, wg_, wu_):
+            return float(np.sum(dh * oracle.glu_fwd(x_, wg_, wu_, "gelu_tanh", mg, mu)))
+
+        eps = 1e-6
+        for name, grad in (("x", dx), ("wg", dwg), ("wu", dwu)):
+            args = {"x": x.copy(), "wg": wg.copy(), "wu": wu.copy()}
+            t = args[name]
+            fd = np.empty_like(t)
+            for idx in np.ndindex(t.shape):
+                v = t[idx]
+                t[idx] = v + eps
+                lp = loss(args["x"], args["wg"], args["wu"])
+                t[idx] = v - eps
+                lm = loss(args["x"], args["wg"], args["wu"])
+                t[idx] = v
+                fd[idx] = (lp - lm) / (2 * eps)
+            err = np.max(np.abs(fd - grad) / np.maximum(1.0, np.abs(grad)))
+            assert err < 1e-7, (mg, mu, name, err)
+
+
 def test_geglu_forward_orientation_with_selection_weights():
     """The gated forward with GELU: g and u pick known x columns."""
     M, N, K = 4, 6, 9
