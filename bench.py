@@ -310,7 +310,7 @@ def main():
         "bwd_tflops_8MNK": round(8.0 * M4 * N4 * K4 / (t_step - t_fwd) / 1e12, 2),
     }
     if not args.no_extra:
-        result["geglu"] = geglu_leg(torch, S, x, wg, wu, h)
+        result["geglu"] = geglu_leg(torch, S, x, wg, wu, h, dh, ws)
         result["fwd_fp8"] = fwd_fp8_leg(torch, S, x, wg, wu)
     del h
     sample_inputs = {k: d4[k] for k in ("x", "wg", "wu", "dh")}
@@ -387,8 +387,9 @@ def act_quant_leg(torch, S, synth, np, dev):
     return res
 
 
-def geglu_leg(torch, S, x, wg, wu, h):
-    """GeGLU forward (GELU-tanh gate) on the headline inputs."""
+def geglu_leg(torch, S, x, wg, wu, h, dh, ws):
+    """GeGLU (GELU-tanh gate) on the headline inputs: the forward, and a
+    training step (forward + backward)."""
     for _ in range(3):
         S.fwd(x, wg, wu, out=h, act="gelu_tanh")
     torch.cuda.synchronize()
@@ -402,8 +403,24 @@ def geglu_leg(torch, S, x, wg, wu, h):
     t = e0.elapsed_time(e1) * 1e-3 / n
     tf = 4.0 * M4 * N4 * K4 / t / 1e12
     log(f"geglu fwd {M4}x{N4}x{K4}: {t * 1e3:.3f} ms, {tf:.1f} TFLOP/s")
+
+    def step():
+        S.fwd(x, wg, wu, out=h, act="gelu_tanh")
+        S.bwd(x, wg, wu, dh, workspace=ws, act="gelu_tanh")
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ts = e0.elapsed_time(e1) * 1e-3 / 5
+    log(f"geglu step {M4}x{N4}x{K4}: {ts * 1e3:.3f} ms, {12.0 * M4 * N4 * K4 / ts / 1e12:.1f} TFLOP/s (12MNK)")
     return {"M": M4, "N": N4, "K": K4, "ms": round(t * 1e3, 4), "TFLOPs": round(tf, 2),
-            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "step_ms": round(ts * 1e3, 4), "step_TFLOPs_12MNK": round(12.0 * M4 * N4 * K4 / ts / 1e12, 2)}
 
 
 def fwd_fp8_leg(torch, S, x, wg, wu):

@@ -148,6 +148,19 @@ int swiglu_bwd_mult(int dtype, int64_t M, int64_t N, int64_t K,
                     void* dx, void* dwg, void* dwu,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward of swiglu_fwd_mult with either gate activation: act = SiLU is
+ * swiglu_bwd_mult; act = SWIGLU_ACT_GELU_TANH (GeGLU) uses, with
+ * t = 2 sqrt(2/pi) (G + 0.044715 G^3) and S = sigmoid(t),
+ *   GELU(G) = G S,   GELU'(G) = S + G S (1 - S) * 2 sqrt(2/pi) (1 + 3 * 0.044715 G^2),
+ *   dg = gate_mult * dh * U * GELU'(G),   du = up_mult * dh * GELU(G)
+ * (product and chain rule on the forward of swiglu_fwd_act).  Workspace,
+ * layouts and errors as swiglu_bwd; unknown act: SWIGLU_ERR_ARG. */
+int swiglu_bwd_act_mult(int act, int dtype, int64_t M, int64_t N, int64_t K,
+                        const void* x, const void* wg, const void* wu, const void* dh,
+                        float gate_mult, float up_mult,
+                        void* dx, void* dwg, void* dwu,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Decode forward for 1 <= M <= 8 tokens, bf16 only: the same h as
  * swiglu_fwd, computed by a weight-streaming kernel that reads each row of
  * Wg and Wu from HBM once for all M tokens and reduces on the vector units

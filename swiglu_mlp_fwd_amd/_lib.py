@@ -34,6 +34,9 @@ SIGNATURES = {
     "swiglu_bwd_mult": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                        ctypes.c_float, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_size_t,
                                        _c_ptr]),
+    "swiglu_bwd_act_mult": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr,
+                                           _c_ptr, _c_ptr, ctypes.c_float, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr,
+                                           _c_ptr, ctypes.c_size_t, _c_ptr]),
     "swiglu_gemv_fwd": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "swiglu_gemv_fwd_act": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                            _c_ptr]),

@@ -84,9 +84,11 @@ size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K) {
   return swg::bwd_layout(dtype, M, N, K).total;
 }
 
-int swiglu_bwd_mult(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
-                    const void* wu, const void* dh, float gate_mult, float up_mult, void* dx, void* dwg,
-                    void* dwu, void* workspace, size_t workspace_bytes, void* stream) {
+int swiglu_bwd_act_mult(int act, int dtype, int64_t M, int64_t N, int64_t K, const void* x,
+                        const void* wg, const void* wu, const void* dh, float gate_mult, float up_mult,
+                        void* dx, void* dwg, void* dwu, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (act != SWIGLU_ACT_SILU && act != SWIGLU_ACT_GELU_TANH) return SWIGLU_ERR_ARG;
   if (!finite_mult(gate_mult) || !finite_mult(up_mult)) return SWIGLU_ERR_ARG;
   int st = swg::validate_bwd(dtype, M, N, K, x, wg, wu, dh, dx, dwg, dwu, workspace,
                              workspace_bytes);
@@ -120,7 +122,7 @@ int swiglu_bwd_mult(int dtype, int64_t M, int64_t N, int64_t K, const void* x, c
     b1.out1 = DT;            // the epilogue also writes D^T [2 Np, Mp]
     b1.ldt = Mp;
   }
-  if ((e = swg::launch_bwd_dswiglu(dt, b1, s)) != hipSuccess) return hip_status(e);
+  if ((e = swg::launch_bwd_dswiglu(dt, static_cast<swg::Act>(act), b1, s)) != hipSuccess) return hip_status(e);
 
   if (dt == swg::Dt::kBF16) {
     // 2. dX [M, K] = D [M, 2 Np] . ([Wg; Wu]^T [K, 2 Np])^T, reducing over
@@ -168,11 +170,18 @@ int swiglu_bwd_mult(int dtype, int64_t M, int64_t N, int64_t K, const void* x, c
   return hip_status(swg::launch_gemm_store(dt, b3, s));
 }
 
+int swiglu_bwd_mult(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                    const void* wu, const void* dh, float gate_mult, float up_mult, void* dx, void* dwg,
+                    void* dwu, void* workspace, size_t workspace_bytes, void* stream) {
+  return swiglu_bwd_act_mult(SWIGLU_ACT_SILU, dtype, M, N, K, x, wg, wu, dh, gate_mult, up_mult, dx, dwg,
+                             dwu, workspace, workspace_bytes, stream);
+}
+
 int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
                const void* wu, const void* dh, void* dx, void* dwg, void* dwu, void* workspace,
                size_t workspace_bytes, void* stream) {
-  return swiglu_bwd_mult(dtype, M, N, K, x, wg, wu, dh, 1.0f, 1.0f, dx, dwg, dwu, workspace,
-                         workspace_bytes, stream);
+  return swiglu_bwd_act_mult(SWIGLU_ACT_SILU, dtype, M, N, K, x, wg, wu, dh, 1.0f, 1.0f, dx, dwg, dwu,
+                             workspace, workspace_bytes, stream);
 }
 
 int swiglu_gemv_fwd_mult(int act, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,

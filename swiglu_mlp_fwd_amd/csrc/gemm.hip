@@ -22,6 +22,7 @@
 //   kDSwiGLU du = dh * SiLU(g), dg = dh * u * s * (1 + g (1 - s)), s = sigma(g)
 //            (the backward of the same stage, Liger-Kernel issue 1383);
 //            bf16 can also write [dg | du] transposed for the dW product;
+//   kDGeGLU  the same with GELU-tanh and its derivative;
 //   kStore   C itself, routed to one of two outputs by row.
 // The gated epilogues first scale the accumulators by the projection
 // multipliers (g <- gmul g, u <- umul u; exact when they are 1), and the
@@ -67,12 +68,42 @@ struct Tile {
   static constexpr int kTM = kWM / 32, kTN = kWN / 32;       // 32x32 MFMA tiles per wave
 };
 
-enum class Epi { kSwiGLU, kGeGLU, kDSwiGLU, kStore, kSwiGLUq, kGeGLUq };
+enum class Epi { kSwiGLU, kGeGLU, kDSwiGLU, kStore, kSwiGLUq, kGeGLUq, kDGeGLU };
 
 // Gated forward epilogues: h = act(g) * u.
 constexpr bool gated_fwd(Epi e) { return e == Epi::kSwiGLU || e == Epi::kGeGLU; }
 // ... with h quantised to E4M3 per 1x32 block (UE8M0 scales).
 constexpr bool gated_q(Epi e) { return e == Epi::kSwiGLUq || e == Epi::kGeGLUq; }
+// Backward epilogues of the gated forward: D = [dg | du].
+constexpr bool gated_bwd(Epi e) { return e == Epi::kDSwiGLU || e == Epi::kDGeGLU; }
+
+// act(z) and act'(z) for the backward epilogues.  SiLU: a = z s,
+// a' = s (1 + z (1 - s)), s = sigma(z).  GELU (tanh form): a = z s and
+// a' = s + z s (1 - s) t'(z) with s = sigma(t), t = z (c1 + c3 z^2),
+// t' = c1 + 3 c3 z^2.  kShort: the short sigma (results rounded to bf16);
+// otherwise the accurate pair sigma, 1 - sigma.
+template <Epi E, bool kShort>
+__device__ __forceinline__ void act_and_grad(float z, float& a, float& da) {
+  if constexpr (E == Epi::kDGeGLU) {
+    const float z2 = z * z;
+    const float t = z * __builtin_fmaf(kGeluC3, z2, kGeluC1);
+    float s, c;
+    if constexpr (kShort) {
+      constexpr float kL2e = 1.44269504088896340736f;
+      s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t * kL2e));
+      c = 1.0f - s;
+    } else {
+      sigmoid_pair_f32(t, s, c);
+    }
+    a = z * s;
+    da = s + a * c * __builtin_fmaf(3.0f * kGeluC3, z2, kGeluC1);
+  } else {
+    float s;
+    if constexpr (kShort) sigmoid_silu_bf16out(z, s, a);
+    else sigmoid_silu_f32(z, s, a);
+    da = s * (1.0f + z * (1.0f - s));
+  }
+}
 
 template <Epi E>
 __device__ __forceinline__ float act_accurate(float g) {
@@ -155,15 +186,15 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[NB][
           const float u = p.umul * acc[NB - 1][i][j][e];
           T* out = static_cast<T*>(p.out0);
           out[(int64_t)row * p.ldo + col] = cvt_out<T>(act_accurate<E>(g) * u);
-        } else if constexpr (E == Epi::kDSwiGLU) {
+        } else if constexpr (gated_bwd(E)) {
           const float g = p.gmul * acc[0][i][j][e];
           const float u = p.umul * acc[NB - 1][i][j][e];
           float dh = 0.0f;
           if (col < p.ncols) dh = load_in<T>(static_cast<const T*>(p.dh) + (int64_t)row * p.lddh + col);
-          float s, sg;
-          sigmoid_silu_f32(g, s, sg);
-          const float du = (dh * sg) * p.umul;
-          const float dg = (dh * u * (s * (1.0f + g * (1.0f - s)))) * p.gmul;
+          float a, da;
+          act_and_grad<E, false>(g, a, da);
+          const float du = (dh * a) * p.umul;
+          const float dg = (dh * u * da) * p.gmul;
           T* out = static_cast<T*>(p.out0) + (int64_t)row * p.ldo;
           out[col] = cvt_out<T>(dg);
           out[p.du_off + col] = cvt_out<T>(du);
@@ -320,7 +351,7 @@ struct EpiLds {
   static constexpr int kCols = TL::kBN;                      // columns per output tile
   static constexpr int kPitch = kCols * (gated_q(E) ? 4 : 2) + 32;   // bytes per staged row
   static constexpr int kRegion = TL::kBM * kPitch;
-  static constexpr int kBytes = (E == Epi::kDSwiGLU ? 2 : 1) * kRegion;
+  static constexpr int kBytes = (gated_bwd(E) ? 2 : 1) * kRegion;
 };
 
 typedef __attribute__((ext_vector_type(4))) short short4_t;
@@ -376,7 +407,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
   auto at = [&](int reg, int row, int col) -> char* { return lds + reg * kRegion + row * kPitch + col * 2; };
 
   float dhv[kTM][kTN][16];
-  if constexpr (E == Epi::kDSwiGLU) {
+  if constexpr (gated_bwd(E)) {
     static_assert(DhPre<TL>::kCPR == kCPR && DhPre<TL>::kPer * kThreads == kBM * kCPR, "dh chunk mapping");
     const bf16* dh = static_cast<const bf16*>(p.dh);
 #pragma unroll
@@ -425,14 +456,13 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
         if constexpr (gated_fwd(E)) {
           const float g = p.gmul * acc[0][i][j][e], u = p.umul * acc[NB - 1][i][j][e];
           *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(act_bf16out<E>(g) * u);
-        } else if constexpr (E == Epi::kDSwiGLU) {
+        } else if constexpr (gated_bwd(E)) {
           const float g = p.gmul * acc[0][i][j][e], u = p.umul * acc[NB - 1][i][j][e];
           const float dh = dhv[i][j][e];
-          float sg, sl;
-          sigmoid_silu_bf16out(g, sg, sl);
-          *reinterpret_cast<bf16*>(at(0, row, col)) =
-              to_bf16((dh * u * (sg * (1.0f + g * (1.0f - sg)))) * p.gmul);
-          *reinterpret_cast<bf16*>(at(1, row, col)) = to_bf16((dh * sl) * p.umul);
+          float a, da;
+          act_and_grad<E, true>(g, a, da);
+          *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16((dh * u * da) * p.gmul);
+          *reinterpret_cast<bf16*>(at(1, row, col)) = to_bf16((dh * a) * p.umul);
         } else {
           *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(acc[0][i][j][e]);
         }
@@ -457,7 +487,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
       if (gcol >= p.ncols) continue;
       put(static_cast<bf16*>(p.out0) + (int64_t)grow * p.ldo + gcol,
           *reinterpret_cast<const u32x4*>(at(0, r, ch * 8)), min(8, p.ncols - gcol));
-    } else if constexpr (E == Epi::kDSwiGLU) {
+    } else if constexpr (gated_bwd(E)) {
       bf16* dst = static_cast<bf16*>(p.out0) + (int64_t)grow * p.ldo + gcol;
       const int nv = min(8, p.n - gcol);
       put(dst, *reinterpret_cast<const u32x4*>(at(0, r, ch * 8)), nv);
@@ -486,7 +516,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
   // their chunks sit in disjoint bank halves with the 288-byte pitch), and
   // swap halves on the second read.  Rows m in [p.m, ldt) of the tile hold
   // zeros (zero x rows and dh), so out1's padding columns are written zero.
-  if constexpr (E == Epi::kDSwiGLU) {
+  if constexpr (gated_bwd(E)) {
     if (p.out1 != nullptr) {
       bf16* dt = static_cast<bf16*>(p.out1);
       constexpr int kNB = kCols / 16, kMQ = kBM / 32;       // 16-column blocks, 32-row groups
@@ -884,7 +914,7 @@ void gemm_dma_kernel(GemmArgs p) {
   };
   DhPre<TL> dpre;
   for (int ks = 0; ks + 1 < nk; ++ks) kstep(ks, true);
-  if constexpr (E == Epi::kDSwiGLU && sizeof(T) == 2) dh_prefetch<TL>(p, tm, tn, tid, dpre);
+  if constexpr (gated_bwd(E) && sizeof(T) == 2) dh_prefetch<TL>(p, tm, tn, tid, dpre);
   if (nk > 0) kstep(nk - 1, false);
 
   if constexpr (gated_q(E)) {
@@ -894,7 +924,7 @@ void gemm_dma_kernel(GemmArgs p) {
     store_tile_fp8<E, NB, TL>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes);
   } else {
     if constexpr (sizeof(T) == 2) {
-      const bool vec = (p.ldo % 8 == 0) && (E != Epi::kDSwiGLU || p.du_off % 8 == 0);
+      const bool vec = (p.ldo % 8 == 0) && (!gated_bwd(E) || p.du_off % 8 == 0);
       if (vec) {
         wait_vmcnt<0>();                      // no DMA still landing in the ring
         __builtin_amdgcn_s_waitcnt(0xC07F);   // own LDS reads done
@@ -973,7 +1003,10 @@ hipError_t launch_fwd_dual_fp8(Act act, const GemmArgs& a, hipStream_t s) {
                                : launch_dma<bf16, Epi::kSwiGLUq, 2, TileDual, 8, 2, 2>(a, s);
 }
 
-hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_bwd_dswiglu(Dt dt, Act act, const GemmArgs& a, hipStream_t s) {
+  if (act == Act::kGeluTanh)
+    return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDGeGLU, 2, TileDual, 8, 2, 2>(a, s)
+                           : launch<float, Epi::kDGeGLU, 2, TileDual>(a, s);
   return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, 2>(a, s)
                          : launch<float, Epi::kDSwiGLU, 2, TileDual>(a, s);
 }

@@ -43,7 +43,7 @@ enum class Act { kSilu = 0, kGeluTanh = 1 };   // the gate activation of the gat
 hipError_t launch_fwd_dual(Dt dt, Act act, const GemmArgs& a, hipStream_t s);  // h = act(g) * u
 // bf16 inputs, h = act(g) * u quantised per 1x32 block (n % 32 == 0).
 hipError_t launch_fwd_dual_fp8(Act act, const GemmArgs& a, hipStream_t s);
-hipError_t launch_bwd_dswiglu(Dt dt, const GemmArgs& a, hipStream_t s);   // D = [dg | du]
+hipError_t launch_bwd_dswiglu(Dt dt, Act act, const GemmArgs& a, hipStream_t s);   // D = [dg | du]
 hipError_t launch_gemm_store(Dt dt, const GemmArgs& a, hipStream_t s);    // C = A B^T
 
 // out[c, col_off + r] = in[r, c] for r < rows, 0 for rows <= r < rows_pad.

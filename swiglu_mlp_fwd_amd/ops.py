@@ -109,8 +109,9 @@ def bwd_workspace_bytes(dtype: torch.dtype, M: int, N: int, K: int) -> int:
 
 
 def bwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, dh: torch.Tensor,
-        workspace: torch.Tensor | None = None, gate_mult: float = 1.0, up_mult: float = 1.0):
-    """(dx, dwg, dwu) of L = sum(dh * h), h = SiLU(gate_mult x Wg^T) * (up_mult x Wu^T).
+        workspace: torch.Tensor | None = None, gate_mult: float = 1.0, up_mult: float = 1.0,
+        act: str = "silu"):
+    """(dx, dwg, dwu) of L = sum(dh * h), h = act(gate_mult x Wg^T) * (up_mult x Wu^T).
     Shapes as in fwd; dh [..., N]."""
     _same(x, wg, wu, dh)
     lead, K = x.shape[:-1], x.shape[-1]
@@ -130,9 +131,11 @@ def bwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, dh: torch.Tensor,
     dx = torch.empty((M, K), dtype=x.dtype, device=x.device)
     dwg = torch.empty((N, K), dtype=x.dtype, device=x.device)
     dwu = torch.empty((N, K), dtype=x.dtype, device=x.device)
-    check("swiglu_bwd_mult", lib().swiglu_bwd_mult(dt, M, N, K, _p(x2), _p(wg), _p(wu), _p(dh2), float(gate_mult),
-                                                   float(up_mult), _p(dx), _p(dwg), _p(dwu), _p(workspace),
-                                                   workspace.numel() * workspace.element_size(), _stream(x)))
+    check("swiglu_bwd_act_mult", lib().swiglu_bwd_act_mult(_act_code(act), dt, M, N, K, _p(x2), _p(wg), _p(wu),
+                                                           _p(dh2), float(gate_mult), float(up_mult), _p(dx),
+                                                           _p(dwg), _p(dwu), _p(workspace),
+                                                           workspace.numel() * workspace.element_size(),
+                                                           _stream(x)))
     return dx.reshape(*lead, K), dwg, dwu
 
 
@@ -235,19 +238,20 @@ class SwiGLUFunction(torch.autograd.Function):
     """Autograd wrapper: forward = fwd, backward = bwd (g and u are recomputed)."""
 
     @staticmethod
-    def forward(ctx, x, wg, wu, gate_mult=1.0, up_mult=1.0):
+    def forward(ctx, x, wg, wu, gate_mult=1.0, up_mult=1.0, act="silu"):
         ctx.save_for_backward(x, wg, wu)
-        ctx.mult = (gate_mult, up_mult)
-        return fwd(x, wg, wu, gate_mult=gate_mult, up_mult=up_mult)
+        ctx.cfg = (gate_mult, up_mult, act)
+        return fwd(x, wg, wu, gate_mult=gate_mult, up_mult=up_mult, act=act)
 
     @staticmethod
     def backward(ctx, dh):
         x, wg, wu = ctx.saved_tensors
-        dx, dwg, dwu = bwd(x, wg, wu, dh, gate_mult=ctx.mult[0], up_mult=ctx.mult[1])
-        return dx, dwg, dwu, None, None
+        gm, um, act = ctx.cfg
+        dx, dwg, dwu = bwd(x, wg, wu, dh, gate_mult=gm, up_mult=um, act=act)
+        return dx, dwg, dwu, None, None, None
 
 
-def swiglu(x, wg, wu, gate_mult: float = 1.0, up_mult: float = 1.0):
-    """Differentiable fused SwiGLU gate/up stage (scalar projection multipliers
-    are constants, not trained)."""
-    return SwiGLUFunction.apply(x, wg, wu, gate_mult, up_mult)
+def swiglu(x, wg, wu, gate_mult: float = 1.0, up_mult: float = 1.0, act: str = "silu"):
+    """Differentiable fused gate/up stage, act "silu" (SwiGLU) or "gelu_tanh"
+    (GeGLU); the scalar projection multipliers are constants, not trained."""
+    return SwiGLUFunction.apply(x, wg, wu, gate_mult, up_mult, act)

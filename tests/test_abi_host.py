@@ -167,6 +167,8 @@ def test_multiplier_validation(L):
     need = L.swiglu_bwd_workspace_bytes(1, 100, 60, 64)
     assert L.swiglu_bwd_mult(1, 100, 60, 64, A, A, A, A, nan, 1.0, A, A, A, A, need, None) == EARG
     assert L.swiglu_bwd_mult(1, 100, 60, 64, A, A, A, A, 0.5, 1.0, A, A, A, A, need - 1, None) == EWS
+    assert L.swiglu_bwd_act_mult(2, 1, 100, 60, 64, A, A, A, A, 1.0, 1.0, A, A, A, A, need, None) == EARG
+    assert L.swiglu_bwd_act_mult(1, 1, 100, 60, 64, A, A, A, A, 1.0, 1.0, A, A, A, A, need - 1, None) == EWS
 
 
 def test_fwd_fp8_validation(L):

@@ -115,7 +115,7 @@ def test_fwd_rank3_flatten_restore():
 
 # ---------------------------------------------------------------- backward
 
-def bwd_bounds(f, dtype, rows=None, cols=None, mult=(1.0, 1.0)):
+def bwd_bounds(f, dtype, rows=None, cols=None, mult=(1.0, 1.0), act="silu"):
     """Elementwise bounds for dX (rows) and dWg/dWu (cols) from |.| products.
 
     dg and du carry: the recompute error of g, u (gamma_{K+1} sum|x||w|)
@@ -139,15 +139,17 @@ def bwd_bounds(f, dtype, rows=None, cols=None, mult=(1.0, 1.0)):
     out = BF16_HALF_ULP if dtype == "bf16" else U32
     GK = gamma(K + 1)
 
+    # |act''| is below 0.5 (SiLU) and 0.8 (GELU-tanh); |act'| below 1.1 and 1.13.
+    d2max, d1max = (0.5, 1.1) if act == "silu" else (0.85, 1.2)
+
     def terms(xs, wgs, wus, dhs):
         g, u = oracle.gate_up(xs, wgs, wus)
-        dg, du = oracle.dswiglu(g, u, dhs)
+        dg, du = oracle.dswiglu(g, u, dhs) if act == "silu" else oracle.dglu(g, u, dhs, act)
         Eg = GK * (np.abs(xs) @ np.abs(wgs).T)
         Eu = GK * (np.abs(xs) @ np.abs(wus).T)
-        s = oracle.sigmoid(g)
-        d1 = np.abs(s * (1 + g * (1 - s)))
-        ddg = np.abs(dh_ := dhs) * (d1 * Eu + 0.5 * np.abs(u) * Eg) + (op + 16 * U32) * np.abs(dg)
-        ddu = np.abs(dh_) * 1.1 * Eg + (op + 16 * U32) * np.abs(du)
+        d1 = np.abs(oracle.ACTIVATION_GRADS[act](g))
+        ddg = np.abs(dh_ := dhs) * (d1 * Eu + d2max * np.abs(u) * Eg) + (op + 16 * U32) * np.abs(dg)
+        ddu = np.abs(dh_) * d1max * Eg + (op + 16 * U32) * np.abs(du)
         return dg, du, ddg, ddu
 
     res = {}
@@ -166,21 +168,21 @@ def bwd_bounds(f, dtype, rows=None, cols=None, mult=(1.0, 1.0)):
         res["dwu"] = (mu * dwu, 2 * abs(mu) * bu + 1e-30)
     # The oracle's own multiplier backward gives the same references.
     if rows is not None:
-        r = oracle.swiglu_bwd_dx_rows(f["x"], f["wg"], f["wu"], dh, rows, mg, mu)
+        r = oracle.swiglu_bwd_dx_rows(f["x"], f["wg"], f["wu"], dh, rows, mg, mu, act)
         assert oracle.normwise_rel_err(r, res["dx"][0]) < 1e-12   # fp64 association only
     return res
 
 
-def check_bwd(d, dtype, rows=None, cols=None, what="bwd", mult=(1.0, 1.0)):
+def check_bwd(d, dtype, rows=None, cols=None, what="bwd", mult=(1.0, 1.0), act="silu"):
     M = d["x"].shape[0]
     N = d["wg"].shape[0]
     rows = np.arange(M) if rows is None else rows
     cols = np.arange(N) if cols is None else cols
     t = to_dev(d)
     f = to_f64(d)
-    dx, dwg, dwu = S.bwd(t["x"], t["wg"], t["wu"], t["dh"], gate_mult=mult[0], up_mult=mult[1])
+    dx, dwg, dwu = S.bwd(t["x"], t["wg"], t["wu"], t["dh"], gate_mult=mult[0], up_mult=mult[1], act=act)
     torch.cuda.synchronize()
-    ref = bwd_bounds(f, dtype, rows, cols, mult)
+    ref = bwd_bounds(f, dtype, rows, cols, mult, act)
     ri = torch.as_tensor(rows, device=DEV)
     ci = torch.as_tensor(cols, device=DEV)
     got = {"dx": host_f64(dx[ri]), "dwg": host_f64(dwg[ci]), "dwu": host_f64(dwu[ci])}
@@ -773,6 +775,46 @@ def test_mult_autograd():
     h = S.swiglu(x, wg, wu, 0.7, 1.3)
     h.backward(t["dh"])
     dx, dwg, dwu = S.bwd(t["x"], t["wg"], t["wu"], t["dh"], gate_mult=0.7, up_mult=1.3)
+    torch.cuda.synchronize()
+    assert torch.equal(x.grad.view(torch.int16), dx.view(torch.int16))
+    assert torch.equal(wg.grad.view(torch.int16), dwg.view(torch.int16))
+    assert torch.equal(wu.grad.view(torch.int16), dwu.view(torch.int16))
+
+
+# ------------------------------------------------------- GeGLU backward
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(300, 520, 264), (33, 17, 40), (257, 640, 520)])
+def test_geglu_bwd_ragged(dt, shape):
+    M, N, K = shape
+    if dt == "bf16":
+        d = synth.train_bf16(M, N, K, seed=16)
+    else:
+        d = synth.gemm_fp32(M, N, K, seed=16)
+        d["dh"] = synth.normal_f32((M, N), 1.0, 16, synth.STREAM_DH)
+    check_bwd(d, dt, what=f"geglu bwd {dt} {shape}", act="gelu_tanh")
+    check_bwd(d, dt, what=f"geglu bwd {dt} {shape} mult=(0.7, 1.3)", act="gelu_tanh", mult=(0.7, 1.3))
+
+
+def test_geglu_bwd_bf16_full_8192x14336x4096_sampled():
+    M, N, K = 8192, 14336, 4096
+    d = synth.train_bf16(M, N, K, seed=0)
+    rs = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, M - 1], rs.integers(0, M, 20)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rs.integers(0, N, 20)]))
+    check_bwd(d, "bf16", rows=rows, cols=cols, what="geglu bwd bf16 8192x14336x4096 (sampled)", act="gelu_tanh")
+    torch.cuda.empty_cache()
+
+
+def test_geglu_autograd():
+    d = synth.train_bf16(24, 48, 64, seed=17)
+    t = to_dev(d)
+    x = t["x"].clone().requires_grad_(True)
+    wg = t["wg"].clone().requires_grad_(True)
+    wu = t["wu"].clone().requires_grad_(True)
+    h = S.swiglu(x, wg, wu, act="gelu_tanh")
+    h.backward(t["dh"])
+    dx, dwg, dwu = S.bwd(t["x"], t["wg"], t["wu"], t["dh"], act="gelu_tanh")
     torch.cuda.synchronize()
     assert torch.equal(x.grad.view(torch.int16), dx.view(torch.int16))
     assert torch.equal(wg.grad.view(torch.int16), dwg.view(torch.int16))
