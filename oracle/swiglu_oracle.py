@@ -320,6 +320,22 @@ def clamp_nan_preserving(v, limit):
     return np.where(v > limit, limit, np.where(v < -limit, -limit, v))
 
 
+def act_fwd(gate, up, clamp_limit=np.inf, act="silu"):
+    """The elementwise gated activation without quantisation ([PTO-20]
+    forward table: the same kernel with fp32 or bf16 output).  Returns
+    (h float64 [rows, cols], clamp_count int): h = act(clamp(gate)) * clamp(up)
+    in exact arithmetic, the clamp and its count as in act_quant."""
+    gate = np.asarray(gate, np.float64)
+    up = np.asarray(up, np.float64)
+    assert up.shape == gate.shape
+    L = float(clamp_limit)
+    count = int(np.count_nonzero(gate > L) + np.count_nonzero(gate < -L)
+                + np.count_nonzero(up > L) + np.count_nonzero(up < -L))
+    with np.errstate(over="ignore", invalid="ignore"):
+        h = ACTIVATIONS[act](clamp_nan_preserving(gate, L)) * clamp_nan_preserving(up, L)
+    return h, count
+
+
 def act_quant(gate, up, clamp_limit=np.inf, act="silu"):
     """Returns (q [rows, cols] uint8 E4M3 codes, scale [rows, cols/32] uint8,
     clamp_count int, h32 [rows, cols] float32).

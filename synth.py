@@ -8,8 +8,9 @@ arithmetic: only random draws, the rounding of draws to the storage format
 Every draw is a function of (seed, stream id), using numpy's PCG64 generator,
 so any tensor can be regenerated on its own.
 
-Stream ids: x=1, Wg=2, Wu=3, dh=4, gate=5, up=6, specials=7 (+100 per extra
-stream when a recipe needs more than one draw for a tensor).
+Stream ids: x=1, Wg=2, Wu=3, dh=4, gate=5, up=6, specials=7, dy=8, row
+weights=9 (+100 per extra stream when a recipe needs more than one draw for a
+tensor).
 """
 from __future__ import annotations
 

@@ -565,6 +565,24 @@ def test_act_quant_geglu_variant_against_torch_gelu():
     assert not np.array_equal(h32, h_silu)
 
 
+def test_act_fwd_against_torch_and_act_quant():
+    """The non-quantised elementwise forward: torch's silu / tanh GELU (library
+    routines) of the clamped gate times the clamped up; rounded to fp32 it is
+    the h that act_quant quantises; the count is act_quant's."""
+    d = synth.act_quant_f32(8, 64, seed=8)
+    g, u = d["gate"].astype(np.float64), d["up"].astype(np.float64)
+    for act, fn in (("silu", torch.nn.functional.silu),
+                    ("gelu_tanh", lambda t: torch.nn.functional.gelu(t, approximate="tanh"))):
+        h, count = oracle.act_fwd(g, u, 3.0, act)
+        ref = (fn(torch.clamp(torch.from_numpy(g), -3.0, 3.0)) * torch.clamp(torch.from_numpy(u), -3.0, 3.0)).numpy()
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(h), nan)
+        np.testing.assert_allclose(h[~nan], ref[~nan], rtol=1e-13, atol=1e-300)
+        _, _, c2, h32 = oracle.act_quant(g, u, 3.0, act)
+        assert count == c2
+        assert np.array_equal(h.astype(np.float32), h32, equal_nan=True)
+
+
 # ------------------------------------------------------------------- metrics
 
 def test_metrics():
