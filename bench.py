@@ -382,6 +382,18 @@ def act_quant_leg(torch, S, synth, np, dev):
         key = ("no_clamp" if math.isinf(L) else "clamp_7") + ("" if act == "silu" else "_geglu")
         res[key] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
         log(f"act_quant {R}x{C} {key}: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
+    # The non-quantised outputs (fp32 and bf16 h).
+    for dt, nb in ((torch.float32, 4), (torch.bfloat16, 2)):
+        hs = [torch.empty((R, C), dtype=dt, device=dev) for _ in range(copies)]
+        calls = [(lambda i=i: S.act_fwd(G[i], U[i], math.inf, out=(hs[i], None))) for _ in range(4) for i in range(copies)]
+        t, _ = graph_time_per_call(torch, calls)
+        nbytes_h = 2 * R * C * 4 + R * C * nb
+        gbs = nbytes_h / t / 1e9
+        key = "act_fwd_" + ("f32" if nb == 4 else "bf16")
+        res[key] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "bytes_per_call": nbytes_h,
+                    "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"act_fwd {R}x{C} {key}: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
+        del hs
     del G, U, outs
     torch.cuda.empty_cache()
     return res

@@ -208,6 +208,25 @@ int swiglu_fwd_fp8(int act, int64_t M, int64_t N, int64_t K,
                    const void* x, const void* wg, const void* wu,
                    uint8_t* q, uint8_t* scale, float* h_out, void* stream);
 
+/* Elementwise gated activation without quantisation (the fp32 and bf16
+ * output formats of the forward table in "quant: add SwiGLU forward/backward
+ * VMI kernels", TileKernels-PTO PR 20, performance section):
+ *   g' = clamp(gate, -L, L), u' = clamp(up, -L, L)   (NaN passes through)
+ *   h  = act(g') * u', formed in fp64 and rounded once to out_dtype
+ *
+ *   act          SWIGLU_ACT_SILU or SWIGLU_ACT_GELU_TANH
+ *   out_dtype    SWIGLU_F32 or SWIGLU_BF16 (the type of h)
+ *   gate, up     [rows, cols] fp32 inputs
+ *   clamp_limit  L > 0, or +INFINITY for no clamp (NaN or L <= 0: error)
+ *   h            [rows, cols] output
+ *   clamp_count  NULL, or one uint64 (8-byte aligned) overwritten with the
+ *                number of gate and up values with |v| > L (NaN not counted)
+ * Layout rule: cols % 8 == 0.  Unknown act: SWIGLU_ERR_ARG; unknown
+ * out_dtype: SWIGLU_ERR_DTYPE. */
+int swiglu_act_fwd(int act, int out_dtype, int64_t rows, int64_t cols,
+                   const float* gate, const float* up, float clamp_limit,
+                   void* h, uint64_t* clamp_count, void* stream);
+
 /* Elementwise SwiGLU with FP8 block quantisation, one pass ("quant: add
  * SwiGLU forward/backward VMI kernels", TileKernels-PTO PR 20, sections
  * overview and implementation notes):

@@ -42,6 +42,8 @@ SIGNATURES = {
                                            _c_ptr]),
     "swiglu_gemv_fwd_mult": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr,
                                             ctypes.c_float, ctypes.c_float, _c_ptr, _c_ptr]),
+    "swiglu_act_fwd": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.c_float,
+                                      _c_ptr, _c_ptr, _c_ptr]),
     "swiglu_act_quant": (ctypes.c_int, [_c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.c_float, _c_ptr, _c_ptr,
                                         _c_ptr, _c_ptr, _c_ptr]),
     "swiglu_act_quant_act": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.c_float, _c_ptr,

@@ -21,7 +21,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswiglu.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "gemm.hip", "transpose.hip", "gemv.hip", "act_quant.hip", "act_bwd.hip", "probe.hip"]
+SOURCES = ["abi.hip", "gemm.hip", "transpose.hip", "gemv.hip", "act_fwd.hip", "act_quant.hip", "act_bwd.hip",
+           "probe.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

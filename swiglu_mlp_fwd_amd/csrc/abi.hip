@@ -204,6 +204,16 @@ int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K, const void* x, const void* 
   return swiglu_gemv_fwd_act(SWIGLU_ACT_SILU, M, N, K, x, wg, wu, h, stream);
 }
 
+int swiglu_act_fwd(int act, int out_dtype, int64_t rows, int64_t cols, const float* gate, const float* up,
+                   float clamp_limit, void* h, uint64_t* clamp_count, void* stream) {
+  if (act != SWIGLU_ACT_SILU && act != SWIGLU_ACT_GELU_TANH) return SWIGLU_ERR_ARG;
+  int st = swg::validate_act_fwd(out_dtype, rows, cols, gate, up, clamp_limit, h, clamp_count);
+  if (st != SWIGLU_OK) return st;
+  const bool clamp = !isinf(clamp_limit);
+  return hip_status(swg::launch_act_fwd(static_cast<swg::Act>(act), as_dt(out_dtype), rows, cols, gate, up,
+                                        clamp_limit, clamp, h, clamp_count, as_stream(stream)));
+}
+
 int swiglu_act_quant_act(int act, int64_t rows, int64_t cols, const float* gate, const float* up,
                          float clamp_limit, uint8_t* q, uint8_t* scale, uint64_t* clamp_count,
                          float* h_out, void* stream) {

@@ -52,20 +52,6 @@ __device__ __forceinline__ void bwd_elem(float g, float u, float dy, double w, f
   acc += (double)dy * (silu * (double)u);
 }
 
-// fp64 -> bf16 with one rounding (to nearest even): round to fp32 by
-// round-to-odd, then to bf16 by RNE.  Round-to-odd keeps the information
-// the second rounding needs (fp32 has 16 more bits than bf16), so the pair
-// equals a direct RNE of d.
-__device__ __forceinline__ uint32_t bf16_bits_rne(double d) {
-  const float f = (float)d;
-  uint32_t b = f32_bits(f);
-  if ((double)f != d && (b & 1u) == 0u && f == f) {
-    // Inexact with an even last bit: the odd neighbour lies toward d.
-    b += (fabs((double)f) > fabs(d)) ? -1 : 1;
-  }
-  return __builtin_bit_cast(uint16_t, to_bf16(bits_f32(b)));
-}
-
 template <typename T> struct Chunk;
 template <> struct Chunk<float> {
   static constexpr int kN = 4;

@@ -90,6 +90,20 @@ __device__ __forceinline__ void sigmoid_pair_f32(float z, float& s, float& c) {
   if (z != z) s = c = z;
 }
 
+// fp64 -> bf16 with one rounding (to nearest even): round to fp32 by
+// round-to-odd, then to bf16 by RNE.  Round-to-odd keeps the information
+// the second rounding needs (fp32 has 16 more bits than bf16), so the pair
+// equals a direct RNE of d.
+__device__ __forceinline__ uint32_t bf16_bits_rne(double d) {
+  const float f = (float)d;
+  uint32_t b = f32_bits(f);
+  if ((double)f != d && (b & 1u) == 0u && f == f) {
+    // Inexact with an even last bit: the odd neighbour lies toward d.
+    b += (fabs((double)f) > fabs(d)) ? -1 : 1;
+  }
+  return __builtin_bit_cast(uint16_t, to_bf16(bits_f32(b)));
+}
+
 // sigma(z) and SiLU(z) for results that are rounded to bf16 right after:
 // sigma = 1 / (1 + 2^(-z log2 e)) with the hardware exp2 and reciprocal
 // (about 13 VALU slots instead of about 25).  The product z log2 e is

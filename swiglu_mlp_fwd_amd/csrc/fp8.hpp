@@ -41,7 +41,7 @@ __device__ __forceinline__ uint32_t e4m3_pair(float h0, float h1, float s) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(h0 * s, h1 * s, 0, false) & 0xFFFFu;
 }
 
-// h = SiLU(g) * u rounded once to fp32.
+// h = SiLU(g) * u in fp64 (swiglu_value: rounded once to fp32).
 //
 // e^-|g| = p 2^n (exp_neg_split); sigma(|g|) = 1 / (1 + e) and
 // sigma(-|g|) = p r 2^n with r = 1 / (1 + e).  The product g u sigma is
@@ -51,7 +51,7 @@ __device__ __forceinline__ uint32_t e4m3_pair(float h0, float h1, float s) {
 // (sigma below 2^-126), keeps its precision.  fp64 multiplies run at the fp32
 // rate on this chip.  Special values follow IEEE: g = -inf gives 2^n -> 0 and
 // -inf * 0 = NaN; g = +inf gives inf * u; NaN propagates.
-__device__ __forceinline__ float swiglu_value(float g, float u) {
+__device__ __forceinline__ double swiglu_value_d(float g, float u) {
 #pragma clang fp contract(off)
   float p;
   int n;
@@ -61,10 +61,13 @@ __device__ __forceinline__ float swiglu_value(float g, float u) {
   r = __builtin_fmaf(r, __builtin_fmaf(-d, r, 1.0f), r);
   const bool pos = g >= 0.0f;
   const double sig = ldexp((double)(pos ? r : p * r), pos ? 0 : n);
-  return (float)(((double)g * (double)u) * sig);
+  return ((double)g * (double)u) * sig;
 }
 
-// h = GELU_tanh(g) * u rounded once to fp32, GELU_tanh(z) = z sigma(t) with
+__device__ __forceinline__ float swiglu_value(float g, float u) { return (float)swiglu_value_d(g, u); }
+
+// h = GELU_tanh(g) * u in fp64 (gelu_value: rounded once to fp32),
+// GELU_tanh(z) = z sigma(t) with
 // t = 2 sqrt(2/pi) (z + 0.044715 z^3) ("VisualGen MLP: cublasLt GELU-tanh
 // epilogue for the unquantized bf16 path", TensorRT-LLM PR 17693, the GELU
 // tanh activation; (1 + tanh y) / 2 = sigma(2 y)).
@@ -74,7 +77,7 @@ __device__ __forceinline__ float swiglu_value(float g, float u) {
 // |t| ~ 100.  |t| (capped at 1024, where e^-|t| is 0 even in fp64) is split
 // as ah + al with ah = fp32(|t|), |al| <= 2^-14; e^-|t| = p 2^n (1 - al)
 // to well under an ulp, and the rest is as in swiglu_value.
-__device__ __forceinline__ float gelu_value(float g, float u) {
+__device__ __forceinline__ double gelu_value_d(float g, float u) {
 #pragma clang fp contract(off)
   constexpr double kC1 = 1.5957691216057308;      // 2 sqrt(2 / pi)
   constexpr double kC3 = 0.071354816272600254;    // 2 sqrt(2 / pi) * 0.044715
@@ -92,7 +95,9 @@ __device__ __forceinline__ float gelu_value(float g, float u) {
   r = __builtin_fmaf(r, __builtin_fmaf(-d, r, 1.0f), r);
   const bool pos = t >= 0.0;
   const double sig = ldexp((double)(pos ? r : p * r), pos ? 0 : n);
-  return (float)((z * (double)u) * sig);
+  return (z * (double)u) * sig;
 }
+
+__device__ __forceinline__ float gelu_value(float g, float u) { return (float)gelu_value_d(g, u); }
 
 }  // namespace swg

@@ -58,6 +58,9 @@ hipError_t launch_act_bwd(Dt dt, int64_t rows, int64_t cols, const void* gate, c
                           const void* dy, const float* weights, float limit, bool clamp,
                           void* dgate, void* dup, float* wgrad, hipStream_t s);
 
+hipError_t launch_act_fwd(Act act, Dt out, int64_t rows, int64_t cols, const float* gate, const float* up,
+                          float limit, bool clamp, void* h, uint64_t* count, hipStream_t s);
+
 hipError_t launch_act_quant(Act act, int64_t rows, int64_t cols, const float* gate, const float* up,
                             float limit, bool clamp, uint8_t* q, uint8_t* scale,
                             uint64_t* count, float* hout, hipStream_t s);

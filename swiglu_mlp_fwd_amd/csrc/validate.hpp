@@ -151,6 +151,22 @@ inline int validate_fwd_fp8(int64_t M, int64_t N, int64_t K, const void* x, cons
   return SWIGLU_OK;
 }
 
+inline int validate_act_fwd(int out_dtype, int64_t rows, int64_t cols, const float* gate, const float* up,
+                            float L, const void* h, const void* count) {
+  int st = check_dtype(out_dtype);
+  if (st) return st;
+  if (rows < 0 || cols < 0) return SWIGLU_ERR_SHAPE;
+  if (cols % 8 != 0) return SWIGLU_ERR_SHAPE;         // 8-element chunks of the flat array
+  if (rows > 0 && cols > (int64_t(1) << 40) / rows) return SWIGLU_ERR_SHAPE;
+  if (!(L > 0.0f)) return SWIGLU_ERR_ARG;             // rejects NaN, zero and negatives
+  if (count != nullptr && !aligned(count, 8)) return SWIGLU_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return SWIGLU_OK;
+  if ((st = check_ptr(gate))) return st;
+  if ((st = check_ptr(up))) return st;
+  if ((st = check_ptr(h))) return st;
+  return SWIGLU_OK;
+}
+
 inline int validate_act_quant(int64_t rows, int64_t cols, const float* gate, const float* up,
                               float L, const void* q, const void* scale, const void* count,
                               const void* hout) {

@@ -156,6 +156,30 @@ def gemv_fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Ten
     return h.reshape(*lead, N)
 
 
+def act_fwd(gate: torch.Tensor, up: torch.Tensor, clamp_limit: float = math.inf, act: str = "silu",
+            out_dtype: torch.dtype = torch.float32, count: bool = True, out=None):
+    """Elementwise act(clamp(gate)) * clamp(up) without quantisation, fp32 in,
+    fp32 or bf16 out.  Returns (h, clamp_count int64 tensor [1] or None);
+    `out` may pass preallocated (h, count)."""
+    _same(gate, up)
+    if gate.dtype != torch.float32:
+        raise TypeError("act_fwd takes fp32 gate/up")
+    if gate.shape != up.shape:
+        raise ValueError("gate and up must have the same shape")
+    cols = gate.shape[-1]
+    rows = math.prod(gate.shape[:-1])
+    g2 = gate.reshape(rows, cols).contiguous()
+    u2 = up.reshape(rows, cols).contiguous()
+    if out is not None:
+        h, cnt = out
+    else:
+        h = torch.empty((rows, cols), dtype=out_dtype, device=gate.device)
+        cnt = torch.empty(1, dtype=torch.int64, device=gate.device) if count else None
+    check("swiglu_act_fwd", lib().swiglu_act_fwd(_act_code(act), _DT[h.dtype], rows, cols, _p(g2), _p(u2),
+                                                 float(clamp_limit), _p(h), _p(cnt), _stream(gate)))
+    return h.reshape(gate.shape), cnt
+
+
 def act_quant(gate: torch.Tensor, up: torch.Tensor, clamp_limit: float = math.inf,
               count: bool = True, h_out: bool = False, out=None, act: str = "silu"):
     """Elementwise SwiGLU (act "silu") or GeGLU ("gelu_tanh") + 1x32 UE8M0/E4M3

@@ -171,6 +171,19 @@ def test_multiplier_validation(L):
     assert L.swiglu_bwd_act_mult(1, 1, 100, 60, 64, A, A, A, A, 1.0, 1.0, A, A, A, A, need - 1, None) == EWS
 
 
+def test_act_fwd_validation(L):
+    f = L.swiglu_act_fwd
+    assert f(2, 0, 4, 64, A, A, 7.0, A, None, None) == EARG           # unknown activation
+    assert f(0, 5, 4, 64, A, A, 7.0, A, None, None) == EDTYPE         # unknown output type
+    assert f(0, 1, 4, 60, A, A, 7.0, A, None, None) == ESHAPE         # cols % 8
+    assert f(0, 0, 4, 64, A, A, 0.0, A, None, None) == EARG
+    assert f(0, 0, 4, 64, A, A, math.nan, A, None, None) == EARG
+    assert f(0, 0, 4, 64, None, A, 7.0, A, None, None) == ENULL
+    assert f(1, 1, 4, 64, A, A, 7.0, None, None, None) == ENULL
+    assert f(0, 0, 4, 64, A, A, 7.0, MIS, None, None) == EALIGN
+    assert f(0, 0, 4, 64, A, A, 7.0, A, 0x10004, None) == EALIGN       # count: 8-byte aligned
+
+
 def test_fwd_fp8_validation(L):
     f = L.swiglu_fwd_fp8
     assert f(2, 4, 64, 8, A, A, A, A, A, None, None) == EARG           # unknown activation

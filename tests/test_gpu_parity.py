@@ -819,3 +819,66 @@ def test_geglu_autograd():
     assert torch.equal(x.grad.view(torch.int16), dx.view(torch.int16))
     assert torch.equal(wg.grad.view(torch.int16), dwg.view(torch.int16))
     assert torch.equal(wu.grad.view(torch.int16), dwu.view(torch.int16))
+
+
+# ------------------------------------------ non-quantised elementwise forward
+
+def check_act_fwd(gate, up, L, act, out_dtype, what):
+    h, cnt = S.act_fwd(dev_f32(gate), dev_f32(up), L, act=act, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    y = h.float().cpu().numpy().astype(np.float64)
+    r, rc = oracle.act_fwd(gate.astype(np.float64), up.astype(np.float64), L, act)
+    assert int(cnt.item()) == rc, f"{what}: clamp count {int(cnt.item())} != {rc}"
+    bf = out_dtype == torch.bfloat16
+    # The reference is the exact h rounded to the output type; NaN and
+    # infinities (also from overflow of the rounding) must match.
+    rr = bf16_rne_f64(r)[0] if bf else r.astype(np.float32).astype(np.float64)
+    nan = np.isnan(rr)
+    assert np.array_equal(np.isnan(y), nan), f"{what}: NaN pattern"
+    inf = np.isinf(rr)
+    assert np.array_equal(y[inf], rr[inf]) and not np.isinf(y[~inf & ~nan]).any(), f"{what}: inf pattern"
+    fin = ~nan & ~inf
+    if bf:
+        # One rounding: equal to RNE(exact) wherever the exact value is
+        # farther from a bf16 midpoint than the arithmetic error (8 fp32 ulps).
+        q, sp = bf16_rne_f64(r[fin])
+        frac = np.abs(r[fin]) / sp
+        to_mid = np.abs(frac - np.floor(frac) - 0.5) * sp
+        safe = to_mid > 8 * ULP32 * np.abs(r[fin]) + TINY32
+        assert np.array_equal(y[fin][safe], q[safe]), f"{what}: not the single rounding of the exact value"
+        assert np.all(np.abs(y[fin] - r[fin]) <= sp * (1 + 1e-9)), f"{what}: off by more than one bf16 step"
+        log(f"{what}: count {rc}, RNE-exact on {int(safe.sum())} of {safe.size}")
+    else:
+        ulp = f32_ulp_distance(y[fin], rr[fin])
+        assert ulp.max(initial=0) <= H_ULP_MAX, f"{what}: h off by {ulp.max()} ulps"
+        log(f"{what}: count {rc}, max ulp {ulp.max(initial=0)}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
+@pytest.mark.parametrize("L", [math.inf, 7.0])
+def test_act_fwd_full_4001x3584(out_dtype, act, L):
+    d = synth.act_quant_f32(4001, 3584, seed=0)
+    check_act_fwd(d["gate"], d["up"], L, act, out_dtype, f"act_fwd {act} {out_dtype} L={L}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(1, 8), (3, 384), (7, 2056), (0, 64)])
+def test_act_fwd_ragged_and_tails(out_dtype, shape):
+    d = synth.act_quant_f32(*shape, seed=9)
+    for act in ("silu", "gelu_tanh"):
+        check_act_fwd(d["gate"], d["up"], 1.5, act, out_dtype, f"act_fwd {act} {shape} {out_dtype}")
+    rs = np.random.default_rng(11)
+    g = rs.uniform(-13.0, 13.0, (64, 256)).astype(np.float32)
+    u = (rs.standard_normal((64, 256)) * np.exp2(rs.integers(-30, 120, (64, 256)))).astype(np.float32)
+    for act in ("silu", "gelu_tanh"):
+        check_act_fwd(g, u, math.inf, act, out_dtype, f"act_fwd {act} tails {out_dtype}")
+
+
+def test_act_fwd_count_reset_without_clamp():
+    d = synth.act_quant_f32(4, 64, seed=1)
+    cnt = torch.full((1,), 99, dtype=torch.int64, device=DEV)
+    h = torch.empty((4, 64), dtype=torch.float32, device=DEV)
+    S.act_fwd(dev_f32(d["gate"]), dev_f32(d["up"]), math.inf, out=(h, cnt))
+    torch.cuda.synchronize()
+    assert cnt.item() == 0
