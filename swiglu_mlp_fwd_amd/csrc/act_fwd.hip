@@ -23,7 +23,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxBlocks = 1024;       // with the count: one same-address atomic per workgroup
-constexpr int kMaxBlocksFree = 4096;   // without it
+constexpr int kMaxBlocksFree = 8192;   // without it
 constexpr int kUnroll = 4;
 
 template <typename TO> __device__ __forceinline__ void store8(TO* h, int64_t c, const double (&v)[8]);
