@@ -114,12 +114,18 @@ def digest_traffic(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(out))
 
 
+# The translation unit of the forward dual GEMM: the kernel file and the
+# headers it includes.
+FWD_KERNEL_SOURCES = ("common.hpp", "fp8.hpp", "gemm.hip", "gemm.hpp")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources with comments and blank space removed, so
-    that a counter measurement stays valid across comment-only edits."""
+    """Hash of the forward kernel's sources with comments and blank space
+    removed, so that a counter measurement stays valid across comment-only
+    edits and changes to other kernels."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "swiglu_mlp_fwd_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    for fn in FWD_KERNEL_SOURCES:
         with open(os.path.join(csrc, fn), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
