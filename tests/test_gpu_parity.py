@@ -882,3 +882,15 @@ def test_act_fwd_count_reset_without_clamp():
     S.act_fwd(dev_f32(d["gate"]), dev_f32(d["up"]), math.inf, out=(h, cnt))
     torch.cuda.synchronize()
     assert cnt.item() == 0
+
+
+@pytest.mark.parametrize("shape", [(37, 50, 36), (5, 129, 4), (130, 33, 260)])
+def test_fp32_reduction_length_not_a_multiple_of_8(shape):
+    """fp32 rows are 16-byte chunks of 4 values: K % 8 == 4 leaves a half
+    chunk pair in the last k-step, for the forward and every backward GEMM."""
+    M, N, K = shape
+    d = synth.gemm_fp32(M, N, K, seed=18)
+    check_fwd(d, "f32", what=f"fwd fp32 {shape}")
+    check_fwd(d, "f32", what=f"geglu fwd fp32 {shape}", act="gelu_tanh")
+    d["dh"] = synth.normal_f32((M, N), 1.0, 18, synth.STREAM_DH)
+    check_bwd(d, "f32", what=f"bwd fp32 {shape}")
