@@ -25,6 +25,10 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kColsPerBlock = 16;  // 8 waves x 2 half-waves
 
+// x exchanged across the half-waves (measured faster from M = 6 up; below,
+// the extra exchange costs more than the LDS reads it saves).
+template <int M> constexpr bool kSplitX = M >= 6 && M % 2 == 0;
+
 template <int M, Act A>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__ x,
                                                         const bf16* __restrict__ wg,
@@ -40,27 +44,60 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__
 
   const int lane = tid & 63;
   const int hl = lane & 31;
-  const int col = (blockIdx.x * (kThreads / 64) + (tid >> 6)) * 2 + (lane >> 5);
-  if (col >= N) return;
+  const int col0 = (blockIdx.x * (kThreads / 64) + (tid >> 6)) * 2;
+  if (col0 >= N) return;                           // the whole wave is past the end
+  const int col = col0 + (lane >> 5);
+  const bool live = col < N;
+  // A half-wave past the end streams the last column again and stores
+  // nothing, so both halves stay active for the cross-half exchange below.
+  const int ccol = live ? col : N - 1;
 
-  const u32x4* rg = reinterpret_cast<const u32x4*>(wg + (int64_t)col * K);
-  const u32x4* ru = reinterpret_cast<const u32x4*>(wu + (int64_t)col * K);
+  const u32x4* rg = reinterpret_cast<const u32x4*>(wg + (int64_t)ccol * K);
+  const u32x4* ru = reinterpret_cast<const u32x4*>(wu + (int64_t)ccol * K);
   float ag[M], au[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) ag[m] = au[m] = 0.0f;
 
+  if constexpr (kSplitX<M>) {
+    // The two half-waves read the same x chunks.  Each reads half of the
+    // M rows (the lower half rows 0..M/2-1, the upper half the rest) and
+    // v_permlane32_swap hands every lane both halves' values: half the LDS
+    // reads of x per weight chunk.
+    constexpr int H = M / 2;
+    const int mb = (lane >> 5) * H;
+#pragma unroll 2
+    for (int c = hl; c < nch; c += 32) {
+      const u32x4 vg = __builtin_nontemporal_load(rg + c);
+      const u32x4 vu = __builtin_nontemporal_load(ru + c);
+#pragma unroll
+      for (int q = 0; q < H; ++q) {
+        const u32x4 xv = xs[(mb + q) * nch + c];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          // r[0]: the lower half's value (row q), r[1]: the upper half's (row H + q).
+          const auto r = __builtin_amdgcn_permlane32_swap(xv[t], xv[t], false, false);
+          const bf16x2 lo = as_bf16x2(r[0]), hi = as_bf16x2(r[1]);
+          ag[q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vg[t]), lo, ag[q], false);
+          au[q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vu[t]), lo, au[q], false);
+          ag[H + q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vg[t]), hi, ag[H + q], false);
+          au[H + q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vu[t]), hi, au[H + q], false);
+        }
+      }
+    }
+  } else {
 #pragma unroll 4
-  for (int c = hl; c < nch; c += 32) {
-    const u32x4 vg = __builtin_nontemporal_load(rg + c);
-    const u32x4 vu = __builtin_nontemporal_load(ru + c);
+    for (int c = hl; c < nch; c += 32) {
+      const u32x4 vg = __builtin_nontemporal_load(rg + c);
+      const u32x4 vu = __builtin_nontemporal_load(ru + c);
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const u32x4 xv = xs[m * nch + c];
+      for (int m = 0; m < M; ++m) {
+        const u32x4 xv = xs[m * nch + c];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x2 xx = as_bf16x2(xv[t]);
-        ag[m] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vg[t]), xx, ag[m], false);
-        au[m] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vu[t]), xx, au[m], false);
+        for (int t = 0; t < 4; ++t) {
+          const bf16x2 xx = as_bf16x2(xv[t]);
+          ag[m] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vg[t]), xx, ag[m], false);
+          au[m] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vu[t]), xx, au[m], false);
+        }
       }
     }
   }
@@ -72,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__
       au[m] += __shfl_xor(au[m], off, 32);
     }
   }
-  if (hl == 0) {
+  if (live && hl == 0) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const float g = gmul * ag[m], u = umul * au[m];

@@ -262,7 +262,7 @@ def test_gemv_full(M, NK):
     check_fwd(d, "bf16", what=f"gemv M={M} N={N} K={K}", via="gemv")
 
 
-@pytest.mark.parametrize("M", [1, 3, 5, 7, 8])
+@pytest.mark.parametrize("M", [1, 3, 5, 6, 7, 8])
 @pytest.mark.parametrize("NK", [(13, 8), (1, 64), (257, 520)])
 def test_gemv_ragged(M, NK):
     N, K = NK
