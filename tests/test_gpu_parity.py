@@ -894,3 +894,29 @@ def test_fp32_reduction_length_not_a_multiple_of_8(shape):
     check_fwd(d, "f32", what=f"geglu fwd fp32 {shape}", act="gelu_tanh")
     d["dh"] = synth.normal_f32((M, N), 1.0, 18, synth.STREAM_DH)
     check_bwd(d, "f32", what=f"bwd fp32 {shape}")
+
+
+# --------------------------------------------------------- maximum sizes
+
+BF16_MAX_LD = (1 << 22) - 64   # largest bf16 row length the 32-bit tile offsets allow
+
+
+def test_bf16_forward_and_backward_at_the_longest_reduction():
+    """K at the bf16 limit: the tile byte offsets of the DMA path reach their
+    largest values (forward, recompute, dX over 2N and the transposes)."""
+    M, N, K = 3, 5, BF16_MAX_LD
+    d = synth.train_bf16(M, N, K, seed=19)
+    check_fwd(d, "bf16", what=f"fwd bf16 K={K}")
+    check_bwd(d, "bf16", what=f"bwd bf16 K={K}")
+    assert S.lib().swiglu_fwd(1, M, N, K + 64, 0x10000, 0x10000, 0x10000, 0x10000, None) == 7   # UNSUPPORTED
+    torch.cuda.empty_cache()
+
+
+def test_bf16_backward_at_the_largest_token_count():
+    """M at the bf16 limit of the dW reduction (x^T and [dg | du]^T rows of
+    round_up(M, 8) elements)."""
+    M, N, K = BF16_MAX_LD, 3, 8
+    d = synth.train_bf16(M, N, K, seed=20)
+    rows = np.array([0, 1, M // 2, M - 1])
+    check_bwd(d, "bf16", rows=rows, what=f"bwd bf16 M={M}")
+    torch.cuda.empty_cache()
