@@ -20,6 +20,9 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 swg::Dt as_dt(int dtype) { return dtype == SWIGLU_BF16 ? swg::Dt::kBF16 : swg::Dt::kF32; }
 
+// Projection multipliers must be finite (NaN or infinity: SWIGLU_ERR_ARG).
+bool finite_mult(float m) { return isfinite(m); }
+
 // Zero-fill of a dense output through the transpose kernel's padding path
 // (a kernel, not a memset node, so callers may capture it in a graph).
 hipError_t fill_zero(int dtype, void* p, int64_t rows, int64_t cols, hipStream_t s) {
@@ -32,10 +35,6 @@ hipError_t fill_zero(int dtype, void* p, int64_t rows, int64_t cols, hipStream_t
 }  // namespace
 
 extern "C" {
-
-namespace {
-bool finite_mult(float m) { return isfinite(m); }
-}  // namespace
 
 int swiglu_fwd_mult(int act, int dtype, int64_t M, int64_t N, int64_t K, const void* x,
                     const void* wg, const void* wu, float gate_mult, float up_mult, void* h,
