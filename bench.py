@@ -284,6 +284,22 @@ def main():
     log(f"step {t_step * 1e3:.3f} ms ({value:.1f} TFLOP/s); fwd {t_fwd * 1e3:.3f} ms ({fwd_tflops:.1f} TFLOP/s); "
         f"host wall {wall:.2f}s")
 
+    # The dense bf16 rate the chip sustains (register-only MFMA loop), as
+    # context for the roofline fraction against the published peak.
+    sink = torch.empty(1024, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        S.probe_mfma(4096, 1024, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        mfma_flops = S.probe_mfma(4096, 1024, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma_tf = mfma_flops / (e0.elapsed_time(e1) * 1e-3 / 5) / 1e12
+    log(f"mfma probe: {mfma_tf:.1f} TFLOP/s sustained ({mfma_tf / PEAK_BF16_TFLOPS:.3f} of the published peak)")
+    del sink
+
     traffic = load_traffic("fwd_dual_gemm_bf16_8192x14336x4096")
     result = {
         "metric": "fused SwiGLU TFLOP/s (M=8192) + cold GB/s (M=1..8), % of roofline",
@@ -310,6 +326,8 @@ def main():
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "avg_launch_ms": round(t_fwd * 1e3, 4),
+            "mfma_probe_TFLOPs": round(mfma_tf, 1),
+            "frac_of_mfma_probe": round(fwd_tflops / mfma_tf, 4),
         },
         "fwd_ms": round(t_fwd * 1e3, 4),
         "bwd_ms": round((t_step - t_fwd) * 1e3, 4),

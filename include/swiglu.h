@@ -305,6 +305,15 @@ int swiglu_act_bwd_dt(int dtype, int64_t rows, int64_t cols,
 int swiglu_probe_read2(const void* a, const void* b, size_t bytes,
                        uint32_t* sink, void* stream);
 
+/* Measurement aid: the dense bf16 matrix-core rate the chip sustains.
+ * `blocks` workgroups of 8 waves each run `iters` iterations of four
+ * independent v_mfma_f32_32x32x16_bf16 on register operands (no memory
+ * traffic): 2 * 32 * 32 * 16 * 4 * 8 * iters * blocks flop per call.  The
+ * roofline peak of the bf16 kernels is the published one; this gives the
+ * ceiling the chip reaches under its power and clock limits beside it.
+ * `sink` receives one float per workgroup (>= blocks floats). */
+int swiglu_probe_mfma(int iters, int blocks, float* sink, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* swiglu_status_str(int status);
 

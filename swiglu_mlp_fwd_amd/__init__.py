@@ -3,12 +3,13 @@
     h = SiLU(x Wg^T) * (x Wu^T)
 
 Python surface (thin marshalling over the C ABI in include/swiglu.h):
-    fwd, fwd_fp8, bwd, gemv_fwd, act_fwd, act_quant, act_bwd, swiglu (autograd), probe_read2
+    fwd, fwd_fp8, bwd, gemv_fwd, act_fwd, act_quant, act_bwd, swiglu (autograd), probe_read2, probe_mfma
 """
 from ._lib import LIB_PATH, SwigluError, lib  # noqa: F401
 from .ops import (  # noqa: F401
-    SwiGLUFunction, act_bwd, act_fwd, act_quant, bwd, bwd_workspace_bytes, fwd, fwd_fp8, gemv_fwd, probe_read2, swiglu,
+    SwiGLUFunction, act_bwd, act_fwd, act_quant, bwd, bwd_workspace_bytes, fwd, fwd_fp8, gemv_fwd, probe_mfma,
+    probe_read2, swiglu,
 )
 
-__all__ = ["fwd", "fwd_fp8", "bwd", "gemv_fwd", "act_fwd", "act_quant", "act_bwd", "swiglu", "SwiGLUFunction", "probe_read2",
+__all__ = ["fwd", "fwd_fp8", "bwd", "gemv_fwd", "act_fwd", "act_quant", "act_bwd", "swiglu", "SwiGLUFunction", "probe_read2", "probe_mfma",
            "bwd_workspace_bytes", "SwigluError", "lib", "LIB_PATH"]

@@ -52,6 +52,7 @@ SIGNATURES = {
                                       _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "swiglu_act_bwd_dt": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                          ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+    "swiglu_probe_mfma": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_ptr, _c_ptr]),
     "swiglu_probe_read2": (ctypes.c_int, [_c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr, _c_ptr]),
     "swiglu_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "swiglu_last_hip_error": (ctypes.c_int, []),

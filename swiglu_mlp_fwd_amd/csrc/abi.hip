@@ -249,6 +249,13 @@ int swiglu_act_bwd(int64_t rows, int64_t cols, const float* gate, const float* u
                            weight_grad, stream);
 }
 
+int swiglu_probe_mfma(int iters, int blocks, float* sink, void* stream) {
+  if (iters < 0 || blocks < 0) return SWIGLU_ERR_SHAPE;
+  if (iters == 0 || blocks == 0) return SWIGLU_OK;
+  if (sink == nullptr) return SWIGLU_ERR_NULL;
+  return hip_status(swg::launch_probe_mfma(iters, blocks, sink, as_stream(stream)));
+}
+
 int swiglu_probe_read2(const void* a, const void* b, size_t bytes, uint32_t* sink, void* stream) {
   if (bytes % 16 != 0) return SWIGLU_ERR_SHAPE;
   if (bytes == 0) return SWIGLU_OK;

@@ -108,8 +108,11 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(double d) {
 // sigma = 1 / (1 + 2^(-z log2 e)) with the hardware exp2 and reciprocal
 // (about 13 VALU slots instead of about 25).  The product z log2 e is
 // rounded once, so sigma carries a relative error of at most
-// |z| * 2^-24 * ln 2 plus a few ulps: below 1e-5 for |z| < 100, far under
-// the 2^-8 of the bf16 rounding that follows.  Limits follow IEEE:
+// |z| * 2^-24 * ln 2 plus a few ulps: below 1e-5 for -87 < z < 100, far
+// under the 2^-8 of the bf16 rounding that follows.  Below z = -87 sigma
+// leaves the normal fp32 range and from z = -88.7 (2^(-z log2 e) overflows)
+// it is 0, so there SiLU(z) keeps only the absolute accuracy of a result
+// below 2^-126 |z|.  Limits follow IEEE:
 // z -> -inf gives sigma = 0 (2^+inf = inf, 1 / inf = 0), so SiLU(-inf) =
 // -inf * 0 = NaN as in the accurate form; z = +inf gives sigma = 1; NaN
 // propagates.

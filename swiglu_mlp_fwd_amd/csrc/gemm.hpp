@@ -65,6 +65,8 @@ hipError_t launch_act_quant(Act act, int64_t rows, int64_t cols, const float* ga
                             float limit, bool clamp, uint8_t* q, uint8_t* scale,
                             uint64_t* count, float* hout, hipStream_t s);
 
+hipError_t launch_probe_mfma(int iters, int blocks, float* sink, hipStream_t s);
+
 hipError_t launch_probe_read2(const void* a, const void* b, size_t bytes, uint32_t* sink,
                               hipStream_t s);
 

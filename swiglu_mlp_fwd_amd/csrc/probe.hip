@@ -43,7 +43,53 @@ __global__ __launch_bounds__(kThreads) void probe_read2_kernel(const u32x4* __re
   if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+// Matrix-core ceiling probe: back-to-back v_mfma_f32_32x32x16_bf16 on
+// register operands, four independent accumulator chains per wave, eight
+// waves per workgroup, no memory traffic in the loop.  The operands are
+// lane-dependent bf16 values of magnitude 2^-7..2^-6 with random signs, so
+// the datapath toggles as it does on real data.  What it measures is the
+// dense bf16 rate the chip sustains under its power and clock limits, the
+// ceiling a GEMM kernel can approach.
+constexpr int kMfmaThreads = 512;
+
+__global__ __launch_bounds__(kMfmaThreads) void probe_mfma_kernel(int iters, float* sink) {
+  const uint32_t tid = blockIdx.x * kMfmaThreads + threadIdx.x;
+  u32x4 a, b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t ha = (tid * 2654435761u) ^ (0x9E3779B9u * (uint32_t)(j + 1));
+    uint32_t hb = (tid * 2246822519u) ^ (0x85EBCA6Bu * (uint32_t)(j + 7));
+    ha ^= ha >> 15;
+    hb ^= hb >> 13;
+    // Two bf16 per word: exponent 120 (2^-7), random mantissa and sign.
+    a[j] = (0x3C003C00u | (ha & 0x007F007Fu)) | (ha & 0x80008000u);
+    b[j] = (0x3C003C00u | (hb & 0x007F007Fu)) | (hb & 0x80008000u);
+  }
+  const bf16x8 av = __builtin_bit_cast(bf16x8, a), bv = __builtin_bit_cast(bf16x8, b);
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.0f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[c], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[c][e];
+  if (threadIdx.x == 0) sink[blockIdx.x] = s;
+}
+
 }  // namespace
+
+hipError_t launch_probe_mfma(int iters, int blocks, float* sink, hipStream_t s) {
+  if (iters <= 0 || blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)blocks), dim3(kMfmaThreads), 0, s, iters, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_probe_read2(const void* a, const void* b, size_t bytes, uint32_t* sink,
                               hipStream_t s) {

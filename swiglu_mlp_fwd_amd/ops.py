@@ -250,6 +250,14 @@ def act_bwd(gate: torch.Tensor, up: torch.Tensor, dy: torch.Tensor, clamp_limit:
     return dg.reshape(gate.shape), du.reshape(gate.shape), wg
 
 
+def probe_mfma(iters: int, blocks: int, sink: torch.Tensor) -> int:
+    """Register-only bf16 MFMA loop; returns the flops one call performs."""
+    if sink.dtype != torch.float32 or sink.numel() < blocks:
+        raise ValueError("sink must be an fp32 tensor of at least `blocks` elements")
+    check("swiglu_probe_mfma", lib().swiglu_probe_mfma(int(iters), int(blocks), _p(sink), _stream(sink)))
+    return 2 * 32 * 32 * 16 * 4 * 8 * int(iters) * int(blocks)
+
+
 def probe_read2(a: torch.Tensor, b: torch.Tensor, sink: torch.Tensor) -> None:
     """Pure read of two equally sized buffers (cold-read floor measurement)."""
     nbytes = a.numel() * a.element_size()

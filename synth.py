@@ -132,6 +132,17 @@ def gemm_fp32(M: int, N: int, K: int, seed: int = 0) -> dict:
     )
 
 
+def small_int_bf16(M: int, N: int, K: int, seed: int = 0) -> dict:
+    """x, Wg, Wu with integer entries uniform in {-3, ..., 3} as bf16 bits:
+    every product and every partial sum over K < 2^20 is an integer below
+    2^24, so fp32 accumulation in any order is exact."""
+    out = {}
+    for name, shape, stream in (("x", (M, K), STREAM_X), ("wg", (N, K), STREAM_WG), ("wu", (N, K), STREAM_WU)):
+        a = rng(seed, stream).integers(-3, 4, size=shape).astype(np.float32)
+        out[name] = f32_to_bf16_bits(a)
+    return out
+
+
 def act_quant_f32(rows: int, cols: int, seed: int = 0, specials: bool = True) -> dict:
     """Elementwise case: gate,up~N(0,2) fp32 (std 2) with 0.1% +-inf/NaN and 1% subnormals."""
     gate = normal_f32((rows, cols), 2.0, seed, STREAM_GATE)

@@ -222,6 +222,12 @@ def test_act_bwd_format_validation(L):
     assert f(1, 4, 64, A, A, A, None, 7.0, A, None, None, None) == ENULL
 
 
+def test_probe_mfma_validation(L):
+    assert L.swiglu_probe_mfma(-1, 4, A, None) == ESHAPE
+    assert L.swiglu_probe_mfma(4, 4, None, None) == ENULL
+    assert L.swiglu_probe_mfma(0, 4, None, None) == OK
+
+
 def test_probe_validation(L):
     assert L.swiglu_probe_read2(A, A, 17, A, None) == ESHAPE
     assert L.swiglu_probe_read2(None, A, 32, A, None) == ENULL

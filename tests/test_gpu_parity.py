@@ -428,6 +428,14 @@ def test_act_quant_deterministic():
 
 # ------------------------------------------------------------------ probe
 
+def test_probe_mfma_runs():
+    sink = torch.zeros(64, dtype=torch.float32, device=DEV)
+    flops = S.probe_mfma(16, 64, sink)
+    torch.cuda.synchronize()
+    assert flops == 2 * 32 * 32 * 16 * 4 * 8 * 16 * 64
+    assert torch.isfinite(sink).all() and torch.count_nonzero(sink).item() > 0
+
+
 def test_probe_read2_runs():
     a = torch.ones(1 << 20, dtype=torch.int32, device=DEV)
     b = torch.ones(1 << 20, dtype=torch.int32, device=DEV)
@@ -920,3 +928,46 @@ def test_bf16_backward_at_the_largest_token_count():
     rows = np.array([0, 1, M // 2, M - 1])
     check_bwd(d, "bf16", rows=rows, what=f"bwd bf16 M={M}")
     torch.cuda.empty_cache()
+
+
+# ------------------------------------- exact accumulation: integer inputs
+
+@pytest.mark.parametrize("shape", [(300, 520, 264), (129, 127, 4096)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_forward_on_small_integers_is_exact_up_to_the_activation(shape, dt):
+    """x, W in {-3..3}: g and u are exact in fp32 whatever the summation
+    order, so h differs from the exact act(g) u only by the activation and
+    the output rounding: fp32 within 8 ulps of the rounded exact value;
+    bf16 the round-to-nearest-even of the exact value wherever it is not
+    within the short sigma's error of a rounding midpoint.  Where sigma(g)
+    is below the smallest normal fp32 (g < -87.3), both sigma forms lose
+    relative precision (the short one flushes to 0): there |h| < 2^-126 |g u|
+    and only that absolute bound is required."""
+    M, N, K = shape
+    d = synth.small_int_bf16(M, N, K, seed=21)
+    if dt == "f32":
+        d = {k: synth.bf16_bits_to_f32(v) for k, v in d.items()}
+    t = to_dev(d)
+    f = to_f64(d)
+    h = S.fwd(t["x"], t["wg"], t["wu"])
+    torch.cuda.synchronize()
+    y = host_f64(h)
+    r = oracle.glu_fwd(f["x"], f["wg"], f["wu"])
+    g, u = oracle.gate_up(f["x"], f["wg"], f["wu"])
+    tail = oracle.sigmoid(g) < 2.0 ** -126
+    assert np.all(np.abs(y[tail] - r[tail]) <= 2.0 ** -126 * np.abs(g[tail] * u[tail]) + 1e-45)
+    keep = ~tail
+    if dt == "f32":
+        ulp = f32_ulp_distance(y[keep], r[keep].astype(np.float32).astype(np.float64))
+        assert ulp.max() <= H_ULP_MAX, f"fp32 h off by {ulp.max()} ulps"
+        log(f"small-integer fwd fp32 {shape}: max ulp {ulp.max()}, {int(tail.sum())} tail elements")
+    else:
+        yk, rk = y[keep], r[keep]
+        q, sp = bf16_rne_f64(rk)
+        frac = np.abs(rk) / sp
+        to_mid = np.abs(frac - np.floor(frac) - 0.5) * sp
+        safe = to_mid > 2e-5 * np.abs(rk) + 1e-30        # twice the short sigma's relative error bound
+        assert np.array_equal(yk[safe], q[safe]), "bf16 h is not the rounding of the exact value"
+        assert np.all(np.abs(yk - rk) <= sp * (1 + 1e-9)), "bf16 h off by more than one step"
+        log(f"small-integer fwd bf16 {shape}: RNE-exact on {int(safe.sum())} of {safe.size}, "
+            f"{int(tail.sum())} tail elements")
