@@ -34,17 +34,22 @@
 // Tiling: a workgroup owns a BM x BN block tile (rows of A x rows of each
 //   B), k-steps of 128 bytes per row (64 bf16 or 32 fp32), and its waves form
 //   a grid in which each wave owns a sub-tile of every B operand made of
-//   32 x 32 MFMA tiles.  The dual GEMMs use 256 x 128 with 8 waves (4 x 2,
-//   64 x 64 per wave per weight), the single-operand GEMMs 256 x 256 with 8
-//   waves (64 x 128 per wave); both were the fastest of the tile shapes
-//   measured at the 8192 x 14336 x 4096 training shapes.  LDS holds two k-steps
-//   (double buffer); rows are stored as eight 16-byte chunks with the chunk
-//   index XOR-swizzled (swz below) so the 16-byte MFMA operand reads are
-//   free of bank conflicts.
-// MFMA operand mapping: lane l supplies row (l & 31) of its 32-row operand
-// tile and the 16-byte chunk (2 kk + (l >> 5)) of the k-step; the same chunk
-// mapping for A and B makes the products pair up correctly whatever order
-// the matrix core uses within a chunk.
+//   MFMA tiles: 16 x 16 x 32 for the bf16 forward and the single-operand
+//   products (that form sustains about 10 % more throughput on this chip than
+//   32 x 32 x 16), 32 x 32 for the bf16 dSwiGLU recompute (whose dh prefetch
+//   leaves no registers for the larger 16 x 16 fragment set) and for fp32.
+//   The dual GEMMs use 256 x 128 with 8 waves (4 x 2, 64 x 64 per wave per
+//   weight), the single-operand GEMMs 256 x 256 with 8 waves (64 x 128 per
+//   wave); both were the fastest of the tile shapes measured at the
+//   8192 x 14336 x 4096 training shapes.  LDS holds two k-steps (double
+//   buffer); rows are stored as eight 16-byte chunks with the chunk index
+//   XOR-swizzled (swz below) so the 16-byte MFMA operand reads are free of
+//   bank conflicts.
+// MFMA operand mapping (32 x 32): lane l supplies row (l & 31) of its 32-row
+// operand tile and the 16-byte chunk (2 kk + (l >> 5)) of the k-step; the
+// same chunk mapping for A and B makes the products pair up correctly
+// whatever order the matrix core uses within a chunk.  16 x 16 x 32: row
+// (l & 15) and chunk (4 kk + (l >> 4)).
 #include <mutex>
 
 #include "common.hpp"
@@ -154,6 +159,26 @@ template <> struct Mma<float> {
   }
 };
 
+// MFMA accumulator layouts.  kMN = 32 (v_mfma_f32_32x32x*): 16 floats per
+// lane, lane l element e at row 8 (e >> 2) + 4 (l >> 5) + (e & 3), column
+// l & 31.  kMN = 16 (v_mfma_f32_16x16x32_bf16): 4 floats per lane, lane l
+// element e at row 4 (l >> 4) + e, column l & 15.  In both, elements 4q ..
+// 4q + 3 are 4 consecutive rows of one column, and the 16 lanes of a group
+// hold one 16-column run of those rows.
+template <int kMN> struct AccL;
+template <> struct AccL<32> {
+  using V = f32x16;
+  static constexpr int kE = 16;
+  __device__ __forceinline__ static int row(int lane, int e) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+  __device__ __forceinline__ static int col(int lane) { return lane & 31; }
+};
+template <> struct AccL<16> {
+  using V = f32x4;
+  static constexpr int kE = 4;
+  __device__ __forceinline__ static int row(int lane, int e) { return 4 * (lane >> 4) + e; }
+  __device__ __forceinline__ static int col(int lane) { return lane & 15; }
+};
+
 template <typename T> __device__ __forceinline__ T cvt_out(float v);
 template <> __device__ __forceinline__ bf16 cvt_out<bf16>(float v) { return to_bf16(v); }
 template <> __device__ __forceinline__ float cvt_out<float>(float v) { return v; }
@@ -162,23 +187,21 @@ template <typename T> __device__ __forceinline__ float load_in(const T* p);
 template <> __device__ __forceinline__ float load_in<bf16>(const bf16* p) { return from_bf16(*p); }
 template <> __device__ __forceinline__ float load_in<float>(const float* p) { return *p; }
 
-// Epilogue shared by both kernels.  32 x 32 accumulator layout: lane l,
-// element e holds row 8 (e >> 2) + 4 (l >> 5) + (e & 3), column l & 31.
-template <typename T, Epi E, int NB, class TL>
-__device__ __forceinline__ void store_tile(const GemmArgs& p, f32x16 (&acc)[NB][TL::kTM][TL::kTN],
+// Epilogue shared by both kernels, for either accumulator layout.
+template <typename T, Epi E, int NB, class TL, int kMN>
+__device__ __forceinline__ void store_tile(const GemmArgs& p,
+                                           typename AccL<kMN>::V (&acc)[NB][TL::kWM / kMN][TL::kWN / kMN],
                                            int tm, int tn, int wm, int wn, int lane) {
-  constexpr int kBM = TL::kBM, kBN = TL::kBN, kTM = TL::kTM, kTN = TL::kTN;
-  constexpr int kWM = TL::kWM, kWN = TL::kWN;
-  const int r32 = lane & 31;
-  const int half = lane >> 5;
+  constexpr int kBM = TL::kBM, kBN = TL::kBN, kWM = TL::kWM, kWN = TL::kWN;
+  constexpr int kTM = kWM / kMN, kTN = kWN / kMN;
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = tm * kBM + wm * kWM + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-        const int col = tn * kBN + wn * kWN + j * 32 + r32;
+      for (int e = 0; e < AccL<kMN>::kE; ++e) {
+        const int row = tm * kBM + wm * kWM + i * kMN + AccL<kMN>::row(lane, e);
+        const int col = tn * kBN + wn * kWN + j * kMN + AccL<kMN>::col(lane);
         if (row >= p.m || col >= p.n) continue;
         if constexpr (gated_fwd(E)) {
           if (col >= p.ncols) continue;
@@ -331,7 +354,7 @@ __global__ __launch_bounds__(TL::kThreads) void gemm_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
+  store_tile<T, E, NB, TL, 32>(p, acc, tm, tn, wm, wn, lane);
 }
 
 // Epilogue through LDS for 16-bit outputs (used by the DMA kernel once its
@@ -390,23 +413,24 @@ __device__ __forceinline__ void dh_prefetch(const GemmArgs& p, int tm, int tn, i
   }
 }
 
-template <Epi E, int NB, class TL>
-__device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[NB][TL::kTM][TL::kTN],
+template <Epi E, int NB, class TL, int kMN>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs& p,
+                                               typename AccL<kMN>::V (&acc)[NB][TL::kWM / kMN][TL::kWN / kMN],
                                                int tm, int tn, int wm, int wn, int lane, int tid,
                                                char* lds, const DhPre<TL>& pre) {
-  constexpr int kBM = TL::kBM, kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
+  constexpr int kBM = TL::kBM, kWM = TL::kWM, kWN = TL::kWN;
+  constexpr int kTM = kWM / kMN, kTN = kWN / kMN, kE = AccL<kMN>::kE;
   constexpr int kThreads = TL::kThreads;
   constexpr int kCols = EpiLds<E, TL>::kCols;
   constexpr int kPitch = EpiLds<E, TL>::kPitch;
   constexpr int kRegion = EpiLds<E, TL>::kRegion;
   constexpr int kCPR = kCols / 8;                           // 16-byte chunks per row
-  const int r32 = lane & 31, half = lane >> 5;
   const int grow0 = tm * kBM, gcol0 = tn * kCols;
 
   // Staged element (row, col) of region `reg`.
   auto at = [&](int reg, int row, int col) -> char* { return lds + reg * kRegion + row * kPitch + col * 2; };
 
-  float dhv[kTM][kTN][16];
+  float dhv[kTM][kTN][kE];
   if constexpr (gated_bwd(E)) {
     static_assert(DhPre<TL>::kCPR == kCPR && DhPre<TL>::kPer * kThreads == kBM * kCPR, "dh chunk mapping");
     const bf16* dh = static_cast<const bf16*>(p.dh);
@@ -426,15 +450,20 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
       *reinterpret_cast<u32x4*>(at(0, r, ch * 8)) = v;
     }
     __syncthreads();
+    // dh in accumulator layout: one transposing read per 4 consecutive rows
+    // of a 16-column run (lane s16 of the group addresses row s16 / 4,
+    // columns 4 (s16 % 4) .. + 3 of the 4 x 16 block; lane i receives
+    // column i).
     const int s16 = lane & 15;
+    const int run0 = AccL<kMN>::col(lane) - s16;            // first column of the lane's 16-column run
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
 #pragma unroll
-        for (int eq = 0; eq < 4; ++eq) {
-          const int row = wm * kWM + i * 32 + 8 * eq + 4 * half + (s16 >> 2);
-          const int col = wn * kWN + j * 32 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+        for (int eq = 0; eq < kE / 4; ++eq) {
+          const int row = wm * kWM + i * kMN + AccL<kMN>::row(lane, 4 * eq) + (s16 >> 2);
+          const int col = wn * kWN + j * kMN + run0 + 4 * (s16 & 3);
           const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_short4_t*)(lds_char_t*)(at(0, row, col)));
 #pragma unroll
@@ -450,9 +479,9 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = wm * kWM + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-        const int col = wn * kWN + j * 32 + r32;
+      for (int e = 0; e < kE; ++e) {
+        const int row = wm * kWM + i * kMN + AccL<kMN>::row(lane, e);
+        const int col = wn * kWN + j * kMN + AccL<kMN>::col(lane);
         if constexpr (gated_fwd(E)) {
           const float g = p.gmul * acc[0][i][j][e], u = p.umul * acc[NB - 1][i][j][e];
           *reinterpret_cast<bf16*>(at(0, row, col)) = to_bf16(act_bf16out<E>(g) * u);
@@ -556,24 +585,25 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, f32x16 (&acc)[
 // block amax (NaN ignored), the UE8M0 exponent and the 32 codes, and writes
 // 32 code bytes, one scale byte and optionally the fp32 h.  Needs n % 32 == 0
 // (whole blocks), row strides that keep 16-byte alignment.
-template <Epi E, int NB, class TL>
-__device__ __forceinline__ void store_tile_fp8(const GemmArgs& p, f32x16 (&acc)[NB][TL::kTM][TL::kTN],
+template <Epi E, int NB, class TL, int kMN>
+__device__ __forceinline__ void store_tile_fp8(const GemmArgs& p,
+                                               typename AccL<kMN>::V (&acc)[NB][TL::kWM / kMN][TL::kWN / kMN],
                                                int tm, int tn, int wm, int wn, int lane, int tid,
                                                char* lds) {
-  constexpr int kBM = TL::kBM, kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
+  constexpr int kBM = TL::kBM, kWM = TL::kWM, kWN = TL::kWN;
+  constexpr int kTM = kWM / kMN, kTN = kWN / kMN;
   constexpr int kThreads = TL::kThreads;
   constexpr int kCols = EpiLds<E, TL>::kCols;
   constexpr int kPitch = EpiLds<E, TL>::kPitch;
-  const int r32 = lane & 31, half = lane >> 5;
   const int grow0 = tm * kBM, gcol0 = tn * kCols;
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = wm * kWM + i * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-        const int col = wn * kWN + j * 32 + r32;
+      for (int e = 0; e < AccL<kMN>::kE; ++e) {
+        const int row = wm * kWM + i * kMN + AccL<kMN>::row(lane, e);
+        const int col = wn * kWN + j * kMN + AccL<kMN>::col(lane);
         const float g = p.gmul * acc[0][i][j][e], u = p.umul * acc[NB - 1][i][j][e];
         const float h = (E == Epi::kGeGLUq ? gelu_tanh_f32(g) : silu_f32(g)) * u;
         *reinterpret_cast<float*>(lds + row * kPitch + col * 4) = h;
@@ -677,12 +707,15 @@ __device__ __forceinline__ void pin_epilogue_args(const GemmArgs& p) {
 // step whose ring slot is refilled next), issue the DMA of step ks + S - 1,
 // then the MFMAs, with the operand fragments of the next half-step read from
 // LDS while the current ones are in the matrix cores.
-template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL>
+template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL, int kMN>
 __global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(TL::kThreads / 256, TL::kThreads / 256)))
 void gemm_dma_kernel(GemmArgs p) {
   constexpr int kBM = TL::kBM, kBN = TL::kBN, kThreads = TL::kThreads;
   constexpr int kWaves = kThreads / 64;
-  constexpr int kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
+  // kMN x kMN MFMA tiles (32 x 32 x 16 or 16 x 16 x 32): each wave's
+  // sub-tile is kTM x kTN of them.
+  constexpr int kWM = TL::kWM, kWN = TL::kWN, kTM = kWM / kMN, kTN = kWN / kMN;
+  static_assert(kMN == 16 || kMN == 32, "MFMA shape");
   constexpr int kRows = kBM + NB * kBN;                 // LDS rows per k-step
   constexpr int kRowBytes = KC * 16;
   constexpr int kStageBytes = kRows * kRowBytes;
@@ -768,7 +801,8 @@ void gemm_dma_kernel(GemmArgs p) {
     }
   };
 
-  f32x16 acc[NB][kTM][kTN];
+  static_assert(sizeof(T) == 2, "the DMA kernel multiplies bf16");
+  typename AccL<kMN>::V acc[NB][kTM][kTN];
 #pragma unroll
   for (int w = 0; w < NB; ++w)
 #pragma unroll
@@ -776,25 +810,30 @@ void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[w][i][j][e] = 0.0f;
+        for (int e = 0; e < AccL<kMN>::kE; ++e) acc[w][i][j][e] = 0.0f;
 
-  const int r32 = lane & 31;
-  const int half = lane >> 5;
+  // MFMA operand mapping: a sub-step covers 1024 / kMN k (16 for 32 x 32,
+  // 32 for 16 x 16), i.e. kCPS = 64 / kMN chunks; lane l supplies row
+  // l % kMN of its operand tile and chunk kCPS kk + l / kMN of the k-step.
+  // The same chunk mapping for A and B pairs the products.
+  constexpr int kCPS = 64 / kMN;
+  const int rl = lane % kMN;
+  const int ql = lane / kMN;
   auto frag = [&](const char* L, int row, int ch) -> u32x4 {
     const int pc = ch ^ ((row >> kSwzShift) & (KC - 1));
     return *reinterpret_cast<const u32x4*>(L + row * kRowBytes + pc * 16);
   };
 
-  // Operand fragments of one half-step (16 k), double-buffered in registers.
+  // Operand fragments of one sub-step, double-buffered in registers.
   u32x4 av[2][kTM], bv[2][NB][kTN];
   auto read_frags = [&](int buf, const char* L, int kk) {
-    const int ch = 2 * kk + half;
+    const int ch = kCPS * kk + ql;
 #pragma unroll
-    for (int i = 0; i < kTM; ++i) av[buf][i] = frag(L, wm * kWM + i * 32 + r32, ch);
+    for (int i = 0; i < kTM; ++i) av[buf][i] = frag(L, wm * kWM + i * kMN + rl, ch);
 #pragma unroll
     for (int w = 0; w < NB; ++w)
 #pragma unroll
-      for (int j = 0; j < kTN; ++j) bv[buf][w][j] = frag(L, kBM + w * kBN + wn * kWN + j * 32 + r32, ch);
+      for (int j = 0; j < kTN; ++j) bv[buf][w][j] = frag(L, kBM + w * kBN + wn * kWN + j * kMN + rl, ch);
   };
   auto mfmas = [&](int buf) {
 #pragma unroll
@@ -802,7 +841,14 @@ void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < kTN; ++j) Mma<T>::run(acc[w][i][j], av[buf][i], bv[buf][w][j]);
+        for (int j = 0; j < kTN; ++j) {
+          if constexpr (kMN == 16)
+            acc[w][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[buf][i]),
+                                                                   __builtin_bit_cast(bf16x8, bv[buf][w][j]),
+                                                                   acc[w][i][j], 0, 0, 0);
+          else
+            Mma<T>::run(acc[w][i][j], av[buf][i], bv[buf][w][j]);
+        }
   };
   // Wait until at most `later` of this wave's DMA steps are still in flight
   // (DMA completes in issue order, so every earlier step has landed), and
@@ -824,7 +870,7 @@ void gemm_dma_kernel(GemmArgs p) {
   // barrier, refill the slot of the step just consumed with step ks + S, and
   // read the next step's first fragments before the last MFMAs of this
   // step.  So no LDS read latency is exposed in the steady state.
-  constexpr int kKK = KC / 2;
+  constexpr int kKK = KC / kCPS;                        // sub-steps per k-step
   static_assert(kKK % 2 == 0, "the next step's first fragments go to buffer 0");
 #pragma unroll
   for (int s0 = 0; s0 < S; ++s0)
@@ -921,7 +967,7 @@ void gemm_dma_kernel(GemmArgs p) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xC07F);
     barrier_no_fence();
-    store_tile_fp8<E, NB, TL>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes);
+    store_tile_fp8<E, NB, TL, kMN>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes);
   } else {
     if constexpr (sizeof(T) == 2) {
       const bool vec = (p.ldo % 8 == 0) && (!gated_bwd(E) || p.du_off % 8 == 0);
@@ -929,11 +975,11 @@ void gemm_dma_kernel(GemmArgs p) {
         wait_vmcnt<0>();                      // no DMA still landing in the ring
         __builtin_amdgcn_s_waitcnt(0xC07F);   // own LDS reads done
         barrier_no_fence();                   // every wave is done with the ring
-        store_tile_lds<E, NB, TL>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes, dpre);
+        store_tile_lds<E, NB, TL, kMN>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes, dpre);
         return;
       }
     }
-    store_tile<T, E, NB, TL>(p, acc, tm, tn, wm, wn, lane);
+    store_tile<T, E, NB, TL, kMN>(p, acc, tm, tn, wm, wn, lane);
   }
 }
 
@@ -957,7 +1003,7 @@ hipError_t allow_lds(size_t lds) {
   return result[dev];
 }
 
-template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL = 0>
+template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL = 0, int kMN = 16>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   const int ntm = (a.m + TL::kBM - 1) / TL::kBM;
   const int ntn = (a.n + TL::kBN - 1) / TL::kBN;
@@ -966,9 +1012,9 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   const size_t ring = (size_t)S * (TL::kBM + NB * TL::kBN) * KC * 16;
   const size_t epi = sizeof(T) == 2 ? (size_t)EpiLds<E, TL>::kBytes : 0;
   const size_t lds = ring > epi ? ring : epi;
-  const hipError_t attr = allow_lds<&gemm_dma_kernel<T, E, NB, TL, KC, S, kIL>>(lds);
+  const hipError_t attr = allow_lds<&gemm_dma_kernel<T, E, NB, TL, KC, S, kIL, kMN>>(lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_dma_kernel<T, E, NB, TL, KC, S, kIL>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
+  hipLaunchKernelGGL((gemm_dma_kernel<T, E, NB, TL, KC, S, kIL, kMN>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1004,10 +1050,12 @@ hipError_t launch_fwd_dual_fp8(Act act, const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dswiglu(Dt dt, Act act, const GemmArgs& a, hipStream_t s) {
+  // 32 x 32 MFMAs here: with the 16 x 16 fragments (twice the registers per
+  // sub-step) the dh tile prefetched into registers would spill.
   if (act == Act::kGeluTanh)
-    return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDGeGLU, 2, TileDual, 8, 2, 2>(a, s)
+    return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDGeGLU, 2, TileDual, 8, 2, 2, 32>(a, s)
                            : launch<float, Epi::kDGeGLU, 2, TileDual>(a, s);
-  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, 2>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, 2, 32>(a, s)
                          : launch<float, Epi::kDSwiGLU, 2, TileDual>(a, s);
 }
 
