@@ -16,12 +16,15 @@
 // type.  gate, up, dy, dgate and dup are all fp32 or all bf16 (the table's
 // fp32 and bf16 formats); weights and weight_grad are fp32.
 //
-// Mapping: a workgroup of 4 waves per row (grid-stride over rows); lane l
-// of the 256 handles the 16-byte chunks l, l + 256, ... of the row (4 fp32
-// or 8 bf16 elements), kUnroll chunks' loads issued before any is used; the
-// row sum is reduced within each wave with xor shuffles, then across the 4
-// waves through LDS in a fixed order.  (4 waves per row measured faster
-// than 1 or 2 at 4001 x 3584.)
+// Mapping with weight_grad: a workgroup of 4 waves per row (grid-stride over
+// rows); lane l of the 256 handles the 16-byte chunks l, l + 256, ... of the
+// row (4 fp32 or 8 bf16 elements), kUnroll chunks' loads issued before any
+// is used; the row sum is reduced within each wave with xor shuffles, then
+// across the 4 waves through LDS in a fixed order.  (4 waves per row
+// measured faster than 1 or 2 at 4001 x 3584.)  Without weight_grad there is
+// no row sum, and the array is walked flat (grid-stride over all chunks, as
+// the forward kernels), which keeps more loads in flight per lane; a chunk's
+// row (for its weight) comes from one division.
 #include "common.hpp"
 #include "gemm.hpp"
 
@@ -159,6 +162,52 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(const T* __restrict__
   }
 }
 
+// Flat mapping, no weight_grad.  Rows hold whole chunks (cols % kN == 0),
+// so chunk c lies in row c / (cols / kN).
+template <typename T, bool kClamp, bool kWeights>
+__global__ __launch_bounds__(kThreads) void act_bwd_flat_kernel(const T* __restrict__ gate,
+                                                                const T* __restrict__ up,
+                                                                const T* __restrict__ dy,
+                                                                const float* __restrict__ weights, float L,
+                                                                T* __restrict__ dgate, T* __restrict__ dup,
+                                                                int64_t nchunks, int64_t row_chunks) {
+  constexpr int kN = Chunk<T>::kN;
+  constexpr int kUnroll = 4;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(gate);
+  const u32x4* u4 = reinterpret_cast<const u32x4*>(up);
+  const u32x4* d4 = reinterpret_cast<const u32x4*>(dy);
+  u32x4* og = reinterpret_cast<u32x4*>(dgate);
+  u32x4* ou = reinterpret_cast<u32x4*>(dup);
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < nchunks; c0 += kUnroll * stride) {
+    u32x4 G[kUnroll], U[kUnroll], D[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t c = c0 + j * stride;
+      if (c < nchunks) {
+        G[j] = __builtin_nontemporal_load(g4 + c);
+        U[j] = __builtin_nontemporal_load(u4 + c);
+        D[j] = __builtin_nontemporal_load(d4 + c);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const int64_t c = c0 + j * stride;
+      if (c >= nchunks) break;
+      const double w = kWeights ? (double)weights[c / row_chunks] : 1.0;
+      float gv[kN], uv[kN], dv[kN];
+      Chunk<T>::unpack(G[j], gv);
+      Chunk<T>::unpack(U[j], uv);
+      Chunk<T>::unpack(D[j], dv);
+      double a[kN], b[kN], unused = 0.0;
+#pragma unroll
+      for (int e = 0; e < kN; ++e) bwd_elem<kClamp>(gv[e], uv[e], dv[e], w, L, a[e], b[e], unused);
+      __builtin_nontemporal_store(Chunk<T>::pack(a), og + c);
+      __builtin_nontemporal_store(Chunk<T>::pack(b), ou + c);
+    }
+  }
+}
+
 template <typename T> constexpr int kSplitOf = 4;   // waves per row
 
 template <typename T, bool kClamp, bool kWeights, bool kGrad>
@@ -169,11 +218,34 @@ void launch_ab(unsigned grid, const void* gate, const void* up, const void* dy, 
                      static_cast<T*>(dg), static_cast<T*>(du), wgrad, rows, cols);
 }
 
+template <typename T, bool kClamp, bool kWeights>
+void launch_flat(const void* gate, const void* up, const void* dy, const float* w, float L, void* dg, void* du,
+                 int64_t rows, int64_t cols, hipStream_t s) {
+  constexpr int kFlatMaxBlocks = 8192;
+  const int64_t nch = rows * (cols / Chunk<T>::kN);
+  if (nch == 0) return;                                 // no elements (cols == 0)
+  const int64_t want = (nch + kThreads - 1) / kThreads;
+  const unsigned grid = (unsigned)(want < kFlatMaxBlocks ? want : kFlatMaxBlocks);
+  hipLaunchKernelGGL((act_bwd_flat_kernel<T, kClamp, kWeights>), dim3(grid), dim3(kThreads), 0, s,
+                     static_cast<const T*>(gate), static_cast<const T*>(up), static_cast<const T*>(dy), w, L,
+                     static_cast<T*>(dg), static_cast<T*>(du), nch, cols / Chunk<T>::kN);
+}
+
 template <typename T>
 void launch_typed(bool clamp, const void* gate, const void* up, const void* dy,
                   const float* weights, float limit, void* dgate, void* dup, float* wgrad, int64_t rows,
                   int64_t cols, hipStream_t s) {
   const bool w = weights != nullptr, g = wgrad != nullptr;
+  if (!g) {
+    if (clamp) {
+      if (w) launch_flat<T, true, true>(gate, up, dy, weights, limit, dgate, dup, rows, cols, s);
+      else launch_flat<T, true, false>(gate, up, dy, weights, limit, dgate, dup, rows, cols, s);
+    } else {
+      if (w) launch_flat<T, false, true>(gate, up, dy, weights, limit, dgate, dup, rows, cols, s);
+      else launch_flat<T, false, false>(gate, up, dy, weights, limit, dgate, dup, rows, cols, s);
+    }
+    return;
+  }
   constexpr int kRowsPerBlock = kThreads / 64 / kSplitOf<T>;
   const int64_t want = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const unsigned grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);

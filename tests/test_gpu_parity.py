@@ -468,7 +468,15 @@ def check_act_bwd(d, L, use_w, what):
     dev = dev_bf16 if bf else dev_f32
     dg, du, wg = S.act_bwd(dev(g), dev(u), dev(dy), L,
                            weights=None if w is None else dev_f32(w), weight_grad=True)
+    # Without weight_grad the kernel walks the array flat instead of by rows;
+    # every element goes through the same arithmetic, so the bits agree.
+    dg2, du2, wg2 = S.act_bwd(dev(g), dev(u), dev(dy), L,
+                              weights=None if w is None else dev_f32(w), weight_grad=False)
     torch.cuda.synchronize()
+    assert wg2 is None
+    ibits = torch.int16 if bf else torch.int32
+    assert torch.equal(dg2.view(ibits), dg.view(ibits)) and torch.equal(du2.view(ibits), du.view(ibits)), \
+        f"{what}: flat mapping differs from the row mapping"
     assert dg.dtype == (torch.bfloat16 if bf else torch.float32)
     dg, du = dg.float().cpu().numpy().astype(np.float64), du.float().cpu().numpy().astype(np.float64)
     wg = wg.cpu().numpy().astype(np.float64)
