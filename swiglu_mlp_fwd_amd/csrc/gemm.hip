@@ -38,10 +38,11 @@
 //   products (that form sustains about 10 % more throughput on this chip than
 //   32 x 32 x 16), 32 x 32 for the bf16 dSwiGLU recompute (whose dh prefetch
 //   leaves no registers for the larger 16 x 16 fragment set) and for fp32.
-//   The dual GEMMs use 256 x 128 with 8 waves (4 x 2, 64 x 64 per wave per
-//   weight), the single-operand GEMMs 256 x 256 with 8 waves (64 x 128 per
-//   wave); both were the fastest of the tile shapes measured at the
-//   8192 x 14336 x 4096 training shapes.  LDS holds two k-steps (double
+//   In bf16 the dual GEMMs use 256 x 128 with 8 waves (4 x 2, 64 x 64 per
+//   wave per weight), the single-operand GEMMs 256 x 256 with 8 waves
+//   (64 x 128 per wave); both were the fastest of the tile shapes measured
+//   at the 8192 x 14336 x 4096 training shapes.  fp32 uses 128 x 64 and
+//   128 x 128 with 4 waves, two workgroups per CU (TileDualF32 below).  LDS holds two k-steps (double
 //   buffer); rows are stored as eight 16-byte chunks with the chunk index
 //   XOR-swizzled (swz below) so the 16-byte MFMA operand reads are free of
 //   bank conflicts.
@@ -60,15 +61,16 @@ namespace swg {
 
 namespace {
 
-constexpr int kChunks = 8;          // 16-byte chunks per row per k-step
 constexpr int kGroupM = 8;          // tile raster: groups of 8 row-tiles
 
 // Block tile kBM x kBN (rows of A x rows of each B), waves in a kWGM x kWGN
 // grid, each wave owning (kBM / kWGM) x (kBN / kWGN) of every B operand.
-template <int BM_, int BN_, int WGM_, int WGN_>
+template <int BM_, int BN_, int WGM_, int WGN_, int OCC_ = 0>
 struct Tile {
   static constexpr int kBM = BM_, kBN = BN_, kWGM = WGM_, kWGN = WGN_;
   static constexpr int kThreads = 64 * WGM_ * WGN_;
+  // Waves per SIMD the register budget is sized for (default: one workgroup per CU).
+  static constexpr int kOcc = OCC_ > 0 ? OCC_ : kThreads / 256;
   static constexpr int kWM = BM_ / WGM_, kWN = BN_ / WGN_;   // wave tile
   static constexpr int kTM = kWM / 32, kTN = kWN / 32;       // 32x32 MFMA tiles per wave
 };
@@ -127,14 +129,12 @@ __device__ __forceinline__ float act_bf16out(float g) {
   }
 }
 
-// Physical 16-byte chunk of logical chunk c in LDS row r.  gfx950 serves a
-// 128-bit LDS read for 16 lanes per cycle across 64 four-byte banks, i.e.
-// 16 distinct 16-byte bank groups (group = (8 r + chunk) mod 16 for 128-byte
-// rows).  The MFMA operand reads put 16 consecutive rows at one logical
-// chunk in a lane group; XOR-ing the chunk with (r >> 1) & 7 gives those 16
-// rows 16 distinct groups, and keeps the 16-byte stores of 2 full rows per
-// 16 lanes conflict-free.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+// LDS swizzle: the physical 16-byte chunk of logical chunk c in LDS row r
+// is c ^ ((r >> 1) & 7) for 128-byte rows.  gfx950 serves a 128-bit LDS read
+// for 16 lanes per cycle across 64 four-byte banks, i.e. 16 distinct 16-byte
+// bank groups (group = (8 r + chunk) mod 16 for 128-byte rows).  The MFMA
+// operand reads put 16 consecutive rows at one logical chunk in a lane group;
+// the XOR gives those 16 rows 16 distinct groups.
 
 // Largest row count a block tile of either operand has.
 template <int BM, int BN>
@@ -187,7 +187,8 @@ template <typename T> __device__ __forceinline__ float load_in(const T* p);
 template <> __device__ __forceinline__ float load_in<bf16>(const bf16* p) { return from_bf16(*p); }
 template <> __device__ __forceinline__ float load_in<float>(const float* p) { return *p; }
 
-// Epilogue shared by both kernels, for either accumulator layout.
+// Scalar epilogue (fp32 outputs, and bf16 outputs whose row stride is not a
+// whole number of 16-byte chunks), for either accumulator layout.
 template <typename T, Epi E, int NB, class TL, int kMN>
 __device__ __forceinline__ void store_tile(const GemmArgs& p,
                                            typename AccL<kMN>::V (&acc)[NB][TL::kWM / kMN][TL::kWN / kMN],
@@ -234,127 +235,6 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p,
           out[col] = cvt_out<T>(acc[0][i][j][e]);
         }
       }
-}
-
-template <typename T, Epi E, int NB, class TL>
-__global__ __launch_bounds__(TL::kThreads) void gemm_kernel(GemmArgs p) {
-  constexpr int kBM = TL::kBM, kBN = TL::kBN, kThreads = TL::kThreads;
-  constexpr int kTM = TL::kTM, kTN = TL::kTN, kWM = TL::kWM, kWN = TL::kWN;
-  constexpr int kRows = kBM + NB * kBN;                 // LDS rows per k-step
-  constexpr int kUnits = kRows * kChunks / kThreads;    // 16-byte loads per thread
-  constexpr int kPer = Mma<T>::kPerChunk;
-  extern __shared__ u32x4 lds[];                        // [2][kRows * kChunks]
-
-  const int ntm = (p.m + kBM - 1) / kBM;
-  const int ntn = (p.n + kBN - 1) / kBN;
-  const int tile = xcd_remap(blockIdx.x, ntm * ntn);
-  const int group = kGroupM * ntn;
-  const int first_m = (tile / group) * kGroupM;
-  const int gm = min(ntm - first_m, kGroupM);
-  const int tm = first_m + (tile % group) % gm;
-  const int tn = (tile % group) / gm;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  // Wave index through readfirstlane: the compiler then knows it is uniform,
-  // so LDS-DMA bases (M0) and buffer descriptors stay in scalar registers.
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / TL::kWGN, wn = wave % TL::kWGN;
-
-  const T* A = static_cast<const T*>(p.a);
-  const T* B0 = static_cast<const T*>(p.b0);
-  const T* B1 = static_cast<const T*>(p.b1);
-  const int nchunk_r = p.r / kPer;                      // r % kPer == 0 (host-checked)
-  const int nk = (nchunk_r + kChunks - 1) / kChunks;
-
-  // Global -> register staging of one k-step.  Thread t moves the 16-byte
-  // chunk (t & 7) of rows (t >> 3) + (kThreads / 8) i of each operand tile.
-  constexpr int kRowsPerPass = kThreads / kChunks;
-  constexpr int kUA = kBM / kRowsPerPass;               // loads for A
-  constexpr int kUB = kBN / kRowsPerPass;               // loads per B
-  static_assert(kUnits == kUA + NB * kUB, "staging split");
-  const int trow = tid >> 3, tch = tid & 7;
-  u32x4 stage[kUnits];
-  auto gload = [&](int ks) {
-    const int kc = ks * kChunks + tch;
-    const bool kin = kc < nchunk_r;
-    const int64_t koff = (int64_t)kc * kPer;
-#pragma unroll
-    for (int i = 0; i < kUA; ++i) {
-      const int g = tm * kBM + trow + kRowsPerPass * i;
-      stage[i] = (kin && g < p.arows) ? *reinterpret_cast<const u32x4*>(A + (int64_t)g * p.lda + koff)
-                                      : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int w = 0; w < NB; ++w) {
-      const T* B = w == 0 ? B0 : B1;
-#pragma unroll
-      for (int i = 0; i < kUB; ++i) {
-        const int g = tn * kBN + trow + kRowsPerPass * i;
-        stage[kUA + w * kUB + i] =
-            (kin && g < p.brows) ? *reinterpret_cast<const u32x4*>(B + (int64_t)g * p.ldb + koff)
-                                 : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-    u32x4* L = lds + buf * (kRows * kChunks);
-#pragma unroll
-    for (int i = 0; i < kUnits; ++i) {
-      const int row = trow + kRowsPerPass * i;          // rows of A, then B0, then B1
-      L[row * kChunks + swz(row, tch)] = stage[i];
-    }
-  };
-
-  f32x16 acc[NB][kTM][kTN];
-#pragma unroll
-  for (int w = 0; w < NB; ++w)
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kTN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[w][i][j][e] = 0.0f;
-
-  if (nk > 0) {
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    if (nk > 1) gload(1);
-  }
-  const int r32 = lane & 31;
-  const int half = lane >> 5;
-  for (int ks = 0; ks < nk; ++ks) {
-    const u32x4* L = lds + (ks & 1) * (kRows * kChunks);
-#pragma unroll
-    for (int kk = 0; kk < kChunks / 2; ++kk) {
-      const int ch = 2 * kk + half;
-      u32x4 av[kTM], bv[NB][kTN];
-#pragma unroll
-      for (int i = 0; i < kTM; ++i) {
-        const int row = wm * kWM + i * 32 + r32;
-        av[i] = L[row * kChunks + swz(row, ch)];
-      }
-#pragma unroll
-      for (int w = 0; w < NB; ++w)
-#pragma unroll
-        for (int j = 0; j < kTN; ++j) {
-          const int row = kBM + w * kBN + wn * kWN + j * 32 + r32;
-          bv[w][j] = L[row * kChunks + swz(row, ch)];
-        }
-#pragma unroll
-      for (int w = 0; w < NB; ++w)
-#pragma unroll
-        for (int i = 0; i < kTM; ++i)
-#pragma unroll
-          for (int j = 0; j < kTN; ++j) Mma<T>::run(acc[w][i][j], av[i], bv[w][j]);
-    }
-    if (ks + 1 < nk) lstore((ks + 1) & 1);
-    if (ks + 2 < nk) gload(ks + 2);
-    __syncthreads();
-  }
-
-  store_tile<T, E, NB, TL, 32>(p, acc, tm, tn, wm, wn, lane);
 }
 
 // Epilogue through LDS for 16-bit outputs (used by the DMA kernel once its
@@ -693,10 +573,10 @@ __device__ __forceinline__ void pin_epilogue_args(const GemmArgs& p) {
   asm volatile("" ::"s"(p.ldt), "s"(p.q_scale), "s"(p.q_h), "s"(p.gmul), "s"(p.umul));
 }
 
-// Second GEMM kernel, used for bf16: the operand tiles go from global memory
+// The GEMM kernel (bf16 and fp32): the operand tiles go from global memory
 // straight into LDS (buffer_load_dwordx4 ... lds, the gfx950 16-byte LDS
 // DMA), through an S-stage ring of KC-chunk k-steps, with no register
-// staging.  Each wave moves a fixed slab of 64 rows of the stage (all in one
+// staging.  Each wave moves a fixed slab of rows of the stage (all in one
 // operand); a DMA instruction writes 1 KiB of LDS in lane order, so the
 // XOR swizzle is applied on the global side: the lane that lands in
 // physical chunk q of row r fetches logical chunk q ^ swizzle(r).  Buffer
@@ -708,7 +588,7 @@ __device__ __forceinline__ void pin_epilogue_args(const GemmArgs& p) {
 // then the MFMAs, with the operand fragments of the next half-step read from
 // LDS while the current ones are in the matrix cores.
 template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL, int kMN>
-__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(TL::kThreads / 256, TL::kThreads / 256)))
+__global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(TL::kOcc, TL::kOcc)))
 void gemm_dma_kernel(GemmArgs p) {
   constexpr int kBM = TL::kBM, kBN = TL::kBN, kThreads = TL::kThreads;
   constexpr int kWaves = kThreads / 64;
@@ -771,7 +651,8 @@ void gemm_dma_kernel(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t rsrc = uniform_rsrc(base, valid * ld * (int64_t)sizeof(T));
   // Lane i of DMA d fills physical chunk (i % KC) of stage row
   // rr = row0 + d * kRowsPerDma + i / KC and fetches logical chunk
-  // (i % KC) ^ swz(rr).  row0 is a multiple of 64, so swz(rr) depends on d
+  // (i % KC) ^ swz(rr), swz(rr) = (rr >> kSwzShift) & (KC - 1).  row0 is a
+  // multiple of 32, so swz(rr) depends on d
   // only through d's low bits: one chunk index per residue of d, and a row
   // offset that is linear in d (kept in two registers per lane).
   constexpr int kLchPeriod = (KC == 8) ? 2 : 1;
@@ -801,7 +682,7 @@ void gemm_dma_kernel(GemmArgs p) {
     }
   };
 
-  static_assert(sizeof(T) == 2, "the DMA kernel multiplies bf16");
+  static_assert(sizeof(T) == 2 || kMN == 32, "fp32 operands use the 32 x 32 x 2 MFMA");
   typename AccL<kMN>::V acc[NB][kTM][kTN];
 #pragma unroll
   for (int w = 0; w < NB; ++w)
@@ -1018,30 +899,23 @@ hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, Epi E, int NB, class TL>
-hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  const int ntm = (a.m + TL::kBM - 1) / TL::kBM;
-  const int ntn = (a.n + TL::kBN - 1) / TL::kBN;
-  const int64_t tiles = (int64_t)ntm * ntn;
-  if (tiles == 0) return hipSuccess;
-  const size_t lds = 2u * (TL::kBM + NB * TL::kBN) * kChunks * sizeof(u32x4);
-  const hipError_t attr = allow_lds<&gemm_kernel<T, E, NB, TL>>(lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_kernel<T, E, NB, TL>), dim3((unsigned)tiles), dim3(TL::kThreads), lds, s, a);
-  return hipGetLastError();
-}
-
 using TileDual = Tile<256, 128, 4, 2>;   // 8 waves, 64 x 64 per wave per weight
 using TileSingle = Tile<256, 256, 4, 2>; // 8 waves, 64 x 128 per wave
+// fp32: the matrix cores take 16 times longer per operand byte, so small
+// tiles cost little in operand traffic, and they fill the 256 CUs more
+// evenly (4001 x 3584: 1,792 tiles of 128 x 64 against 448 of 256 x 128);
+// 4 waves, two workgroups per CU.
+using TileDualF32 = Tile<128, 64, 2, 2, 2>;     // 64 x 32 per wave per weight
+using TileSingleF32 = Tile<128, 128, 2, 2, 2>;  // 64 x 64 per wave
 
 }  // namespace
 
 hipError_t launch_fwd_dual(Dt dt, Act act, const GemmArgs& a, hipStream_t s) {
   if (act == Act::kGeluTanh)
     return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kGeGLU, 2, TileDual, 8, 2, 2>(a, s)
-                           : launch<float, Epi::kGeGLU, 2, TileDual>(a, s);
+                           : launch_dma<float, Epi::kGeGLU, 2, TileDualF32, 8, 2, 2, 32>(a, s);
   return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2, 2>(a, s)
-                         : launch<float, Epi::kSwiGLU, 2, TileDual>(a, s);
+                         : launch_dma<float, Epi::kSwiGLU, 2, TileDualF32, 8, 2, 2, 32>(a, s);
 }
 
 hipError_t launch_fwd_dual_fp8(Act act, const GemmArgs& a, hipStream_t s) {
@@ -1054,14 +928,14 @@ hipError_t launch_bwd_dswiglu(Dt dt, Act act, const GemmArgs& a, hipStream_t s) 
   // sub-step) the dh tile prefetched into registers would spill.
   if (act == Act::kGeluTanh)
     return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDGeGLU, 2, TileDual, 8, 2, 2, 32>(a, s)
-                           : launch<float, Epi::kDGeGLU, 2, TileDual>(a, s);
+                           : launch_dma<float, Epi::kDGeGLU, 2, TileDualF32, 8, 2, 2, 32>(a, s);
   return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, 2, 32>(a, s)
-                         : launch<float, Epi::kDSwiGLU, 2, TileDual>(a, s);
+                         : launch_dma<float, Epi::kDSwiGLU, 2, TileDualF32, 8, 2, 2, 32>(a, s);
 }
 
 hipError_t launch_gemm_store(Dt dt, const GemmArgs& a, hipStream_t s) {
   return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kStore, 1, TileSingle, 8, 2, 2>(a, s)
-                         : launch<float, Epi::kStore, 1, TileSingle>(a, s);
+                         : launch_dma<float, Epi::kStore, 1, TileSingleF32, 8, 2, 2, 32>(a, s);
 }
 
 }  // namespace swg
