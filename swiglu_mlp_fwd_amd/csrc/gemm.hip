@@ -585,7 +585,7 @@ __device__ __forceinline__ void pin_epilogue_args(const GemmArgs& p) {
 // zero with no branch.  Per k-step: wait for this wave's DMA of the step,
 // one barrier (every wave's data has landed, and every wave has finished the
 // step whose ring slot is refilled next), issue the DMA of step ks + S - 1,
-// then the MFMAs, with the operand fragments of the next half-step read from
+// then the MFMAs, with the operand fragments of the next sub-step read from
 // LDS while the current ones are in the matrix cores.
 template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL, int kMN>
 __global__ __launch_bounds__(TL::kThreads) __attribute__((amdgpu_waves_per_eu(TL::kOcc, TL::kOcc)))
@@ -693,9 +693,10 @@ void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
         for (int e = 0; e < AccL<kMN>::kE; ++e) acc[w][i][j][e] = 0.0f;
 
-  // MFMA operand mapping: a sub-step covers 1024 / kMN k (16 for 32 x 32,
-  // 32 for 16 x 16), i.e. kCPS = 64 / kMN chunks; lane l supplies row
-  // l % kMN of its operand tile and chunk kCPS kk + l / kMN of the k-step.
+  // MFMA operand mapping: a sub-step covers kCPS = 64 / kMN 16-byte chunks
+  // of the k-step (16 bf16 k for 32 x 32 x 16, 32 for 16 x 16 x 32, 8 fp32 k
+  // for 32 x 32 x 2 taken 4 MFMAs at a time); lane l supplies row l % kMN of
+  // its operand tile and chunk kCPS kk + l / kMN of the k-step.
   // The same chunk mapping for A and B pairs the products.
   constexpr int kCPS = 64 / kMN;
   const int rl = lane % kMN;
@@ -745,9 +746,9 @@ void gemm_dma_kernel(GemmArgs p) {
   };
 
   // Schedule.  The ring holds S steps; the prologue fills it.  The
-  // fragments of half-step kk + 1 are read before the MFMAs of half-step kk
+  // fragments of sub-step kk + 1 are read before the MFMAs of sub-step kk
   // (scheduling fences keep the two register sets apart), and the step
-  // boundary sits inside the last half-step: wait for the next step's DMA,
+  // boundary sits inside the last sub-step: wait for the next step's DMA,
   // barrier, refill the slot of the step just consumed with step ks + S, and
   // read the next step's first fragments before the last MFMAs of this
   // step.  So no LDS read latency is exposed in the steady state.
@@ -774,7 +775,7 @@ void gemm_dma_kernel(GemmArgs p) {
       constexpr int kRd = kTM + NB * kTN;
       if (kk + 1 < kKK) {
         if constexpr (kIL >= 2) {
-          // Fragment reads of the next half-step spread between the MFMAs.
+          // Fragment reads of the next sub-step spread between the MFMAs.
           __builtin_amdgcn_sched_barrier(0);
           read_frags((kk + 1) & 1, L, kk + 1);
           mfmas(kk & 1);
@@ -814,7 +815,7 @@ void gemm_dma_kernel(GemmArgs p) {
           }
           read_frags(0, lds_bytes + ((ks + 1) % S) * kStageBytes, 0);
           // The DMA instructions of the refill go one by one between the
-          // MFMAs of this half-step instead of stalling the matrix core.
+          // MFMAs of this sub-step instead of stalling the matrix core.
           __builtin_amdgcn_sched_barrier(0);
           issue(ks + S);
           mfmas(kk & 1);
