@@ -42,10 +42,10 @@
 //   wave per weight), the single-operand GEMMs 256 x 256 with 8 waves
 //   (64 x 128 per wave); both were the fastest of the tile shapes measured
 //   at the 8192 x 14336 x 4096 training shapes.  fp32 uses 128 x 64 and
-//   128 x 128 with 4 waves, two workgroups per CU (TileDualF32 below).  LDS holds two k-steps (double
-//   buffer); rows are stored as eight 16-byte chunks with the chunk index
-//   XOR-swizzled (swz below) so the 16-byte MFMA operand reads are free of
-//   bank conflicts.
+//   128 x 128 with 4 waves, two workgroups per CU (TileDualF32 below).
+//   LDS holds two k-steps (double buffer); rows are stored as eight 16-byte
+//   chunks with the chunk index XOR-swizzled (see the LDS swizzle below) so
+//   the 16-byte MFMA operand reads are free of bank conflicts.
 // MFMA operand mapping (32 x 32): lane l supplies row (l & 31) of its 32-row
 // operand tile and the 16-byte chunk (2 kk + (l >> 5)) of the k-step; the
 // same chunk mapping for A and B makes the products pair up correctly
