@@ -72,7 +72,6 @@ struct Tile {
   // Waves per SIMD the register budget is sized for (default: one workgroup per CU).
   static constexpr int kOcc = OCC_ > 0 ? OCC_ : kThreads / 256;
   static constexpr int kWM = BM_ / WGM_, kWN = BN_ / WGN_;   // wave tile
-  static constexpr int kTM = kWM / 32, kTN = kWN / 32;       // 32x32 MFMA tiles per wave
 };
 
 enum class Epi { kSwiGLU, kGeGLU, kDSwiGLU, kStore, kSwiGLUq, kGeGLUq, kDGeGLU };
