@@ -286,17 +286,21 @@ def main():
 
     # The dense bf16 rate the chip sustains (register-only MFMA loop), as
     # context for the roofline fraction against the published peak.
+    # The clock takes a few calls to settle under this load: the best of three
+    # rounds of five calls after a warm-up.
     sink = torch.empty(1024, dtype=torch.float32, device=dev)
-    for _ in range(2):
+    for _ in range(3):
         S.probe_mfma(4096, 1024, sink)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        mfma_flops = S.probe_mfma(4096, 1024, sink)
-    e1.record()
-    torch.cuda.synchronize()
-    mfma_tf = mfma_flops / (e0.elapsed_time(e1) * 1e-3 / 5) / 1e12
+    mfma_tf = 0.0
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            mfma_flops = S.probe_mfma(4096, 1024, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        mfma_tf = max(mfma_tf, mfma_flops / (e0.elapsed_time(e1) * 1e-3 / 5) / 1e12)
     log(f"mfma probe: {mfma_tf:.1f} TFLOP/s sustained ({mfma_tf / PEAK_BF16_TFLOPS:.3f} of the published peak)")
     del sink
 

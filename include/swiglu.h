@@ -306,9 +306,10 @@ int swiglu_probe_read2(const void* a, const void* b, size_t bytes,
                        uint32_t* sink, void* stream);
 
 /* Measurement aid: the dense bf16 matrix-core rate the chip sustains.
- * `blocks` workgroups of 8 waves each run `iters` iterations of four
- * independent v_mfma_f32_32x32x16_bf16 on register operands (no memory
- * traffic): 2 * 32 * 32 * 16 * 4 * 8 * iters * blocks flop per call.  The
+ * `blocks` workgroups of 8 waves each run `iters` iterations of eight
+ * independent v_mfma_f32_16x16x32_bf16 (the form the bf16 forward uses) on
+ * register operands (no memory traffic): 2 * 16 * 16 * 32 * 8 * 8 * iters *
+ * blocks flop per call.  The
  * roofline peak of the bf16 kernels is the published one; this gives the
  * ceiling the chip reaches under its power and clock limits beside it.
  * `sink` receives one float per workgroup (>= blocks floats). */

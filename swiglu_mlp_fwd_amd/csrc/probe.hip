@@ -43,9 +43,10 @@ __global__ __launch_bounds__(kThreads) void probe_read2_kernel(const u32x4* __re
   if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
-// Matrix-core ceiling probe: back-to-back v_mfma_f32_32x32x16_bf16 on
-// register operands, four independent accumulator chains per wave, eight
-// waves per workgroup, no memory traffic in the loop.  The operands are
+// Matrix-core ceiling probe: back-to-back v_mfma_f32_16x16x32_bf16 (the
+// form the forward and the dX/dW products use) on register operands, eight
+// independent accumulator chains per wave, eight waves per workgroup, no
+// memory traffic in the loop.  The operands are
 // lane-dependent bf16 values of magnitude 2^-7..2^-6 with random signs, so
 // the datapath toggles as it does on real data.  What it measures is the
 // dense bf16 rate the chip sustains under its power and clock limits, the
@@ -66,20 +67,20 @@ __global__ __launch_bounds__(kMfmaThreads) void probe_mfma_kernel(int iters, flo
     b[j] = (0x3C003C00u | (hb & 0x007F007Fu)) | (hb & 0x80008000u);
   }
   const bf16x8 av = __builtin_bit_cast(bf16x8, a), bv = __builtin_bit_cast(bf16x8, b);
-  f32x16 acc[4];
+  f32x4 acc[8];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < 8; ++c)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[c][e] = 0.0f;
+    for (int e = 0; e < 4; ++e) acc[c][e] = 0.0f;
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[c], 0, 0, 0);
+    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[c], 0, 0, 0);
   }
   float s = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < 8; ++c)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s += acc[c][e];
+    for (int e = 0; e < 4; ++e) s += acc[c][e];
   if (threadIdx.x == 0) sink[blockIdx.x] = s;
 }
 

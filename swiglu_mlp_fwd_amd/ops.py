@@ -255,7 +255,7 @@ def probe_mfma(iters: int, blocks: int, sink: torch.Tensor) -> int:
     if sink.dtype != torch.float32 or sink.numel() < blocks:
         raise ValueError("sink must be an fp32 tensor of at least `blocks` elements")
     check("swiglu_probe_mfma", lib().swiglu_probe_mfma(int(iters), int(blocks), _p(sink), _stream(sink)))
-    return 2 * 32 * 32 * 16 * 4 * 8 * int(iters) * int(blocks)
+    return 2 * 16 * 16 * 32 * 8 * 8 * int(iters) * int(blocks)
 
 
 def probe_read2(a: torch.Tensor, b: torch.Tensor, sink: torch.Tensor) -> None:
