@@ -67,9 +67,10 @@ enum swiglu_dtype { SWIGLU_F32 = 0, SWIGLU_BF16 = 1 };
  *
  *   x  [M, K], wg [N, K], wu [N, K]  (inputs, dtype)
  *   h  [M, N]                        (output, dtype)
- * Layout rule: K % 8 == 0 for bf16 and K % 4 == 0 for fp32 (16-byte rows);
- * bf16 also needs K <= 2^22 - 64 (else SWIGLU_ERR_UNSUPPORTED).
- * K == 0 gives h = 0. */
+ * Layout rule: K % 8 == 0 for bf16 and K % 4 == 0 for fp32 (16-byte rows),
+ * and K <= 2^22 - 64 for both (the kernels address an operand tile of 512
+ * bytes per unit of row stride with 32-bit offsets; else
+ * SWIGLU_ERR_UNSUPPORTED).  K == 0 gives h = 0. */
 int swiglu_fwd(int dtype, int64_t M, int64_t N, int64_t K,
                const void* x, const void* wg, const void* wu, void* h,
                void* stream);
@@ -129,8 +130,10 @@ size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K);
  *   workspace: device buffer of at least swiglu_bwd_workspace_bytes(...)
  *              bytes, 256-byte aligned; contents are scratch.
  * Layout rule: K % 8 == 0 for bf16, K % 4 == 0 for fp32; M and N are free
- * (padded operands are zero-filled).  bf16 also needs K, 2 * round_up(N, 64)
- * and round_up(M, 8) at most 2^22 - 64 (else SWIGLU_ERR_UNSUPPORTED). */
+ * (padded operands are zero-filled).  K, 2 * Np and round_up(M, 8) must be
+ * at most 2^22 - 64, with Np = round_up(N, 64) for bf16 and round_up(N, 8)
+ * for fp32 (32-bit tile offsets, as for swiglu_fwd; else
+ * SWIGLU_ERR_UNSUPPORTED). */
 int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K,
                const void* x, const void* wg, const void* wu, const void* dh,
                void* dx, void* dwg, void* dwu,

@@ -68,8 +68,14 @@ inline BwdLayout bwd_layout(int dtype, int64_t M, int64_t N, int64_t K) {
   return L;
 }
 
-// The bf16 kernels address a 256-row operand tile with 32-bit byte offsets.
-constexpr int64_t kMaxLdBf16 = (int64_t(1) << 22) - 64;
+// The GEMM kernels address an operand tile through a buffer descriptor whose
+// size and byte offsets are 32-bit: a tile spans at most 512 bytes per unit
+// of row stride (256 bf16 rows or 128 fp32 rows), and the out-of-range
+// offset 2^31 must lie past it, so every row stride a GEMM reads with (K for
+// the forward products, 2 Np and Mp for the backward ones) is capped for
+// both element types.  The cap is also the largest padded row count the
+// transposes' grids cover (65,535 tiles of 64 rows).
+constexpr int64_t kMaxLd = (int64_t(1) << 22) - 64;
 
 inline int validate_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
                         const void* wu, const void* h) {
@@ -78,7 +84,7 @@ inline int validate_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* 
   if ((st = check_dims(M, N, K))) return st;
   if (K % chunk_elems(dtype) != 0) return SWIGLU_ERR_SHAPE;
   if (!tiles_fit(M, N)) return SWIGLU_ERR_UNSUPPORTED;
-  if (dtype == SWIGLU_BF16 && K > kMaxLdBf16) return SWIGLU_ERR_UNSUPPORTED;
+  if (K > kMaxLd) return SWIGLU_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return SWIGLU_OK;
   if ((st = check_ptr(h))) return st;
   if (K > 0) {
@@ -98,8 +104,7 @@ inline int validate_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* 
   if (K % chunk_elems(dtype) != 0) return SWIGLU_ERR_SHAPE;
   const BwdLayout L = bwd_layout(dtype, M, N, K);
   if (!tiles_fit(M, L.Np) || !tiles_fit(M, K) || !tiles_fit(2 * L.Np, K)) return SWIGLU_ERR_UNSUPPORTED;
-  if (dtype == SWIGLU_BF16 && (K > kMaxLdBf16 || 2 * L.Np > kMaxLdBf16 || L.Mp > kMaxLdBf16))
-    return SWIGLU_ERR_UNSUPPORTED;
+  if (K > kMaxLd || 2 * L.Np > kMaxLd || L.Mp > kMaxLd) return SWIGLU_ERR_UNSUPPORTED;
   if (K == 0) return SWIGLU_OK;                       // every output is empty
   if (M > 0 && (st = check_ptr(dx))) return st;
   if (N > 0 && (st = check_ptr(dwg))) return st;
@@ -138,7 +143,7 @@ inline int validate_fwd_fp8(int64_t M, int64_t N, int64_t K, const void* x, cons
   if ((st = check_dims(M, N, K))) return st;
   if (K % chunk_elems(SWIGLU_BF16) != 0 || N % 32 != 0) return SWIGLU_ERR_SHAPE;
   if (!tiles_fit(M, N)) return SWIGLU_ERR_UNSUPPORTED;
-  if (K > kMaxLdBf16) return SWIGLU_ERR_UNSUPPORTED;
+  if (K > kMaxLd) return SWIGLU_ERR_UNSUPPORTED;
   if (h_out != nullptr && !aligned(h_out, 16)) return SWIGLU_ERR_ALIGN;
   if (M == 0 || N == 0) return SWIGLU_OK;
   if ((st = check_ptr(q))) return st;

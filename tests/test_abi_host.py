@@ -105,13 +105,30 @@ def test_workspace_layout_formula(L):
         assert L.swiglu_bwd_workspace_bytes(1, M, N, K) == want
 
 
-def test_bf16_leading_dimension_limit(L):
+@pytest.mark.parametrize("dt", [0, 1])
+def test_leading_dimension_limit(L, dt):
+    # Both element types: an operand tile spans 512 bytes per unit of row
+    # stride (256 bf16 rows, 128 fp32 rows) and is addressed with 32-bit
+    # offsets, so every stride a GEMM reads with is capped at 2^22 - 64.
     EUNSUP = 7
     lim = (1 << 22) - 64
-    assert L.swiglu_fwd(1, 4, 4, lim + 64, A, A, A, A, None) == EUNSUP
-    assert L.swiglu_bwd_workspace_bytes(1, 4, lim // 2, 8) > 0
-    need = L.swiglu_bwd_workspace_bytes(1, 4, lim // 2 + 64, 8)
-    assert L.swiglu_bwd(1, 4, lim // 2 + 64, 8, A, A, A, A, A, A, A, A, need, None) == EUNSUP
+    npad = 64 if dt == 1 else 8
+    # forward: K at the limit is accepted (validation only: M = 0), K past it is not
+    assert L.swiglu_fwd(dt, 0, 4, lim, None, None, None, None, None) == OK
+    assert L.swiglu_fwd(dt, 4, 4, lim + 64, A, A, A, A, None) == EUNSUP
+    assert L.swiglu_fwd_act(0, dt, 4, 4, lim + 8, A, A, A, A, None) == EUNSUP
+    assert L.swiglu_fwd_mult(0, dt, 4, 4, lim + 8, A, A, A, 1.0, 1.0, A, None) == EUNSUP
+    # backward: K, 2 Np and Mp
+    need = L.swiglu_bwd_workspace_bytes(dt, 4, 4, lim + 64)
+    assert L.swiglu_bwd(dt, 4, 4, lim + 64, A, A, A, A, A, A, A, A, need, None) == EUNSUP
+    assert L.swiglu_bwd_workspace_bytes(dt, 4, lim // 2, 8) > 0
+    n_big = lim // 2 + npad                       # 2 Np = lim + 2 npad
+    need = L.swiglu_bwd_workspace_bytes(dt, 4, n_big, 8)
+    assert L.swiglu_bwd(dt, 4, n_big, 8, A, A, A, A, A, A, A, A, need, None) == EUNSUP
+    m_big = lim + 8                               # Mp = lim + 8
+    need = L.swiglu_bwd_workspace_bytes(dt, m_big, 4, 8)
+    assert L.swiglu_bwd(dt, m_big, 4, 8, A, A, A, A, A, A, A, A, need, None) == EUNSUP
+    assert L.swiglu_bwd_act_mult(0, dt, m_big, 4, 8, A, A, A, A, 1.0, 1.0, A, A, A, A, need, None) == EUNSUP
 
 
 def test_gemv_validation(L):
