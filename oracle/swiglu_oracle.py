@@ -142,11 +142,6 @@ def glu_fwd(x, wg, wu, act="silu", gate_mult=1.0, up_mult=1.0):
     return ACTIVATIONS[act](gate_mult * g) * (up_mult * u)
 
 
-def glu_fwd_rows(x, wg, wu, rows, act="silu", gate_mult=1.0, up_mult=1.0):
-    """Rows `rows` of glu_fwd, computed one row at a time."""
-    return glu_fwd(np.asarray(x, np.float64)[rows], wg, wu, act, gate_mult, up_mult)
-
-
 def swiglu_fwd(x, wg, wu):
     """h[M,N] = SiLU(x Wg^T) * (x Wu^T), float64.
 
