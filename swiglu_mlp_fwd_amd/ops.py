@@ -1,9 +1,11 @@
 """PyTorch-facing wrappers of libswiglu.
 
-Argument marshalling only: tensors are checked, made contiguous, outputs are
-allocated with torch.empty on the input's device, and the library is called
-on the current HIP stream.  Every step of the computation runs in the HIP
-kernels behind the C ABI.
+Argument marshalling only: shapes, dtypes and devices of inputs and of any
+caller-supplied output are checked before the library is called (the C ABI
+sees raw pointers, so a wrong shape would be read or written past its
+tensor), inputs are made contiguous, outputs are allocated with torch.empty
+on the input's device, and the library is called on the current HIP stream.
+Every step of the computation runs in the HIP kernels behind the C ABI.
 
 Inputs of rank >= 3 are viewed as [M, K] and the output restored to the
 leading shape ("VisualGen MLP: cublasLt GELU-tanh epilogue for the
@@ -41,14 +43,46 @@ def _stream(t: torch.Tensor) -> int:
 
 
 def _same(*ts):
+    """Inputs of one call share dtype and device."""
     d, dev = ts[0].dtype, ts[0].device
     for t in ts[1:]:
         if t.dtype != d:
             raise TypeError(f"dtype mismatch: {t.dtype} vs {d}")
         if t.device != dev:
             raise ValueError(f"device mismatch: {t.device} vs {dev}")
-    if dev.type != "cuda":
+
+
+def _on_gpu(t: torch.Tensor) -> None:
+    """Checked after every shape check, so a malformed call fails the same way
+    with or without a GPU; the library itself only ever sees device pointers."""
+    if t.device.type != "cuda":
         raise ValueError("libswiglu operates on GPU tensors only")
+
+
+def _weights(wg: torch.Tensor, wu: torch.Tensor, K: int) -> int:
+    """N of Wg, Wu [N, K] (the nn.Linear layout)."""
+    if wg.dim() != 2:
+        raise ValueError(f"Wg must be [N, K], got {tuple(wg.shape)}")
+    N = wg.shape[0]
+    if tuple(wg.shape) != (N, K) or tuple(wu.shape) != (N, K):
+        raise ValueError(f"weights must be [N, K] = [{N}, {K}], got {tuple(wg.shape)}, {tuple(wu.shape)}")
+    return N
+
+
+def _check_out(t: torch.Tensor | None, name: str, shape, dtype: torch.dtype, device: torch.device) -> None:
+    """A caller-supplied output: the kernels write exactly `shape` elements of
+    `dtype` through its data pointer, so anything else would be written past
+    or beside the tensor."""
+    if t is None:
+        raise ValueError(f"{name}: an output tensor is required here")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def _p(t: torch.Tensor | None) -> int | None:
@@ -60,16 +94,16 @@ def fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor |
     """h = act(gate_mult * x Wg^T) * (up_mult * x Wu^T), act "silu" (SwiGLU) or
     "gelu_tanh" (GeGLU).  x [..., K], Wg/Wu [N, K] -> h [..., N]."""
     _same(x, wg, wu)
+    _dtype_code(x)
     lead, K = x.shape[:-1], x.shape[-1]
-    N = wg.shape[0]
-    if wg.shape != (N, K) or wu.shape != (N, K):
-        raise ValueError(f"weights must be [N, K] = [{N}, {K}], got {tuple(wg.shape)}, {tuple(wu.shape)}")
+    N = _weights(wg, wu, K)
     M = math.prod(lead)
+    if out is not None:
+        _check_out(out, "out", (M, N), x.dtype, x.device)
+    _on_gpu(x)
     x2 = x.reshape(M, K).contiguous()
     wg, wu = wg.contiguous(), wu.contiguous()
     h = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
-    if out is not None and (out.shape != (M, N) or out.dtype != x.dtype or not out.is_contiguous()):
-        raise ValueError("out must be a contiguous [M, N] tensor of the input dtype")
     check("swiglu_fwd_mult", lib().swiglu_fwd_mult(_act_code(act), _dtype_code(x), M, N, K, _p(x2), _p(wg), _p(wu),
                                                    float(gate_mult), float(up_mult), _p(h), _stream(x)))
     return h.reshape(*lead, N)
@@ -86,16 +120,19 @@ def fwd_fp8(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, act: str = "sil
     if x.dtype != torch.bfloat16:
         raise TypeError("fwd_fp8 takes bf16 inputs")
     lead, K = x.shape[:-1], x.shape[-1]
-    N = wg.shape[0]
-    if wg.shape != (N, K) or wu.shape != (N, K):
-        raise ValueError(f"weights must be [N, K] = [{N}, {K}], got {tuple(wg.shape)}, {tuple(wu.shape)}")
+    N = _weights(wg, wu, K)
     M = math.prod(lead)
-    x2 = x.reshape(M, K).contiguous()
-    wg, wu = wg.contiguous(), wu.contiguous()
     dev = x.device
     if out is not None:
         q, scale, h = out
-    else:
+        _check_out(q, "q", (M, N), torch.uint8, dev)
+        _check_out(scale, "scale", (M, N // 32 if N % 32 == 0 else 0), torch.uint8, dev)
+        if h is not None:
+            _check_out(h, "h", (M, N), torch.float32, dev)
+    _on_gpu(x)
+    x2 = x.reshape(M, K).contiguous()
+    wg, wu = wg.contiguous(), wu.contiguous()
+    if out is None:
         q = torch.empty((M, N), dtype=torch.uint8, device=dev)
         scale = torch.empty((M, N // 32 if N % 32 == 0 else 0), dtype=torch.uint8, device=dev)
         h = torch.empty((M, N), dtype=torch.float32, device=dev) if h_out else None
@@ -110,27 +147,36 @@ def bwd_workspace_bytes(dtype: torch.dtype, M: int, N: int, K: int) -> int:
 
 def bwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, dh: torch.Tensor,
         workspace: torch.Tensor | None = None, gate_mult: float = 1.0, up_mult: float = 1.0,
-        act: str = "silu"):
+        act: str = "silu", out=None):
     """(dx, dwg, dwu) of L = sum(dh * h), h = act(gate_mult x Wg^T) * (up_mult x Wu^T).
-    Shapes as in fwd; dh [..., N]."""
+    Shapes as in fwd; dh [..., N].  `out` may pass preallocated (dx [M, K],
+    dwg [N, K], dwu [N, K]); `workspace` a uint8 device buffer of at least
+    bwd_workspace_bytes(...) bytes (a smaller or missing one is replaced)."""
     _same(x, wg, wu, dh)
+    dt = _dtype_code(x)
     lead, K = x.shape[:-1], x.shape[-1]
-    N = wg.shape[0]
+    N = _weights(wg, wu, K)
     M = math.prod(lead)
-    if dh.shape != (*lead, N):
+    if tuple(dh.shape) != (*lead, N):
         raise ValueError(f"dh must be {(*lead, N)}, got {tuple(dh.shape)}")
+    if out is not None:
+        dx, dwg, dwu = out
+        _check_out(dx, "dx", (M, K), x.dtype, x.device)
+        _check_out(dwg, "dwg", (N, K), x.dtype, x.device)
+        _check_out(dwu, "dwu", (N, K), x.dtype, x.device)
+    if workspace is not None and (workspace.device != x.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the device of x")
+    _on_gpu(x)
     x2 = x.reshape(M, K).contiguous()
     dh2 = dh.reshape(M, N).contiguous()
     wg, wu = wg.contiguous(), wu.contiguous()
-    if dh2.shape[0] != M:
-        raise ValueError("dh must have the leading shape of x")
-    dt = _dtype_code(x)
     need = int(lib().swiglu_bwd_workspace_bytes(dt, M, N, K))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    dx = torch.empty((M, K), dtype=x.dtype, device=x.device)
-    dwg = torch.empty((N, K), dtype=x.dtype, device=x.device)
-    dwu = torch.empty((N, K), dtype=x.dtype, device=x.device)
+    if out is None:
+        dx = torch.empty((M, K), dtype=x.dtype, device=x.device)
+        dwg = torch.empty((N, K), dtype=x.dtype, device=x.device)
+        dwu = torch.empty((N, K), dtype=x.dtype, device=x.device)
     check("swiglu_bwd_act_mult", lib().swiglu_bwd_act_mult(_act_code(act), dt, M, N, K, _p(x2), _p(wg), _p(wu),
                                                            _p(dh2), float(gate_mult), float(up_mult), _p(dx),
                                                            _p(dwg), _p(dwu), _p(workspace),
@@ -146,8 +192,11 @@ def gemv_fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Ten
     if x.dtype != torch.bfloat16:
         raise TypeError("gemv_fwd is bf16 only")
     lead, K = x.shape[:-1], x.shape[-1]
-    N = wg.shape[0]
+    N = _weights(wg, wu, K)
     M = math.prod(lead)
+    if out is not None:
+        _check_out(out, "out", (M, N), x.dtype, x.device)
+    _on_gpu(x)
     x2 = x.reshape(M, K).contiguous()
     wg, wu = wg.contiguous(), wu.contiguous()
     h = out if out is not None else torch.empty((M, N), dtype=x.dtype, device=x.device)
@@ -168,11 +217,19 @@ def act_fwd(gate: torch.Tensor, up: torch.Tensor, clamp_limit: float = math.inf,
         raise ValueError("gate and up must have the same shape")
     cols = gate.shape[-1]
     rows = math.prod(gate.shape[:-1])
-    g2 = gate.reshape(rows, cols).contiguous()
-    u2 = up.reshape(rows, cols).contiguous()
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"act_fwd writes float32 or bfloat16 h, got {out_dtype}")
     if out is not None:
         h, cnt = out
-    else:
+        if h is None or h.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("out h must be a float32 or bfloat16 tensor")
+        _check_out(h, "h", (rows, cols), h.dtype, gate.device)
+        if cnt is not None:
+            _check_out(cnt, "count", (1,), torch.int64, gate.device)
+    _on_gpu(gate)
+    g2 = gate.reshape(rows, cols).contiguous()
+    u2 = up.reshape(rows, cols).contiguous()
+    if out is None:
         h = torch.empty((rows, cols), dtype=out_dtype, device=gate.device)
         cnt = torch.empty(1, dtype=torch.int64, device=gate.device) if count else None
     check("swiglu_act_fwd", lib().swiglu_act_fwd(_act_code(act), _DT[h.dtype], rows, cols, _p(g2), _p(u2),
@@ -196,12 +253,19 @@ def act_quant(gate: torch.Tensor, up: torch.Tensor, clamp_limit: float = math.in
         raise ValueError("gate and up must have the same shape")
     cols = gate.shape[-1]
     rows = math.prod(gate.shape[:-1])
-    g2 = gate.reshape(rows, cols).contiguous()
-    u2 = up.reshape(rows, cols).contiguous()
     dev = gate.device
     if out is not None:
         q, scale, cnt, h = out
-    else:
+        _check_out(q, "q", (rows, cols), torch.uint8, dev)
+        _check_out(scale, "scale", (rows, cols // 32 if cols % 32 == 0 else 0), torch.uint8, dev)
+        if cnt is not None:
+            _check_out(cnt, "count", (1,), torch.int64, dev)
+        if h is not None:
+            _check_out(h, "h", (rows, cols), torch.float32, dev)
+    _on_gpu(gate)
+    g2 = gate.reshape(rows, cols).contiguous()
+    u2 = up.reshape(rows, cols).contiguous()
+    if out is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
         scale = torch.empty((rows, cols // 32 if cols % 32 == 0 else 0), dtype=torch.uint8, device=dev)
         cnt = torch.empty(1, dtype=torch.int64, device=dev) if count else None
@@ -228,20 +292,24 @@ def act_bwd(gate: torch.Tensor, up: torch.Tensor, dy: torch.Tensor, clamp_limit:
         raise ValueError("gate, up and dy must have the same shape")
     cols = gate.shape[-1]
     rows = math.prod(gate.shape[:-1])
-    g2 = gate.reshape(rows, cols).contiguous()
-    u2 = up.reshape(rows, cols).contiguous()
-    d2 = dy.reshape(rows, cols).contiguous()
-    w = None
     if weights is not None:
         if weights.dtype != torch.float32 or weights.device != gate.device:
             raise TypeError("weights must be an fp32 tensor on the device of gate")
         if weights.numel() != rows:
             raise ValueError(f"weights must have {rows} elements")
-        w = weights.reshape(rows).contiguous()
     dev = gate.device
     if out is not None:
         dg, du, wg = out
-    else:
+        _check_out(dg, "dgate", (rows, cols), gate.dtype, dev)
+        _check_out(du, "dup", (rows, cols), gate.dtype, dev)
+        if wg is not None:
+            _check_out(wg, "weight_grad", (rows,), torch.float32, dev)
+    _on_gpu(gate)
+    g2 = gate.reshape(rows, cols).contiguous()
+    u2 = up.reshape(rows, cols).contiguous()
+    d2 = dy.reshape(rows, cols).contiguous()
+    w = None if weights is None else weights.reshape(rows).contiguous()
+    if out is None:
         dg = torch.empty((rows, cols), dtype=gate.dtype, device=dev)
         du = torch.empty((rows, cols), dtype=gate.dtype, device=dev)
         wg = torch.empty(rows, dtype=torch.float32, device=dev) if weight_grad else None
