@@ -143,6 +143,19 @@ def small_int_bf16(M: int, N: int, K: int, seed: int = 0) -> dict:
     return out
 
 
+def small_int_i8(M: int, N: int, K: int, seed: int = 0, amp: int = 1) -> dict:
+    """x, Wg, Wu with integer entries uniform in {-amp, ..., amp}, as int8
+    (amp <= 127).  Every such integer is exact in bf16 and fp32, so the
+    arrays convert exactly to either storage format.  With amp = 1 every
+    partial sum over K < 2^24 is an integer of magnitude at most K, so fp32
+    accumulation in any order is exact, also at the longest reductions the
+    library accepts; int8 keeps the host footprint of those shapes small."""
+    out = {}
+    for name, shape, stream in (("x", (M, K), STREAM_X), ("wg", (N, K), STREAM_WG), ("wu", (N, K), STREAM_WU)):
+        out[name] = rng(seed, stream).integers(-amp, amp + 1, size=shape, dtype=np.int8)
+    return out
+
+
 def act_quant_f32(rows: int, cols: int, seed: int = 0, specials: bool = True) -> dict:
     """Elementwise case: gate,up~N(0,2) fp32 (std 2) with 0.1% +-inf/NaN and 1% subnormals."""
     gate = normal_f32((rows, cols), 2.0, seed, STREAM_GATE)

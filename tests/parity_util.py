@@ -13,6 +13,8 @@ Tolerances, with their derivation:
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import torch
 
@@ -21,6 +23,50 @@ import synth
 
 U32 = 2.0 ** -24
 BF16_HALF_ULP = 2.0 ** -8   # unit roundoff of bf16 (8 significant bits)
+
+
+GUARD_BYTES = 4096   # a multiple of 256: the view keeps the buffer's alignment
+
+
+def _guard_pattern(device) -> torch.Tensor:
+    return ((torch.arange(2 * GUARD_BYTES, dtype=torch.int64) * 37 + 11) % 251).to(torch.uint8).to(device)
+
+
+class Guarded:
+    """A device output that sits inside a larger buffer.
+
+    GUARD_BYTES on each side hold a fixed byte pattern, and the output itself
+    is filled with 0xFF bytes (NaN for bf16 and fp32, the NaN code for E4M3):
+    an element the kernel leaves unwritten then fails the comparison, and a
+    byte written before or after the output fails check().
+    """
+
+    def __init__(self, shape, dtype, device="cuda"):
+        self.shape = tuple(int(v) for v in shape)
+        self.n = math.prod(self.shape) * torch.empty((), dtype=dtype).element_size()
+        self.pattern = _guard_pattern(device)
+        self.buf = torch.empty(self.n + 2 * GUARD_BYTES, dtype=torch.uint8, device=device)
+        self.buf[:GUARD_BYTES].copy_(self.pattern[:GUARD_BYTES])
+        self.buf[GUARD_BYTES + self.n:].copy_(self.pattern[GUARD_BYTES:])
+        self.buf[GUARD_BYTES:GUARD_BYTES + self.n].fill_(0xFF)
+        self.t = self.buf[GUARD_BYTES:GUARD_BYTES + self.n].view(dtype).view(self.shape)
+
+    def check(self, what: str) -> None:
+        torch.cuda.synchronize()
+        head = self.buf[:GUARD_BYTES]
+        tail = self.buf[GUARD_BYTES + self.n:]
+        assert torch.equal(head, self.pattern[:GUARD_BYTES]), f"{what}: bytes written before the output"
+        assert torch.equal(tail, self.pattern[GUARD_BYTES:]), f"{what}: bytes written past the output"
+
+
+def guarded(shape, dtype, device="cuda") -> Guarded:
+    return Guarded(shape, dtype, device)
+
+
+def check_guards(what: str, *gs) -> None:
+    for i, g in enumerate(gs):
+        if g is not None:
+            g.check(f"{what} (output {i})")
 
 
 def gamma(n: int, u: float = U32) -> float:

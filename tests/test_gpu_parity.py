@@ -16,8 +16,8 @@ import torch
 
 import oracle
 import synth
-from parity_util import (BF16_HALF_ULP, U32, assert_gates, assert_within, dev_bf16, dev_f32, f64_of,
-                         fwd_bound, gamma, host_f64)
+from parity_util import (BF16_HALF_ULP, U32, assert_gates, assert_within, check_guards, dev_bf16, dev_f32, f64_of,
+                         fwd_bound, gamma, guarded, host_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,11 +47,14 @@ def to_f64(d: dict) -> dict:
 def check_fwd(d, dtype, rows=None, what="fwd", via="dual", act="silu", mult=(1.0, 1.0)):
     t = to_dev(d)
     f = to_f64(d)
+    M, N = t["x"].shape[0], t["wg"].shape[0]
+    hg = guarded((M, N), t["x"].dtype)
     if via == "dual":
-        h = S.fwd(t["x"], t["wg"], t["wu"], act=act, gate_mult=mult[0], up_mult=mult[1])
+        h = S.fwd(t["x"], t["wg"], t["wu"], act=act, gate_mult=mult[0], up_mult=mult[1], out=hg.t)
     else:
-        h = S.gemv_fwd(t["x"], t["wg"], t["wu"], act=act, gate_mult=mult[0], up_mult=mult[1])
+        h = S.gemv_fwd(t["x"], t["wg"], t["wu"], act=act, gate_mult=mult[0], up_mult=mult[1], out=hg.t)
     torch.cuda.synchronize()
+    check_guards(what, hg)
     y = host_f64(h if rows is None else h[torch.as_tensor(rows, device=DEV)])
     ref, bound = fwd_bound(f["x"], f["wg"], f["wu"], dtype, rows, act, mult[0], mult[1])
     e, c = assert_gates(y, ref, dtype, what)
@@ -180,8 +183,14 @@ def check_bwd(d, dtype, rows=None, cols=None, what="bwd", mult=(1.0, 1.0), act="
     cols = np.arange(N) if cols is None else cols
     t = to_dev(d)
     f = to_f64(d)
-    dx, dwg, dwu = S.bwd(t["x"], t["wg"], t["wu"], t["dh"], gate_mult=mult[0], up_mult=mult[1], act=act)
+    K = t["x"].shape[1]
+    dt = t["x"].dtype
+    outs = [guarded((M, K), dt), guarded((N, K), dt), guarded((N, K), dt)]
+    ws = guarded((max(S.bwd_workspace_bytes(dt, M, N, K), 1),), torch.uint8)
+    dx, dwg, dwu = S.bwd(t["x"], t["wg"], t["wu"], t["dh"], gate_mult=mult[0], up_mult=mult[1], act=act,
+                         out=tuple(g.t for g in outs), workspace=ws.t)
     torch.cuda.synchronize()
+    check_guards(what, *outs, ws)
     ref = bwd_bounds(f, dtype, rows, cols, mult, act)
     ri = torch.as_tensor(rows, device=DEV)
     ci = torch.as_tensor(cols, device=DEV)
@@ -298,8 +307,11 @@ H_ULP_MAX = 8   # the device activation is within this many fp32 ulps of the rou
 
 def check_act_quant(gate, up, L, what, act="silu"):
     rows, cols = gate.shape
-    q, sc, cnt, h = S.act_quant(dev_f32(gate), dev_f32(up), L, count=True, h_out=True, act=act)
+    gs = [guarded((rows, cols), torch.uint8), guarded((rows, cols // 32), torch.uint8),
+          guarded((1,), torch.int64), guarded((rows, cols), torch.float32)]
+    q, sc, cnt, h = S.act_quant(dev_f32(gate), dev_f32(up), L, act=act, out=tuple(g.t for g in gs))
     torch.cuda.synchronize()
+    check_guards(what, *gs)
     q, sc, h = q.cpu().numpy(), sc.cpu().numpy(), h.cpu().numpy()
     rq, rs, rc, rh = oracle.act_quant(gate.astype(np.float64), up.astype(np.float64), L, act=act)
     # 1. clamp count: exact.
@@ -466,13 +478,18 @@ def check_act_bwd(d, L, use_w, what):
     bf = g.dtype == np.uint16
     w = d["weights"] if use_w else None
     dev = dev_bf16 if bf else dev_f32
-    dg, du, wg = S.act_bwd(dev(g), dev(u), dev(dy), L,
-                           weights=None if w is None else dev_f32(w), weight_grad=True)
+    tdt = torch.bfloat16 if bf else torch.float32
+    R, C = g.shape
+    gs = [guarded((R, C), tdt), guarded((R, C), tdt), guarded((R,), torch.float32)]
+    gs2 = [guarded((R, C), tdt), guarded((R, C), tdt)]
+    dg, du, wg = S.act_bwd(dev(g), dev(u), dev(dy), L, weights=None if w is None else dev_f32(w),
+                           out=tuple(x.t for x in gs))
     # Without weight_grad the kernel walks the array flat instead of by rows;
     # every element goes through the same arithmetic, so the bits agree.
-    dg2, du2, wg2 = S.act_bwd(dev(g), dev(u), dev(dy), L,
-                              weights=None if w is None else dev_f32(w), weight_grad=False)
+    dg2, du2, wg2 = S.act_bwd(dev(g), dev(u), dev(dy), L, weights=None if w is None else dev_f32(w),
+                              out=(gs2[0].t, gs2[1].t, None))
     torch.cuda.synchronize()
+    check_guards(what, *gs, *gs2)
     assert wg2 is None
     ibits = torch.int16 if bf else torch.int32
     assert torch.equal(dg2.view(ibits), dg.view(ibits)) and torch.equal(du2.view(ibits), du.view(ibits)), \
@@ -647,9 +664,13 @@ def check_fwd_fp8(d, rows=None, act="silu", what="fwd_fp8"):
     """
     t = to_dev(d)
     f = to_f64(d)
-    q, sc, h = S.fwd_fp8(t["x"], t["wg"], t["wu"], act=act, h_out=True)
-    q2, sc2, none = S.fwd_fp8(t["x"], t["wg"], t["wu"], act=act, h_out=False)
+    M, N = t["x"].shape[0], t["wg"].shape[0]
+    gs = [guarded((M, N), torch.uint8), guarded((M, N // 32), torch.uint8), guarded((M, N), torch.float32)]
+    gs2 = [guarded((M, N), torch.uint8), guarded((M, N // 32), torch.uint8)]
+    q, sc, h = S.fwd_fp8(t["x"], t["wg"], t["wu"], act=act, out=tuple(g.t for g in gs))
+    q2, sc2, none = S.fwd_fp8(t["x"], t["wg"], t["wu"], act=act, out=(gs2[0].t, gs2[1].t, None))
     torch.cuda.synchronize()
+    check_guards(what, *gs, *gs2)
     assert none is None
     assert torch.equal(q, q2) and torch.equal(sc, sc2), f"{what}: output differs without h_out"
     sel = slice(None) if rows is None else torch.as_tensor(rows, device=DEV)
@@ -840,8 +861,10 @@ def test_geglu_autograd():
 # ------------------------------------------ non-quantised elementwise forward
 
 def check_act_fwd(gate, up, L, act, out_dtype, what):
-    h, cnt = S.act_fwd(dev_f32(gate), dev_f32(up), L, act=act, out_dtype=out_dtype)
+    gs = [guarded(gate.shape, out_dtype), guarded((1,), torch.int64)]
+    h, cnt = S.act_fwd(dev_f32(gate), dev_f32(up), L, act=act, out=(gs[0].t, gs[1].t))
     torch.cuda.synchronize()
+    check_guards(what, *gs)
     y = h.float().cpu().numpy().astype(np.float64)
     r, rc = oracle.act_fwd(gate.astype(np.float64), up.astype(np.float64), L, act)
     assert int(cnt.item()) == rc, f"{what}: clamp count {int(cnt.item())} != {rc}"
@@ -926,6 +949,87 @@ def test_bf16_forward_and_backward_at_the_longest_reduction():
     check_bwd(d, "bf16", what=f"bwd bf16 K={K}")
     assert S.lib().swiglu_fwd(1, M, N, K + 64, 0x10000, 0x10000, 0x10000, 0x10000, None) == 7   # UNSUPPORTED
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_full_tiles_at_the_longest_reduction(dt):
+    """K at the limit with M and N large enough that an operand tile's buffer
+    descriptor spans its full 512 bytes x K (128 fp32 rows, 256 bf16 rows):
+    its size and the largest in-range offsets sit just below 2^31, with the
+    out-of-range offset 2^31 right past them.  These descriptors are the
+    forward's and the backward recompute's.  x, Wg, Wu in {-1, 0, 1}: every
+    partial sum of g and u is an integer of magnitude <= K < 2^24, exact in
+    fp32 whatever the order, so h must be within 8 fp32 ulps of the exact
+    value (fp32) or its round-to-nearest-even (bf16, away from midpoints).
+    dX (both types) and dWg, dWu (fp32) are held to the gates and to an
+    elementwise bound of their reductions on sampled rows and columns."""
+    K = BF16_MAX_LD
+    M = N = 128 if dt == "f32" else 256
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    d = synth.small_int_i8(M, N, K, seed=22)
+    dh = synth.normal_f32((M, N), 1.0, 22, synth.STREAM_DH)
+    if dt == "bf16":
+        dh = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(dh))
+    # int8 -> fp32 / bf16 on the device is exact for these values
+    t = {k: torch.from_numpy(v).to(DEV).to(tdt) for k, v in d.items()}
+    t["dh"] = dev_f32(dh).to(tdt)
+    log(f"limit {dt}: M=N={M} K={K}, inputs ready")
+    hg = guarded((M, N), tdt)
+    S.fwd(t["x"], t["wg"], t["wu"], out=hg.t)
+    outs = [guarded((M, K), tdt), guarded((N, K), tdt), guarded((N, K), tdt)]
+    ws = guarded((S.bwd_workspace_bytes(tdt, M, N, K),), torch.uint8)
+    S.bwd(t["x"], t["wg"], t["wu"], t["dh"], out=tuple(g.t for g in outs), workspace=ws.t)
+    torch.cuda.synchronize()
+    check_guards(f"limit {dt}", hg, *outs, ws)
+    rows = np.array([0, M // 2 + 1, M - 1])
+    cols = np.array([0, N // 2 + 1, N - 1])
+    ri, ci = torch.as_tensor(rows, device=DEV), torch.as_tensor(cols, device=DEV)
+    y, dxd = host_f64(hg.t[ri]), host_f64(outs[0].t[ri])
+    dwgd, dwud = host_f64(outs[1].t[ci]), host_f64(outs[2].t[ci])
+    del t, hg, outs, ws
+    torch.cuda.empty_cache()
+    log(f"limit {dt}: device done")
+    wg, wu = d["wg"].astype(np.float64), d["wu"].astype(np.float64)
+    xr, dhf = d["x"][rows].astype(np.float64), dh.astype(np.float64)
+    # forward: exact g, u on the sampled rows
+    g, u = oracle.gate_up(xr, wg, wu)
+    r = oracle.glu_fwd(xr, wg, wu)
+    tail = oracle.sigmoid(g) < 2.0 ** -126
+    assert np.all(np.abs(y[tail] - r[tail]) <= 2.0 ** -126 * np.abs(g[tail] * u[tail]) + 1e-45)
+    keep = ~tail
+    if dt == "f32":
+        ulp = f32_ulp_distance(y[keep], r[keep].astype(np.float32).astype(np.float64))
+        assert ulp.max(initial=0) <= H_ULP_MAX, f"limit fp32 h off by {ulp.max()} ulps"
+    else:
+        q, sp = bf16_rne_f64(r[keep])
+        frac = np.abs(r[keep]) / sp
+        safe = np.abs(frac - np.floor(frac) - 0.5) * sp > 2e-5 * np.abs(r[keep]) + 1e-30
+        assert np.array_equal(y[keep][safe], q[safe]), "limit bf16 h is not the rounding of the exact value"
+    # dX rows: dg, du carry a few fp32 ulps of the activation (and the bf16
+    # operand rounding); the reduction over 2N adds gamma_{2N+1}.  With
+    # |x|, |W| <= 1 the sums of |dg||W| (over n) and |dg||x| (over m) are at
+    # most the sums of |dg|, which keeps the bounds free of K-long arrays.
+    op = BF16_HALF_ULP if dt == "bf16" else 0.0
+    outu = BF16_HALF_ULP if dt == "bf16" else U32
+    checks = []
+    dg, du = oracle.dswiglu(g, u, dhf[rows])
+    dxr = oracle.swiglu_bwd_dx_rows(xr, wg, wu, dhf[rows], np.arange(len(rows)))
+    absx = (np.abs(dg).sum(axis=1) + np.abs(du).sum(axis=1))[:, None]
+    checks.append(("dx", dxd, dxr, 2 * ((gamma(2 * N + 1) + op + 16 * U32) * absx + outu * np.abs(dxr)) + 1e-30))
+    if dt == "f32":
+        del wg, wu
+        x = d["x"].astype(np.float64)
+        wgc, wuc = d["wg"][cols].astype(np.float64), d["wu"][cols].astype(np.float64)
+        dwgr, dwur = oracle.swiglu_bwd_dw_rows(x, wgc, wuc, dhf[:, cols], np.arange(len(cols)))
+        gc, uc = oracle.gate_up(x, wgc, wuc)
+        dgc, duc = oracle.dswiglu(gc, uc, dhf[:, cols])
+        for name, yv, rv, dd in (("dwg", dwgd, dwgr, dgc), ("dwu", dwud, dwur, duc)):
+            b = 2 * ((gamma(M + 1) + 16 * U32) * np.abs(dd).sum(axis=0)[:, None] + outu * np.abs(rv)) + 1e-30
+            checks.append((name, yv, rv, b))
+    for name, yv, rv, b in checks:
+        e, c = assert_gates(yv, rv, dt, f"limit {dt} {name}")
+        ratio = assert_within(yv, rv, b, f"limit {dt} {name}")
+        log(f"limit {dt} {name}: normwise {e:.3e} cosine {c:.7f} bound-ratio {ratio:.3f}")
 
 
 def test_bf16_backward_at_the_largest_token_count():
