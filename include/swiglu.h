@@ -24,8 +24,11 @@
  *     enqueued and no output has been written.  Sizes of zero are valid and
  *     enqueue only what is needed to give the outputs their defined values.
  *   - Calls are thread-safe: the library's only global state is a
- *     thread-local record of the last HIP error and a once-per-device kernel
- *     attribute (the larger dynamic LDS size), set under call_once.
+ *     thread-local record of the last HIP error, a once-per-device kernel
+ *     attribute (the larger dynamic LDS size) and the address of
+ *     swiglu_bwd_noalloc's static scratch buffer on each device, both set
+ *     under call_once.  swiglu_bwd_noalloc alone shares device memory
+ *     between calls (see there).
  */
 #ifndef SWIGLU_H_
 #define SWIGLU_H_
@@ -46,7 +49,9 @@ enum swiglu_status {
   SWIGLU_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
   SWIGLU_ERR_ARG = 6,         /* any other invalid argument (e.g. clamp limit)  */
   SWIGLU_ERR_UNSUPPORTED = 7, /* valid request this build does not implement    */
-  SWIGLU_ERR_HIP = 8          /* a HIP launch failed; see swiglu_last_hip_error */
+  SWIGLU_ERR_HIP = 8,         /* a HIP launch failed; see swiglu_last_hip_error */
+  SWIGLU_ERR_SCRATCH = 9      /* needs more scratch than swiglu_bwd_noalloc's
+                                 static buffer (SWIGLU_NOALLOC_SCRATCH_BYTES)  */
 };
 
 /* Element type of x, Wg, Wu, dh and of every output of a call.  Accumulation
@@ -163,6 +168,35 @@ int swiglu_bwd_act_mult(int act, int dtype, int64_t M, int64_t N, int64_t K,
                         float gate_mult, float up_mult,
                         void* dx, void* dwg, void* dwu,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of swiglu_bwd_noalloc's scratch buffer: 128 MiB of device memory on
+ * every GPU the library runs on, held until the process ends. */
+#define SWIGLU_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* swiglu_bwd_act_mult without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid allocation.  The backward's scratch
+ * (the [dg | du] tile, its transpose, x^T and [Wg; Wu]^T) lives in a static
+ * device array of SWIGLU_NOALLOC_SCRATCH_BYTES inside the library; the call
+ * allocates nothing (no hipMalloc, no library allocator) and the caller still
+ * passes every input and output.  Results are bit-identical to
+ * swiglu_bwd_act_mult.
+ * Limits and sharing:
+ *   - a problem whose swiglu_bwd_workspace_bytes(dtype, M, N, K) exceeds
+ *     SWIGLU_NOALLOC_SCRATCH_BYTES returns SWIGLU_ERR_SCRATCH (nothing is
+ *     enqueued);
+ *   - every call on one GPU uses that GPU's one buffer, and the buffer keeps
+ *     whatever the last call left in it (nothing in it needs to start at
+ *     zero: every call writes each scratch element it reads).  Calls whose
+ *     work overlaps on one GPU (concurrent streams, or threads without an
+ *     ordering between their streams) race on the buffer and give wrong
+ *     results; order them on one stream or use swiglu_bwd_act_mult with
+ *     separate workspaces.
+ * Arguments, layouts and the other errors as swiglu_bwd_act_mult. */
+int swiglu_bwd_noalloc(int act, int dtype, int64_t M, int64_t N, int64_t K,
+                       const void* x, const void* wg, const void* wu, const void* dh,
+                       float gate_mult, float up_mult,
+                       void* dx, void* dwg, void* dwu, void* stream);
 
 /* Decode forward for 1 <= M <= 8 tokens, bf16 only: the same h as
  * swiglu_fwd, computed by a weight-streaming kernel that reads each row of

@@ -15,6 +15,8 @@ SWIGLU_F32 = 0
 SWIGLU_BF16 = 1
 SWIGLU_ACT_SILU = 0
 SWIGLU_ACT_GELU_TANH = 1
+SWIGLU_ERR_SCRATCH = 9
+NOALLOC_SCRATCH_BYTES = 128 << 20    # SWIGLU_NOALLOC_SCRATCH_BYTES
 
 _c_i64 = ctypes.c_int64
 _c_ptr = ctypes.c_void_p
@@ -37,6 +39,9 @@ SIGNATURES = {
     "swiglu_bwd_act_mult": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr,
                                            _c_ptr, _c_ptr, ctypes.c_float, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr,
                                            _c_ptr, ctypes.c_size_t, _c_ptr]),
+    "swiglu_bwd_noalloc": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr,
+                                          _c_ptr, _c_ptr, ctypes.c_float, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr,
+                                          _c_ptr]),
     "swiglu_gemv_fwd": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "swiglu_gemv_fwd_act": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                            _c_ptr]),

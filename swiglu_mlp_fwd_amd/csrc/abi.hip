@@ -2,6 +2,8 @@
 // caller's stream.  No allocation, no synchronisation.
 #include <math.h>
 
+#include <mutex>
+
 #include "gemm.hpp"
 #include "swiglu.h"
 #include "validate.hpp"
@@ -30,6 +32,36 @@ hipError_t fill_zero(int dtype, void* p, int64_t rows, int64_t cols, hipStream_t
   // Transposing a [0, rows] input with rows_pad = cols writes zeros into
   // out[c, r] for c < rows, r < cols, i.e. the whole [rows, cols] array.
   return swg::launch_transpose(as_dt(dtype), nullptr, 0, 0, (int)rows, p, cols, 0, (int)cols, s);
+}
+
+}  // namespace
+
+// The backward's scratch for swiglu_bwd_noalloc: a file-scope device array,
+// so the entry point never allocates.  In host code `scratch` is only a
+// handle for the runtime: its device address on the current GPU comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[SWIGLU_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device (each GPU holds its own
+// copy at its own address), looked up on the first call on that device.
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static void* addr[kMaxDevices];
+  static hipError_t result[kMaxDevices];
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    result[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    addr[dev] = p;
+  });
+  *out = addr[dev];
+  return result[dev];
 }
 
 }  // namespace
@@ -183,6 +215,26 @@ int swiglu_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const 
                              workspace, workspace_bytes, stream);
 }
 
+int swiglu_bwd_noalloc(int act, int dtype, int64_t M, int64_t N, int64_t K, const void* x,
+                       const void* wg, const void* wu, const void* dh, float gate_mult, float up_mult,
+                       void* dx, void* dwg, void* dwu, void* stream) {
+  if (act != SWIGLU_ACT_SILU && act != SWIGLU_ACT_GELU_TANH) return SWIGLU_ERR_ARG;
+  if (!finite_mult(gate_mult) || !finite_mult(up_mult)) return SWIGLU_ERR_ARG;
+  // Everything but the workspace is checked first, so the errors are those
+  // of swiglu_bwd_act_mult; then the scratch bound.
+  int st = swg::validate_bwd(dtype, M, N, K, x, wg, wu, dh, dx, dwg, dwu, nullptr, 0);
+  if (st != SWIGLU_OK && st != SWIGLU_ERR_WORKSPACE) return st;
+  if (st == SWIGLU_OK)          // a call that needs no workspace (K, M or N is 0)
+    return swiglu_bwd_act_mult(act, dtype, M, N, K, x, wg, wu, dh, gate_mult, up_mult, dx, dwg, dwu,
+                               nullptr, 0, stream);
+  if (swg::bwd_layout(dtype, M, N, K).total > SWIGLU_NOALLOC_SCRATCH_BYTES) return SWIGLU_ERR_SCRATCH;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return swiglu_bwd_act_mult(act, dtype, M, N, K, x, wg, wu, dh, gate_mult, up_mult, dx, dwg, dwu, ws,
+                             SWIGLU_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int swiglu_gemv_fwd_mult(int act, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
                          const void* wu, float gate_mult, float up_mult, void* h, void* stream) {
   if (act != SWIGLU_ACT_SILU && act != SWIGLU_ACT_GELU_TANH) return SWIGLU_ERR_ARG;
@@ -275,6 +327,7 @@ const char* swiglu_status_str(int status) {
     case SWIGLU_ERR_ARG: return "invalid argument";
     case SWIGLU_ERR_UNSUPPORTED: return "unsupported size";
     case SWIGLU_ERR_HIP: return "HIP launch error";
+    case SWIGLU_ERR_SCRATCH: return "problem needs more scratch than the static buffer holds";
     default: return "unknown status";
   }
 }

@@ -185,6 +185,34 @@ def bwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, dh: torch.Tensor,
     return dx.reshape(*lead, K), dwg, dwu
 
 
+def bwd_noalloc(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, dh: torch.Tensor, out,
+                gate_mult: float = 1.0, up_mult: float = 1.0, act: str = "silu"):
+    """bwd into preallocated (dx, dwg, dwu) with the library's static scratch
+    instead of a workspace: the library allocates nothing.  Inputs must
+    already be contiguous (no copies are made).  Calls that overlap on one
+    GPU share the scratch and race; problems larger than the scratch raise
+    (SWIGLU_ERR_SCRATCH)."""
+    _same(x, wg, wu, dh)
+    dt = _dtype_code(x)
+    lead, K = x.shape[:-1], x.shape[-1]
+    N = _weights(wg, wu, K)
+    M = math.prod(lead)
+    if tuple(dh.shape) != (*lead, N):
+        raise ValueError(f"dh must be {(*lead, N)}, got {tuple(dh.shape)}")
+    dx, dwg, dwu = out
+    _check_out(dx, "dx", (M, K), x.dtype, x.device)
+    _check_out(dwg, "dwg", (N, K), x.dtype, x.device)
+    _check_out(dwu, "dwu", (N, K), x.dtype, x.device)
+    for t, name in ((x, "x"), (wg, "wg"), (wu, "wu"), (dh, "dh")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _on_gpu(x)
+    check("swiglu_bwd_noalloc", lib().swiglu_bwd_noalloc(_act_code(act), dt, M, N, K, _p(x), _p(wg), _p(wu), _p(dh),
+                                                         float(gate_mult), float(up_mult), _p(dx), _p(dwg),
+                                                         _p(dwu), _stream(x)))
+    return dx, dwg, dwu
+
+
 def gemv_fwd(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, out: torch.Tensor | None = None,
              act: str = "silu", gate_mult: float = 1.0, up_mult: float = 1.0) -> torch.Tensor:
     """Decode forward for M <= 8 tokens (bf16): same result as fwd."""

@@ -55,7 +55,7 @@ def test_library_exports_every_header_symbol(L):
 def test_version_and_status_strings(L):
     assert L.swiglu_version() >= 100
     assert L.swiglu_status_str(0) == b"ok"
-    for s in range(1, 9):
+    for s in range(1, 10):
         assert L.swiglu_status_str(s) not in (b"ok", b"unknown status")
     assert L.swiglu_status_str(99) == b"unknown status"
     assert L.swiglu_last_hip_error() == 0
@@ -266,3 +266,23 @@ def test_product_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "synth" not in text, fn
+
+
+def test_bwd_noalloc_validation(L):
+    # Errors as swiglu_bwd_act_mult's, then the static-scratch bound; every
+    # case returns before any HIP call.
+    f = L.swiglu_bwd_noalloc
+    ESCRATCH = 9
+    assert f(2, 1, 4, 64, 8, A, A, A, A, 1.0, 1.0, A, A, A, None) == EARG          # unknown activation
+    assert f(0, 1, 4, 64, 8, A, A, A, A, math.nan, 1.0, A, A, A, None) == EARG     # multiplier
+    assert f(0, 5, 4, 64, 8, A, A, A, A, 1.0, 1.0, A, A, A, None) == EDTYPE
+    assert f(0, 1, 4, 64, 12, A, A, A, A, 1.0, 1.0, A, A, A, None) == ESHAPE       # bf16: K % 8
+    assert f(0, 1, 4, 64, 8, None, A, A, A, 1.0, 1.0, A, A, A, None) == ENULL
+    assert f(0, 1, 4, 64, 8, A, A, A, A, 1.0, 1.0, MIS, A, A, None) == EALIGN
+    assert f(0, 1, 4, 64, (1 << 22), A, A, A, A, 1.0, 1.0, A, A, A, None) == EUNSUP
+    assert f(0, 1, 4, 64, 0, None, None, None, None, 1.0, 1.0, None, None, None, None) == OK   # K == 0: nothing to do
+    big = (4096, 8192, 4096)
+    assert L.swiglu_bwd_workspace_bytes(1, *big) > _lib.NOALLOC_SCRATCH_BYTES
+    assert f(0, 1, *big, A, A, A, A, 1.0, 1.0, A, A, A, None) == ESCRATCH
+    assert f(1, 0, *big, A, A, A, A, 1.0, 1.0, A, A, A, None) == ESCRATCH
+    assert L.swiglu_status_str(ESCRATCH) == b"problem needs more scratch than the static buffer holds"
