@@ -113,8 +113,9 @@ int swiglu_fwd_mult(int act, int dtype, int64_t M, int64_t N, int64_t K,
                     const void* x, const void* wg, const void* wu,
                     float gate_mult, float up_mult, void* h, void* stream);
 
-/* Bytes of device workspace swiglu_bwd needs for these sizes (0 on invalid
- * sizes).  It holds [dg | du], its transpose, x^T and the transposed weight
+/* Bytes of device workspace swiglu_bwd needs for these sizes: 0 for sizes
+ * swiglu_bwd rejects (invalid, or past its limits), so the result never
+ * wraps.  It holds [dg | du], its transpose, x^T and the transposed weight
  * pair. */
 size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K);
 

@@ -111,8 +111,7 @@ int swiglu_fwd_fp8(int act, int64_t M, int64_t N, int64_t K, const void* x, cons
 }
 
 size_t swiglu_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K) {
-  if (swg::check_dtype(dtype) != SWIGLU_OK || swg::check_dims(M, N, K) != SWIGLU_OK) return 0;
-  return swg::bwd_layout(dtype, M, N, K).total;
+  return swg::bwd_workspace_total(dtype, M, N, K);
 }
 
 int swiglu_bwd_act_mult(int act, int dtype, int64_t M, int64_t N, int64_t K, const void* x,
@@ -227,7 +226,7 @@ int swiglu_bwd_noalloc(int act, int dtype, int64_t M, int64_t N, int64_t K, cons
   if (st == SWIGLU_OK)          // a call that needs no workspace (K, M or N is 0)
     return swiglu_bwd_act_mult(act, dtype, M, N, K, x, wg, wu, dh, gate_mult, up_mult, dx, dwg, dwu,
                                nullptr, 0, stream);
-  if (swg::bwd_layout(dtype, M, N, K).total > SWIGLU_NOALLOC_SCRATCH_BYTES) return SWIGLU_ERR_SCRATCH;
+  if (swg::bwd_workspace_total(dtype, M, N, K) > SWIGLU_NOALLOC_SCRATCH_BYTES) return SWIGLU_ERR_SCRATCH;
   void* ws = nullptr;
   const hipError_t e = scratch_address(&ws);
   if (e != hipSuccess) return hip_status(e);

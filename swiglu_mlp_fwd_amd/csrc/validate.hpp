@@ -95,16 +95,32 @@ inline int validate_fwd(int dtype, int64_t M, int64_t N, int64_t K, const void* 
   return SWIGLU_OK;
 }
 
-inline int validate_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
-                        const void* wu, const void* dh, const void* dx, const void* dwg,
-                        const void* dwu, const void* ws, size_t ws_bytes) {
+// The sizes the backward accepts, pointers aside: valid dims, grids that fit,
+// and every row stride its GEMMs read with (K, 2 Np, Mp) within kMaxLd.  Within
+// these limits every region of bwd_layout is below 2^46 bytes, so its sizes
+// cannot wrap.
+inline int bwd_shape_status(int dtype, int64_t M, int64_t N, int64_t K) {
   int st = check_dtype(dtype);
   if (st) return st;
   if ((st = check_dims(M, N, K))) return st;
   if (K % chunk_elems(dtype) != 0) return SWIGLU_ERR_SHAPE;
+  const int64_t Mp = round_up(M, 8), Np = round_up(N, dtype == SWIGLU_BF16 ? 64 : 8);
+  if (K > kMaxLd || 2 * Np > kMaxLd || Mp > kMaxLd) return SWIGLU_ERR_UNSUPPORTED;
+  if (!tiles_fit(M, Np) || !tiles_fit(M, K) || !tiles_fit(2 * Np, K)) return SWIGLU_ERR_UNSUPPORTED;
+  return SWIGLU_OK;
+}
+
+// Workspace bytes of a backward the library accepts; 0 for any other sizes.
+inline size_t bwd_workspace_total(int dtype, int64_t M, int64_t N, int64_t K) {
+  return bwd_shape_status(dtype, M, N, K) == SWIGLU_OK ? bwd_layout(dtype, M, N, K).total : 0;
+}
+
+inline int validate_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
+                        const void* wu, const void* dh, const void* dx, const void* dwg,
+                        const void* dwu, const void* ws, size_t ws_bytes) {
+  int st = bwd_shape_status(dtype, M, N, K);
+  if (st) return st;
   const BwdLayout L = bwd_layout(dtype, M, N, K);
-  if (!tiles_fit(M, L.Np) || !tiles_fit(M, K) || !tiles_fit(2 * L.Np, K)) return SWIGLU_ERR_UNSUPPORTED;
-  if (K > kMaxLd || 2 * L.Np > kMaxLd || L.Mp > kMaxLd) return SWIGLU_ERR_UNSUPPORTED;
   if (K == 0) return SWIGLU_OK;                       // every output is empty
   if (M > 0 && (st = check_ptr(dx))) return st;
   if (N > 0 && (st = check_ptr(dwg))) return st;

@@ -119,16 +119,20 @@ def test_leading_dimension_limit(L, dt):
     assert L.swiglu_fwd_act(0, dt, 4, 4, lim + 8, A, A, A, A, None) == EUNSUP
     assert L.swiglu_fwd_mult(0, dt, 4, 4, lim + 8, A, A, A, 1.0, 1.0, A, None) == EUNSUP
     # backward: K, 2 Np and Mp
-    need = L.swiglu_bwd_workspace_bytes(dt, 4, 4, lim + 64)
-    assert L.swiglu_bwd(dt, 4, 4, lim + 64, A, A, A, A, A, A, A, A, need, None) == EUNSUP
-    assert L.swiglu_bwd_workspace_bytes(dt, 4, lim // 2, 8) > 0
-    n_big = lim // 2 + npad                       # 2 Np = lim + 2 npad
-    need = L.swiglu_bwd_workspace_bytes(dt, 4, n_big, 8)
-    assert L.swiglu_bwd(dt, 4, n_big, 8, A, A, A, A, A, A, A, A, need, None) == EUNSUP
+    assert L.swiglu_bwd_workspace_bytes(dt, 4, 4, lim + 64) == 0
+    assert L.swiglu_bwd(dt, 4, 4, lim + 64, A, A, A, A, A, A, A, A, 1 << 62, None) == EUNSUP
+    n_ok = (lim // 2) // npad * npad              # largest N with 2 Np <= lim
+    assert L.swiglu_bwd_workspace_bytes(dt, 4, n_ok, 8) > 0
+    n_big = n_ok + 1                              # 2 Np = 2 n_ok + 2 npad > lim
+    assert L.swiglu_bwd_workspace_bytes(dt, 4, n_big, 8) == 0    # sizes the backward rejects have no size
+    assert L.swiglu_bwd(dt, 4, n_big, 8, A, A, A, A, A, A, A, A, 1 << 62, None) == EUNSUP
     m_big = lim + 8                               # Mp = lim + 8
-    need = L.swiglu_bwd_workspace_bytes(dt, m_big, 4, 8)
-    assert L.swiglu_bwd(dt, m_big, 4, 8, A, A, A, A, A, A, A, A, need, None) == EUNSUP
-    assert L.swiglu_bwd_act_mult(0, dt, m_big, 4, 8, A, A, A, A, 1.0, 1.0, A, A, A, A, need, None) == EUNSUP
+    assert L.swiglu_bwd_workspace_bytes(dt, m_big, 4, 8) == 0
+    assert L.swiglu_bwd(dt, m_big, 4, 8, A, A, A, A, A, A, A, A, 1 << 62, None) == EUNSUP
+    assert L.swiglu_bwd_act_mult(0, dt, m_big, 4, 8, A, A, A, A, 1.0, 1.0, A, A, A, A, 1 << 62, None) == EUNSUP
+    assert L.swiglu_bwd_workspace_bytes(dt, lim, 4, 8) > 0                 # Mp = lim is accepted
+    # huge sizes never wrap to a small workspace
+    assert L.swiglu_bwd_workspace_bytes(dt, (1 << 31) - 1, (1 << 31) - 1, 8) == 0
 
 
 def test_gemv_validation(L):
