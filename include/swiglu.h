@@ -207,7 +207,9 @@ int swiglu_bwd_noalloc(int act, int dtype, int64_t M, int64_t N, int64_t K,
  * primitive for M = 1, 2, 4, 8 bound by the cold weight read).
  *
  *   x [M, K], wg/wu [N, K] (bf16 inputs), h [M, N] (bf16 output)
- * Layout rule: K % 8 == 0 and M * K * 2 <= 65536 (x is staged in LDS);
+ * Layout rule: K % 8 == 0 and M * K * 2 <= 163840 (x is staged in one
+ * workgroup's 160 KiB of LDS: K <= 10240 at M = 8, which covers the
+ * page's LLaMA-2 7B/13B, LLaMA-3 8B and GPT-NeoX-20B up/gate shapes);
  * larger x gives SWIGLU_ERR_UNSUPPORTED. */
 int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K,
                     const void* x, const void* wg, const void* wu, void* h,
@@ -334,6 +336,19 @@ int swiglu_act_bwd_dt(int dtype, int64_t rows, int64_t cols,
                       const float* weights, float clamp_limit,
                       void* dgate, void* dup, float* weight_grad, void* stream);
 
+/* Measurement aid: the decode kernel's read-only twin.  The same launch as
+ * swiglu_gemv_fwd for (M, N, K) -- grid, LDS footprint, staging of x and
+ * every weight load, in the same order and unrolling -- with no arithmetic:
+ * the loaded words are folded into one uint32 per column, written to
+ * `sink` [N].  Its time is the floor of the decode kernel's access pattern
+ * on the same buffers ("Fused SwiGLU benchmark", section HBM
+ * re-measurement: the fused kernel against a pure-read loop over the same
+ * rotated weights).  Arguments and errors as swiglu_gemv_fwd (sink in place
+ * of h, 4-byte aligned). */
+int swiglu_probe_gemv_read(int64_t M, int64_t N, int64_t K,
+                           const void* x, const void* wg, const void* wu, uint32_t* sink,
+                           void* stream);
+
 /* Measurement aid: a pure streaming read of two device buffers of `bytes`
  * bytes each (16-byte multiples), the cold-read floor against which the
  * decode kernel is judged ("Fused SwiGLU benchmark", section HBM
@@ -361,6 +376,11 @@ int swiglu_last_hip_error(void);
 
 /* Library version: major * 10000 + minor * 100 + patch. */
 int swiglu_version(void);
+
+/* Hash of the sources and compiler flags this library was built from (16
+ * hex digits, static string), so a caller can tell a stale build from a
+ * current one. */
+const char* swiglu_source_hash(void);
 
 #ifdef __cplusplus
 }

@@ -1,7 +1,9 @@
 """ctypes loader for libswiglu.so (the C ABI declared in include/swiglu.h).
 
 The library is loaded from this package directory only; there is no fallback
-of any kind: if it is missing or fails to load, every call raises.
+of any kind: if it is missing, fails to load, or was built from sources other
+than the ones in the tree (its embedded source hash differs), every call
+raises.
 """
 from __future__ import annotations
 
@@ -58,10 +60,12 @@ SIGNATURES = {
     "swiglu_act_bwd_dt": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                          ctypes.c_float, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "swiglu_probe_mfma": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_ptr, _c_ptr]),
+    "swiglu_probe_gemv_read": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "swiglu_probe_read2": (ctypes.c_int, [_c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr, _c_ptr]),
     "swiglu_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "swiglu_last_hip_error": (ctypes.c_int, []),
     "swiglu_version": (ctypes.c_int, []),
+    "swiglu_source_hash": (ctypes.c_char_p, []),
 }
 
 _lock = threading.Lock()
@@ -91,10 +95,20 @@ def lib() -> ctypes.CDLL:
                     f"{LIB_PATH} is not built; run `python -m swiglu_mlp_fwd_amd.build` "
                     "(there is no non-HIP fallback)")
             L = ctypes.CDLL(LIB_PATH)
+            from .build import source_hash
+            current = source_hash()
+            if not hasattr(L, "swiglu_source_hash"):
+                raise RuntimeError(f"{LIB_PATH} is stale (it has no source hash); rebuild with "
+                                   "`python -m swiglu_mlp_fwd_amd.build`")
             for name, (res, args) in SIGNATURES.items():
                 f = getattr(L, name)
                 f.restype = res
                 f.argtypes = args
+            built = L.swiglu_source_hash().decode()
+            if built != current:
+                raise RuntimeError(
+                    f"{LIB_PATH} is stale: built from sources with hash {built}, the tree's sources hash to "
+                    f"{current}; rebuild with `python -m swiglu_mlp_fwd_amd.build`")
             _lib = L
     return _lib
 

@@ -9,6 +9,7 @@ is compiled with packed-fp32 instructions disabled.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -36,6 +37,20 @@ HIPCC_FLAGS = [
 ]
 
 
+def source_hash() -> str:
+    """Hash of everything the library is built from: every file under csrc/,
+    the public header and the compiler flags.  It is compiled into the
+    library (swiglu_source_hash) and compared on load, so a library built
+    from other sources is refused instead of silently tested."""
+    h = hashlib.sha256()
+    files = sorted(os.path.join("csrc", f) for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp", ".h")))
+    for rel in files + [os.path.join("..", "include", "swiglu.h")]:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+    h.update(" ".join(HIPCC_FLAGS).encode())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -45,8 +60,8 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, f'-DSWIGLU_SOURCE_HASH="{source_hash()}"', "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -8,6 +8,11 @@
 #include "swiglu.h"
 #include "validate.hpp"
 
+// Set by the build (a hash of the sources and flags); see swiglu_source_hash.
+#ifndef SWIGLU_SOURCE_HASH
+#define SWIGLU_SOURCE_HASH "unknown"
+#endif
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -307,6 +312,17 @@ int swiglu_probe_mfma(int iters, int blocks, float* sink, void* stream) {
   return hip_status(swg::launch_probe_mfma(iters, blocks, sink, as_stream(stream)));
 }
 
+int swiglu_probe_gemv_read(int64_t M, int64_t N, int64_t K, const void* x, const void* wg, const void* wu,
+                           uint32_t* sink, void* stream) {
+  // h is checked for 16-byte alignment by the GEMV's validation; the sink
+  // only needs 4 (one word per column).
+  int st = swg::validate_gemv(M, N, K, x, wg, wu, x);
+  if (st != SWIGLU_OK || M == 0 || N == 0) return st;
+  if (sink == nullptr) return SWIGLU_ERR_NULL;
+  if (!swg::aligned(sink, 4)) return SWIGLU_ERR_ALIGN;
+  return hip_status(swg::launch_gemv_read_twin((int)M, (int)N, (int)K, x, wg, wu, sink, as_stream(stream)));
+}
+
 int swiglu_probe_read2(const void* a, const void* b, size_t bytes, uint32_t* sink, void* stream) {
   if (bytes % 16 != 0) return SWIGLU_ERR_SHAPE;
   if (bytes == 0) return SWIGLU_OK;
@@ -334,5 +350,7 @@ const char* swiglu_status_str(int status) {
 int swiglu_last_hip_error(void) { return g_last_hip_error; }
 
 int swiglu_version(void) { return 100; }
+
+const char* swiglu_source_hash(void) { return SWIGLU_SOURCE_HASH; }
 
 }  // extern "C"

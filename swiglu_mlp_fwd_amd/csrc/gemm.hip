@@ -51,8 +51,6 @@
 // same chunk mapping for A and B makes the products pair up correctly
 // whatever order the matrix core uses within a chunk.  16 x 16 x 32: row
 // (l & 15) and chunk (4 kk + (l >> 4)).
-#include <mutex>
-
 #include "common.hpp"
 #include "fp8.hpp"
 #include "gemm.hpp"
@@ -796,6 +794,11 @@ void gemm_dma_kernel(GemmArgs p) {
           wait_dma(S - 2);
           barrier_no_fence();
           if constexpr (kIL == 3) {
+            // The next step's first fragment reads go between the MFMAs
+            // with the refill DMAs (one read and one DMA per group of
+            // MFMAs) instead of all at once after the barrier: 3.3 % faster
+            // for the forward dual GEMM at 8192 x 14336 x 4096, 0.9 % slower
+            // for the backward's products, bit-identical either way.
             __builtin_amdgcn_sched_barrier(0);
             read_frags(0, lds_bytes + ((ks + 1) % S) * kStageBytes, 0);
             issue(ks + S);
@@ -864,26 +867,6 @@ void gemm_dma_kernel(GemmArgs p) {
   }
 }
 
-// Allows `Kernel` more than the default 64 KiB of dynamic LDS.  The
-// attribute belongs to the kernel on the current device, so it is set once
-// per (kernel, device); concurrent first calls are serialised by call_once.
-template <auto Kernel>
-hipError_t allow_lds(size_t lds) {
-  constexpr int kMaxDevices = 64;
-  static std::once_flag once[kMaxDevices];
-  static hipError_t result[kMaxDevices];
-  int dev = 0;
-  const hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  auto set = [&] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)lds);
-  };
-  if (dev < 0 || dev >= kMaxDevices) return set();
-  std::call_once(once[dev], [&] { result[dev] = set(); });
-  return result[dev];
-}
-
 template <typename T, Epi E, int NB, class TL, int KC, int S, int kIL = 0, int kMN = 16>
 hipError_t launch_dma(const GemmArgs& a, hipStream_t s) {
   const int ntm = (a.m + TL::kBM - 1) / TL::kBM;
@@ -910,17 +893,19 @@ using TileSingleF32 = Tile<128, 128, 2, 2, 2>;  // 64 x 64 per wave
 
 }  // namespace
 
+// The bf16 forward products use the interleaved step boundary (kIL = 3),
+// the backward's the plain one (kIL = 2): each the faster at the training shape.
 hipError_t launch_fwd_dual(Dt dt, Act act, const GemmArgs& a, hipStream_t s) {
   if (act == Act::kGeluTanh)
-    return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kGeGLU, 2, TileDual, 8, 2, 2>(a, s)
+    return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kGeGLU, 2, TileDual, 8, 2, 3>(a, s)
                            : launch_dma<float, Epi::kGeGLU, 2, TileDualF32, 8, 2, 2, 32>(a, s);
-  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2, 2>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kSwiGLU, 2, TileDual, 8, 2, 3>(a, s)
                          : launch_dma<float, Epi::kSwiGLU, 2, TileDualF32, 8, 2, 2, 32>(a, s);
 }
 
 hipError_t launch_fwd_dual_fp8(Act act, const GemmArgs& a, hipStream_t s) {
-  return act == Act::kGeluTanh ? launch_dma<bf16, Epi::kGeGLUq, 2, TileDual, 8, 2, 2>(a, s)
-                               : launch_dma<bf16, Epi::kSwiGLUq, 2, TileDual, 8, 2, 2>(a, s);
+  return act == Act::kGeluTanh ? launch_dma<bf16, Epi::kGeGLUq, 2, TileDual, 8, 2, 3>(a, s)
+                               : launch_dma<bf16, Epi::kSwiGLUq, 2, TileDual, 8, 2, 3>(a, s);
 }
 
 hipError_t launch_bwd_dswiglu(Dt dt, Act act, const GemmArgs& a, hipStream_t s) {

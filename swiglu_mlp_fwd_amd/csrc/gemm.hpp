@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace swg {
 
 // C[m, n] = sum_r A[m, r] * B[n, r]: both operands have the reduction index
@@ -40,6 +42,28 @@ struct GemmArgs {
 enum class Dt { kF32 = 0, kBF16 = 1 };
 enum class Act { kSilu = 0, kGeluTanh = 1 };   // the gate activation of the gated forward
 
+// Allows `Kernel` up to `lds` bytes of dynamic LDS (the default limit is
+// 64 KiB; gfx950 has 160 KiB per workgroup).  The attribute belongs to the
+// kernel on the current device, so it is set once per (kernel, device) with
+// the largest size that kernel is ever launched with; concurrent first calls
+// are serialised by call_once.
+template <auto Kernel>
+hipError_t allow_lds(size_t lds) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static hipError_t result[kMaxDevices];
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  auto set = [&] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds);
+  };
+  if (dev < 0 || dev >= kMaxDevices) return set();
+  std::call_once(once[dev], [&] { result[dev] = set(); });
+  return result[dev];
+}
+
 hipError_t launch_fwd_dual(Dt dt, Act act, const GemmArgs& a, hipStream_t s);  // h = act(g) * u
 // bf16 inputs, h = act(g) * u quantised per 1x32 block (n % 32 == 0).
 hipError_t launch_fwd_dual_fp8(Act act, const GemmArgs& a, hipStream_t s);
@@ -53,6 +77,11 @@ hipError_t launch_transpose(Dt dt, const void* in, int64_t ld_in, int rows, int 
 
 hipError_t launch_gemv(Act act, int M, int N, int K, const void* x, const void* wg, const void* wu,
                        void* h, float gmul, float umul, hipStream_t s);
+
+// The decode kernel's read-only twin: the same grid, LDS and weight loads,
+// no arithmetic; sink receives one word per column.
+hipError_t launch_gemv_read_twin(int M, int N, int K, const void* x, const void* wg, const void* wu,
+                                 uint32_t* sink, hipStream_t s);
 
 hipError_t launch_act_bwd(Dt dt, int64_t rows, int64_t cols, const void* gate, const void* up,
                           const void* dy, const float* weights, float limit, bool clamp,

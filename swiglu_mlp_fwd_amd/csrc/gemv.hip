@@ -12,7 +12,16 @@
 // j, j+32, ...); x [M, K] is staged once per workgroup in LDS and each 16-byte
 // chunk of it is reused for both weights.  Per lane the 2M partial sums are
 // reduced across the half-wave with butterfly shuffles; lane 0 of the half
-// applies SiLU(g) * u and stores the M outputs of its column.
+// applies SiLU(g) * u and stores the M outputs of its column.  x may take up
+// the whole 160 KiB of a workgroup's LDS (M K <= 81,920): up to 64 KiB two
+// workgroups share a CU, beyond it one (the LLaMA-2 13B and GPT-NeoX-20B
+// up/gate shapes of the benchmark page at M = 8: 80 and 96 KiB).
+//
+// The read-only twin (kTwin) is the same kernel with the same grid, LDS
+// footprint, x staging and weight loads, and no arithmetic: each lane folds
+// the loaded words into one value.  Its time is the floor of this access
+// pattern, the counterpart on the same buffers of the benchmark page's
+// pure-read loop.
 #include "common.hpp"
 #include "gemm.hpp"
 
@@ -29,12 +38,12 @@ constexpr int kColsPerBlock = 16;  // 8 waves x 2 half-waves
 // the extra exchange costs more than the LDS reads it saves).
 template <int M> constexpr bool kSplitX = M >= 6 && M % 2 == 0;
 
-template <int M, Act A>
+template <int M, Act A, bool kTwin>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__ x,
                                                         const bf16* __restrict__ wg,
                                                         const bf16* __restrict__ wu,
                                                         bf16* __restrict__ h, int N, int K,
-                                                        float gmul, float umul) {
+                                                        float gmul, float umul, uint32_t* __restrict__ sink) {
   extern __shared__ u32x4 xs[];  // [M][K / 8]
   const int nch = K >> 3;
   const int tid = threadIdx.x;
@@ -58,7 +67,27 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__
 #pragma unroll
   for (int m = 0; m < M; ++m) ag[m] = au[m] = 0.0f;
 
-  if constexpr (kSplitX<M>) {
+  if constexpr (kTwin) {
+    // The weight stream of the branch below that this M takes (same loads,
+    // same unrolling), folded into one word.
+    uint32_t fold = 0;
+    auto eat = [&](int c) {
+      const u32x4 vg = __builtin_nontemporal_load(rg + c);
+      const u32x4 vu = __builtin_nontemporal_load(ru + c);
+      fold ^= vg[0] ^ vg[1] ^ vg[2] ^ vg[3] ^ vu[0] ^ vu[1] ^ vu[2] ^ vu[3];
+    };
+    if constexpr (kSplitX<M>) {
+#pragma unroll 2
+      for (int c = hl; c < nch; c += 32) eat(c);
+    } else {
+#pragma unroll 4
+      for (int c = hl; c < nch; c += 32) eat(c);
+    }
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) fold ^= __shfl_xor(fold, off, 32);
+    if (live && hl == 0) sink[col] = fold;
+    return;
+  } else if constexpr (kSplitX<M>) {
     // The two half-waves read the same x chunks.  Each reads half of the
     // M rows (the lower half rows 0..M/2-1, the upper half the rest) and
     // v_permlane32_swap hands every lane both halves' values: half the LDS
@@ -119,29 +148,36 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__
   }
 }
 
-template <int M, Act A>
+constexpr size_t kMaxLds = 160 * 1024;   // gfx950: LDS of one workgroup
+
+template <int M, Act A, bool kTwin>
 hipError_t launch_m(int N, int K, const void* x, const void* wg, const void* wu, void* h,
-                    float gm, float um, hipStream_t s) {
+                    float gm, float um, uint32_t* sink, hipStream_t s) {
   const unsigned blocks = (unsigned)((N + kColsPerBlock - 1) / kColsPerBlock);
   const size_t lds = (size_t)M * K * 2;
-  hipLaunchKernelGGL((gemv_kernel<M, A>), dim3(blocks), dim3(kThreads), lds, s,
+  if (lds > kMaxLds) return hipErrorInvalidValue;        // the host checks M K <= 81,920
+  if (lds > 64 * 1024) {
+    const hipError_t e = allow_lds<&gemv_kernel<M, A, kTwin>>(kMaxLds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((gemv_kernel<M, A, kTwin>), dim3(blocks), dim3(kThreads), lds, s,
                      static_cast<const bf16*>(x), static_cast<const bf16*>(wg),
-                     static_cast<const bf16*>(wu), static_cast<bf16*>(h), N, K, gm, um);
+                     static_cast<const bf16*>(wu), static_cast<bf16*>(h), N, K, gm, um, sink);
   return hipGetLastError();
 }
 
-template <Act A>
+template <Act A, bool kTwin>
 hipError_t launch_act(int M, int N, int K, const void* x, const void* wg, const void* wu, void* h,
-                      float gm, float um, hipStream_t s) {
+                      float gm, float um, uint32_t* sink, hipStream_t s) {
   switch (M) {
-    case 1: return launch_m<1, A>(N, K, x, wg, wu, h, gm, um, s);
-    case 2: return launch_m<2, A>(N, K, x, wg, wu, h, gm, um, s);
-    case 3: return launch_m<3, A>(N, K, x, wg, wu, h, gm, um, s);
-    case 4: return launch_m<4, A>(N, K, x, wg, wu, h, gm, um, s);
-    case 5: return launch_m<5, A>(N, K, x, wg, wu, h, gm, um, s);
-    case 6: return launch_m<6, A>(N, K, x, wg, wu, h, gm, um, s);
-    case 7: return launch_m<7, A>(N, K, x, wg, wu, h, gm, um, s);
-    case 8: return launch_m<8, A>(N, K, x, wg, wu, h, gm, um, s);
+    case 1: return launch_m<1, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
+    case 2: return launch_m<2, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
+    case 3: return launch_m<3, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
+    case 4: return launch_m<4, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
+    case 5: return launch_m<5, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
+    case 6: return launch_m<6, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
+    case 7: return launch_m<7, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
+    case 8: return launch_m<8, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -150,8 +186,13 @@ hipError_t launch_act(int M, int N, int K, const void* x, const void* wg, const 
 
 hipError_t launch_gemv(Act act, int M, int N, int K, const void* x, const void* wg, const void* wu,
                        void* h, float gmul, float umul, hipStream_t s) {
-  return act == Act::kGeluTanh ? launch_act<Act::kGeluTanh>(M, N, K, x, wg, wu, h, gmul, umul, s)
-                               : launch_act<Act::kSilu>(M, N, K, x, wg, wu, h, gmul, umul, s);
+  return act == Act::kGeluTanh ? launch_act<Act::kGeluTanh, false>(M, N, K, x, wg, wu, h, gmul, umul, nullptr, s)
+                               : launch_act<Act::kSilu, false>(M, N, K, x, wg, wu, h, gmul, umul, nullptr, s);
+}
+
+hipError_t launch_gemv_read_twin(int M, int N, int K, const void* x, const void* wg, const void* wu,
+                                 uint32_t* sink, hipStream_t s) {
+  return launch_act<Act::kSilu, true>(M, N, K, x, wg, wu, nullptr, 1.0f, 1.0f, sink, s);
 }
 
 }  // namespace swg

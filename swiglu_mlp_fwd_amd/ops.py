@@ -354,6 +354,24 @@ def probe_mfma(iters: int, blocks: int, sink: torch.Tensor) -> int:
     return 2 * 16 * 16 * 32 * 8 * 8 * int(iters) * int(blocks)
 
 
+def probe_gemv_read(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, sink: torch.Tensor) -> None:
+    """The decode kernel's read-only twin on these buffers (same launch as
+    gemv_fwd, no arithmetic): one int32 word per column into sink [N]."""
+    _same(x, wg, wu)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("probe_gemv_read is bf16 only")
+    lead, K = x.shape[:-1], x.shape[-1]
+    N = _weights(wg, wu, K)
+    M = math.prod(lead)
+    if sink.dtype != torch.int32 or sink.numel() < N or not sink.is_contiguous() or sink.device != x.device:
+        raise ValueError(f"sink must be a contiguous int32 tensor of at least {N} elements on the device of x")
+    if not (x.is_contiguous() and wg.is_contiguous() and wu.is_contiguous()):
+        raise ValueError("probe_gemv_read takes contiguous tensors")
+    _on_gpu(x)
+    check("swiglu_probe_gemv_read", lib().swiglu_probe_gemv_read(M, N, K, _p(x), _p(wg), _p(wu), _p(sink),
+                                                                 _stream(x)))
+
+
 def probe_read2(a: torch.Tensor, b: torch.Tensor, sink: torch.Tensor) -> None:
     """Pure read of two equally sized buffers (cold-read floor measurement)."""
     nbytes = a.numel() * a.element_size()

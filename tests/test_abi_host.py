@@ -140,7 +140,16 @@ def test_gemv_validation(L):
     assert f(9, 16, 64, A, A, A, A, None) == ESHAPE
     assert f(-1, 16, 64, A, A, A, A, None) == ESHAPE
     assert f(2, 16, 60, A, A, A, A, None) == ESHAPE
-    assert f(8, 16, 8192, A, A, A, A, None) == EUNSUP          # x does not fit the LDS stage
+    assert f(8, 16, 10248, A, A, A, A, None) == EUNSUP         # x (8 x 10248 bf16) does not fit 160 KiB of LDS
+    assert f(8, 0, 10240, A, A, A, A, None) == OK               # 160 KiB exactly is accepted (N = 0: no launch)
+    assert f(1, 16, 81928, A, A, A, A, None) == EUNSUP
+    p = L.swiglu_probe_gemv_read
+    assert p(8, 16, 10248, A, A, A, A, None) == EUNSUP
+    assert p(9, 16, 64, A, A, A, A, None) == ESHAPE
+    assert p(2, 16, 64, A, A, A, None, None) == ENULL
+    assert p(2, 16, 64, A, A, A, 0x10002, None) == EALIGN       # sink: 4-byte aligned
+    assert p(2, 16, 64, MIS, A, A, A, None) == EALIGN
+    assert p(0, 16, 64, None, None, None, None, None) == OK
     assert f(2, 16, 64, A, None, A, A, None) == ENULL
     assert f(2, 16, 64, A, A, A, MIS, None) == EALIGN
     assert f(0, 16, 64, None, None, None, None, None) == OK
@@ -290,3 +299,22 @@ def test_bwd_noalloc_validation(L):
     assert f(0, 1, *big, A, A, A, A, 1.0, 1.0, A, A, A, None) == ESCRATCH
     assert f(1, 0, *big, A, A, A, A, 1.0, 1.0, A, A, A, None) == ESCRATCH
     assert L.swiglu_status_str(ESCRATCH) == b"problem needs more scratch than the static buffer holds"
+
+
+def test_library_is_built_from_the_tree(L):
+    # The loaded library carries the hash of the sources it was built from.
+    from swiglu_mlp_fwd_amd.build import source_hash
+    assert L.swiglu_source_hash().decode() == source_hash()
+
+
+def test_a_stale_library_is_refused(monkeypatch):
+    # Sources that hash differently from the library's embedded hash: the
+    # loader raises instead of handing out the library.
+    import swiglu_mlp_fwd_amd.build as B
+    monkeypatch.setattr(B, "source_hash", lambda: "0000000000000000")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="stale"):
+        _lib.lib()
+    monkeypatch.undo()
+    _lib._lib = None
+    assert _lib.lib() is not None

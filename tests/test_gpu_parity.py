@@ -264,8 +264,12 @@ def test_autograd_matches_explicit_backward():
 # ----------------------------------------------------------------- decode
 
 @pytest.mark.parametrize("M", [1, 2, 4, 8])
-@pytest.mark.parametrize("NK", [(6912, 1536), (11008, 4096)])
+@pytest.mark.parametrize("NK", [(6912, 1536), (11008, 4096), (13824, 5120), (24576, 6144)])
 def test_gemv_full(M, NK):
+    """Every element, at the benchmark page's decode shapes: (6912, 1536), the
+    LLaMA-7B-like (11008, 4096), and the wide LLaMA-2 13B (13824, 5120) and
+    GPT-NeoX-20B (24576, 6144) up/gate shapes, whose x at M = 8 (80 and
+    96 KiB) takes more than the default 64 KiB of LDS."""
     N, K = NK
     d = synth.decode_bf16(M, N, K, seed=0)
     check_fwd(d, "bf16", what=f"gemv M={M} N={N} K={K}", via="gemv")
@@ -446,6 +450,23 @@ def test_probe_mfma_runs():
     torch.cuda.synchronize()
     assert flops == 2 * 32 * 32 * 16 * 4 * 8 * 16 * 64
     assert torch.isfinite(sink).all() and torch.count_nonzero(sink).item() > 0
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 6912, 1536), (8, 11008, 4096), (8, 24576, 6144), (3, 257, 520),
+                                   (6, 13, 8)])
+def test_probe_gemv_read_reads_every_weight(M, N, K):
+    """The decode kernel's read-only twin: column n's word is the XOR of every
+    32-bit word of Wg[n, :] and Wu[n, :], so a skipped or repeated load shows."""
+    d = synth.decode_bf16(M, N, K, seed=3)
+    t = to_dev(d)
+    sink = torch.full((N + 64,), -1, dtype=torch.int32, device=DEV)
+    S.probe_gemv_read(t["x"], t["wg"], t["wu"], sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    want = (np.bitwise_xor.reduce(d["wg"].view(np.uint32), axis=1) ^
+            np.bitwise_xor.reduce(d["wu"].view(np.uint32), axis=1))
+    assert np.array_equal(got[:N], want), "the twin's fold differs from the weights' XOR"
+    assert np.all(got[N:] == np.uint32(0xFFFFFFFF)), "the twin wrote past its N columns"
 
 
 def test_probe_read2_runs():
