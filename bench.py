@@ -9,22 +9,35 @@ h = SiLU(x Wg^T) * (x Wu^T) followed by the backward (dX, dWg, dWu).
 value = algorithmic TFLOP/s of that step, 12 M N K flops per step (4 M N K
 forward, 8 M N K for dX and dW; the recompute of g and u in the backward is
 not credited).  Inputs are synthetic (seed 0) and resident in HBM before the
-timed region starts.
+timed region starts; --warmup steps, then --steps timed steps, eager.
 
-The same run also measures, after the timed region and outside `value`:
-  decode   the M=1..8 weight-streaming forward at (N,K)=(6912,1536) with 16
-           rotated weight copies and (11008,4096) with 4 copies (each call
-           reads cold weights), in GB/s, beside a pure dual-stream read of
-           the same buffers (the cold-read floor);
-  act_quant the elementwise SwiGLU + FP8 block quantisation of [4001, 3584]
-           fp32 inputs (4 rotated copies), in GB/s;
-  act_bwd  the elementwise SwiGLU backward on [4001, 3584] fp32 gate/up/dy
-           (4 rotated copies): clamp 0.5 without weights, and per-row weights
-           with the weight gradient and no clamp, in GB/s;
-  fp32     the IEEE-fp32 fused forward at M=4001, K=2048, N=3584, in TFLOP/s;
-  geglu    the GeGLU forward (GELU-tanh gate) at the headline shape, in TFLOP/s;
-  cpu_baseline  the fp64 oracle on a row sample of the headline workload,
-           timed on the host cores.
+After the headline, every workload of the stage is measured with the
+protocol of "Fused SwiGLU benchmark" (AstrAI docs/developer/swiglu_benchmark.md,
+opening section): per variant one HIP graph of --iters calls over rotated
+buffers, --graph-warmup eager calls first, then --trials trials in
+A-B-C-C-B-A order across the variants of a leg, device time from HIP events
+around each graph launch; every sample is kept with p50/p90/p99 per call,
+eager per-call times beside them, the kernel launches per call, and the
+error of one call's output against the fp64 oracle (max / mean absolute
+error, cosine).  The oracle's own time on the host cores is recorded per
+configuration (the headline's on a row sample, extrapolated and labelled).
+Legs:
+  train_fwd   forward variants at the headline shape (SwiGLU, GeGLU, and
+              both with the FP8-quantised output), TFLOP/s;
+  train_bwd   the backward (SwiGLU, GeGLU), TFLOP/s on 8 M N K;
+  decode      M = 1, 2, 4, 8 at (N, K) = (6912, 1536), (11008, 4096),
+              (13824, 5120), (24576, 6144) with rotated weight copies well
+              past the 256 MB Infinity Cache, GB/s, beside the kernel's
+              read-only twin and a dual-stream read of the same buffers; the
+              floor is the faster of the two;
+  act_quant   elementwise SwiGLU + 1x32 FP8 quantisation of [4001, 3584] fp32
+              (clamp off, L = 7 with count, GELU-tanh), beside the
+              quantiser's load/store twin, GB/s; the non-quantised forward
+              (fp32 and bf16 h);
+  act_bwd     the elementwise backward (fp32 with clamp, fp32 with row
+              weights and weight_grad, bf16 with clamp), GB/s;
+  fp32        the IEEE-fp32 dual GEMM at M=4001, K=2048, N=3584, TFLOP/s;
+  tiny_fp32   forward + backward at x[4, 64], W[128, 64].
 """
 from __future__ import annotations
 
@@ -45,6 +58,15 @@ PEAK_FP32_TFLOPS = 157.3      # dense fp32 matrix, MI355X
 PEAK_HBM_GBS = 8000.0         # HBM3E, MI355X
 
 M4, N4, K4 = 8192, 14336, 4096
+DECODE_SHAPES = ((6912, 1536, 16), (11008, 4096, 4), (13824, 5120, 2), (24576, 6144, 2))   # (N, K, copies)
+AQ_R, AQ_C = 4001, 3584
+F32_M, F32_N, F32_K = 4001, 3584, 2048
+
+# Kernel launches per library call (from the entry points' code): the bf16
+# backward runs the recompute, two weight transposes, the dX product, the x
+# transpose and the dW product; the fp32 one transposes D as well.
+LAUNCHES = {"fwd": 1, "bwd_bf16": 6, "bwd_f32": 7, "gemv": 1, "act_quant_count": 2, "act_quant": 1,
+            "act_fwd_count": 2, "act_fwd": 1, "act_bwd": 1}
 
 
 def log(*a):
@@ -56,76 +78,63 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target host time of the oracle sample")
+    p.add_argument("--trials", type=int, default=10, help="A-B-C-C-B-A trials per leg")
+    p.add_argument("--iters", type=int, default=100, help="calls per graph (decode and elementwise legs)")
+    p.add_argument("--gemm-iters", type=int, default=20, help="calls per graph of the 8192x14336x4096 and fp32 legs")
+    p.add_argument("--graph-warmup", type=int, default=20, help="eager calls per variant before capture")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target host time of the headline oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-extra", action="store_true", help="skip the decode / act_quant / fp32 legs")
-    p.add_argument("--only", choices=["step", "fwd", "decode", "act_quant", "act_bwd", "fp32", "fwd_fp8", "traffic"], default=None,
-                   help="profiling aid: run one leg only (no JSON contract); 'traffic' runs the headline "
-                        "forward and a 1 GiB copy (the counter calibration) for the --pmc runs")
-    p.add_argument("--digest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
-                   help="read the counter_collection.csv files of two rocprofv3 --pmc runs of "
-                        "'--only traffic' (FETCH_SIZE, then WRITE_SIZE) and write profiles/traffic.json")
+    p.add_argument("--no-extra", action="store_true", help="headline only")
+    p.add_argument("--only", default=None,
+                   choices=["step", "fwd", "train_fwd", "train_bwd", "decode", "act_quant", "act_bwd", "fp32", "tiny",
+                            "traffic", "traffic_decode", "traffic_act_quant", "traffic_act_fwd", "traffic_act_bwd"],
+                   help="profiling aid: run one leg only (no JSON contract); 'traffic*' runs a kernel and a 1 GiB "
+                        "copy (the counter calibration) for the --pmc runs")
+    p.add_argument("--digest-traffic", nargs=3, metavar=("NAME", "FETCH_CSV", "WRITE_CSV"), default=None,
+                   help="read the counter_collection.csv files of two rocprofv3 --pmc runs of a 'traffic*' leg "
+                        "(FETCH_SIZE, then WRITE_SIZE) and record NAME in profiles/traffic.json")
     return p.parse_args()
 
 
+# ------------------------------------------------------------------ traffic
+
 COPY_BYTES = 1 << 30            # calibration copy: reads and writes this many bytes per launch
-FWD_KERNEL_TAG = "gemm_dma_kernelIDF16bLNS0_3EpiE0E"   # mangled-name fragment of the bf16 fused forward
 COPY_KERNEL_TAG = "copy"
-
-
-def digest_traffic(fetch_csv: str, write_csv: str) -> None:
-    """HBM bytes per launch of the fused forward from two --pmc runs: the
-    FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the forward kernel,
-    each scaled by (known bytes / counter reading) of a plain 1 GiB copy
-    measured in the same run."""
-    import csv
-
-    def per_kernel(path, counter):
-        vals = {}
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
-                continue
-            name = r["Kernel_Name"]
-            tag = "fwd" if FWD_KERNEL_TAG in name else ("copy" if COPY_KERNEL_TAG in name else None)
-            if tag is None:
-                continue
-            vals.setdefault(tag, {}).setdefault(r["Dispatch_Id"], 0.0)
-            vals[tag][r["Dispatch_Id"]] += float(r["Counter_Value"])
-        return {k: sum(v.values()) / len(v) for k, v in vals.items()}
-
-    f = per_kernel(fetch_csv, "FETCH_SIZE")
-    w = per_kernel(write_csv, "WRITE_SIZE")
-    sf = COPY_BYTES / (f["copy"] * 1024.0)
-    sw = COPY_BYTES / (w["copy"] * 1024.0)
-    fetch_b = f["fwd"] * 1024.0 * sf
-    write_b = w["fwd"] * 1024.0 * sw
-    out = {"fwd_dual_gemm_bf16_8192x14336x4096": {
-        "source_hash": kernel_source_hash(),
-        "bytes_per_launch": round(fetch_b + write_b),
-        "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
-        "fetch_kib_raw": round(f["fwd"], 1), "write_kib_raw": round(w["fwd"], 1),
-        "copy_fetch_kib_raw": round(f["copy"], 1), "copy_write_kib_raw": round(w["copy"], 1),
-        "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
-        "algorithmic_bytes": (M4 * K4 + 2 * N4 * K4 + M4 * N4) * 2}}
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    with open(path, "w") as fh:
-        json.dump(out, fh, indent=1)
-        fh.write("\n")
-    print(json.dumps(out))
-
 
 # The translation unit of the forward dual GEMM: the kernel file and the
 # headers it includes.
 FWD_KERNEL_SOURCES = ("common.hpp", "fp8.hpp", "gemm.hip", "gemm.hpp")
 
+# name -> (mangled-name fragment of the kernel, its translation unit, algorithmic bytes per launch)
+TRAFFIC_KERNELS = {
+    "fwd_dual_gemm_bf16_8192x14336x4096": (
+        "gemm_dma_kernelIDF16bLNS0_3EpiE0E", FWD_KERNEL_SOURCES,
+        (M4 * K4 + 2 * N4 * K4 + M4 * N4) * 2),
+    "gemv_bf16_M8_11008x4096": (
+        "gemv_kernelILi8ELNS_3ActE0ELb0E", ("common.hpp", "gemv.hip", "gemm.hpp"),
+        2 * 11008 * 4096 * 2 + 8 * 4096 * 2 + 8 * 11008 * 2),
+    "gemv_bf16_M1_11008x4096": (
+        "gemv_kernelILi1ELNS_3ActE0ELb0E", ("common.hpp", "gemv.hip", "gemm.hpp"),
+        2 * 11008 * 4096 * 2 + 4096 * 2 + 11008 * 2),
+    "act_quant_4001x3584": (
+        "act_quant_kernelILNS_3ActE0ELb0ELb0ELb0ELb0E", ("common.hpp", "fp8.hpp", "act_quant.hip", "gemm.hpp"),
+        2 * AQ_R * AQ_C * 4 + AQ_R * AQ_C + AQ_R * AQ_C // 32),
+    "act_fwd_bf16_4001x3584": (
+        "act_fwd_kernelILNS_3ActE0EDF16bLb0ELb0E", ("common.hpp", "fp8.hpp", "act_fwd.hip", "gemm.hpp"),
+        2 * AQ_R * AQ_C * 4 + AQ_R * AQ_C * 2),
+    "act_bwd_f32_4001x3584": (
+        "act_bwd_flat_kernelIfLb1ELb0E", ("common.hpp", "act_bwd.hip", "gemm.hpp"),
+        5 * AQ_R * AQ_C * 4),
+}
 
-def kernel_source_hash() -> str:
-    """Hash of the forward kernel's sources with comments and blank space
-    removed, so that a counter measurement stays valid across comment-only
-    edits and changes to other kernels."""
+
+def kernel_source_hash(files=FWD_KERNEL_SOURCES) -> str:
+    """Hash of a kernel's translation unit with comments and blank space
+    removed, so a counter measurement stays valid across comment-only edits
+    and changes to other kernels."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "swiglu_mlp_fwd_amd", "csrc")
-    for fn in FWD_KERNEL_SOURCES:
+    for fn in files:
         with open(os.path.join(csrc, fn), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -135,9 +144,55 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def digest_traffic(name: str, fetch_csv: str, write_csv: str) -> None:
+    """HBM bytes per launch of one kernel from two --pmc runs: its FETCH_SIZE /
+    WRITE_SIZE counters (KiB per dispatch), each scaled by (known bytes /
+    counter reading) of a plain 1 GiB copy measured in the same run."""
+    import csv
+    tag, files, algo = TRAFFIC_KERNELS[name]
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            kname = r["Kernel_Name"]
+            key = "k" if tag in kname else ("copy" if COPY_KERNEL_TAG in kname else None)
+            if key is None:
+                continue
+            vals.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+            vals[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: sum(v.values()) / len(v) for k, v in vals.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    sf = COPY_BYTES / (f["copy"] * 1024.0)
+    sw = COPY_BYTES / (w["copy"] * 1024.0)
+    fetch_b = f["k"] * 1024.0 * sf
+    write_b = w["k"] * 1024.0 * sw
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            out = json.load(fh)
+    except (OSError, ValueError):
+        out = {}
+    out[name] = {
+        "source_hash": kernel_source_hash(files),
+        "bytes_per_launch": round(fetch_b + write_b),
+        "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+        "fetch_kib_raw": round(f["k"], 1), "write_kib_raw": round(w["k"], 1),
+        "copy_fetch_kib_raw": round(f["copy"], 1), "copy_write_kib_raw": round(w["copy"], 1),
+        "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
+        "algorithmic_bytes": algo}
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({name: out[name]}))
+
+
 def load_traffic(name: str):
     """HBM traffic per launch measured by rocprofv3 counters for `name`, if the
-    committed measurement was taken on the current kernel sources."""
+    committed measurement was taken on the current sources of that kernel."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(p) as f:
@@ -145,49 +200,126 @@ def load_traffic(name: str):
     except (OSError, ValueError):
         return None
     e = t.get(name)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    files = TRAFFIC_KERNELS[name][1] if name in TRAFFIC_KERNELS else FWD_KERNEL_SOURCES
+    if not e or e.get("source_hash") != kernel_source_hash(files):
         return None
     return e.get("bytes_per_launch")
 
 
-class Timer:
-    """HIP events on the current stream (the stream the library launches on)."""
+# ------------------------------------------------------------------ timing protocol
 
-    def __init__(self, torch):
+def pct(xs, q):
+    s = sorted(xs)
+    if not s:
+        return None
+    k = (len(s) - 1) * q / 100.0
+    lo, hi = math.floor(k), math.ceil(k)
+    return s[lo] + (s[hi] - s[lo]) * (k - lo)
+
+
+class Protocol:
+    """A-B-C-C-B-A trials over one HIP graph per variant."""
+
+    def __init__(self, torch, trials, graph_warmup):
         self.torch = torch
+        self.trials = trials
+        self.graph_warmup = graph_warmup
 
-    def ev(self):
-        return self.torch.cuda.Event(enable_timing=True)
-
-
-def graph_time_per_call(torch, calls, reps=5):
-    """Capture `calls` (a list of closures launching one library call each) in
-    one HIP graph, replay it `reps` times, return seconds per call."""
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for c in calls:  # warm once outside capture
-            c()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        for c in calls:
-            c()
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    samples = []
-    for _ in range(reps):
-        e0.record()
-        g.replay()
-        e1.record()
+    def _graph(self, calls):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            calls[0]()
+        torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        samples.append(e0.elapsed_time(e1) * 1e-3 / len(calls))
-    del g
-    samples.sort()
-    return samples[len(samples) // 2], samples
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        return g
 
+    def run(self, variants: dict) -> dict:
+        """variants: name -> list of closures, each launching one library call
+        (the list is one graph's calls, rotating over buffers).  Returns
+        per-call statistics in microseconds per variant."""
+        torch = self.torch
+        names = list(variants)
+        for n in names:                                  # eager warm-up
+            calls = variants[n]
+            for i in range(self.graph_warmup):
+                calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        graphs = {n: self._graph(variants[n]) for n in names}
+        for n in names:
+            graphs[n].replay()
+        torch.cuda.synchronize()
+        samples = {n: [] for n in names}
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2 * len(names))]
+        for _ in range(self.trials):
+            order = names + names[::-1]
+            for k, n in enumerate(order):
+                ev[k][0].record()
+                graphs[n].replay()
+                ev[k][1].record()
+            torch.cuda.synchronize()
+            for k, n in enumerate(order):
+                samples[n].append(ev[k][0].elapsed_time(ev[k][1]) * 1e3 / len(variants[n]))
+        eager = {n: [] for n in names}
+        for _ in range(3):
+            for n in names:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for c in variants[n]:
+                    c()
+                e1.record()
+                torch.cuda.synchronize()
+                eager[n].append(e0.elapsed_time(e1) * 1e3 / len(variants[n]))
+        del graphs
+        out = {}
+        for n in names:
+            xs = samples[n]
+            out[n] = {"p50_us": round(pct(xs, 50), 3), "p90_us": round(pct(xs, 90), 3), "p99_us": round(pct(xs, 99), 3),
+                      "mean_us": round(sum(xs) / len(xs), 3), "samples_us": [round(v, 3) for v in xs],
+                      "eager_p50_us": round(pct(eager[n], 50), 3), "calls_per_graph": len(variants[n])}
+        return out
+
+
+def err_stats(np, y, r):
+    """max / mean absolute error and cosine of y against the oracle r (finite
+    elements of r; non-finite positions must match)."""
+    import oracle
+    y = np.asarray(y, np.float64).reshape(-1)
+    r = np.asarray(r, np.float64).reshape(-1)
+    fin = np.isfinite(r)
+    same_nonfinite = bool(np.array_equal(np.isnan(y[~fin]), np.isnan(r[~fin])))
+    d = np.abs(y[fin] - r[fin])
+    return {"max_abs_err": float(d.max(initial=0.0)), "mean_abs_err": float(d.mean()) if d.size else 0.0,
+            "cosine": round(float(oracle.cosine(y[fin], r[fin])), 9) if d.size else 1.0,
+            "normwise_rel_err": float(oracle.normwise_rel_err(y[fin], r[fin])) if d.size else 0.0,
+            "nonfinite_match": same_nonfinite}
+
+
+def host_cores():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # noqa: BLE001
+        blas = n
+    return n, blas
+
+
+def timed(fn):
+    t = time.perf_counter()
+    r = fn()
+    return r, time.perf_counter() - t
+
+
+# ------------------------------------------------------------------ main
 
 def main():
     args = parse()
@@ -210,11 +342,26 @@ def main():
     import swiglu_mlp_fwd_amd as S
     import synth
 
+    S.lib()           # refuses a library built from other sources
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    P = Protocol(torch, args.trials, args.graph_warmup)
+    ctx = dict(torch=torch, S=S, synth=synth, np=np, dev=dev, P=P, args=args)
 
     def to_dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    ctx["to_dev_bf16"] = to_dev_bf16
+
+    if args.only in ("decode", "act_quant", "act_bwd", "fp32", "tiny", "traffic_decode", "traffic_act_quant",
+                     "traffic_act_fwd", "traffic_act_bwd"):
+        leg = {"decode": decode_leg, "act_quant": act_quant_leg, "act_bwd": act_bwd_leg, "fp32": fp32_leg,
+               "tiny": tiny_leg, "traffic_decode": traffic_decode, "traffic_act_quant": traffic_act_quant,
+               "traffic_act_fwd": traffic_act_fwd, "traffic_act_bwd": traffic_act_bwd}[args.only]
+        res = leg(ctx)
+        if args.only.startswith("traffic"):
+            copy_calibration(torch, dev, args.steps)
+        log(json.dumps(res)[:2000] if res else "done")
+        return
 
     # ------------------------------------------------------------ headline
     t0 = time.time()
@@ -222,12 +369,14 @@ def main():
     x, wg, wu, dh = (to_dev_bf16(d4[k]) for k in ("x", "wg", "wu", "dh"))
     ws = torch.empty(S.bwd_workspace_bytes(torch.bfloat16, M4, N4, K4), dtype=torch.uint8, device=dev)
     h = torch.empty((M4, N4), dtype=torch.bfloat16, device=dev)
+    grads = (torch.empty((M4, K4), dtype=torch.bfloat16, device=dev), torch.empty((N4, K4), dtype=torch.bfloat16, device=dev),
+             torch.empty((N4, K4), dtype=torch.bfloat16, device=dev))
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
 
     def step():
         S.fwd(x, wg, wu, out=h)
-        return S.bwd(x, wg, wu, dh, workspace=ws)
+        S.bwd(x, wg, wu, dh, workspace=ws, out=grads)
 
     if args.only in ("step", "fwd", "traffic"):
         for _ in range(args.warmup + args.steps):
@@ -236,28 +385,16 @@ def main():
             else:
                 S.fwd(x, wg, wu, out=h)
         if args.only == "traffic":
-            del ws
+            del ws, grads
             torch.cuda.empty_cache()
-            src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
-            dst = torch.empty_like(src)
-            for _ in range(args.steps):
-                dst.copy_(src)
+            copy_calibration(torch, dev, args.steps)
         torch.cuda.synchronize()
         log("done")
         return
-    if args.only == "fwd_fp8":
-        fwd_fp8_leg(torch, S, x, wg, wu)
-        log("done")
-        return
-    if args.only in ("decode", "act_quant", "act_bwd", "fp32"):  # noqa: SIM102
-        del x, wg, wu, dh, ws, h
-        torch.cuda.empty_cache()
-        leg = {"decode": lambda: decode_leg(torch, S, synth, np, dev, to_dev_bf16),
-               "act_quant": lambda: act_quant_leg(torch, S, synth, np, dev),
-               "act_bwd": lambda: act_bwd_leg(torch, S, synth, np, dev),
-               "fp32": lambda: fp32_leg(torch, S, synth, np, dev)}[args.only]
-        leg()
-        log("done")
+    train = dict(x=x, wg=wg, wu=wu, dh=dh, ws=ws, h=h, grads=grads, d4=d4)
+    if args.only in ("train_fwd", "train_bwd"):
+        res = (train_fwd_leg if args.only == "train_fwd" else train_bwd_leg)(ctx, train)
+        log(json.dumps(res)[:2000])
         return
 
     for _ in range(args.warmup):
@@ -272,12 +409,13 @@ def main():
         fwd_ev[i][0].record()
         S.fwd(x, wg, wu, out=h)
         fwd_ev[i][1].record()
-        S.bwd(x, wg, wu, dh, workspace=ws)
+        S.bwd(x, wg, wu, dh, workspace=ws, out=grads)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     t_step = start.elapsed_time(end) * 1e-3 / args.steps
-    t_fwd = sum(a.elapsed_time(b) for a, b in fwd_ev) * 1e-3 / args.steps
+    fwd_samples = [a.elapsed_time(b) * 1e-3 for a, b in fwd_ev]
+    t_fwd = sum(fwd_samples) / args.steps
     flops_step = 12.0 * M4 * N4 * K4
     value = flops_step / t_step / 1e12
     fwd_tflops = 4.0 * M4 * N4 * K4 / t_fwd / 1e12
@@ -285,9 +423,8 @@ def main():
         f"host wall {wall:.2f}s")
 
     # The dense bf16 rate the chip sustains (register-only MFMA loop), as
-    # context for the roofline fraction against the published peak.
-    # The clock takes a few calls to settle under this load: the best of three
-    # rounds of five calls after a warm-up.
+    # context for the roofline fraction against the published peak: the best
+    # of three rounds of five calls after a warm-up (the clock settles).
     sink = torch.empty(1024, dtype=torch.float32, device=dev)
     for _ in range(3):
         S.probe_mfma(4096, 1024, sink)
@@ -305,6 +442,7 @@ def main():
     del sink
 
     traffic = load_traffic("fwd_dual_gemm_bf16_8192x14336x4096")
+    ncores, blas = host_cores()
     result = {
         "metric": "fused SwiGLU TFLOP/s (M=8192) + cold GB/s (M=1..8), % of roofline",
         "value": round(value, 2),
@@ -330,69 +468,204 @@ def main():
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "avg_launch_ms": round(t_fwd * 1e3, 4),
+            "launch_ms_samples": [round(v * 1e3, 4) for v in fwd_samples],
             "mfma_probe_TFLOPs": round(mfma_tf, 1),
             "frac_of_mfma_probe": round(fwd_tflops / mfma_tf, 4),
         },
         "fwd_ms": round(t_fwd * 1e3, 4),
         "bwd_ms": round((t_step - t_fwd) * 1e3, 4),
         "bwd_tflops_8MNK": round(8.0 * M4 * N4 * K4 / (t_step - t_fwd) / 1e12, 2),
+        "host": {"cores": ncores, "blas_threads": blas},
+        "protocol": {"trials": args.trials, "order": "A-B-C-C-B-A", "graph_warmup_calls": args.graph_warmup,
+                     "calls_per_graph": args.iters, "calls_per_graph_gemm": args.gemm_iters,
+                     "timing": "HIP events around each graph launch; per-call time = graph time / calls",
+                     "eager": "3 x (calls per graph) eager calls, events around each batch"},
+        "legs": {},
+        "oracle": {},
     }
     if not args.no_extra:
-        result["geglu"] = geglu_leg(torch, S, x, wg, wu, h, dh, ws)
-        result["fwd_fp8"] = fwd_fp8_leg(torch, S, x, wg, wu)
-    del h
+        result["legs"]["train_fwd"] = train_fwd_leg(ctx, train, result["oracle"])
+        result["legs"]["train_bwd"] = train_bwd_leg(ctx, train, result["oracle"])
+    del h, grads, train
     sample_inputs = {k: d4[k] for k in ("x", "wg", "wu", "dh")}
-    del x, wg, wu, dh, ws
+    del x, wg, wu, dh, ws, d4
     torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------ extra legs
+    # ------------------------------------------------------------ other legs
     if not args.no_extra:
-        result["decode"] = decode_leg(torch, S, synth, np, dev, to_dev_bf16)
-        result["act_quant"] = act_quant_leg(torch, S, synth, np, dev)
-        result["act_bwd"] = act_bwd_leg(torch, S, synth, np, dev)
-        result["fp32"] = fp32_leg(torch, S, synth, np, dev)
+        result["legs"]["decode"] = decode_leg(ctx, result["oracle"])
+        result["legs"]["act_quant"] = act_quant_leg(ctx, result["oracle"])
+        result["legs"]["act_bwd"] = act_bwd_leg(ctx, result["oracle"])
+        result["legs"]["fp32"] = fp32_leg(ctx, result["oracle"])
+        result["legs"]["tiny_fp32"] = tiny_leg(ctx, result["oracle"])
 
     # ------------------------------------------------------------ cpu baseline
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(np, synth, sample_inputs, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(np, synth, sample_inputs, args.cpu_seconds, value)
 
     print(json.dumps(result), flush=True)
 
 
-def decode_leg(torch, S, synth, np, dev, to_dev_bf16):
-    out = {"unit": "GB/s", "bytes": "2*N*K*2 + M*K*2 + M*N*2 per call", "shapes": []}
-    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
-    for (N, K, copies) in ((6912, 1536, 16), (11008, 4096, 4)):
+def copy_calibration(torch, dev, n):
+    """A plain device copy of 1 GiB, the known-size reference for the HBM counters."""
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(max(n, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ legs
+
+def train_fwd_leg(ctx, t, oracle_times=None):
+    """Forward variants at the headline shape; TFLOP/s and error on sampled rows."""
+    torch, S, np, P, args = ctx["torch"], ctx["S"], ctx["np"], ctx["P"], ctx["args"]
+    import oracle
+    x, wg, wu, h = t["x"], t["wg"], t["wu"], t["h"]
+    dev = x.device
+    q = torch.empty((M4, N4), dtype=torch.uint8, device=dev)
+    sc = torch.empty((M4, N4 // 32), dtype=torch.uint8, device=dev)
+    h2 = torch.empty_like(h)
+    n = args.gemm_iters
+    variants = {
+        "swiglu": [lambda: S.fwd(x, wg, wu, out=h)] * n,
+        "geglu": [lambda: S.fwd(x, wg, wu, out=h2, act="gelu_tanh")] * n,
+        "swiglu_fp8": [lambda: S.fwd_fp8(x, wg, wu, out=(q, sc, None))] * n,
+        "geglu_fp8": [lambda: S.fwd_fp8(x, wg, wu, act="gelu_tanh", out=(q, sc, None))] * n,
+    }
+    stats = P.run(variants)
+    flops = 4.0 * M4 * N4 * K4
+    for k, v in stats.items():
+        v["TFLOPs_p50"] = round(flops / (v["p50_us"] * 1e-6) / 1e12, 2)
+        v["frac_of_bf16_peak"] = round(v["TFLOPs_p50"] / PEAK_BF16_TFLOPS, 4)
+        v["launches_per_call"] = LAUNCHES["fwd"]
+        log(f"train_fwd {k}: p50 {v['p50_us'] / 1e3:.4f} ms, {v['TFLOPs_p50']:.1f} TFLOP/s "
+            f"(eager {v['eager_p50_us'] / 1e3:.4f} ms)")
+    # error on 64 sampled rows (the oracle computes them one by one)
+    rows = np.unique(np.concatenate([[0, M4 - 1], np.random.default_rng(4).integers(0, M4, 62)]))
+    d4, synth = t["d4"], ctx["synth"]
+    f = {k: synth.bf16_bits_to_f32(d4[k]).astype(np.float64) for k in ("wg", "wu")}
+    xr = synth.bf16_bits_to_f32(d4["x"][rows]).astype(np.float64)
+    ri = torch.as_tensor(rows, device=dev)
+    for act, out in (("silu", h), ("gelu_tanh", h2)):
+        S.fwd(x, wg, wu, out=out, act=act)
+        torch.cuda.synchronize()
+        ref, secs = timed(lambda: oracle.glu_fwd(xr, f["wg"], f["wu"], act))
+        key = "swiglu" if act == "silu" else "geglu"
+        stats[key]["vs_oracle_sampled_rows"] = err_stats(np, out[ri].float().cpu().numpy(), ref)
+        stats[key]["vs_oracle_rows"] = len(rows)
+        if act == "silu" and oracle_times is not None:
+            oracle_times["train_fwd_sampled"] = {"seconds": round(secs, 3), "rows": len(rows),
+                                                 "seconds_full_extrapolated": round(secs * M4 / len(rows), 2),
+                                                 "note": "full-size time extrapolated linearly in rows"}
+    for act, key in (("silu", "swiglu_fp8"), ("gelu_tanh", "geglu_fp8")):
+        S.fwd_fp8(x, wg, wu, act=act, out=(q, sc, None))
+        torch.cuda.synchronize()
+        qq = q[ri].cpu().numpy()
+        ee = sc[ri].cpu().numpy().astype(np.int64) - 127
+        deq = oracle.e4m3_decode(qq) * np.exp2(np.repeat(ee, 32, axis=1).astype(np.float64))
+        ref = oracle.glu_fwd(xr, f["wg"], f["wu"], act)
+        stats[key]["vs_oracle_sampled_rows"] = err_stats(np, deq, ref)
+        stats[key]["note"] = "error of the dequantised E4M3 codes x 2^E against the exact h"
+    del q, sc, h2
+    return {"M": M4, "N": N4, "K": K4, "flops_per_call": "4*M*N*K", "variants": stats}
+
+
+def train_bwd_leg(ctx, t, oracle_times=None):
+    """The backward at the headline shape (SwiGLU, GeGLU); TFLOP/s on 8 M N K."""
+    torch, S, np, P, args = ctx["torch"], ctx["S"], ctx["np"], ctx["P"], ctx["args"]
+    import oracle
+    x, wg, wu, dh, ws, grads = t["x"], t["wg"], t["wu"], t["dh"], t["ws"], t["grads"]
+    n = args.gemm_iters
+    variants = {"swiglu": [lambda: S.bwd(x, wg, wu, dh, workspace=ws, out=grads)] * n,
+                "geglu": [lambda: S.bwd(x, wg, wu, dh, workspace=ws, out=grads, act="gelu_tanh")] * n}
+    stats = P.run(variants)
+    for k, v in stats.items():
+        v["TFLOPs_8MNK_p50"] = round(8.0 * M4 * N4 * K4 / (v["p50_us"] * 1e-6) / 1e12, 2)
+        v["TFLOPs_12MNK_incl_recompute_p50"] = round(12.0 * M4 * N4 * K4 / (v["p50_us"] * 1e-6) / 1e12, 2)
+        v["launches_per_call"] = LAUNCHES["bwd_bf16"]
+        log(f"train_bwd {k}: p50 {v['p50_us'] / 1e3:.4f} ms (eager {v['eager_p50_us'] / 1e3:.4f} ms)")
+    S.bwd(x, wg, wu, dh, workspace=ws, out=grads)
+    torch.cuda.synchronize()
+    d4, synth = t["d4"], ctx["synth"]
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, M4 - 1], rng.integers(0, M4, 30)]))
+    cols = np.unique(np.concatenate([[0, N4 - 1], rng.integers(0, N4, 30)]))
+    f = {k: synth.bf16_bits_to_f32(d4[k]).astype(np.float64) for k in ("x", "wg", "wu", "dh")}
+    (dxr, sx) = timed(lambda: oracle.swiglu_bwd_dx_rows(f["x"], f["wg"], f["wu"], f["dh"], rows))
+    ((dwgr, dwur), sw) = timed(lambda: oracle.swiglu_bwd_dw_rows(f["x"], f["wg"], f["wu"], f["dh"], cols))
+    dev = x.device
+    stats["swiglu"]["vs_oracle_sampled"] = {
+        "dx_rows": err_stats(np, grads[0][torch.as_tensor(rows, device=dev)].float().cpu().numpy(), dxr),
+        "dwg_rows": err_stats(np, grads[1][torch.as_tensor(cols, device=dev)].float().cpu().numpy(), dwgr),
+        "dwu_rows": err_stats(np, grads[2][torch.as_tensor(cols, device=dev)].float().cpu().numpy(), dwur),
+        "sampled": f"{len(rows)} rows of dX, {len(cols)} rows of dWg and dWu"}
+    if oracle_times is not None:
+        oracle_times["train_bwd_sampled"] = {"seconds": round(sx + sw, 3),
+                                             "sampled": f"{len(rows)} rows of dX, {len(cols)} rows of dWg, dWu"}
+    return {"M": M4, "N": N4, "K": K4, "variants": stats}
+
+
+def decode_leg(ctx, oracle_times=None):
+    torch, S, np, P, args, synth = ctx["torch"], ctx["S"], ctx["np"], ctx["P"], ctx["args"], ctx["synth"]
+    import oracle
+    dev, to_dev_bf16 = ctx["dev"], ctx["to_dev_bf16"]
+    out = {"unit": "GB/s", "bytes": "2*N*K*2 + M*K*2 + M*N*2 per call", "launches_per_call": LAUNCHES["gemv"],
+           "floor": "those bytes over the faster p50 time of the read-only twin and the dual-stream read, per M",
+           "shapes": []}
+    for (N, K, copies) in DECODE_SHAPES:
         d = synth.decode_bf16(8, N, K, seed=0)
         wg0, wu0 = to_dev_bf16(d["wg"]), to_dev_bf16(d["wu"])
         W = [(wg0.clone(), wu0.clone()) for _ in range(copies)]
         del wg0, wu0
-        reps_per_graph = 4
-        probe_calls = [(lambda a=a, b=b: S.probe_read2(a, b, sink)) for _ in range(reps_per_graph) for (a, b) in W]
-        t_probe, _ = graph_time_per_call(torch, probe_calls)
-        floor = 2 * N * K * 2 / t_probe / 1e9
-        entry = {"N": N, "K": K, "copies": copies,
-                 "working_set_MB": round(copies * 2 * N * K * 2 / 1e6, 1),
-                 "read_floor_GBs": round(floor, 1), "per_M": []}
+        wgf = synth.bf16_bits_to_f32(d["wg"]).astype(np.float64)
+        wuf = synth.bf16_bits_to_f32(d["wu"]).astype(np.float64)
+        sink = torch.zeros(max(4096, N), dtype=torch.int32, device=dev)
+        entry = {"N": N, "K": K, "copies": copies, "working_set_MB": round(copies * 2 * N * K * 2 / 1e6, 1), "per_M": []}
+        reps = max(1, args.iters // copies)
         for M in (1, 2, 4, 8):
             x = to_dev_bf16(d["x"][:M].copy())
             outs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
-            calls = [(lambda a=a, b=b, o=o: S.gemv_fwd(x, a, b, out=o))
-                     for _ in range(reps_per_graph) for (a, b), o in zip(W, outs)]
-            t, _ = graph_time_per_call(torch, calls)
+            variants = {
+                "gemv": [(lambda a=a, b=b, o=o: S.gemv_fwd(x, a, b, out=o)) for _ in range(reps) for (a, b), o in zip(W, outs)],
+                "twin": [(lambda a=a, b=b: S.probe_gemv_read(x, a, b, sink)) for _ in range(reps) for (a, b) in W],
+                "stream": [(lambda a=a, b=b: S.probe_read2(a, b, sink)) for _ in range(reps) for (a, b) in W],
+            }
+            st = P.run(variants)
+            # One byte basis for all three: the decode call's algorithmic
+            # bytes over each variant's time, so the floor is the faster of
+            # the twin and the stream and frac_of_floor a ratio of times.
             nbytes = 2 * N * K * 2 + M * K * 2 + M * N * 2
-            gbs = nbytes / t / 1e9
-            entry["per_M"].append({"M": M, "us": round(t * 1e6, 3), "GBs": round(gbs, 1),
-                                   "frac_of_floor": round(gbs / floor, 4), "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)})
-            log(f"decode N={N} K={K} M={M}: {t * 1e6:.2f} us, {gbs:.0f} GB/s ({gbs / floor:.1%} of read floor {floor:.0f})")
+            gbs = {k: nbytes / (v["p50_us"] * 1e-6) / 1e9 for k, v in st.items()}
+            floor = max(gbs["twin"], gbs["stream"])
+            S.gemv_fwd(x, W[0][0], W[0][1], out=outs[0])
+            torch.cuda.synchronize()
+            xf = synth.bf16_bits_to_f32(d["x"][:M]).astype(np.float64)
+            ref, secs = timed(lambda: oracle.glu_fwd(xf, wgf, wuf))
+            e = {"M": M, "us_p50": st["gemv"]["p50_us"], "us_p90": st["gemv"]["p90_us"], "us_p99": st["gemv"]["p99_us"],
+                 "GBs": round(gbs["gemv"], 1), "floor_GBs": round(floor, 1),
+                 "twin_us_p50": st["twin"]["p50_us"], "stream_us_p50": st["stream"]["p50_us"],
+                 "frac_of_floor": round(gbs["gemv"] / floor, 4), "frac_of_8TBs": round(gbs["gemv"] / PEAK_HBM_GBS, 4),
+                 "eager_us_p50": st["gemv"]["eager_p50_us"],
+                 "vs_oracle": err_stats(np, outs[0].float().cpu().numpy(), ref),
+                 "samples_us": {k: v["samples_us"] for k, v in st.items()}}
+            entry["per_M"].append(e)
+            if oracle_times is not None:
+                oracle_times[f"decode_{N}x{K}_M{M}"] = {"seconds": round(secs, 4), "full": True,
+                                                        "GBs": round(nbytes / secs / 1e9, 2)}
+            log(f"decode N={N} K={K} M={M}: {e['us_p50']:.2f} us, {e['GBs']:.0f} GB/s ({e['frac_of_floor']:.1%} of "
+                f"floor {floor:.0f}: twin {gbs['twin']:.0f}, stream {gbs['stream']:.0f}; {e['frac_of_8TBs']:.1%} of 8 TB/s)")
         out["shapes"].append(entry)
-        del W
+        del W, sink
         torch.cuda.empty_cache()
     return out
 
 
-def act_quant_leg(torch, S, synth, np, dev):
-    R, C = 4001, 3584
+def act_quant_leg(ctx, oracle_times=None):
+    torch, S, np, P, args, synth = ctx["torch"], ctx["S"], ctx["np"], ctx["P"], ctx["args"], ctx["synth"]
+    import oracle
+    dev = ctx["dev"]
+    R, C = AQ_R, AQ_C
     d = synth.act_quant_f32(R, C, seed=0)
     g0, u0 = torch.from_numpy(d["gate"]).to(dev), torch.from_numpy(d["up"]).to(dev)
     copies = 4
@@ -402,165 +675,240 @@ def act_quant_leg(torch, S, synth, np, dev):
     outs = [(torch.empty((R, C), dtype=torch.uint8, device=dev), torch.empty((R, C // 32), dtype=torch.uint8, device=dev),
              torch.empty(1, dtype=torch.int64, device=dev), None) for _ in range(copies)]
     nbytes = 2 * R * C * 4 + R * C + R * C // 32
-    res = {"rows": R, "cols": C, "copies": copies, "bytes_per_call": nbytes, "unit": "GB/s"}
-    for act, L in (("silu", math.inf), ("silu", 7.0), ("gelu_tanh", math.inf)):
-        calls = [(lambda i=i: S.act_quant(G[i], U[i], L, out=outs[i], act=act)) for _ in range(4) for i in range(copies)]
-        t, _ = graph_time_per_call(torch, calls)
-        gbs = nbytes / t / 1e9
-        key = ("no_clamp" if math.isinf(L) else "clamp_7") + ("" if act == "silu" else "_geglu")
-        res[key] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
-        log(f"act_quant {R}x{C} {key}: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
-    # The non-quantised outputs (fp32 and bf16 h).
+    reps = max(1, args.iters // copies)
+    variants = {
+        "no_clamp": [(lambda i=i: S.act_quant(G[i], U[i], math.inf, out=outs[i])) for _ in range(reps) for i in range(copies)],
+        "clamp_7": [(lambda i=i: S.act_quant(G[i], U[i], 7.0, out=outs[i])) for _ in range(reps) for i in range(copies)],
+        "no_clamp_geglu": [(lambda i=i: S.act_quant(G[i], U[i], math.inf, out=outs[i], act="gelu_tanh"))
+                           for _ in range(reps) for i in range(copies)],
+        "stream_twin": [(lambda i=i: S.probe_act_quant_stream(G[i], U[i], outs[i][0], outs[i][1]))
+                        for _ in range(reps) for i in range(copies)],
+    }
+    st = P.run(variants)
+    floor = nbytes / (st["stream_twin"]["p50_us"] * 1e-6) / 1e9
+    res = {"rows": R, "cols": C, "copies": copies, "bytes_per_call": nbytes, "unit": "GB/s",
+           "stream_floor_GBs": round(floor, 1), "variants": st}
+    for k, v in st.items():
+        v["GBs_p50"] = round(nbytes / (v["p50_us"] * 1e-6) / 1e9, 1)
+        v["frac_of_8TBs"] = round(v["GBs_p50"] / PEAK_HBM_GBS, 4)
+        v["frac_of_stream_floor"] = round(v["GBs_p50"] / floor, 4)
+        v["launches_per_call"] = LAUNCHES["act_quant_count"] if k == "clamp_7" else LAUNCHES["act_quant"]
+        log(f"act_quant {R}x{C} {k}: {v['p50_us']:.2f} us, {v['GBs_p50']:.0f} GB/s "
+            f"({v['frac_of_stream_floor']:.1%} of the twin's {floor:.0f})")
+    # against the oracle (clamp off and L = 7), from the inputs
+    g64, u64 = d["gate"].astype(np.float64), d["up"].astype(np.float64)
+    for key, L in (("no_clamp", math.inf), ("clamp_7", 7.0)):
+        q, s, cnt, _ = S.act_quant(G[0], U[0], L, out=outs[0])
+        torch.cuda.synchronize()
+        (rq, rs, rc, _), secs = timed(lambda: oracle.act_quant(g64, u64, L))
+        qn, sn = q.cpu().numpy(), s.cpu().numpy()
+        nan = (rq & 0x7F) == 0x7F
+        dist = np.abs(oracle.e4m3_ordinal(qn[~nan]) - oracle.e4m3_ordinal(rq[~nan]))
+        st[key]["vs_oracle"] = {"scale_bytes_equal_frac": float((sn == rs).mean()),
+                                "codes_equal_frac": float((qn == rq).mean()),
+                                "max_code_ulp": int(dist.max(initial=0)),
+                                "nan_positions_match": bool(np.array_equal((qn & 0x7F) == 0x7F, nan)),
+                                "clamp_count_match": int(cnt.item()) == int(rc)}
+        if oracle_times is not None:
+            oracle_times[f"act_quant_{key}"] = {"seconds": round(secs, 3), "full": True,
+                                                "GBs": round(nbytes / secs / 1e9, 3)}
+    # the non-quantised forward (fp32 and bf16 h)
+    fv = {}
+    hs = {}
     for dt, nb in ((torch.float32, 4), (torch.bfloat16, 2)):
-        hs = [torch.empty((R, C), dtype=dt, device=dev) for _ in range(copies)]
-        calls = [(lambda i=i: S.act_fwd(G[i], U[i], math.inf, out=(hs[i], None))) for _ in range(4) for i in range(copies)]
-        t, _ = graph_time_per_call(torch, calls)
-        nbytes_h = 2 * R * C * 4 + R * C * nb
-        gbs = nbytes_h / t / 1e9
-        key = "act_fwd_" + ("f32" if nb == 4 else "bf16")
-        res[key] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "bytes_per_call": nbytes_h,
-                    "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
-        log(f"act_fwd {R}x{C} {key}: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
-        del hs
-    del G, U, outs
+        key = "f32_h" if nb == 4 else "bf16_h"
+        hs[key] = [torch.empty((R, C), dtype=dt, device=dev) for _ in range(copies)]
+        fv[key] = [(lambda i=i, hh=hs[key]: S.act_fwd(G[i], U[i], math.inf, out=(hh[i], None)))
+                   for _ in range(reps) for i in range(copies)]
+    st2 = P.run(fv)
+    for key, v in st2.items():
+        nb = 4 if key == "f32_h" else 2
+        v["bytes_per_call"] = 2 * R * C * 4 + R * C * nb
+        v["GBs_p50"] = round(v["bytes_per_call"] / (v["p50_us"] * 1e-6) / 1e9, 1)
+        v["frac_of_8TBs"] = round(v["GBs_p50"] / PEAK_HBM_GBS, 4)
+        v["launches_per_call"] = LAUNCHES["act_fwd"]
+        S.act_fwd(G[0], U[0], math.inf, out=(hs[key][0], None))
+        torch.cuda.synchronize()
+        ref, secs = timed(lambda: oracle.act_fwd(g64, u64, math.inf)[0])
+        v["vs_oracle"] = err_stats(np, hs[key][0].float().cpu().numpy(), ref)
+        if oracle_times is not None and key == "f32_h":
+            oracle_times["act_fwd"] = {"seconds": round(secs, 3), "full": True}
+        log(f"act_fwd {R}x{C} {key}: {v['p50_us']:.2f} us, {v['GBs_p50']:.0f} GB/s")
+    res["act_fwd"] = st2
+    del G, U, outs, hs
     torch.cuda.empty_cache()
     return res
 
 
-def geglu_leg(torch, S, x, wg, wu, h, dh, ws):
-    """GeGLU (GELU-tanh gate) on the headline inputs: the forward, and a
-    training step (forward + backward)."""
-    for _ in range(3):
-        S.fwd(x, wg, wu, out=h, act="gelu_tanh")
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 10
-    e0.record()
-    for _ in range(n):
-        S.fwd(x, wg, wu, out=h, act="gelu_tanh")
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / n
-    tf = 4.0 * M4 * N4 * K4 / t / 1e12
-    log(f"geglu fwd {M4}x{N4}x{K4}: {t * 1e3:.3f} ms, {tf:.1f} TFLOP/s")
-
-    def step():
-        S.fwd(x, wg, wu, out=h, act="gelu_tanh")
-        S.bwd(x, wg, wu, dh, workspace=ws, act="gelu_tanh")
-
-    for _ in range(2):
-        step()
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(5):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ts = e0.elapsed_time(e1) * 1e-3 / 5
-    log(f"geglu step {M4}x{N4}x{K4}: {ts * 1e3:.3f} ms, {12.0 * M4 * N4 * K4 / ts / 1e12:.1f} TFLOP/s (12MNK)")
-    return {"M": M4, "N": N4, "K": K4, "ms": round(t * 1e3, 4), "TFLOPs": round(tf, 2),
-            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "step_ms": round(ts * 1e3, 4), "step_TFLOPs_12MNK": round(12.0 * M4 * N4 * K4 / ts / 1e12, 2)}
-
-
-def fwd_fp8_leg(torch, S, x, wg, wu):
-    """Forward with the 1x32 E4M3 quantisation of h fused into the epilogue,
-    on the headline inputs (no h_out): h leaves as 1-byte codes + scales."""
-    dev = x.device
-    q = torch.empty((M4, N4), dtype=torch.uint8, device=dev)
-    sc = torch.empty((M4, N4 // 32), dtype=torch.uint8, device=dev)
-    res = {"M": M4, "N": N4, "K": K4}
-    for act in ("silu", "gelu_tanh"):
-        for _ in range(3):
-            S.fwd_fp8(x, wg, wu, act=act, out=(q, sc, None))
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n = 10
-        e0.record()
-        for _ in range(n):
-            S.fwd_fp8(x, wg, wu, act=act, out=(q, sc, None))
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / n
-        tf = 4.0 * M4 * N4 * K4 / t / 1e12
-        log(f"fwd_fp8 {act} {M4}x{N4}x{K4}: {t * 1e3:.3f} ms, {tf:.1f} TFLOP/s")
-        res[act] = {"ms": round(t * 1e3, 4), "TFLOPs": round(tf, 2),
-                    "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-    del q, sc
-    return res
-
-
-def act_bwd_leg(torch, S, synth, np, dev):
-    R, C = 4001, 3584
+def act_bwd_leg(ctx, oracle_times=None):
+    torch, S, np, P, args, synth = ctx["torch"], ctx["S"], ctx["np"], ctx["P"], ctx["args"], ctx["synth"]
+    import oracle
+    dev = ctx["dev"]
+    R, C = AQ_R, AQ_C
     d = synth.act_bwd_f32(R, C, seed=0)
     copies = 4
+    reps = max(1, args.iters // copies)
     ins = [tuple(torch.from_numpy(d[k]).to(dev) for k in ("gate", "up", "dy", "weights")) for _ in range(copies)]
+    ins16 = [tuple(t.to(torch.bfloat16) for t in i[:3]) for i in ins]
     outs = [(torch.empty((R, C), dtype=torch.float32, device=dev), torch.empty((R, C), dtype=torch.float32, device=dev),
              torch.empty(R, dtype=torch.float32, device=dev)) for _ in range(copies)]
-    res = {"rows": R, "cols": C, "copies": copies, "unit": "GB/s"}
-    for key, L, use_w in (("clamp_0.5", 0.5, False), ("weights_wgrad", math.inf, True)):
-        nbytes = 5 * R * C * 4 + (2 * R * 4 if use_w else 0)
-        calls = [(lambda i=i: S.act_bwd(ins[i][0], ins[i][1], ins[i][2], L, weights=ins[i][3] if use_w else None,
-                                        out=(outs[i][0], outs[i][1], outs[i][2] if use_w else None)))
-                 for _ in range(4) for i in range(copies)]
-        t, _ = graph_time_per_call(torch, calls)
-        gbs = nbytes / t / 1e9
-        res[key] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "bytes_per_call": nbytes,
-                    "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
-        log(f"act_bwd {R}x{C} {key}: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
-    del ins, outs
-    # bf16 tensors (weights and weight_grad fp32).
-    ins = [tuple(t.to(torch.bfloat16) for t in (torch.from_numpy(d[k]).to(dev) for k in ("gate", "up", "dy")))
-           for _ in range(copies)]
-    outs = [(torch.empty((R, C), dtype=torch.bfloat16, device=dev), torch.empty((R, C), dtype=torch.bfloat16, device=dev))
-            for _ in range(copies)]
-    nbytes = 5 * R * C * 2
-    calls = [(lambda i=i: S.act_bwd(ins[i][0], ins[i][1], ins[i][2], 0.5, out=(outs[i][0], outs[i][1], None)))
-             for _ in range(4) for i in range(copies)]
-    t, _ = graph_time_per_call(torch, calls)
-    gbs = nbytes / t / 1e9
-    res["bf16_clamp_0.5"] = {"us": round(t * 1e6, 3), "GBs": round(gbs, 1), "bytes_per_call": nbytes,
-                             "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4)}
-    log(f"act_bwd {R}x{C} bf16_clamp_0.5: {t * 1e6:.2f} us, {gbs:.0f} GB/s")
-    del ins, outs
+    outs16 = [(torch.empty((R, C), dtype=torch.bfloat16, device=dev), torch.empty((R, C), dtype=torch.bfloat16, device=dev))
+              for _ in range(copies)]
+    variants = {
+        "f32_clamp_0.5": [(lambda i=i: S.act_bwd(*ins[i][:3], 0.5, out=(outs[i][0], outs[i][1], None)))
+                          for _ in range(reps) for i in range(copies)],
+        "f32_weights_wgrad": [(lambda i=i: S.act_bwd(*ins[i][:3], math.inf, weights=ins[i][3], out=outs[i]))
+                              for _ in range(reps) for i in range(copies)],
+        "bf16_clamp_0.5": [(lambda i=i: S.act_bwd(*ins16[i], 0.5, out=(outs16[i][0], outs16[i][1], None)))
+                           for _ in range(reps) for i in range(copies)],
+    }
+    st = P.run(variants)
+    nb = {"f32_clamp_0.5": 5 * R * C * 4, "f32_weights_wgrad": 5 * R * C * 4 + 2 * R * 4, "bf16_clamp_0.5": 5 * R * C * 2}
+    for k, v in st.items():
+        v["bytes_per_call"] = nb[k]
+        v["GBs_p50"] = round(nb[k] / (v["p50_us"] * 1e-6) / 1e9, 1)
+        v["frac_of_8TBs"] = round(v["GBs_p50"] / PEAK_HBM_GBS, 4)
+        v["launches_per_call"] = LAUNCHES["act_bwd"]
+        log(f"act_bwd {R}x{C} {k}: {v['p50_us']:.2f} us, {v['GBs_p50']:.0f} GB/s")
+    g, u, dy = (d[k].astype(np.float64) for k in ("gate", "up", "dy"))
+    S.act_bwd(*ins[0][:3], 0.5, out=(outs[0][0], outs[0][1], None))
+    torch.cuda.synchronize()
+    (rg, ru, _), secs = timed(lambda: oracle.act_bwd(g, u, dy, 0.5, None))
+    st["f32_clamp_0.5"]["vs_oracle"] = {"dgate": err_stats(np, outs[0][0].cpu().numpy(), rg),
+                                        "dup": err_stats(np, outs[0][1].cpu().numpy(), ru)}
+    if oracle_times is not None:
+        oracle_times["act_bwd_f32_clamp_0.5"] = {"seconds": round(secs, 3), "full": True,
+                                                 "GBs": round(nb["f32_clamp_0.5"] / secs / 1e9, 3)}
+    del ins, ins16, outs, outs16
     torch.cuda.empty_cache()
-    return res
+    return {"rows": R, "cols": C, "copies": copies, "unit": "GB/s", "variants": st}
 
 
-def fp32_leg(torch, S, synth, np, dev):
-    M, N, K = 4001, 3584, 2048
+def fp32_leg(ctx, oracle_times=None):
+    torch, S, np, P, args, synth = ctx["torch"], ctx["S"], ctx["np"], ctx["P"], ctx["args"], ctx["synth"]
+    import oracle
+    dev = ctx["dev"]
+    M, N, K = F32_M, F32_N, F32_K
     d = synth.gemm_fp32(M, N, K, seed=0)
     x, wg, wu = (torch.from_numpy(d[k]).to(dev) for k in ("x", "wg", "wu"))
     h = torch.empty((M, N), dtype=torch.float32, device=dev)
-    for _ in range(3):
-        S.fwd(x, wg, wu, out=h)
+    h2 = torch.empty_like(h)
+    n = args.gemm_iters
+    st = P.run({"swiglu": [lambda: S.fwd(x, wg, wu, out=h)] * n,
+                "geglu": [lambda: S.fwd(x, wg, wu, out=h2, act="gelu_tanh")] * n})
+    for k, v in st.items():
+        v["TFLOPs_p50"] = round(4.0 * M * N * K / (v["p50_us"] * 1e-6) / 1e12, 2)
+        v["frac_of_fp32_peak"] = round(v["TFLOPs_p50"] / PEAK_FP32_TFLOPS, 4)
+        v["launches_per_call"] = LAUNCHES["fwd"]
+        log(f"fp32 fwd {M}x{N}x{K} {k}: {v['p50_us'] / 1e3:.3f} ms, {v['TFLOPs_p50']:.1f} TFLOP/s")
+    S.fwd(x, wg, wu, out=h)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 10
-    e0.record()
-    for _ in range(n):
-        S.fwd(x, wg, wu, out=h)
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / n
-    tf = 4.0 * M * N * K / t / 1e12
-    log(f"fp32 fwd {M}x{N}x{K}: {t * 1e3:.3f} ms, {tf:.1f} TFLOP/s")
-    del x, wg, wu, h
+    ref, secs = timed(lambda: oracle.glu_fwd(d["x"], d["wg"], d["wu"]))
+    st["swiglu"]["vs_oracle"] = err_stats(np, h.cpu().numpy(), ref)
+    if oracle_times is not None:
+        oracle_times["fp32_fwd_4001x3584x2048"] = {"seconds": round(secs, 3), "full": True,
+                                                   "TFLOPs": round(4.0 * M * N * K / secs / 1e12, 4)}
+    del x, wg, wu, h, h2
     torch.cuda.empty_cache()
-    return {"M": M, "N": N, "K": K, "ms": round(t * 1e3, 4), "TFLOPs": round(tf, 2),
-            "frac_of_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4)}
+    return {"M": M, "N": N, "K": K, "variants": st}
 
 
-def cpu_baseline(np, synth, d, target_s):
+def tiny_leg(ctx, oracle_times=None):
+    torch, S, np, P, args, synth = ctx["torch"], ctx["S"], ctx["np"], ctx["P"], ctx["args"], ctx["synth"]
+    import oracle
+    dev = ctx["dev"]
+    d = synth.tiny_fp32(seed=0)
+    t = {k: torch.from_numpy(v).to(dev) for k, v in d.items()}
+    h = torch.empty((4, 128), dtype=torch.float32, device=dev)
+    grads = (torch.empty((4, 64), dtype=torch.float32, device=dev), torch.empty((128, 64), dtype=torch.float32, device=dev),
+             torch.empty((128, 64), dtype=torch.float32, device=dev))
+    ws = torch.empty(S.bwd_workspace_bytes(torch.float32, 4, 128, 64), dtype=torch.uint8, device=dev)
+    st = P.run({"fwd": [lambda: S.fwd(t["x"], t["wg"], t["wu"], out=h)] * args.iters,
+                "bwd": [lambda: S.bwd(t["x"], t["wg"], t["wu"], t["dh"], workspace=ws, out=grads)] * args.iters})
+    st["fwd"]["launches_per_call"] = LAUNCHES["fwd"]
+    st["bwd"]["launches_per_call"] = LAUNCHES["bwd_f32"]
+    S.fwd(t["x"], t["wg"], t["wu"], out=h)
+    S.bwd(t["x"], t["wg"], t["wu"], t["dh"], workspace=ws, out=grads)
+    torch.cuda.synchronize()
+    f = {k: v.astype(np.float64) for k, v in d.items()}
+    (rh, sf) = timed(lambda: oracle.swiglu_fwd(f["x"], f["wg"], f["wu"]))
+    (rb, sb) = timed(lambda: oracle.swiglu_bwd(f["x"], f["wg"], f["wu"], f["dh"]))
+    st["fwd"]["vs_oracle"] = err_stats(np, h.cpu().numpy(), rh)
+    st["bwd"]["vs_oracle"] = {k: err_stats(np, y.cpu().numpy(), r) for k, y, r in zip(("dx", "dwg", "dwu"), grads, rb)}
+    if oracle_times is not None:
+        oracle_times["tiny_fp32_fwd_bwd"] = {"seconds": round(sf + sb, 5), "full": True}
+    log(f"tiny fp32: fwd {st['fwd']['p50_us']:.2f} us, bwd {st['bwd']['p50_us']:.2f} us")
+    return {"M": 4, "N": 128, "K": 64, "variants": st}
+
+
+# ------------------------------------------------------------------ traffic legs (counter runs)
+
+def traffic_decode(ctx):
+    """gemv at (11008, 4096), M = 1 and 8, 4 rotated copies, a few calls each."""
+    torch, S, synth = ctx["torch"], ctx["S"], ctx["synth"]
+    d = synth.decode_bf16(8, 11008, 4096, seed=0)
+    wg0, wu0 = ctx["to_dev_bf16"](d["wg"]), ctx["to_dev_bf16"](d["wu"])
+    W = [(wg0.clone(), wu0.clone()) for _ in range(4)]
+    for M in (1, 8):
+        x = ctx["to_dev_bf16"](d["x"][:M].copy())
+        o = torch.empty((M, 11008), dtype=torch.bfloat16, device=ctx["dev"])
+        for _ in range(2):
+            for a, b in W:
+                S.gemv_fwd(x, a, b, out=o)
+    torch.cuda.synchronize()
+    return None
+
+
+def _aq_inputs(ctx):
+    torch, synth = ctx["torch"], ctx["synth"]
+    d = synth.act_quant_f32(AQ_R, AQ_C, seed=0)
+    return [(torch.from_numpy(d["gate"]).to(ctx["dev"]), torch.from_numpy(d["up"]).to(ctx["dev"])) for _ in range(4)]
+
+
+def traffic_act_quant(ctx):
+    torch, S = ctx["torch"], ctx["S"]
+    ins = _aq_inputs(ctx)
+    q = torch.empty((AQ_R, AQ_C), dtype=torch.uint8, device=ctx["dev"])
+    s = torch.empty((AQ_R, AQ_C // 32), dtype=torch.uint8, device=ctx["dev"])
+    for _ in range(2):
+        for g, u in ins:
+            S.act_quant(g, u, math.inf, out=(q, s, None, None))
+    torch.cuda.synchronize()
+    return None
+
+
+def traffic_act_fwd(ctx):
+    torch, S = ctx["torch"], ctx["S"]
+    ins = _aq_inputs(ctx)
+    h = torch.empty((AQ_R, AQ_C), dtype=torch.bfloat16, device=ctx["dev"])
+    for _ in range(2):
+        for g, u in ins:
+            S.act_fwd(g, u, math.inf, out=(h, None))
+    torch.cuda.synchronize()
+    return None
+
+
+def traffic_act_bwd(ctx):
+    torch, S, synth = ctx["torch"], ctx["S"], ctx["synth"]
+    d = synth.act_bwd_f32(AQ_R, AQ_C, seed=0)
+    ins = [tuple(torch.from_numpy(d[k]).to(ctx["dev"]) for k in ("gate", "up", "dy")) for _ in range(4)]
+    dg = torch.empty((AQ_R, AQ_C), dtype=torch.float32, device=ctx["dev"])
+    du = torch.empty_like(dg)
+    for _ in range(2):
+        for g, u, dy in ins:
+            S.act_bwd(g, u, dy, 0.5, out=(dg, du, None))
+    torch.cuda.synchronize()
+    return None
+
+
+# ------------------------------------------------------------------ cpu baseline
+
+def cpu_baseline(np, synth, d, target_s, gpu_value):
     """The fp64 oracle, as it stands, on the first m rows of the headline
     workload: forward for those rows and the backward contributions of those
     rows (dX rows, and dWg/dWu summed over the m rows only)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
-    except Exception:  # noqa: BLE001
-        cores = os.cpu_count() or 1
+    ncores, blas = host_cores()
     wg = synth.bf16_bits_to_f32(d["wg"]).astype(np.float64)
     wu = synth.bf16_bits_to_f32(d["wu"]).astype(np.float64)
 
@@ -578,10 +926,14 @@ def cpu_baseline(np, synth, d, target_s):
     m = int(max(m0, min(M4, m0 * target_s / max(t0, 1e-3))))
     t = run(m)
     flops = 12.0 * m * N4 * K4
-    log(f"cpu oracle: {m} rows in {t:.1f}s on {cores} threads -> {flops / t / 1e12:.4f} TFLOP/s")
-    return {"value": round(flops / t / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    v = flops / t / 1e12
+    log(f"cpu oracle: {m} rows in {t:.1f}s on {blas} BLAS threads ({ncores} cores) -> {v:.4f} TFLOP/s")
+    return {"value": round(v, 5), "unit": "TFLOP/s", "cores": blas, "kind": "oracle",
             "sample": f"fp64 numpy oracle forward + backward on the first {m} of {M4} rows of the headline "
-                      f"workload (12*m*N*K flops credited, as for value); {t:.1f}s"}
+                      f"workload (12*m*N*K flops credited, as for value); {t:.1f}s",
+            "host_cores": ncores, "seconds": round(t, 2),
+            "seconds_full_extrapolated": round(t * M4 / m, 2),
+            "gpu_over_oracle": round(gpu_value / v, 1)}
 
 
 if __name__ == "__main__":

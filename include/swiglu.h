@@ -336,6 +336,26 @@ int swiglu_act_bwd_dt(int dtype, int64_t rows, int64_t cols,
                       const float* weights, float clamp_limit,
                       void* dgate, void* dup, float* weight_grad, void* stream);
 
+/* swiglu_act_bwd_dt with dgate and dup in E4M3 (the backward table's fmt
+ * e4m3, read as the format of dgate and dup, as fmt is the format of h in the
+ * forward table; the implementation notes' FP8 output cast without
+ * saturation, keeping NaN).  Each output leaves as the quantiser's 1x32
+ * blocks: its exact value is rounded once to fp32, the block's amax (NaN
+ * ignored) gives the smallest E with amax <= 448 * 2^E (byte E + 127, 0xFF
+ * when amax is infinite), and each value is coded as E4M3FN(v * 2^-E), ties
+ * to even, NaN and infinities as NaN.
+ *
+ *   gate, up, dy        [rows, cols] inputs of `dtype` (SWIGLU_F32 or SWIGLU_BF16)
+ *   weights, weight_grad as swiglu_act_bwd (fp32, NULL allowed)
+ *   q_dgate, q_dup      [rows, cols] uint8 E4M3FN codes (16-byte aligned)
+ *   scale_dgate, scale_dup  [rows, cols / 32] uint8 UE8M0 bytes
+ * Layout rule: cols % 32 == 0 (whole blocks), else SWIGLU_ERR_SHAPE. */
+int swiglu_act_bwd_fp8(int dtype, int64_t rows, int64_t cols,
+                       const void* gate, const void* up, const void* dy,
+                       const float* weights, float clamp_limit,
+                       uint8_t* q_dgate, uint8_t* scale_dgate, uint8_t* q_dup, uint8_t* scale_dup,
+                       float* weight_grad, void* stream);
+
 /* Measurement aid: the decode kernel's read-only twin.  The same launch as
  * swiglu_gemv_fwd for (M, N, K) -- grid, LDS footprint, staging of x and
  * every weight load, in the same order and unrolling -- with no arithmetic:
@@ -348,6 +368,30 @@ int swiglu_act_bwd_dt(int dtype, int64_t rows, int64_t cols,
 int swiglu_probe_gemv_read(int64_t M, int64_t N, int64_t K,
                            const void* x, const void* wg, const void* wu, uint32_t* sink,
                            void* stream);
+
+/* Measurement aid: the quantiser's twin.  The launch of swiglu_act_quant
+ * without clamp, count or h_out -- grid, loads of gate and up, stores of q
+ * and scale, in the same mapping -- with no arithmetic: the stored bytes are
+ * folds of the loaded words.  Its time is the floor of the quantiser's byte
+ * pattern (8 bytes read, 1 + 1/32 written per element) on the same buffers.
+ * Arguments, layouts and errors as swiglu_act_quant. */
+int swiglu_probe_act_quant_stream(int64_t rows, int64_t cols, const float* gate, const float* up,
+                                  uint8_t* q, uint8_t* scale, void* stream);
+
+/* Test aid for the FP8 encoders shared by every quantising path: scans the
+ * fp32 bit patterns first..last (inclusive) and appends to `out` the pair
+ * (p, result) for p = first and for each pattern p > first whose result
+ * differs from that of p - 1, incrementing *count once per pair (the caller
+ * zeroes *count; `out` holds 2 * capacity uint32, at most `capacity` pairs
+ * are stored, in no particular order).  kind 0: the E4M3FN code of
+ * the value at scale 1 (nearest, ties to even, NOSAT, NaN kept); kind 1: the
+ * UE8M0 scale byte of the value taken as a block amax.  Over patterns of one
+ * sign the value is monotone in the pattern, so the returned list is the
+ * whole function, which a test compares with an independent encoder over
+ * all 2^32 patterns.  Errors: kind not 0 or 1 (SWIGLU_ERR_ARG), last < first
+ * (SWIGLU_ERR_SHAPE), NULL or misaligned out / count. */
+int swiglu_probe_fp8_transitions(int kind, uint32_t first, uint32_t last, uint32_t* out, uint32_t capacity,
+                                 uint32_t* count, void* stream);
 
 /* Measurement aid: a pure streaming read of two device buffers of `bytes`
  * bytes each (16-byte multiples), the cold-read floor against which the

@@ -404,6 +404,22 @@ def act_bwd(gate, up, dy, clamp_limit=np.inf, weights=None):
     return dgate, dup, weight_grad
 
 
+def act_bwd_fp8(gate, up, dy, clamp_limit=np.inf, weights=None):
+    """The backward with E4M3 outputs ([PTO-20] backward table, fmt e4m3; the
+    implementation notes' NOSAT FP8 output cast).  Reading: fmt is the format
+    of dgate and dup, as it is of h in the forward table, so each leaves in the
+    forward's 1x32 format; gate, up and dy keep their own type (bf16 or fp32).
+    dgate and dup are act_bwd's exact values rounded once to fp32, the
+    precision in which both sides take the scale and code decisions, then
+    quantised by quantize_1x32.  weight_grad is act_bwd's.
+    Returns (q_dgate, scale_dgate, q_dup, scale_dup, weight_grad)."""
+    dgate, dup, weight_grad = act_bwd(gate, up, dy, clamp_limit, weights)
+    with np.errstate(over="ignore", invalid="ignore"):
+        qg, sg = quantize_1x32(dgate.astype(np.float32))
+        qu, su = quantize_1x32(dup.astype(np.float32))
+    return qg, sg, qu, su, weight_grad
+
+
 # ---------------------------------------------------------------------------
 # Comparison metrics (test infrastructure, float64).
 # ---------------------------------------------------------------------------

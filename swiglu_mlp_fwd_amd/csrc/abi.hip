@@ -298,6 +298,17 @@ int swiglu_act_bwd_dt(int dtype, int64_t rows, int64_t cols, const void* gate, c
                                         clamp, dgate, dup, weight_grad, as_stream(stream)));
 }
 
+int swiglu_act_bwd_fp8(int dtype, int64_t rows, int64_t cols, const void* gate, const void* up, const void* dy,
+                       const float* weights, float clamp_limit, uint8_t* q_dgate, uint8_t* scale_dgate,
+                       uint8_t* q_dup, uint8_t* scale_dup, float* weight_grad, void* stream) {
+  int st = swg::validate_act_bwd_fp8(dtype, rows, cols, gate, up, dy, weights, clamp_limit, q_dgate, scale_dgate,
+                                     q_dup, scale_dup, weight_grad);
+  if (st != SWIGLU_OK || rows == 0) return st;
+  const bool clamp = !isinf(clamp_limit);
+  return hip_status(swg::launch_act_bwd_fp8(as_dt(dtype), rows, cols, gate, up, dy, weights, clamp_limit, clamp,
+                                            q_dgate, scale_dgate, q_dup, scale_dup, weight_grad, as_stream(stream)));
+}
+
 int swiglu_act_bwd(int64_t rows, int64_t cols, const float* gate, const float* up, const float* dy,
                    const float* weights, float clamp_limit, float* dgate, float* dup,
                    float* weight_grad, void* stream) {
@@ -321,6 +332,22 @@ int swiglu_probe_gemv_read(int64_t M, int64_t N, int64_t K, const void* x, const
   if (sink == nullptr) return SWIGLU_ERR_NULL;
   if (!swg::aligned(sink, 4)) return SWIGLU_ERR_ALIGN;
   return hip_status(swg::launch_gemv_read_twin((int)M, (int)N, (int)K, x, wg, wu, sink, as_stream(stream)));
+}
+
+int swiglu_probe_act_quant_stream(int64_t rows, int64_t cols, const float* gate, const float* up, uint8_t* q,
+                                  uint8_t* scale, void* stream) {
+  int st = swg::validate_act_quant(rows, cols, gate, up, INFINITY, q, scale, nullptr, nullptr);
+  if (st != SWIGLU_OK || rows == 0 || cols == 0) return st;
+  return hip_status(swg::launch_act_quant_twin(rows, cols, gate, up, q, scale, as_stream(stream)));
+}
+
+int swiglu_probe_fp8_transitions(int kind, uint32_t first, uint32_t last, uint32_t* out, uint32_t capacity,
+                                 uint32_t* count, void* stream) {
+  if (kind != 0 && kind != 1) return SWIGLU_ERR_ARG;
+  if (last < first) return SWIGLU_ERR_SHAPE;
+  if (out == nullptr || count == nullptr) return SWIGLU_ERR_NULL;
+  if (!swg::aligned(out, 4) || !swg::aligned(count, 4)) return SWIGLU_ERR_ALIGN;
+  return hip_status(swg::launch_probe_transitions(first, last, kind, out, capacity, count, as_stream(stream)));
 }
 
 int swiglu_probe_read2(const void* a, const void* b, size_t bytes, uint32_t* sink, void* stream) {

@@ -26,6 +26,7 @@
 // the forward kernels), which keeps more loads in flight per lane; a chunk's
 // row (for its weight) comes from one division.
 #include "common.hpp"
+#include "fp8.hpp"
 #include "gemm.hpp"
 
 namespace swg {
@@ -83,14 +84,59 @@ template <> struct Chunk<bf16> {
   }
 };
 
-template <typename T, int kSplit, bool kClamp, bool kWeights, bool kGrad>
+// Where dgate and dup go: tensors of the input type, or (kFp8) E4M3 codes
+// [rows, cols] with a UE8M0 scale byte per 1x32 block [rows, cols / 32].
+struct BwdOut {
+  void* dgate;
+  void* dup;
+  uint8_t* sg;       // kFp8: scales of dgate
+  uint8_t* su;       // kFp8: scales of dup
+};
+
+// One output chunk of kN values starting at flat element e0 (a multiple of
+// kN).  kFp8: the values are rounded once to fp32 (the precision of the
+// scale and code decisions, as in the quantiser); a 1x32 block spans the
+// 32 / kN lanes that hold its consecutive chunks (whole blocks, since
+// cols % 32 == 0 and those lanes take consecutive chunks), so its amax
+// (NaN ignored) is reduced across them with xor-shuffles; the first lane of
+// the block stores its scale byte.
+template <typename T, bool kFp8>
+__device__ __forceinline__ void put_chunk(void* base, uint8_t* scale, int64_t e0, const double (&v)[Chunk<T>::kN]) {
+  constexpr int kN = Chunk<T>::kN;
+  if constexpr (!kFp8) {
+    __builtin_nontemporal_store(Chunk<T>::pack(v), reinterpret_cast<u32x4*>(base) + e0 / kN);
+  } else {
+    constexpr int kLanes = 32 / kN;
+    float f[kN];
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kN; ++e) {
+      f[e] = (float)v[e];
+      amax = fmaxf(amax, fabsf(f[e]));                  // maxNum: NaN ignored
+    }
+#pragma unroll
+    for (int off = 1; off < kLanes; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const int E = block_exponent(amax);
+    const float sc = ldexpf(1.0f, -E);
+    uint8_t* q = static_cast<uint8_t*>(base) + e0;
+    if constexpr (kN == 8) {
+      const uint32_t lo = e4m3_pair(f[0], f[1], sc) | (e4m3_pair(f[2], f[3], sc) << 16);
+      const uint32_t hi = e4m3_pair(f[4], f[5], sc) | (e4m3_pair(f[6], f[7], sc) << 16);
+      __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(q));
+    } else {
+      __builtin_nontemporal_store(e4m3_pair(f[0], f[1], sc) | (e4m3_pair(f[2], f[3], sc) << 16),
+                                  reinterpret_cast<uint32_t*>(q));
+    }
+    if ((e0 & 31) == 0) scale[e0 >> 5] = (uint8_t)(E + 127);
+  }
+}
+
+template <typename T, int kSplit, bool kClamp, bool kWeights, bool kGrad, bool kFp8>
 __global__ __launch_bounds__(kThreads) void act_bwd_kernel(const T* __restrict__ gate,
                                                            const T* __restrict__ up,
                                                            const T* __restrict__ dy,
                                                            const float* __restrict__ weights, float L,
-                                                           T* __restrict__ dgate,
-                                                           T* __restrict__ dup,
-                                                           float* __restrict__ wgrad, int64_t rows,
+                                                           BwdOut out, float* __restrict__ wgrad, int64_t rows,
                                                            int64_t cols) {
   constexpr int kN = Chunk<T>::kN;
   constexpr int kUnroll = 4;                        // chunks per lane in flight
@@ -111,8 +157,6 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(const T* __restrict__
     const u32x4* g4 = reinterpret_cast<const u32x4*>(gate + r * cols);
     const u32x4* u4 = reinterpret_cast<const u32x4*>(up + r * cols);
     const u32x4* d4 = reinterpret_cast<const u32x4*>(dy + r * cols);
-    u32x4* og = reinterpret_cast<u32x4*>(dgate + r * cols);
-    u32x4* ou = reinterpret_cast<u32x4*>(dup + r * cols);
     double acc = 0.0;
     for (int64_t c0 = lp; c0 < nch; c0 += 64 * kSplit * kUnroll) {
       u32x4 G[kUnroll], U[kUnroll], D[kUnroll];
@@ -136,8 +180,8 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(const T* __restrict__
         double a[kN], b[kN];
 #pragma unroll
         for (int e = 0; e < kN; ++e) bwd_elem<kClamp>(gv[e], uv[e], dv[e], w, L, a[e], b[e], acc);
-        __builtin_nontemporal_store(Chunk<T>::pack(a), og + c);
-        __builtin_nontemporal_store(Chunk<T>::pack(b), ou + c);
+        put_chunk<T, kFp8>(out.dgate, out.sg, r * cols + c * kN, a);
+        put_chunk<T, kFp8>(out.dup, out.su, r * cols + c * kN, b);
       }
     }
     if (kGrad) {
@@ -164,21 +208,18 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(const T* __restrict__
 
 // Flat mapping, no weight_grad.  Rows hold whole chunks (cols % kN == 0),
 // so chunk c lies in row c / (cols / kN).
-template <typename T, bool kClamp, bool kWeights>
+template <typename T, bool kClamp, bool kWeights, bool kFp8>
 __global__ __launch_bounds__(kThreads) void act_bwd_flat_kernel(const T* __restrict__ gate,
                                                                 const T* __restrict__ up,
                                                                 const T* __restrict__ dy,
                                                                 const float* __restrict__ weights, float L,
-                                                                T* __restrict__ dgate, T* __restrict__ dup,
-                                                                int64_t nchunks, int64_t row_chunks) {
+                                                                BwdOut out, int64_t nchunks, int64_t row_chunks) {
   constexpr int kN = Chunk<T>::kN;
   constexpr int kUnroll = 4;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   const u32x4* g4 = reinterpret_cast<const u32x4*>(gate);
   const u32x4* u4 = reinterpret_cast<const u32x4*>(up);
   const u32x4* d4 = reinterpret_cast<const u32x4*>(dy);
-  u32x4* og = reinterpret_cast<u32x4*>(dgate);
-  u32x4* ou = reinterpret_cast<u32x4*>(dup);
   for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < nchunks; c0 += kUnroll * stride) {
     u32x4 G[kUnroll], U[kUnroll], D[kUnroll];
 #pragma unroll
@@ -202,60 +243,58 @@ __global__ __launch_bounds__(kThreads) void act_bwd_flat_kernel(const T* __restr
       double a[kN], b[kN], unused = 0.0;
 #pragma unroll
       for (int e = 0; e < kN; ++e) bwd_elem<kClamp>(gv[e], uv[e], dv[e], w, L, a[e], b[e], unused);
-      __builtin_nontemporal_store(Chunk<T>::pack(a), og + c);
-      __builtin_nontemporal_store(Chunk<T>::pack(b), ou + c);
+      put_chunk<T, kFp8>(out.dgate, out.sg, c * kN, a);
+      put_chunk<T, kFp8>(out.dup, out.su, c * kN, b);
     }
   }
 }
 
 template <typename T> constexpr int kSplitOf = 4;   // waves per row
 
-template <typename T, bool kClamp, bool kWeights, bool kGrad>
+template <typename T, bool kFp8, bool kClamp, bool kWeights, bool kGrad>
 void launch_ab(unsigned grid, const void* gate, const void* up, const void* dy, const float* w,
-               float L, void* dg, void* du, float* wgrad, int64_t rows, int64_t cols, hipStream_t s) {
-  hipLaunchKernelGGL((act_bwd_kernel<T, kSplitOf<T>, kClamp, kWeights, kGrad>), dim3(grid), dim3(kThreads), 0, s,
-                     static_cast<const T*>(gate), static_cast<const T*>(up), static_cast<const T*>(dy), w, L,
-                     static_cast<T*>(dg), static_cast<T*>(du), wgrad, rows, cols);
+               float L, const BwdOut& out, float* wgrad, int64_t rows, int64_t cols, hipStream_t s) {
+  hipLaunchKernelGGL((act_bwd_kernel<T, kSplitOf<T>, kClamp, kWeights, kGrad, kFp8>), dim3(grid), dim3(kThreads), 0, s,
+                     static_cast<const T*>(gate), static_cast<const T*>(up), static_cast<const T*>(dy), w, L, out,
+                     wgrad, rows, cols);
 }
 
-template <typename T, bool kClamp, bool kWeights>
-void launch_flat(const void* gate, const void* up, const void* dy, const float* w, float L, void* dg, void* du,
+template <typename T, bool kFp8, bool kClamp, bool kWeights>
+void launch_flat(const void* gate, const void* up, const void* dy, const float* w, float L, const BwdOut& out,
                  int64_t rows, int64_t cols, hipStream_t s) {
   constexpr int kFlatMaxBlocks = 8192;
   const int64_t nch = rows * (cols / Chunk<T>::kN);
   if (nch == 0) return;                                 // no elements (cols == 0)
   const int64_t want = (nch + kThreads - 1) / kThreads;
   const unsigned grid = (unsigned)(want < kFlatMaxBlocks ? want : kFlatMaxBlocks);
-  hipLaunchKernelGGL((act_bwd_flat_kernel<T, kClamp, kWeights>), dim3(grid), dim3(kThreads), 0, s,
-                     static_cast<const T*>(gate), static_cast<const T*>(up), static_cast<const T*>(dy), w, L,
-                     static_cast<T*>(dg), static_cast<T*>(du), nch, cols / Chunk<T>::kN);
+  hipLaunchKernelGGL((act_bwd_flat_kernel<T, kClamp, kWeights, kFp8>), dim3(grid), dim3(kThreads), 0, s,
+                     static_cast<const T*>(gate), static_cast<const T*>(up), static_cast<const T*>(dy), w, L, out,
+                     nch, cols / Chunk<T>::kN);
 }
 
-template <typename T>
+template <typename T, bool kFp8>
 void launch_typed(bool clamp, const void* gate, const void* up, const void* dy,
-                  const float* weights, float limit, void* dgate, void* dup, float* wgrad, int64_t rows,
+                  const float* weights, float limit, const BwdOut& out, float* wgrad, int64_t rows,
                   int64_t cols, hipStream_t s) {
   const bool w = weights != nullptr, g = wgrad != nullptr;
   if (!g) {
     if (clamp) {
-      if (w) launch_flat<T, true, true>(gate, up, dy, weights, limit, dgate, dup, rows, cols, s);
-      else launch_flat<T, true, false>(gate, up, dy, weights, limit, dgate, dup, rows, cols, s);
+      if (w) launch_flat<T, kFp8, true, true>(gate, up, dy, weights, limit, out, rows, cols, s);
+      else launch_flat<T, kFp8, true, false>(gate, up, dy, weights, limit, out, rows, cols, s);
     } else {
-      if (w) launch_flat<T, false, true>(gate, up, dy, weights, limit, dgate, dup, rows, cols, s);
-      else launch_flat<T, false, false>(gate, up, dy, weights, limit, dgate, dup, rows, cols, s);
+      if (w) launch_flat<T, kFp8, false, true>(gate, up, dy, weights, limit, out, rows, cols, s);
+      else launch_flat<T, kFp8, false, false>(gate, up, dy, weights, limit, out, rows, cols, s);
     }
     return;
   }
   constexpr int kRowsPerBlock = kThreads / 64 / kSplitOf<T>;
   const int64_t want = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const unsigned grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);
-#define SWG_AB(C, W, G) launch_ab<T, C, W, G>(grid, gate, up, dy, weights, limit, dgate, dup, wgrad, rows, cols, s)
+#define SWG_AB(C, W) launch_ab<T, kFp8, C, W, true>(grid, gate, up, dy, weights, limit, out, wgrad, rows, cols, s)
   if (clamp) {
-    if (w) { if (g) SWG_AB(true, true, true); else SWG_AB(true, true, false); }
-    else { if (g) SWG_AB(true, false, true); else SWG_AB(true, false, false); }
+    if (w) SWG_AB(true, true); else SWG_AB(true, false);
   } else {
-    if (w) { if (g) SWG_AB(false, true, true); else SWG_AB(false, true, false); }
-    else { if (g) SWG_AB(false, false, true); else SWG_AB(false, false, false); }
+    if (w) SWG_AB(false, true); else SWG_AB(false, false);
   }
 #undef SWG_AB
 }
@@ -266,10 +305,23 @@ hipError_t launch_act_bwd(Dt dt, int64_t rows, int64_t cols, const void* gate, c
                           const void* dy, const float* weights, float limit, bool clamp,
                           void* dgate, void* dup, float* wgrad, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  const BwdOut out{dgate, dup, nullptr, nullptr};
   if (dt == Dt::kBF16)
-    launch_typed<bf16>(clamp, gate, up, dy, weights, limit, dgate, dup, wgrad, rows, cols, s);
+    launch_typed<bf16, false>(clamp, gate, up, dy, weights, limit, out, wgrad, rows, cols, s);
   else
-    launch_typed<float>(clamp, gate, up, dy, weights, limit, dgate, dup, wgrad, rows, cols, s);
+    launch_typed<float, false>(clamp, gate, up, dy, weights, limit, out, wgrad, rows, cols, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_bwd_fp8(Dt dt, int64_t rows, int64_t cols, const void* gate, const void* up,
+                              const void* dy, const float* weights, float limit, bool clamp, uint8_t* q_dgate,
+                              uint8_t* s_dgate, uint8_t* q_dup, uint8_t* s_dup, float* wgrad, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const BwdOut out{q_dgate, q_dup, s_dgate, s_dup};
+  if (dt == Dt::kBF16)
+    launch_typed<bf16, true>(clamp, gate, up, dy, weights, limit, out, wgrad, rows, cols, s);
+  else
+    launch_typed<float, true>(clamp, gate, up, dy, weights, limit, out, wgrad, rows, cols, s);
   return hipGetLastError();
 }
 

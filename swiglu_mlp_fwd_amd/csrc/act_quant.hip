@@ -28,7 +28,10 @@ constexpr int kMaxBlocks = 1024;       // with the count: 4 workgroups per CU (o
 constexpr int kMaxBlocksFree = 4096;   // without it
 constexpr int kUnroll = 4;         // chunks per lane per loop iteration
 
-template <Act A, bool kClamp, bool kCount, bool kHout>
+// kTwin: the same kernel with the same grid, loads and stores and no
+// arithmetic (the stored bytes are folds of the loaded words): the floor of
+// this kernel's byte pattern, 8 bytes read and 1 + 1/32 written per element.
+template <Act A, bool kClamp, bool kCount, bool kHout, bool kTwin = false>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float* __restrict__ gate,
                                                              const float* __restrict__ up, float L,
                                                              uint8_t* __restrict__ q,
@@ -62,6 +65,15 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float* __rest
     const int64_t c = c0 + j * stride;
     if (c >= nchunks) break;
     const f32x4 g0 = G0[j], g1 = G1[j], u0 = U0[j], u1 = U1[j];
+    if constexpr (kTwin) {
+      const uint32_t lo = f32_bits(g0[0]) ^ f32_bits(g0[1]) ^ f32_bits(g0[2]) ^ f32_bits(g0[3]) ^ f32_bits(u0[0]) ^
+                          f32_bits(u0[1]) ^ f32_bits(u0[2]) ^ f32_bits(u0[3]);
+      const uint32_t hi = f32_bits(g1[0]) ^ f32_bits(g1[1]) ^ f32_bits(g1[2]) ^ f32_bits(g1[3]) ^ f32_bits(u1[0]) ^
+                          f32_bits(u1[1]) ^ f32_bits(u1[2]) ^ f32_bits(u1[3]);
+      *reinterpret_cast<u32x2*>(q + 8 * c) = u32x2{lo, hi};
+      if ((threadIdx.x & 3) == 0) scale[c >> 2] = (uint8_t)(lo ^ hi);
+      continue;
+    }
     float h[8];
     float amax = 0.0f;
 #pragma unroll
@@ -139,6 +151,17 @@ void launch_aq_variant(bool counting, bool clamp, unsigned grid, const float* ga
 }
 
 }  // namespace
+
+hipError_t launch_act_quant_twin(int64_t rows, int64_t cols, const float* gate, const float* up, uint8_t* q,
+                                 uint8_t* scale, hipStream_t s) {
+  const int64_t nchunks = rows * cols / 8;
+  if (nchunks == 0) return hipSuccess;
+  const int64_t want = (nchunks + kThreads - 1) / kThreads;
+  const unsigned grid = (unsigned)(want < kMaxBlocksFree ? want : kMaxBlocksFree);
+  hipLaunchKernelGGL((act_quant_kernel<Act::kSilu, false, false, false, true>), dim3(grid), dim3(kThreads), 0, s,
+                     gate, up, 0.0f, q, scale, nullptr, nullptr, nchunks);
+  return hipGetLastError();
+}
 
 hipError_t launch_act_quant(Act act, int64_t rows, int64_t cols, const float* gate, const float* up,
                             float limit, bool clamp, uint8_t* q, uint8_t* scale, uint64_t* count,

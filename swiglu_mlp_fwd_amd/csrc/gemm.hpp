@@ -87,12 +87,25 @@ hipError_t launch_act_bwd(Dt dt, int64_t rows, int64_t cols, const void* gate, c
                           const void* dy, const float* weights, float limit, bool clamp,
                           void* dgate, void* dup, float* wgrad, hipStream_t s);
 
+// The same with dgate and dup as E4M3 codes and UE8M0 scales per 1x32 block.
+hipError_t launch_act_bwd_fp8(Dt dt, int64_t rows, int64_t cols, const void* gate, const void* up,
+                              const void* dy, const float* weights, float limit, bool clamp, uint8_t* q_dgate,
+                              uint8_t* s_dgate, uint8_t* q_dup, uint8_t* s_dup, float* wgrad, hipStream_t s);
+
 hipError_t launch_act_fwd(Act act, Dt out, int64_t rows, int64_t cols, const float* gate, const float* up,
                           float limit, bool clamp, void* h, uint64_t* count, hipStream_t s);
 
 hipError_t launch_act_quant(Act act, int64_t rows, int64_t cols, const float* gate, const float* up,
                             float limit, bool clamp, uint8_t* q, uint8_t* scale,
                             uint64_t* count, float* hout, hipStream_t s);
+
+// The quantiser's twin: its grid, loads and stores without arithmetic (the
+// unclamped launch, no count, no h_out).
+hipError_t launch_act_quant_twin(int64_t rows, int64_t cols, const float* gate, const float* up, uint8_t* q,
+                                 uint8_t* scale, hipStream_t s);
+
+hipError_t launch_probe_transitions(uint32_t first, uint32_t last, int kind, uint32_t* out, uint32_t capacity,
+                                    uint32_t* count, hipStream_t s);
 
 hipError_t launch_probe_mfma(int iters, int blocks, float* sink, hipStream_t s);
 

@@ -5,6 +5,7 @@
 // which the decode kernel's weight stream is compared on the same rotated
 // buffers.
 #include "common.hpp"
+#include "fp8.hpp"
 #include "gemm.hpp"
 
 namespace swg {
@@ -84,7 +85,54 @@ __global__ __launch_bounds__(kMfmaThreads) void probe_mfma_kernel(int iters, flo
   if (threadIdx.x == 0) sink[blockIdx.x] = s;
 }
 
+// Exhaustive check aid for the FP8 encoders: over the fp32 bit patterns
+// [first, last], each thread walks a contiguous run and reports `first` and
+// every pattern p whose result differs from that of p - 1, as the pair
+// (p, result) (atomic append; the order of the list is arbitrary).  kind 0: the E4M3 code of the value at
+// scale 1 (e4m3_pair, the path of every quantiser); kind 1: the UE8M0 byte of
+// the value taken as a block amax (block_exponent).  On a run of patterns
+// of one sign the value is monotone in the pattern, and both functions are
+// monotone step functions of the value, so the list determines every result.
+__device__ __forceinline__ uint32_t encode_probe(uint32_t p, int kind) {
+  const float v = bits_f32(p);
+  if (kind == 0) return e4m3_pair(v, 0.0f, 1.0f) & 0xFFu;
+  return (uint32_t)(block_exponent(v) + 127);
+}
+
+constexpr int kRun = 4096;     // patterns per thread
+
+__global__ __launch_bounds__(256) void probe_transitions_kernel(uint32_t first, uint32_t last, int kind,
+                                                                uint32_t* __restrict__ out, uint32_t capacity,
+                                                                uint32_t* __restrict__ count) {
+  const uint64_t t = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  const uint64_t lo = (uint64_t)first + t * kRun;
+  if (lo > last) return;
+  const uint64_t hi = min((uint64_t)last, lo + kRun - 1);
+  // The first pattern of the range always starts a run.
+  uint32_t prev = lo > first ? encode_probe((uint32_t)(lo - 1), kind) : ~0u;
+  for (uint64_t p = lo; p <= hi; ++p) {
+    const uint32_t c = encode_probe((uint32_t)p, kind);
+    if (c != prev) {
+      const uint32_t i = atomicAdd(count, 1u);
+      if (i < capacity) {
+        out[2 * i] = (uint32_t)p;
+        out[2 * i + 1] = c;
+      }
+    }
+    prev = c;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_probe_transitions(uint32_t first, uint32_t last, int kind, uint32_t* out, uint32_t capacity,
+                                    uint32_t* count, hipStream_t s) {
+  const uint64_t n = (uint64_t)last - first + 1;
+  const uint64_t threads = (n + kRun - 1) / kRun;
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  hipLaunchKernelGGL(probe_transitions_kernel, dim3(grid), dim3(256), 0, s, first, last, kind, out, capacity, count);
+  return hipGetLastError();
+}
 
 hipError_t launch_probe_mfma(int iters, int blocks, float* sink, hipStream_t s) {
   if (iters <= 0 || blocks <= 0) return hipSuccess;

@@ -232,4 +232,25 @@ inline int validate_act_bwd(int dtype, int64_t rows, int64_t cols, const void* g
   return SWIGLU_OK;
 }
 
+inline int validate_act_bwd_fp8(int dtype, int64_t rows, int64_t cols, const void* gate, const void* up,
+                                const void* dy, const float* weights, float L, const void* qg, const void* sg,
+                                const void* qu, const void* su, const float* wgrad) {
+  int st = check_dtype(dtype);
+  if (st) return st;
+  if (rows < 0 || cols < 0) return SWIGLU_ERR_SHAPE;
+  if (cols % 32 != 0) return SWIGLU_ERR_SHAPE;        // whole 1x32 blocks per row
+  if (rows > 0 && cols > (int64_t(1) << 40) / rows) return SWIGLU_ERR_SHAPE;
+  if (!(L > 0.0f)) return SWIGLU_ERR_ARG;             // rejects NaN, zero and negatives
+  if (weights != nullptr && !aligned(weights, 4)) return SWIGLU_ERR_ALIGN;
+  if (wgrad != nullptr && !aligned(wgrad, 4)) return SWIGLU_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return SWIGLU_OK;
+  if ((st = check_ptr(gate))) return st;
+  if ((st = check_ptr(up))) return st;
+  if ((st = check_ptr(dy))) return st;
+  if ((st = check_ptr(qg))) return st;
+  if ((st = check_ptr(qu))) return st;
+  if (sg == nullptr || su == nullptr) return SWIGLU_ERR_NULL;
+  return SWIGLU_OK;
+}
+
 }  // namespace swg

@@ -346,6 +346,51 @@ def act_bwd(gate: torch.Tensor, up: torch.Tensor, dy: torch.Tensor, clamp_limit:
     return dg.reshape(gate.shape), du.reshape(gate.shape), wg
 
 
+def act_bwd_fp8(gate: torch.Tensor, up: torch.Tensor, dy: torch.Tensor, clamp_limit: float = math.inf,
+                weights: torch.Tensor | None = None, weight_grad: bool = False, out=None):
+    """act_bwd with dgate and dup quantised per 1x32 block (E4M3FN codes, UE8M0
+    scales).  gate, up, dy are fp32 or bf16; weights and weight_grad fp32.
+    Returns (q_dgate, scale_dgate, q_dup, scale_dup, weight_grad or None);
+    `out` may pass those five preallocated (weight_grad may be None)."""
+    _same(gate, up, dy)
+    if gate.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("act_bwd_fp8 takes fp32 or bf16 gate/up/dy")
+    if gate.shape != up.shape or gate.shape != dy.shape:
+        raise ValueError("gate, up and dy must have the same shape")
+    cols = gate.shape[-1]
+    rows = math.prod(gate.shape[:-1])
+    if weights is not None:
+        if weights.dtype != torch.float32 or weights.device != gate.device:
+            raise TypeError("weights must be an fp32 tensor on the device of gate")
+        if weights.numel() != rows:
+            raise ValueError(f"weights must have {rows} elements")
+    dev = gate.device
+    nb = cols // 32 if cols % 32 == 0 else 0
+    if out is not None:
+        qg, sg, qu, su, wg = out
+        _check_out(qg, "q_dgate", (rows, cols), torch.uint8, dev)
+        _check_out(sg, "scale_dgate", (rows, nb), torch.uint8, dev)
+        _check_out(qu, "q_dup", (rows, cols), torch.uint8, dev)
+        _check_out(su, "scale_dup", (rows, nb), torch.uint8, dev)
+        if wg is not None:
+            _check_out(wg, "weight_grad", (rows,), torch.float32, dev)
+    _on_gpu(gate)
+    g2 = gate.reshape(rows, cols).contiguous()
+    u2 = up.reshape(rows, cols).contiguous()
+    d2 = dy.reshape(rows, cols).contiguous()
+    w = None if weights is None else weights.reshape(rows).contiguous()
+    if out is None:
+        qg = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        qu = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        sg = torch.empty((rows, nb), dtype=torch.uint8, device=dev)
+        su = torch.empty((rows, nb), dtype=torch.uint8, device=dev)
+        wg = torch.empty(rows, dtype=torch.float32, device=dev) if weight_grad else None
+    check("swiglu_act_bwd_fp8", lib().swiglu_act_bwd_fp8(_dtype_code(gate), rows, cols, _p(g2), _p(u2), _p(d2), _p(w),
+                                                         float(clamp_limit), _p(qg), _p(sg), _p(qu), _p(su), _p(wg),
+                                                         _stream(gate)))
+    return qg, sg, qu, su, wg
+
+
 def probe_mfma(iters: int, blocks: int, sink: torch.Tensor) -> int:
     """Register-only bf16 MFMA loop; returns the flops one call performs."""
     if sink.dtype != torch.float32 or sink.numel() < blocks:
@@ -370,6 +415,22 @@ def probe_gemv_read(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, sink: t
     _on_gpu(x)
     check("swiglu_probe_gemv_read", lib().swiglu_probe_gemv_read(M, N, K, _p(x), _p(wg), _p(wu), _p(sink),
                                                                  _stream(x)))
+
+
+def probe_act_quant_stream(gate: torch.Tensor, up: torch.Tensor, q: torch.Tensor, scale: torch.Tensor) -> None:
+    """The quantiser's twin on these buffers (its loads and stores, no
+    arithmetic); q and scale receive folds of the input words."""
+    _same(gate, up)
+    if gate.dtype != torch.float32 or gate.shape != up.shape or gate.dim() != 2:
+        raise ValueError("gate and up must be fp32 [rows, cols]")
+    rows, cols = gate.shape
+    _check_out(q, "q", (rows, cols), torch.uint8, gate.device)
+    _check_out(scale, "scale", (rows, cols // 32 if cols % 32 == 0 else 0), torch.uint8, gate.device)
+    if not (gate.is_contiguous() and up.is_contiguous()):
+        raise ValueError("probe_act_quant_stream takes contiguous inputs")
+    _on_gpu(gate)
+    check("swiglu_probe_act_quant_stream", lib().swiglu_probe_act_quant_stream(rows, cols, _p(gate), _p(up), _p(q),
+                                                                               _p(scale), _stream(gate)))
 
 
 def probe_read2(a: torch.Tensor, b: torch.Tensor, sink: torch.Tensor) -> None:

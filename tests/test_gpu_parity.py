@@ -469,6 +469,85 @@ def test_probe_gemv_read_reads_every_weight(M, N, K):
     assert np.all(got[N:] == np.uint32(0xFFFFFFFF)), "the twin wrote past its N columns"
 
 
+@pytest.mark.parametrize("shape", [(4001, 3584), (3, 384), (1, 32)])
+def test_probe_act_quant_stream_moves_the_quantiser_bytes(shape):
+    """The quantiser's twin writes, for each 8-element chunk, the XOR of the
+    chunk's first four gate and up words and of its last four (8 bytes of q),
+    and for each 1x32 block the low byte of the XOR of its first chunk's two
+    words: every input is read and exactly the quantiser's outputs written."""
+    R, C = shape
+    d = synth.act_quant_f32(R, C, seed=6)
+    gs = [guarded((R, C), torch.uint8), guarded((R, C // 32), torch.uint8)]
+    S.probe_act_quant_stream(dev_f32(d["gate"]), dev_f32(d["up"]), gs[0].t, gs[1].t)
+    torch.cuda.synchronize()
+    check_guards(f"act_quant twin {shape}", *gs)
+    gw = d["gate"].view(np.uint32).reshape(-1, 2, 4)
+    uw = d["up"].view(np.uint32).reshape(-1, 2, 4)
+    fold = np.bitwise_xor.reduce(gw, axis=2) ^ np.bitwise_xor.reduce(uw, axis=2)      # [chunks, 2]
+    got = gs[0].t.cpu().numpy().reshape(-1).view(np.uint32).reshape(-1, 2)
+    assert np.array_equal(got, fold)
+    first = fold.reshape(-1, 4, 2)[:, 0, :]                                            # first chunk of each block
+    want_s = ((first[:, 0] ^ first[:, 1]) & 0xFF).astype(np.uint8)
+    assert np.array_equal(gs[1].t.cpu().numpy().reshape(-1), want_s)
+
+
+def _device_runs(kind, first, last, cap=8192):
+    """The device's result as runs: sorted (start pattern, result) pairs."""
+    out = torch.zeros(2 * cap, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    st = S.lib().swiglu_probe_fp8_transitions(kind, first, last, out.data_ptr(), cap, cnt.data_ptr(),
+                                               torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    n = int(cnt.item())
+    assert 0 < n <= cap
+    pairs = out[:2 * n].cpu().numpy().view(np.uint32).reshape(n, 2)
+    return pairs[np.argsort(pairs[:, 0])]
+
+
+def _check_runs(runs, last, oracle_fn, what):
+    """Each run [a, b] of constant device result c: the oracle at a and at b
+    must be c.  Over patterns of one sign the fp32 value is monotone in the
+    pattern and the oracle is a monotone step function of the value (nearest
+    rounding on a sorted lattice, the overflow and NaN class above it; the
+    smallest sufficient power of two for the scale), so equal ends mean the
+    oracle is c on the whole run: every pattern of the range is compared."""
+    starts = runs[:, 0].astype(np.int64)
+    ends = np.append(starts[1:] - 1, last)
+    codes = runs[:, 1]
+    for pts in (starts, ends):
+        vals = pts.astype(np.uint32).view(np.float32)
+        want = oracle_fn(vals)
+        bad = np.nonzero(want != codes)[0]
+        assert bad.size == 0, (f"{what}: device {codes[bad[:4]]} vs oracle {want[bad[:4]]} at patterns "
+                               f"{[hex(int(v)) for v in pts[bad[:4]]]}")
+
+
+def test_e4m3_encoder_on_all_fp32_patterns():
+    """The device E4M3 encoding (v_cvt_pk_fp8_f32 at scale 1, the path of every
+    quantiser here) against the oracle's encoder on all 2^32 fp32 patterns:
+    the device scans them in order and returns its runs of constant code, and
+    the oracle is checked at both ends of every run.  Codes are compared
+    exactly, NaN sign included."""
+    def oracle_codes(v):
+        return oracle.e4m3_encode(v.astype(np.float64)).astype(np.uint32)
+    for first, last in ((0x00000000, 0x7FFFFFFF), (0x80000000, 0xFFFFFFFF)):
+        runs = _device_runs(0, first, last)
+        _check_runs(runs, last, oracle_codes, f"e4m3 patterns {first:#x}..{last:#x}")
+        log(f"e4m3 {first:#x}..{last:#x}: {len(runs)} runs, all equal to the oracle")
+
+
+def test_ue8m0_scale_on_all_amax_patterns():
+    """The device UE8M0 byte of a block amax (block_exponent) against the
+    oracle's ue8m0_byte(ue8m0_exponent(amax)) on every non-negative fp32
+    pattern up to +inf (amax ignores NaN, so it is never NaN)."""
+    def oracle_bytes(v):
+        return oracle.ue8m0_byte(oracle.ue8m0_exponent(v.astype(np.float64))).astype(np.uint32)
+    runs = _device_runs(1, 0x00000000, 0x7F800000)
+    _check_runs(runs, 0x7F800000, oracle_bytes, "ue8m0 amax patterns")
+    log(f"ue8m0: {len(runs)} runs, all equal to the oracle")
+
+
 def test_probe_read2_runs():
     a = torch.ones(1 << 20, dtype=torch.int32, device=DEV)
     b = torch.ones(1 << 20, dtype=torch.int32, device=DEV)
@@ -589,6 +668,125 @@ def test_act_bwd_bf16_ragged_and_specials(shape):
     d = synth.act_bwd_bf16(rows, cols, seed=3, specials=True)
     for L in (math.inf, 1.5):
         check_act_bwd(d, L, True, f"act_bwd bf16 {shape} L={L} specials")
+
+
+# ------------------------------------- act_bwd with E4M3 outputs (next f1)
+
+def check_act_bwd_fp8(d, L, use_w, what):
+    """dgate and dup as 1x32 E4M3 blocks.
+
+    1. same precision: the fp32-output backward on the same values (bf16
+       inputs widened exactly) gives the once-rounded fp32 dgate and dup the
+       quantiser works on; the oracle's 1x32 quantiser applied to them must
+       give the device's scale bytes and codes bit for bit, and weight_grad
+       must equal the fp32 path's bit for bit;
+    2. from the inputs: against the oracle's E4M3 backward, scales bit-exact
+       except blocks whose exact amax lies within the fp32 path's 8-ulp bound
+       of a scale boundary 1.75 * 2^k, codes within 1 ulp elsewhere, NaN codes
+       exactly where the oracle has them."""
+    g, u, dy = d["gate"], d["up"], d["dy"]
+    bf = g.dtype == np.uint16
+    R, C = g.shape
+    dev = dev_bf16 if bf else dev_f32
+    w = d["weights"] if use_w else None
+    gs = [guarded((R, C), torch.uint8), guarded((R, C // 32), torch.uint8), guarded((R, C), torch.uint8),
+          guarded((R, C // 32), torch.uint8), guarded((R,), torch.float32)]
+    S.act_bwd_fp8(dev(g), dev(u), dev(dy), L, weights=None if w is None else dev_f32(w),
+                  out=(gs[0].t, gs[1].t, gs[2].t, gs[3].t, gs[4].t if use_w else None))
+    # the flat mapping (no weight_grad) must give the same bytes
+    gs2 = [guarded((R, C), torch.uint8), guarded((R, C // 32), torch.uint8), guarded((R, C), torch.uint8),
+           guarded((R, C // 32), torch.uint8)]
+    S.act_bwd_fp8(dev(g), dev(u), dev(dy), L, weights=None if w is None else dev_f32(w),
+                  out=(gs2[0].t, gs2[1].t, gs2[2].t, gs2[3].t, None))
+    f32 = {k: f64_of(d[k]).astype(np.float32) for k in ("gate", "up", "dy")}
+    dg32, du32, wg32 = S.act_bwd(dev_f32(f32["gate"]), dev_f32(f32["up"]), dev_f32(f32["dy"]), L,
+                                 weights=None if w is None else dev_f32(w), weight_grad=True)
+    torch.cuda.synchronize()
+    check_guards(what, *gs, *gs2)
+    qg, sg, qu, su = (x.t.cpu().numpy() for x in gs[:4])
+    for a, b in zip(gs[:4], gs2):
+        assert torch.equal(a.t, b.t), f"{what}: the row and flat mappings differ"
+    # 1. same precision
+    for name, q, sc, v in (("dgate", qg, sg, dg32), ("dup", qu, su, du32)):
+        oq, os_ = oracle.quantize_1x32(v.cpu().numpy())
+        assert np.array_equal(sc, os_), f"{what} {name}: scales differ from quantise(fp32 backward)"
+        nq = (oq & 0x7F) == 0x7F
+        assert np.array_equal((q & 0x7F) == 0x7F, nq), f"{what} {name}: NaN codes differ"
+        assert np.array_equal(q[~nq], oq[~nq]), f"{what} {name}: codes differ from quantise(fp32 backward)"
+    if use_w:
+        assert torch.equal(gs[4].t.view(torch.int32), wg32.view(torch.int32)), f"{what}: weight_grad differs"
+    # 2. from the inputs
+    g64, u64, dy64 = (f64_of(d[k]) for k in ("gate", "up", "dy"))
+    w64 = None if w is None else w.astype(np.float64)
+    rqg, rsg, rqu, rsu, _ = oracle.act_bwd_fp8(g64, u64, dy64, L, w64)
+    rdg, rdu, _ = oracle.act_bwd(g64, u64, dy64, L, w64)
+    for name, q, sc, rq, rs, rv in (("dgate", qg, sg, rqg, rsg, rdg), ("dup", qu, su, rqu, rsu, rdu)):
+        nan = (rq & 0x7F) == 0x7F
+        assert np.array_equal((q & 0x7F) == 0x7F, nan), f"{what} {name}: NaN positions differ from the oracle"
+        diff = sc != rs
+        if diff.any():
+            blocks = rv.astype(np.float32).astype(np.float64).reshape(R, C // 32, 32)
+            amax = np.where(np.isnan(blocks), 0, np.abs(blocks)).max(axis=2)[diff]
+            _, ex = np.frexp(amax)
+            bnd = 1.75 * np.exp2(ex - 1.0)
+            near = np.abs(amax - bnd) <= H_ULP_MAX * np.spacing(bnd.astype(np.float32)).astype(np.float64)
+            assert near.all(), f"{what} {name}: {int((~near).sum())} scale bytes differ away from a boundary"
+        same = np.repeat(~diff, 32, axis=1) & ~nan
+        dist = np.abs(oracle.e4m3_ordinal(q[same]) - oracle.e4m3_ordinal(rq[same]))
+        assert dist.max(initial=0) <= 1, f"{what} {name}: a code is {dist.max()} ulps from the oracle's"
+        log(f"{what} {name}: scale diffs {int(diff.sum())}, codes off by 1: {int((dist == 1).sum())} of {dist.size}")
+
+
+@pytest.mark.parametrize("bf", [True, False])
+@pytest.mark.parametrize("L,use_w", [(0.5, False), (math.inf, True), (7.0, True)])
+def test_act_bwd_fp8_full_4001x3584(bf, L, use_w):
+    d = (synth.act_bwd_bf16 if bf else synth.act_bwd_f32)(4001, 3584, seed=0)
+    check_act_bwd_fp8(d, L, use_w, f"act_bwd_fp8 {'bf16' if bf else 'f32'} L={L} w={use_w}")
+
+
+@pytest.mark.parametrize("bf", [True, False])
+@pytest.mark.parametrize("shape", [(1, 32), (3, 384), (7, 2048), (65, 96)])
+def test_act_bwd_fp8_ragged_and_specials(bf, shape):
+    d = (synth.act_bwd_bf16 if bf else synth.act_bwd_f32)(*shape, seed=13, specials=True)
+    for L, use_w in ((math.inf, True), (1.5, False)):
+        check_act_bwd_fp8(d, L, use_w, f"act_bwd_fp8 {shape} {'bf16' if bf else 'f32'} L={L} specials")
+
+
+def _load_bwd_fp8_cases():
+    with open(os.path.join(GOLDEN, "act_bwd_fp8_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _load_bwd_fp8_cases(), ids=lambda c: c["name"])
+def test_act_bwd_fp8_hand_cases_on_device(case):
+    """The hand-derived cases of tests/golden/act_bwd_fp8_cases.json, fp32
+    inputs, on the device: scales and codes as derived by hand."""
+    rows, cols = case["rows"], case["cols"]
+
+    def fill(spec):
+        a = np.full(rows * cols, _hexf(spec["fill"]), dtype=np.float64)
+        for k, v in spec.get("set", {}).items():
+            a[int(k)] = _hexf(v)
+        return a.astype(np.float32).reshape(rows, cols)
+    g, u, dy = fill(case["gate"]), fill(case["up"]), fill(case["dy"])
+    w = None if case["weights"] is None else dev_f32(np.array([_hexf(v) for v in case["weights"]], np.float32))
+    qg, sg, qu, su, wg = S.act_bwd_fp8(dev_f32(g), dev_f32(u), dev_f32(dy), _hexf(case["clamp"]), weights=w,
+                                       weight_grad=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(sg.cpu().numpy(), np.array(case["expect_dgate_scale"], dtype=np.uint8))
+    assert np.array_equal(su.cpu().numpy(), np.array(case["expect_dup_scale"], dtype=np.uint8))
+    for q, exp in ((qg, case["expect_dgate_codes"]), (qu, case["expect_dup_codes"])):
+        for i, c in enumerate(q.cpu().numpy().reshape(-1)):
+            want = exp.get(str(i), exp["default"])
+            if want == "nan":
+                assert (c & 0x7F) == 0x7F, (case["name"], i, hex(c))
+            else:
+                assert c == want, (case["name"], i, hex(c), want)
+    want = np.array([_hexf(v) for v in case["expect_weight_grad"]])
+    got = wg.cpu().numpy().astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.allclose(got[~nan], want[~nan], rtol=2 ** -22, atol=0)
 
 
 def test_act_bwd_without_weight_grad_and_empty():

@@ -519,6 +519,61 @@ def test_act_quant_hand_cases(case):
             assert c == want, (i, hex(c), hex(want))
 
 
+def load_act_bwd_fp8_cases():
+    with open(os.path.join(GOLDEN, "act_bwd_fp8_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+def _expect_codes(q, exp, what):
+    for i, c in enumerate(q.reshape(-1)):
+        want = exp.get(str(i), exp["default"])
+        if want == "nan":
+            assert (c & 0x7F) == 0x7F, (what, i, hex(c))
+        else:
+            assert c == want, (what, i, hex(c), hex(want))
+
+
+@pytest.mark.parametrize("case", load_act_bwd_fp8_cases(), ids=lambda c: c["name"])
+def test_act_bwd_fp8_hand_cases(case):
+    """The E4M3-output backward on hand-derived blocks (tests/golden): which
+    output is which, the factor SiLU'(0) = 1/2, the row weight, the clamp's
+    gradient stop, NaN passing, and the [rows, cols/32] scale layout."""
+    rows, cols = case["rows"], case["cols"]
+    gate = _fill(case["gate"], rows * cols).reshape(rows, cols).astype(np.float64)
+    up = _fill(case["up"], rows * cols).reshape(rows, cols).astype(np.float64)
+    dy = _fill(case["dy"], rows * cols).reshape(rows, cols).astype(np.float64)
+    w = None if case["weights"] is None else np.array([_hexf(v) for v in case["weights"]])
+    qg, sg, qu, su, wg = oracle.act_bwd_fp8(gate, up, dy, _hexf(case["clamp"]), w)
+    np.testing.assert_array_equal(sg, np.array(case["expect_dgate_scale"], dtype=np.uint8))
+    np.testing.assert_array_equal(su, np.array(case["expect_dup_scale"], dtype=np.uint8))
+    _expect_codes(qg, case["expect_dgate_codes"], "dgate")
+    _expect_codes(qu, case["expect_dup_codes"], "dup")
+    want = np.array([_hexf(v) for v in case["expect_weight_grad"]])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(wg), nan)
+    np.testing.assert_allclose(wg[~nan], want[~nan], rtol=1e-12, atol=0)
+
+
+def test_act_bwd_fp8_is_the_quantised_fp32_backward_on_random_blocks():
+    """On random inputs with specials the E4M3 backward equals, block by block,
+    a linear-search UE8M0 exponent and an exhaustive nearest-code search on the
+    once-rounded fp32 dgate and dup (brute force, not the oracle's encoder)."""
+    d = synth.act_bwd_f32(3, 64, seed=12, specials=True)
+    g, u, dy = (d[k].astype(np.float64) for k in ("gate", "up", "dy"))
+    qg, sg, qu, su, _ = oracle.act_bwd_fp8(g, u, dy, 1.5, d["weights"].astype(np.float64))
+    dg, du, _ = oracle.act_bwd(g, u, dy, 1.5, d["weights"].astype(np.float64))
+    for q, sc, v in ((qg, sg, dg), (qu, su, du)):
+        vb = v.astype(np.float32).astype(np.float64).reshape(3, 2, 32)
+        for r in range(3):
+            for b in range(2):
+                blk = vb[r, b]
+                fin = blk[~np.isnan(blk)]
+                amax = np.max(np.abs(fin)) if fin.size else 0.0
+                E = 128 if np.isinf(amax) else next(e for e in range(-127, 128) if amax <= 448.0 * 2.0 ** e)
+                assert sc[r, b] == E + 127
+                np.testing.assert_array_equal(q[r, b * 32:(b + 1) * 32], _encode_bruteforce(blk * 2.0 ** -E))
+
+
 def test_act_quant_random_blocks_vs_bruteforce():
     """Random blocks: every scale by linear search and every code by exhaustive search."""
     d = synth.act_quant_f32(4, 64, seed=3, specials=True)
