@@ -87,7 +87,7 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="headline only")
     p.add_argument("--only", default=None,
                    choices=["step", "fwd", "train_fwd", "train_bwd", "decode", "act_quant", "act_bwd", "fp32", "tiny",
-                            "traffic", "traffic_decode", "traffic_act_quant", "traffic_act_fwd", "traffic_act_bwd"],
+                            "fwd_k_sweep", "traffic", "traffic_decode", "traffic_act_quant", "traffic_act_fwd", "traffic_act_bwd"],
                    help="profiling aid: run one leg only (no JSON contract); 'traffic*' runs a kernel and a 1 GiB "
                         "copy (the counter calibration) for the --pmc runs")
     p.add_argument("--digest-traffic", nargs=3, metavar=("NAME", "FETCH_CSV", "WRITE_CSV"), default=None,
@@ -105,25 +105,33 @@ COPY_KERNEL_TAG = "copy"
 # headers it includes.
 FWD_KERNEL_SOURCES = ("common.hpp", "fp8.hpp", "gemm.hip", "gemm.hpp")
 
-# name -> (mangled-name fragment of the kernel, its translation unit, algorithmic bytes per launch)
+# name -> (name fragments of the kernel -- mangled, and as the profiler
+# demangles it --, its translation unit, algorithmic bytes per launch)
 TRAFFIC_KERNELS = {
     "fwd_dual_gemm_bf16_8192x14336x4096": (
-        "gemm_dma_kernelIDF16bLNS0_3EpiE0E", FWD_KERNEL_SOURCES,
+        ("gemm_dma_kernelIDF16bLNS0_3EpiE0E",), FWD_KERNEL_SOURCES,
         (M4 * K4 + 2 * N4 * K4 + M4 * N4) * 2),
     "gemv_bf16_M8_11008x4096": (
-        "gemv_kernelILi8ELNS_3ActE0ELb0E", ("common.hpp", "gemv.hip", "gemm.hpp"),
+        ("gemv_kernelILi8ELNS_3ActE0ELb0E", "gemv_kernel<8, (swg::Act)0, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
         2 * 11008 * 4096 * 2 + 8 * 4096 * 2 + 8 * 11008 * 2),
     "gemv_bf16_M1_11008x4096": (
-        "gemv_kernelILi1ELNS_3ActE0ELb0E", ("common.hpp", "gemv.hip", "gemm.hpp"),
+        ("gemv_kernelILi1ELNS_3ActE0ELb0E", "gemv_kernel<1, (swg::Act)0, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
         2 * 11008 * 4096 * 2 + 4096 * 2 + 11008 * 2),
+    "gemv_bf16_M8_24576x6144": (
+        ("gemv_phased_kernelILi8ELNS_3ActE0ELb0E", "gemv_phased_kernel<8, (swg::Act)0, false>"),
+        ("common.hpp", "gemv.hip", "gemm.hpp"),
+        2 * 24576 * 6144 * 2 + 8 * 6144 * 2 + 8 * 24576 * 2),
     "act_quant_4001x3584": (
-        "act_quant_kernelILNS_3ActE0ELb0ELb0ELb0ELb0E", ("common.hpp", "fp8.hpp", "act_quant.hip", "gemm.hpp"),
+        ("act_quant_kernelILNS_3ActE0ELb0ELb0ELb0ELb0E", "act_quant_kernel<(swg::Act)0, false, false, false, false>"),
+        ("common.hpp", "fp8.hpp", "act_quant.hip", "gemm.hpp"),
         2 * AQ_R * AQ_C * 4 + AQ_R * AQ_C + AQ_R * AQ_C // 32),
     "act_fwd_bf16_4001x3584": (
-        "act_fwd_kernelILNS_3ActE0EDF16bLb0ELb0E", ("common.hpp", "fp8.hpp", "act_fwd.hip", "gemm.hpp"),
+        ("act_fwd_kernelILNS_3ActE0EDF16bLb0ELb0E", "act_fwd_kernel<(swg::Act)0, __bf16, false, false>"),
+        ("common.hpp", "fp8.hpp", "act_fwd.hip", "gemm.hpp"),
         2 * AQ_R * AQ_C * 4 + AQ_R * AQ_C * 2),
     "act_bwd_f32_4001x3584": (
-        "act_bwd_flat_kernelIfLb1ELb0E", ("common.hpp", "act_bwd.hip", "gemm.hpp"),
+        ("act_bwd_flat_kernelIfLb1ELb0E", "act_bwd_flat_kernel<float, true, false, false>"),
+        ("common.hpp", "act_bwd.hip", "gemm.hpp"),
         5 * AQ_R * AQ_C * 4),
 }
 
@@ -149,7 +157,7 @@ def digest_traffic(name: str, fetch_csv: str, write_csv: str) -> None:
     WRITE_SIZE counters (KiB per dispatch), each scaled by (known bytes /
     counter reading) of a plain 1 GiB copy measured in the same run."""
     import csv
-    tag, files, algo = TRAFFIC_KERNELS[name]
+    tags, files, algo = TRAFFIC_KERNELS[name]
 
     def per_kernel(path, counter):
         vals = {}
@@ -157,12 +165,17 @@ def digest_traffic(name: str, fetch_csv: str, write_csv: str) -> None:
             if r["Counter_Name"] != counter:
                 continue
             kname = r["Kernel_Name"]
-            key = "k" if tag in kname else ("copy" if COPY_KERNEL_TAG in kname else None)
+            key = "k" if any(t in kname for t in tags) else ("copy" if COPY_KERNEL_TAG in kname else None)
             if key is None:
                 continue
             vals.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
             vals[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
-        return {k: sum(v.values()) / len(v) for k, v in vals.items()}
+        # The kernel: mean over its dispatches.  The calibration: the 1 GiB
+        # copies, the largest copy dispatches (a leg's own buffer clones are
+        # copies too, and smaller).
+        copies = sorted(vals.get("copy", {}).values())
+        top = [v for v in copies if v >= 0.9 * copies[-1]]
+        return {"k": sum(vals["k"].values()) / len(vals["k"]), "copy": sum(top) / len(top)}
 
     f = per_kernel(fetch_csv, "FETCH_SIZE")
     w = per_kernel(write_csv, "WRITE_SIZE")
@@ -204,6 +217,17 @@ def load_traffic(name: str):
     if not e or e.get("source_hash") != kernel_source_hash(files):
         return None
     return e.get("bytes_per_launch")
+
+
+def traffic_table():
+    """Every counter-measured kernel whose sources are unchanged since the
+    measurement: HBM bytes per launch against its algorithmic bytes."""
+    out = {}
+    for name, (_, _, algo) in TRAFFIC_KERNELS.items():
+        b = load_traffic(name)
+        if b is not None:
+            out[name] = {"bytes": b, "algorithmic": algo, "ratio": round(b / algo, 3)}
+    return out
 
 
 # ------------------------------------------------------------------ timing protocol
@@ -352,10 +376,11 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
     ctx["to_dev_bf16"] = to_dev_bf16
 
-    if args.only in ("decode", "act_quant", "act_bwd", "fp32", "tiny", "traffic_decode", "traffic_act_quant",
-                     "traffic_act_fwd", "traffic_act_bwd"):
+    if args.only in ("decode", "act_quant", "act_bwd", "fp32", "tiny", "fwd_k_sweep", "traffic_decode",
+                     "traffic_act_quant", "traffic_act_fwd", "traffic_act_bwd"):
         leg = {"decode": decode_leg, "act_quant": act_quant_leg, "act_bwd": act_bwd_leg, "fp32": fp32_leg,
-               "tiny": tiny_leg, "traffic_decode": traffic_decode, "traffic_act_quant": traffic_act_quant,
+               "tiny": tiny_leg, "fwd_k_sweep": fwd_k_sweep_leg,
+               "traffic_decode": traffic_decode, "traffic_act_quant": traffic_act_quant,
                "traffic_act_fwd": traffic_act_fwd, "traffic_act_bwd": traffic_act_bwd}[args.only]
         res = leg(ctx)
         if args.only.startswith("traffic"):
@@ -480,6 +505,7 @@ def main():
                      "calls_per_graph": args.iters, "calls_per_graph_gemm": args.gemm_iters,
                      "timing": "HIP events around each graph launch; per-call time = graph time / calls",
                      "eager": "3 x (calls per graph) eager calls, events around each batch"},
+        "traffic_by_kernel": traffic_table(),
         "legs": {},
         "oracle": {},
     }
@@ -679,6 +705,10 @@ def act_quant_leg(ctx, oracle_times=None):
     variants = {
         "no_clamp": [(lambda i=i: S.act_quant(G[i], U[i], math.inf, out=outs[i])) for _ in range(reps) for i in range(copies)],
         "clamp_7": [(lambda i=i: S.act_quant(G[i], U[i], 7.0, out=outs[i])) for _ in range(reps) for i in range(copies)],
+        # The clamp without its count: the difference to clamp_7 is what the
+        # count costs (its zeroing launch and the per-workgroup atomics).
+        "clamp_7_no_count": [(lambda i=i: S.act_quant(G[i], U[i], 7.0, out=(outs[i][0], outs[i][1], None, None)))
+                             for _ in range(reps) for i in range(copies)],
         "no_clamp_geglu": [(lambda i=i: S.act_quant(G[i], U[i], math.inf, out=outs[i], act="gelu_tanh"))
                            for _ in range(reps) for i in range(copies)],
         "stream_twin": [(lambda i=i: S.probe_act_quant_stream(G[i], U[i], outs[i][0], outs[i][1]))
@@ -841,21 +871,53 @@ def tiny_leg(ctx, oracle_times=None):
     return {"M": 4, "N": 128, "K": 64, "variants": st}
 
 
+def fwd_k_sweep_leg(ctx, oracle_times=None):
+    """The bf16 forward at M = 8192, N = 14336 and K = 1024 .. 8192, and the
+    least-squares line t = a + b K through the p50 times: a is the part of a
+    launch that does not scale with the reduction (ring prologue, epilogue,
+    workgroup turnover)."""
+    torch, S, np, P, args = ctx["torch"], ctx["S"], ctx["np"], ctx["P"], ctx["args"]
+    dev = ctx["dev"]
+    M, N = M4, N4
+    g = torch.Generator(device=dev).manual_seed(0)
+    times = {}
+    for K in (1024, 2048, 4096, 8192):
+        x = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
+        wg = (torch.randn(N, K, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+        wu = (torch.randn(N, K, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+        h = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        st = P.run({"fwd": [lambda: S.fwd(x, wg, wu, out=h)] * args.gemm_iters})
+        times[K] = st["fwd"]["p50_us"]
+        log(f"fwd K={K}: {times[K] / 1e3:.4f} ms, {4 * M * N * K / times[K] / 1e6:.1f} TFLOP/s")
+        del x, wg, wu, h
+        torch.cuda.empty_cache()
+    ks = np.array(sorted(times), dtype=np.float64)
+    b, a = np.polyfit(ks, np.array([times[int(k)] for k in ks]), 1)
+    log(f"fit: t = {a:.1f} us + {b * 1000:.1f} us per 1000 K; fixed share at K = {K4}: {a / times[K4]:.3f}")
+    return {"M": M, "N": N, "p50_us": times, "intercept_us": round(a, 2), "us_per_1000_K": round(b * 1000, 2)}
+
+
 # ------------------------------------------------------------------ traffic legs (counter runs)
 
 def traffic_decode(ctx):
-    """gemv at (11008, 4096), M = 1 and 8, 4 rotated copies, a few calls each."""
+    """gemv at (11008, 4096), M = 1 and 8 (x staged whole), 4 rotated copies,
+    and at (24576, 6144), M = 8 (x staged in phases), 2 copies; a few calls
+    each."""
     torch, S, synth = ctx["torch"], ctx["S"], ctx["synth"]
-    d = synth.decode_bf16(8, 11008, 4096, seed=0)
-    wg0, wu0 = ctx["to_dev_bf16"](d["wg"]), ctx["to_dev_bf16"](d["wu"])
-    W = [(wg0.clone(), wu0.clone()) for _ in range(4)]
-    for M in (1, 8):
-        x = ctx["to_dev_bf16"](d["x"][:M].copy())
-        o = torch.empty((M, 11008), dtype=torch.bfloat16, device=ctx["dev"])
-        for _ in range(2):
-            for a, b in W:
-                S.gemv_fwd(x, a, b, out=o)
-    torch.cuda.synchronize()
+    for (N, K, copies, Ms) in ((11008, 4096, 4, (1, 8)), (24576, 6144, 2, (8,))):
+        d = synth.decode_bf16(8, N, K, seed=0)
+        wg0, wu0 = ctx["to_dev_bf16"](d["wg"]), ctx["to_dev_bf16"](d["wu"])
+        W = [(wg0.clone(), wu0.clone()) for _ in range(copies)]
+        del wg0, wu0
+        for M in Ms:
+            x = ctx["to_dev_bf16"](d["x"][:M].copy())
+            o = torch.empty((M, N), dtype=torch.bfloat16, device=ctx["dev"])
+            for _ in range(2):
+                for a, b in W:
+                    S.gemv_fwd(x, a, b, out=o)
+        torch.cuda.synchronize()
+        del W
+        torch.cuda.empty_cache()
     return None
 
 

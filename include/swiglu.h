@@ -48,7 +48,7 @@ enum swiglu_status {
   SWIGLU_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
   SWIGLU_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
   SWIGLU_ERR_ARG = 6,         /* any other invalid argument (e.g. clamp limit)  */
-  SWIGLU_ERR_UNSUPPORTED = 7, /* valid request this build does not implement    */
+  SWIGLU_ERR_UNSUPPORTED = 7, /* valid request the library does not implement   */
   SWIGLU_ERR_HIP = 8,         /* a HIP launch failed; see swiglu_last_hip_error */
   SWIGLU_ERR_SCRATCH = 9      /* needs more scratch than swiglu_bwd_noalloc's
                                  static buffer (SWIGLU_NOALLOC_SCRATCH_BYTES)  */
@@ -207,10 +207,8 @@ int swiglu_bwd_noalloc(int act, int dtype, int64_t M, int64_t N, int64_t K,
  * primitive for M = 1, 2, 4, 8 bound by the cold weight read).
  *
  *   x [M, K], wg/wu [N, K] (bf16 inputs), h [M, N] (bf16 output)
- * Layout rule: K % 8 == 0 and M * K * 2 <= 163840 (x is staged in one
- * workgroup's 160 KiB of LDS: K <= 10240 at M = 8, which covers the
- * page's LLaMA-2 7B/13B, LLaMA-3 8B and GPT-NeoX-20B up/gate shapes);
- * larger x gives SWIGLU_ERR_UNSUPPORTED. */
+ * Layout rule: K % 8 == 0; no other limit on K (x is staged through LDS in
+ * phases along K). */
 int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K,
                     const void* x, const void* wg, const void* wu, void* h,
                     void* stream);
@@ -260,7 +258,8 @@ int swiglu_fwd_fp8(int act, int64_t M, int64_t N, int64_t K,
  *   clamp_limit  L > 0, or +INFINITY for no clamp (NaN or L <= 0: error)
  *   h            [rows, cols] output
  *   clamp_count  NULL, or one uint64 (8-byte aligned) overwritten with the
- *                number of gate and up values with |v| > L (NaN not counted)
+ *                number of gate and up values with |v| > L (NaN not counted);
+ *                counted as in swiglu_act_quant
  * Layout rule: cols % 8 == 0.  Unknown act: SWIGLU_ERR_ARG; unknown
  * out_dtype: SWIGLU_ERR_DTYPE. */
 int swiglu_act_fwd(int act, int out_dtype, int64_t rows, int64_t cols,
@@ -283,7 +282,12 @@ int swiglu_act_fwd(int act, int out_dtype, int64_t rows, int64_t cols,
  *   q            [rows, cols] uint8 E4M3FN codes (output)
  *   scale        [rows, cols / 32] uint8 UE8M0 bytes (output)
  *   clamp_count  NULL, or one uint64 overwritten with the number of gate and
- *                up values with |v| > L (NaN not counted)
+ *                up values with |v| > L (NaN not counted).  With the clamp on,
+ *                each workgroup's count goes to a slot of a library-owned
+ *                device array and a second launch sums the slots into
+ *                *clamp_count.  Counting calls take the array's 16 regions
+ *                in turn, so at most 16 counting calls of this function
+ *                and swiglu_act_fwd may be in flight on one GPU at once.
  *   h_out        NULL, or [rows, cols] fp32 that also receives h itself (the
  *                page's kernel likewise keeps a non-quantised output mode)
  * Layout rule: cols % 32 == 0 (the 1x32 blocks tile each row). */
@@ -357,7 +361,7 @@ int swiglu_act_bwd_fp8(int dtype, int64_t rows, int64_t cols,
                        float* weight_grad, void* stream);
 
 /* Measurement aid: the decode kernel's read-only twin.  The same launch as
- * swiglu_gemv_fwd for (M, N, K) -- grid, LDS footprint, staging of x and
+ * swiglu_gemv_fwd for (M, N, K) -- grid, LDS footprint, phased staging of x and
  * every weight load, in the same order and unrolling -- with no arithmetic:
  * the loaded words are folded into one uint32 per column, written to
  * `sink` [N].  Its time is the floor of the decode kernel's access pattern
@@ -395,7 +399,7 @@ int swiglu_probe_fp8_transitions(int kind, uint32_t first, uint32_t last, uint32
 
 /* Measurement aid: a pure streaming read of two device buffers of `bytes`
  * bytes each (16-byte multiples), the cold-read floor against which the
- * decode kernel is judged ("Fused SwiGLU benchmark", section HBM
+ * decode kernel is measured ("Fused SwiGLU benchmark", section HBM
  * re-measurement: the fused kernel is compared with a dual-stream pure-read
  * loop over rotated weight copies).  Writes one word per workgroup to `sink`
  * (>= 4096 uint32 words) so the reads cannot be elided. */

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libswiglu.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "gemm.hip", "transpose.hip", "gemv.hip", "act_fwd.hip", "act_quant.hip", "act_bwd.hip",
-           "probe.hip"]
+           "count.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

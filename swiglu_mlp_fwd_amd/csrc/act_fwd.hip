@@ -12,7 +12,8 @@
 // Mapping as in the quantiser: the array is flat (the activation is
 // elementwise), each lane takes 8 consecutive elements (two 16-byte loads
 // per input) with kUnroll chunks' loads issued before any is used; the clamp
-// count is reduced per workgroup and added with one atomic.
+// count is reduced per workgroup into the workgroup's slot and the slots are
+// summed by a second launch (count.hip).
 #include "common.hpp"
 #include "fp8.hpp"
 #include "gemm.hpp"
@@ -22,8 +23,8 @@ namespace swg {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxBlocks = 1024;       // with the count: one same-address atomic per workgroup
-constexpr int kMaxBlocksFree = 8192;   // without it
+constexpr int kMaxBlocks = 8192;
+static_assert(kMaxBlocks <= kCountSlots, "one count slot per workgroup");
 constexpr int kUnroll = 4;
 
 template <typename TO> __device__ __forceinline__ void store8(TO* h, int64_t c, const double (&v)[8]);
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void act_fwd_kernel(const float* __restri
                                                            const float* __restrict__ up, float L,
                                                            TO* __restrict__ h,
                                                            unsigned long long* __restrict__ count,
-                                                           int64_t nchunks) {
+                                                           uint32_t* __restrict__ slots, int64_t nchunks) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   uint32_t cnt = 0;
   if (!kCount && count != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *count = 0ull;
@@ -92,24 +93,25 @@ __global__ __launch_bounds__(kThreads) void act_fwd_kernel(const float* __restri
       uint32_t t = 0;
 #pragma unroll
       for (int w = 0; w < kThreads / 64; ++w) t += wsum[w];
-      if (t != 0) atomicAdd(count, (unsigned long long)t);
+      slots[blockIdx.x] = t;
     }
   }
 }
 
-__global__ void zero_count_kernel(unsigned long long* p) { *p = 0ull; }
-
 template <Act A, typename TO>
 void launch_typed(bool counting, bool clamp, unsigned grid, const float* gate, const float* up, float L,
-                  void* h, uint64_t* count, int64_t nchunks, hipStream_t s) {
+                  void* h, uint64_t* count, uint32_t* slots, int64_t nchunks, hipStream_t s) {
   auto* cnt = reinterpret_cast<unsigned long long*>(count);
   TO* out = static_cast<TO*>(h);
   if (counting)
-    hipLaunchKernelGGL((act_fwd_kernel<A, TO, true, true>), dim3(grid), dim3(kThreads), 0, s, gate, up, L, out, cnt, nchunks);
+    hipLaunchKernelGGL((act_fwd_kernel<A, TO, true, true>), dim3(grid), dim3(kThreads), 0, s, gate, up, L, out, cnt,
+                       slots, nchunks);
   else if (clamp)
-    hipLaunchKernelGGL((act_fwd_kernel<A, TO, true, false>), dim3(grid), dim3(kThreads), 0, s, gate, up, L, out, cnt, nchunks);
+    hipLaunchKernelGGL((act_fwd_kernel<A, TO, true, false>), dim3(grid), dim3(kThreads), 0, s, gate, up, L, out, cnt,
+                       slots, nchunks);
   else
-    hipLaunchKernelGGL((act_fwd_kernel<A, TO, false, false>), dim3(grid), dim3(kThreads), 0, s, gate, up, L, out, cnt, nchunks);
+    hipLaunchKernelGGL((act_fwd_kernel<A, TO, false, false>), dim3(grid), dim3(kThreads), 0, s, gate, up, L, out, cnt,
+                       slots, nchunks);
 }
 
 }  // namespace
@@ -118,21 +120,27 @@ hipError_t launch_act_fwd(Act act, Dt out, int64_t rows, int64_t cols, const flo
                           float limit, bool clamp, void* h, uint64_t* count, hipStream_t s) {
   const bool counting = clamp && count != nullptr;
   const int64_t nchunks = rows * cols / 8;
-  if (counting || (count != nullptr && nchunks == 0))
-    hipLaunchKernelGGL(zero_count_kernel, dim3(1), dim3(1), 0, s, reinterpret_cast<unsigned long long*>(count));
-  if (nchunks > 0) {
-    const int64_t want = (nchunks + kThreads - 1) / kThreads;
-    const int64_t cap = counting ? kMaxBlocks : kMaxBlocksFree;
-    const unsigned grid = (unsigned)(want < cap ? want : cap);
-    if (act == Act::kGeluTanh) {
-      if (out == Dt::kBF16) launch_typed<Act::kGeluTanh, bf16>(counting, clamp, grid, gate, up, limit, h, count, nchunks, s);
-      else launch_typed<Act::kGeluTanh, float>(counting, clamp, grid, gate, up, limit, h, count, nchunks, s);
-    } else {
-      if (out == Dt::kBF16) launch_typed<Act::kSilu, bf16>(counting, clamp, grid, gate, up, limit, h, count, nchunks, s);
-      else launch_typed<Act::kSilu, float>(counting, clamp, grid, gate, up, limit, h, count, nchunks, s);
-    }
+  if (nchunks == 0) {
+    // Nothing to walk: a given counter receives 0.
+    return count != nullptr ? launch_count_sum(nullptr, 0, count, s) : hipSuccess;
   }
-  return hipGetLastError();
+  uint32_t* slots = nullptr;
+  if (counting) {
+    const hipError_t e = count_slots(&slots);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t want = (nchunks + kThreads - 1) / kThreads;
+  const unsigned grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);
+  if (act == Act::kGeluTanh) {
+    if (out == Dt::kBF16) launch_typed<Act::kGeluTanh, bf16>(counting, clamp, grid, gate, up, limit, h, count, slots, nchunks, s);
+    else launch_typed<Act::kGeluTanh, float>(counting, clamp, grid, gate, up, limit, h, count, slots, nchunks, s);
+  } else {
+    if (out == Dt::kBF16) launch_typed<Act::kSilu, bf16>(counting, clamp, grid, gate, up, limit, h, count, slots, nchunks, s);
+    else launch_typed<Act::kSilu, float>(counting, clamp, grid, gate, up, limit, h, count, slots, nchunks, s);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !counting) return e;
+  return launch_count_sum(slots, (int)grid, count, s);
 }
 
 }  // namespace swg

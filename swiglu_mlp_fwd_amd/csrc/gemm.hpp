@@ -83,6 +83,13 @@ hipError_t launch_gemv(Act act, int M, int N, int K, const void* x, const void* 
 hipError_t launch_gemv_read_twin(int M, int N, int K, const void* x, const void* wg, const void* wu,
                                  uint32_t* sink, hipStream_t s);
 
+// Clamp counts without same-address atomics (count.hip): a counting launch
+// of at most kCountSlots workgroups writes workgroup b's count to slots[b],
+// then launch_count_sum adds slots[0, nblocks) into *count (overwriting it).
+constexpr int kCountSlots = 8192;
+hipError_t count_slots(uint32_t** slots);   // this call's slots on the current device
+hipError_t launch_count_sum(const uint32_t* slots, int nblocks, uint64_t* count, hipStream_t s);
+
 hipError_t launch_act_bwd(Dt dt, int64_t rows, int64_t cols, const void* gate, const void* up,
                           const void* dy, const float* weights, float limit, bool clamp,
                           void* dgate, void* dup, float* wgrad, hipStream_t s);

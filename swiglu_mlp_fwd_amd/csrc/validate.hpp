@@ -136,16 +136,12 @@ inline int validate_bwd(int dtype, int64_t M, int64_t N, int64_t K, const void* 
   return SWIGLU_OK;
 }
 
-// The decode kernel stages x [M, K] (bf16) in one workgroup's LDS.
-constexpr int64_t kMaxGemvX = 160 * 1024;
-
 inline int validate_gemv(int64_t M, int64_t N, int64_t K, const void* x, const void* wg,
                          const void* wu, const void* h) {
   if (M < 0 || M > 8) return SWIGLU_ERR_SHAPE;
   int st = check_dims(M, N, K);
   if (st) return st;
   if (K % 8 != 0) return SWIGLU_ERR_SHAPE;
-  if (M * K * 2 > kMaxGemvX) return SWIGLU_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return SWIGLU_OK;
   if ((st = check_ptr(h))) return st;
   if (K > 0) {

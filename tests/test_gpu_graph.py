@@ -71,7 +71,10 @@ def test_training_step_and_quantiser_replay_in_a_graph():
         torch.cuda.synchronize()
         for i, (got, want) in enumerate(zip(captured, eager)):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {rep}, output {i}"
-        # eager work between replays
+        # eager work between replays, counting calls among it (they take the
+        # other regions of the library's count slots)
         _ = S.fwd(x, wg, wu)
+        for _ in range(rep + 1):
+            _ = S.act_quant(gate, up, 0.5)
         torch.cuda.synchronize()
     assert math.isfinite(float(eager[0].float().abs().max()))
