@@ -106,21 +106,21 @@ COPY_KERNEL_TAG = "copy"
 FWD_KERNEL_SOURCES = ("common.hpp", "fp8.hpp", "gemm.hip", "gemm.hpp")
 
 # name -> (name fragments of the kernel -- mangled, and as the profiler
-# demangles it --, its translation unit, algorithmic bytes per launch)
+# demangles it --, its translation unit, algorithmic bytes per launch[, grid
+# size in work-items, where one kernel serves several measured shapes])
 TRAFFIC_KERNELS = {
     "fwd_dual_gemm_bf16_8192x14336x4096": (
         ("gemm_dma_kernelIDF16bLNS0_3EpiE0E",), FWD_KERNEL_SOURCES,
         (M4 * K4 + 2 * N4 * K4 + M4 * N4) * 2),
     "gemv_bf16_M8_11008x4096": (
-        ("gemv_kernelILi8ELNS_3ActE0ELb0E", "gemv_kernel<8, (swg::Act)0, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
-        2 * 11008 * 4096 * 2 + 8 * 4096 * 2 + 8 * 11008 * 2),
+        ("gemv_mfma_kernelILNS_3ActE0ELb0E", "gemv_mfma_kernel<(swg::Act)0, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
+        2 * 11008 * 4096 * 2 + 8 * 4096 * 2 + 8 * 11008 * 2, 11008 // 16 * 512),
     "gemv_bf16_M1_11008x4096": (
         ("gemv_kernelILi1ELNS_3ActE0ELb0E", "gemv_kernel<1, (swg::Act)0, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
         2 * 11008 * 4096 * 2 + 4096 * 2 + 11008 * 2),
     "gemv_bf16_M8_24576x6144": (
-        ("gemv_phased_kernelILi8ELNS_3ActE0ELb0E", "gemv_phased_kernel<8, (swg::Act)0, false>"),
-        ("common.hpp", "gemv.hip", "gemm.hpp"),
-        2 * 24576 * 6144 * 2 + 8 * 6144 * 2 + 8 * 24576 * 2),
+        ("gemv_mfma_kernelILNS_3ActE0ELb0E", "gemv_mfma_kernel<(swg::Act)0, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
+        2 * 24576 * 6144 * 2 + 8 * 6144 * 2 + 8 * 24576 * 2, 24576 // 16 * 512),
     "act_quant_4001x3584": (
         ("act_quant_kernelILNS_3ActE0ELb0ELb0ELb0ELb0E", "act_quant_kernel<(swg::Act)0, false, false, false, false>"),
         ("common.hpp", "fp8.hpp", "act_quant.hip", "gemm.hpp"),
@@ -157,7 +157,8 @@ def digest_traffic(name: str, fetch_csv: str, write_csv: str) -> None:
     WRITE_SIZE counters (KiB per dispatch), each scaled by (known bytes /
     counter reading) of a plain 1 GiB copy measured in the same run."""
     import csv
-    tags, files, algo = TRAFFIC_KERNELS[name]
+    tags, files, algo = TRAFFIC_KERNELS[name][:3]
+    grid = TRAFFIC_KERNELS[name][3] if len(TRAFFIC_KERNELS[name]) > 3 else None
 
     def per_kernel(path, counter):
         vals = {}
@@ -165,7 +166,8 @@ def digest_traffic(name: str, fetch_csv: str, write_csv: str) -> None:
             if r["Counter_Name"] != counter:
                 continue
             kname = r["Kernel_Name"]
-            key = "k" if any(t in kname for t in tags) else ("copy" if COPY_KERNEL_TAG in kname else None)
+            mine = any(t in kname for t in tags) and (grid is None or int(r["Grid_Size"]) == grid)
+            key = "k" if mine else ("copy" if COPY_KERNEL_TAG in kname else None)
             if key is None:
                 continue
             vals.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
@@ -223,7 +225,8 @@ def traffic_table():
     """Every counter-measured kernel whose sources are unchanged since the
     measurement: HBM bytes per launch against its algorithmic bytes."""
     out = {}
-    for name, (_, _, algo) in TRAFFIC_KERNELS.items():
+    for name, entry in TRAFFIC_KERNELS.items():
+        algo = entry[2]
         b = load_traffic(name)
         if b is not None:
             out[name] = {"bytes": b, "algorithmic": algo, "ratio": round(b / algo, 3)}

@@ -201,14 +201,15 @@ int swiglu_bwd_noalloc(int act, int dtype, int64_t M, int64_t N, int64_t K,
 
 /* Decode forward for 1 <= M <= 8 tokens, bf16 only: the same h as
  * swiglu_fwd, computed by a weight-streaming kernel that reads each row of
- * Wg and Wu from HBM once for all M tokens and reduces on the vector units
- * ("Fused SwiGLU benchmark", AstrAI docs/developer/swiglu_benchmark.md,
- * sections L20 findings and HBM re-measurement: a fused BF16 SwiGLU
- * primitive for M = 1, 2, 4, 8 bound by the cold weight read).
+ * Wg and Wu from HBM once for all M tokens ("Fused SwiGLU benchmark",
+ * AstrAI docs/developer/swiglu_benchmark.md, sections L20 findings and HBM
+ * re-measurement: a fused BF16 SwiGLU primitive for M = 1, 2, 4, 8 bound by
+ * the cold weight read).  M <= 3 reduces on the vector units, M >= 4 on the
+ * matrix cores; fp32 accumulation in a fixed order either way, so results
+ * are deterministic.
  *
  *   x [M, K], wg/wu [N, K] (bf16 inputs), h [M, N] (bf16 output)
- * Layout rule: K % 8 == 0; no other limit on K (x is staged through LDS in
- * phases along K). */
+ * Layout rule: K % 8 == 0; no other limit on K. */
 int swiglu_gemv_fwd(int64_t M, int64_t N, int64_t K,
                     const void* x, const void* wg, const void* wu, void* h,
                     void* stream);
@@ -361,10 +362,10 @@ int swiglu_act_bwd_fp8(int dtype, int64_t rows, int64_t cols,
                        float* weight_grad, void* stream);
 
 /* Measurement aid: the decode kernel's read-only twin.  The same launch as
- * swiglu_gemv_fwd for (M, N, K) -- grid, LDS footprint, phased staging of x and
- * every weight load, in the same order and unrolling -- with no arithmetic:
- * the loaded words are folded into one uint32 per column, written to
- * `sink` [N].  Its time is the floor of the decode kernel's access pattern
+ * swiglu_gemv_fwd for (M, N, K) -- the same kernel's grid, LDS footprint,
+ * x loads and weight loads (and, for M >= 4, the weights' trip through LDS),
+ * in the same order and unrolling -- with no arithmetic: sink[n] receives
+ * the XOR of every 32-bit word of Wg[n, :] and Wu[n, :], for sink [N].  Its time is the floor of the decode kernel's access pattern
  * on the same buffers ("Fused SwiGLU benchmark", section HBM
  * re-measurement: the fused kernel against a pure-read loop over the same
  * rotated weights).  Arguments and errors as swiglu_gemv_fwd (sink in place

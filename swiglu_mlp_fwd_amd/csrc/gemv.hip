@@ -1,30 +1,32 @@
-// Decode forward, 1 <= M <= 8 tokens, bf16: h = SiLU(x Wg^T) * (x Wu^T).
+// Decode forward, 1 <= M <= 8 tokens, bf16: h = act(x Wg^T) * (x Wu^T).
 //
 // The work is bound by reading Wg and Wu from HBM once ("Fused SwiGLU
 // benchmark", AstrAI docs/developer/swiglu_benchmark.md, sections L20
 // findings and HBM re-measurement: the wide shapes are weight-bandwidth
 // dominated and the fused kernel sits at the dual-stream cold-read floor).
-// No matrix cores: the dot products run on the vector ALU with the bf16 dot2
-// instruction (two bf16 products accumulated into fp32 per lane-op).
+// Two kernels, each streaming every weight row once for all M tokens:
 //
-// Mapping: each half-wave (32 lanes) owns one output column n and streams
-// the rows Wg[n, :] and Wu[n, :] with 16-byte loads (lane j reads chunks
-// j, j+32, ...); x [M, K] is staged in LDS and each 16-byte chunk of it is
-// reused for both weights.  Per lane the 2M partial sums are reduced across
-// the half-wave with butterfly shuffles; lane 0 of the half applies
-// act(g) * u and stores the M outputs of its column.
+// M <= 3, vector ALU: each half-wave (32 lanes) owns one output column n
+// and streams the rows Wg[n, :] and Wu[n, :] with 16-byte loads (lane j
+// reads chunks j, j+32, ...), 512 contiguous bytes per row per instruction;
+// x [M, K] is staged in LDS and each 16-byte chunk of it is reused for both
+// weights.  The dot products use the bf16 dot2 instruction (two bf16
+// products into fp32 per lane-op); per lane the 2M partial sums are reduced
+// across the half-wave with butterfly shuffles, and lane 0 of the half
+// applies act(g) * u and stores the M outputs of its column.  x up to
+// 64 KiB is staged whole, larger x in K-phases of at most about 36 KiB
+// (stage x[:, phase], stream that phase's weights, move on), so there is no
+// limit on K.
 //
-// x up to 64 KiB (M K <= 32768) is staged whole; larger x in K-phases of at
-// most about 36 KiB: the workgroup stages x[:, phase], streams the weights
-// of that phase, and moves on.  Then four workgroups (32 waves, the most a
-// CU holds) share a CU's 160 KiB of LDS whatever K is, where x staged whole
-// at M = 8, K = 6144 (96 KiB) left one.  There is no limit on K.
+// M >= 4, matrix cores: see gemv_mfma_kernel below.  From M = 4 the vector
+// ALU kernel is bound by its M LDS reads of x and 8 M dot2 per 16-byte
+// weight chunk; the matrix cores take a whole 16 x 16 x 32 product per
+// instruction.
 //
-// The read-only twin (kTwin) is the same kernel with the same grid, LDS
-// footprint, x staging and weight loads, and no arithmetic: each lane folds
-// the loaded words into one value.  Its time is the floor of this access
-// pattern, the counterpart on the same buffers of the benchmark page's
-// pure-read loop.
+// Each kernel has a read-only twin (kTwin): the same grid, LDS footprint,
+// staging and loads, and no arithmetic; each lane folds the loaded weight
+// words into one value.  Its time is the floor of that access pattern, the
+// counterpart on the same buffers of the benchmark page's pure-read loop.
 #include "common.hpp"
 #include "gemm.hpp"
 
@@ -32,17 +34,13 @@ namespace swg {
 
 namespace {
 
-// 8 waves: x is staged once per 16 columns.
+// Vector-ALU kernel: 8 waves, x is staged once per 16 columns.
 constexpr int kThreads = 512;
 constexpr int kColsPerBlock = 16;  // 8 waves x 2 half-waves
 // x up to this size is staged whole (at 64 KiB two workgroups still share
 // a CU); beyond it, in phases of at most kPhaseBytes (four per CU).
 constexpr int kWholeBytes = 64 * 1024;
 constexpr int kPhaseBytes = 36 * 1024;
-
-// x exchanged across the half-waves (measured faster from M = 6 up; below,
-// the extra exchange costs more than the LDS reads it saves).
-template <int M> constexpr bool kSplitX = M >= 6 && M % 2 == 0;
 
 // One half-wave's pass over chunks [0, nc) of its column's weight rows
 // rg, ru, against x chunks xs[m * stride + c]: dot products into ag, au,
@@ -53,46 +51,15 @@ __device__ __forceinline__ void stream_chunks(const u32x4* __restrict__ rg, cons
                                               float (&ag)[M], float (&au)[M], uint32_t& fold) {
   const int hl = lane & 31;
   if constexpr (kTwin) {
-    // The weight stream of the branch below that this M takes (same loads,
-    // same unrolling), folded into one word.
+    // The weight stream of the branch below (same loads, same unrolling),
+    // folded into one word.
     auto eat = [&](int c) {
       const u32x4 vg = __builtin_nontemporal_load(rg + c);
       const u32x4 vu = __builtin_nontemporal_load(ru + c);
       fold ^= vg[0] ^ vg[1] ^ vg[2] ^ vg[3] ^ vu[0] ^ vu[1] ^ vu[2] ^ vu[3];
     };
-    if constexpr (kSplitX<M>) {
-#pragma unroll 2
-      for (int c = hl; c < nc; c += 32) eat(c);
-    } else {
 #pragma unroll 4
-      for (int c = hl; c < nc; c += 32) eat(c);
-    }
-  } else if constexpr (kSplitX<M>) {
-    // The two half-waves read the same x chunks.  Each reads half of the
-    // M rows (the lower half rows 0..M/2-1, the upper half the rest) and
-    // v_permlane32_swap hands every lane both halves' values: half the LDS
-    // reads of x per weight chunk.
-    constexpr int H = M / 2;
-    const int mb = (lane >> 5) * H;
-#pragma unroll 2
-    for (int c = hl; c < nc; c += 32) {
-      const u32x4 vg = __builtin_nontemporal_load(rg + c);
-      const u32x4 vu = __builtin_nontemporal_load(ru + c);
-#pragma unroll
-      for (int q = 0; q < H; ++q) {
-        const u32x4 xv = xs[(mb + q) * stride + c];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          // r[0]: the lower half's value (row q), r[1]: the upper half's (row H + q).
-          const auto r = __builtin_amdgcn_permlane32_swap(xv[t], xv[t], false, false);
-          const bf16x2 lo = as_bf16x2(r[0]), hi = as_bf16x2(r[1]);
-          ag[q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vg[t]), lo, ag[q], false);
-          au[q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vu[t]), lo, au[q], false);
-          ag[H + q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vg[t]), hi, ag[H + q], false);
-          au[H + q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vu[t]), hi, au[H + q], false);
-        }
-      }
-    }
+    for (int c = hl; c < nc; c += 32) eat(c);
   } else {
 #pragma unroll 4
     for (int c = hl; c < nc; c += 32) {
@@ -162,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const bf16* __restrict__
   const int col = col0 + (lane >> 5);
   const bool live = col < N;
   // A half-wave past the end streams the last column again and stores
-  // nothing, so both halves stay active for the cross-half exchange.
+  // nothing.
   const int ccol = live ? col : N - 1;
 
   const u32x4* rg = reinterpret_cast<const u32x4*>(wg + (int64_t)ccol * K);
@@ -217,6 +184,165 @@ __global__ __launch_bounds__(kThreads) void gemv_phased_kernel(const bf16* __res
   finish_column<M, A, kTwin>(ag, au, fold, live, lane & 31, col, N, gmul, umul, h, sink);
 }
 
+// ---------------------------------------------------------------- matrix cores, M >= 4
+//
+// From M = 4 on, the dot products go to v_mfma_f32_16x16x32_bf16 with the
+// weights as the first operand (16 output columns) and x as the second (16
+// token rows, rows M..15 zero).  The MFMA operand layout gives each lane one
+// row and 16 bytes of k, i.e. 64 contiguous bytes per row per instruction,
+// which streams from HBM at only about 5 TB/s; so the weights are loaded
+// coalesced instead (a quarter-wave per row, 256 contiguous bytes of Wg or
+// Wu per row per instruction), written to a wave-private LDS tile, and read
+// back in operand layout.  x comes from L2 straight into operand registers.
+//
+// A workgroup owns 16 columns and its 8 waves split the reduction into
+// slabs of 128 k (wave w takes slabs [w S / 8, (w + 1) S / 8) of S); each
+// wave keeps 16 x 16 partial sums of g and u (4 + 4 floats per lane), the
+// partials meet in LDS, and wave 0 adds them in wave order, applies
+// act(g) * u and stores h.  Weight rows past N and k past K load as zero.
+constexpr int kMxWaves = 8;
+constexpr int kMxThreads = kMxWaves * 64;
+constexpr int kMxSlabK = 128;                    // k per slab
+constexpr int kMxCPR = kMxSlabK / 8;             // 16-byte chunks per row per slab (16)
+constexpr int kMxRowsPerInst = 64 / kMxCPR;      // rows one load instruction covers (4)
+constexpr int kMxInst = 16 / kMxRowsPerInst;     // load instructions per weight per slab (4)
+constexpr int kMxSteps = kMxSlabK / 32;          // MFMA k-steps per slab (4)
+constexpr int kMxTile = 16 * kMxCPR;             // 16-byte chunks in one weight's slab tile
+constexpr size_t kMxLds = (size_t)kMxWaves * 2 * kMxTile * 16;   // 64 KiB
+static_assert(kMxLds >= (size_t)2 * kMxWaves * 64 * 16, "the reduction fits the tiles' LDS");
+
+// kTwin: the same loads, LDS tiles and exchange with no arithmetic; sink[n]
+// receives the XOR of every word of Wg[n, :] and Wu[n, :] as read back from
+// the LDS tiles (x is loaded as in the kernel and not folded).
+template <Act A, bool kTwin>
+__global__ __launch_bounds__(kMxThreads) void gemv_mfma_kernel(const bf16* __restrict__ x,
+                                                               const bf16* __restrict__ wg,
+                                                               const bf16* __restrict__ wu,
+                                                               bf16* __restrict__ h, int M, int N, int K,
+                                                               float gmul, float umul,
+                                                               uint32_t* __restrict__ sink) {
+  extern __shared__ u32x4 lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * 16;
+  const int nch = K >> 3;                         // K % 8 == 0
+  const int nslab = (nch + kMxCPR - 1) / kMxCPR;
+  const int s0 = (int)((int64_t)wave * nslab / kMxWaves);
+  const int s1 = (int)((int64_t)(wave + 1) * nslab / kMxWaves);
+  u32x4* tg = lds + wave * 2 * kMxTile;           // this wave's tiles: Wg, then Wu
+  u32x4* tu = tg + kMxTile;
+
+  // Loads: instruction i covers rows 4 i + lane / 16, chunk lane % 16 of the slab.
+  const int lc = lane % kMxCPR, lr = lane / kMxCPR;
+  // Operands: lane l supplies row l % 16 and chunk 4 j + l / 16 of k-step j.
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const bool xrow = r16 < M;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(x + (int64_t)(xrow ? r16 : 0) * K);
+  const u32x4* wg4 = reinterpret_cast<const u32x4*>(wg);
+  const u32x4* wu4 = reinterpret_cast<const u32x4*>(wu);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  f32x4 acc_g = {0.0f, 0.0f, 0.0f, 0.0f}, acc_u = acc_g;
+  uint32_t fold = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int c = s * kMxCPR + lc;
+    u32x4 vg[kMxInst], vu[kMxInst], vx[kMxSteps];
+#pragma unroll
+    for (int i = 0; i < kMxInst; ++i) {
+      const int n = n0 + i * kMxRowsPerInst + lr;
+      const bool in = n < N && c < nch;
+      const int64_t off = in ? (int64_t)n * nch + c : 0;
+      vg[i] = in ? __builtin_nontemporal_load(wg4 + off) : zero;
+      vu[i] = in ? __builtin_nontemporal_load(wu4 + off) : zero;
+    }
+#pragma unroll
+    for (int j = 0; j < kMxSteps; ++j) {
+      const int cx = s * kMxCPR + 4 * j + q4;
+      vx[j] = (xrow && cx < nch) ? xr[cx] : zero;
+    }
+    // Row r, chunk c of a tile sits at chunk c ^ (r & 15): the 16 lanes that
+    // write one row and the 16 that read one chunk of 16 rows each hit 16
+    // distinct 16-byte bank groups.
+#pragma unroll
+    for (int i = 0; i < kMxInst; ++i) {
+      const int r = i * kMxRowsPerInst + lr;
+      tg[r * kMxCPR + (lc ^ r)] = vg[i];
+      tu[r * kMxCPR + (lc ^ r)] = vu[i];
+    }
+#pragma unroll
+    for (int j = 0; j < kMxSteps; ++j) {
+      const int pc = (4 * j + q4) ^ r16;
+      const u32x4 ag = tg[r16 * kMxCPR + pc];
+      const u32x4 au = tu[r16 * kMxCPR + pc];
+      if constexpr (kTwin) {
+        fold ^= ag[0] ^ ag[1] ^ ag[2] ^ ag[3] ^ au[0] ^ au[1] ^ au[2] ^ au[3];
+        asm volatile("" ::"v"(vx[j]));          // x is loaded as in the kernel
+      } else {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, vx[j]);
+        acc_g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ag), b, acc_g, 0, 0, 0);
+        acc_u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, au), b, acc_u, 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();                                // every wave is done with its tiles
+  if constexpr (kTwin) {
+    uint32_t* rf = reinterpret_cast<uint32_t*>(lds);
+    rf[wave * 64 + lane] = fold;
+    __syncthreads();
+    if (wave != 0) return;
+    uint32_t f = 0;
+    for (int w = 0; w < kMxWaves; ++w) f ^= rf[w * 64 + lane];
+    f ^= __shfl_xor(f, 16);                       // the 4 lanes of a row
+    f ^= __shfl_xor(f, 32);
+    if (lane < 16 && n0 + lane < N) sink[n0 + lane] = f;
+    return;
+  }
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
+  red[wave * 64 + lane] = acc_g;
+  red[(kMxWaves + wave) * 64 + lane] = acc_u;
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 g = red[lane], u = red[kMxWaves * 64 + lane];
+  for (int w = 1; w < kMxWaves; ++w) {
+    g += red[w * 64 + lane];
+    u += red[(kMxWaves + w) * 64 + lane];
+  }
+  if (!xrow) return;
+  // Accumulator layout: lane l element e is column n0 + 4 (l / 16) + e of token row l % 16.
+  const int nb = n0 + 4 * q4;
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float gv = gmul * g[e], uv = umul * u[e];
+    const float a = (A == Act::kGeluTanh) ? gelu_tanh_f32(gv) : silu_f32(gv);
+    o[e] = __builtin_bit_cast(uint16_t, to_bf16(a * uv));
+  }
+  bf16* dst = h + (int64_t)r16 * N + nb;
+  if ((N & 3) == 0 && nb + 3 < N) {               // 8-byte aligned: h is 16-byte aligned, N % 4 == 0
+    *reinterpret_cast<u32x2*>(dst) = u32x2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (nb + e < N) dst[e] = __builtin_bit_cast(bf16, (uint16_t)o[e]);
+  }
+}
+
+// M from which the matrix-core kernel is used: at M = 8 it streams 22-34 %
+// faster than the vector-ALU kernel at the benchmark shapes, at M = 4 0-4 %
+// faster; at M = 1 the vector-ALU kernel is up to 12 % faster.
+constexpr int kMfmaFromM = 4;
+
+template <Act A, bool kTwin>
+hipError_t launch_mfma(int M, int N, int K, const void* x, const void* wg, const void* wu, void* h,
+                       float gm, float um, uint32_t* sink, hipStream_t s) {
+  const unsigned blocks = (unsigned)((N + 15) / 16);
+  hipLaunchKernelGGL((gemv_mfma_kernel<A, kTwin>), dim3(blocks), dim3(kMxThreads), kMxLds, s,
+                     static_cast<const bf16*>(x), static_cast<const bf16*>(wg), static_cast<const bf16*>(wu),
+                     static_cast<bf16*>(h), M, N, K, gm, um, sink);
+  return hipGetLastError();
+}
+
 // Chunks of each x row per phase: the fewest equal phases of at most
 // kPhaseBytes, each a multiple of 32 chunks (one pass of a half-wave), which
 // may add up to 31 chunks per row to a phase.
@@ -249,15 +375,11 @@ hipError_t launch_m(int N, int K, const void* x, const void* wg, const void* wu,
 template <Act A, bool kTwin>
 hipError_t launch_act(int M, int N, int K, const void* x, const void* wg, const void* wu, void* h,
                       float gm, float um, uint32_t* sink, hipStream_t s) {
+  if (M >= kMfmaFromM && M <= 8) return launch_mfma<A, kTwin>(M, N, K, x, wg, wu, h, gm, um, sink, s);
   switch (M) {
     case 1: return launch_m<1, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
     case 2: return launch_m<2, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
     case 3: return launch_m<3, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
-    case 4: return launch_m<4, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
-    case 5: return launch_m<5, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
-    case 6: return launch_m<6, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
-    case 7: return launch_m<7, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
-    case 8: return launch_m<8, A, kTwin>(N, K, x, wg, wu, h, gm, um, sink, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -268,8 +268,8 @@ def test_autograd_matches_explicit_backward():
 def test_gemv_full(M, NK):
     """Every element, at the benchmark page's decode shapes: (6912, 1536), the
     LLaMA-7B-like (11008, 4096), and the wide LLaMA-2 13B (13824, 5120) and
-    GPT-NeoX-20B (24576, 6144) up/gate shapes, whose x at M = 8 (80 and
-    96 KiB) is staged in phases along K."""
+    GPT-NeoX-20B (24576, 6144) up/gate shapes.  M = 1, 2 run the vector-ALU
+    kernel, M = 4, 8 the matrix-core one."""
     N, K = NK
     d = synth.decode_bf16(M, N, K, seed=0)
     check_fwd(d, "bf16", what=f"gemv M={M} N={N} K={K}", via="gemv")
@@ -283,16 +283,18 @@ def test_gemv_ragged(M, NK):
     check_fwd(d, "bf16", what=f"gemv M={M} N={N} K={K}", via="gemv")
 
 
-@pytest.mark.parametrize("M,N,K", [(8, 300, 20480), (5, 77, 16392), (3, 129, 10928), (8, 16, 4104)])
-def test_gemv_phased_x(M, N, K):
-    """x past 64 KiB goes through LDS in phases along K: 320 KiB of x in 9
-    phases (8 of 288 chunks per row, then 256); 5 rows of 2049 chunks, i.e.
-    four phases of 416 chunks and a ragged last one of 385; 3 rows of 1366
-    chunks (704 and 662); and 64.1 KiB, one chunk per row past whole
-    staging (288 and 225)."""
+@pytest.mark.parametrize("M,N,K", [(8, 300, 20480), (5, 77, 16392), (8, 16, 4104), (3, 129, 10928),
+                                   (1, 40, 40968), (2, 33, 32776)])
+def test_gemv_long_reductions(M, N, K):
+    """Long reductions through both decode kernels.  M >= 4 runs on the
+    matrix cores, whose 8 waves split K into 128-wide slabs: 160 slabs, 20
+    per wave; 129 slabs, the last holding one 16-byte chunk; 33 slabs.  M <=
+    3 with x past 64 KiB stages x through LDS in phases along K: 3 rows of
+    1366 chunks (phases of 704 and 662), 1 row of 5121 (three phases), 2 rows
+    of 4097 (four phases, the last ragged)."""
     d = synth.decode_bf16(M, N, K, seed=7)
-    check_fwd(d, "bf16", what=f"gemv phased M={M} N={N} K={K}", via="gemv")
-    # the read-only twin walks the same phases and still reads every weight once
+    check_fwd(d, "bf16", what=f"gemv M={M} N={N} K={K}", via="gemv")
+    # the read-only twin walks the same loads and still reads every weight once
     t = to_dev(d)
     sink = torch.full((N + 64,), -1, dtype=torch.int32, device=DEV)
     S.probe_gemv_read(t["x"], t["wg"], t["wu"], sink)
