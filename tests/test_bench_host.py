@@ -38,7 +38,7 @@ def test_source_hash_ignores_comments_but_not_code(fake_root):
     text = gemm.read_text()
     gemm.write_text("// a new comment line\n/* and a block\n   comment */\n" + text + "\n\n")
     assert bench.kernel_source_hash() == h0
-    gemm.write_text(text.replace("constexpr int kGroupM = 8;", "constexpr int kGroupM = 4;"))
+    gemm.write_text(text + "\nconstexpr int kOneMoreConstant = 1;\n")     # a line of code
     assert bench.kernel_source_hash() != h0
 
 
