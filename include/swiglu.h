@@ -25,10 +25,13 @@
  *     enqueue only what is needed to give the outputs their defined values.
  *   - Calls are thread-safe: the library's only global state is a
  *     thread-local record of the last HIP error, a once-per-device kernel
- *     attribute (the larger dynamic LDS size) and the address of
- *     swiglu_bwd_noalloc's static scratch buffer on each device, both set
- *     under call_once.  swiglu_bwd_noalloc alone shares device memory
- *     between calls (see there).
+ *     attribute (the larger dynamic LDS size), the addresses of two static
+ *     device arrays on each device (swiglu_bwd_noalloc's scratch buffer and
+ *     the clamp count's slots), all set under call_once, and the counter
+ *     that hands the count slots' regions out in turn.  A call's device
+ *     arrays are those of the device its stream belongs to.
+ *     swiglu_bwd_noalloc and the counting calls of swiglu_act_quant and
+ *     swiglu_act_fwd alone share device memory between calls (see there).
  */
 #ifndef SWIGLU_H_
 #define SWIGLU_H_

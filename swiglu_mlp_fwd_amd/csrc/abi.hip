@@ -49,20 +49,21 @@ static __device__ __align__(256) unsigned char scratch[SWIGLU_NOALLOC_SCRATCH_BY
 
 namespace {
 
-// Device address of `scratch` on the current device (each GPU holds its own
-// copy at its own address), looked up on the first call on that device.
-hipError_t scratch_address(void** out) {
+// Device address of `scratch` on the device `stream` belongs to (each GPU
+// holds its own copy at its own address), looked up on the first call on
+// that device.
+hipError_t scratch_address(hipStream_t stream, void** out) {
   constexpr int kMaxDevices = 64;
   static std::once_flag once[kMaxDevices];
   static void* addr[kMaxDevices];
   static hipError_t result[kMaxDevices];
   int dev = 0;
-  const hipError_t e = hipGetDevice(&dev);
+  const hipError_t e = swg::stream_device(stream, &dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::call_once(once[dev], [dev] {
     void* p = nullptr;
-    result[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    result[dev] = swg::symbol_address_on(dev, HIP_SYMBOL(scratch), &p);
     addr[dev] = p;
   });
   *out = addr[dev];
@@ -233,7 +234,7 @@ int swiglu_bwd_noalloc(int act, int dtype, int64_t M, int64_t N, int64_t K, cons
                                nullptr, 0, stream);
   if (swg::bwd_workspace_total(dtype, M, N, K) > SWIGLU_NOALLOC_SCRATCH_BYTES) return SWIGLU_ERR_SCRATCH;
   void* ws = nullptr;
-  const hipError_t e = scratch_address(&ws);
+  const hipError_t e = scratch_address(as_stream(stream), &ws);
   if (e != hipSuccess) return hip_status(e);
   return swiglu_bwd_act_mult(act, dtype, M, N, K, x, wg, wu, dh, gate_mult, up_mult, dx, dwg, dwu, ws,
                              SWIGLU_NOALLOC_SCRATCH_BYTES, stream);

@@ -126,7 +126,7 @@ hipError_t launch_act_fwd(Act act, Dt out, int64_t rows, int64_t cols, const flo
   }
   uint32_t* slots = nullptr;
   if (counting) {
-    const hipError_t e = count_slots(&slots);
+    const hipError_t e = count_slots(s, &slots);
     if (e != hipSuccess) return e;
   }
   const int64_t want = (nchunks + kThreads - 1) / kThreads;

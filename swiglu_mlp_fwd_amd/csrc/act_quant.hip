@@ -176,7 +176,7 @@ hipError_t launch_act_quant(Act act, int64_t rows, int64_t cols, const float* ga
   }
   uint32_t* slots = nullptr;
   if (counting) {
-    const hipError_t e = count_slots(&slots);
+    const hipError_t e = count_slots(s, &slots);
     if (e != hipSuccess) return e;
   }
   const int64_t want = (nchunks + kThreads - 1) / kThreads;

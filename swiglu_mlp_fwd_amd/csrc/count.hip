@@ -57,20 +57,17 @@ __global__ __launch_bounds__(kSumThreads) void sum_slots_kernel(const uint32_t* 
   if (threadIdx.x == 0) *out = part[0];
 }
 
-// Device address of the slot array on the current device (each GPU holds
-// its own copy), looked up on the first call on that device.
-hipError_t slot_array_address(uint32_t** out) {
+// Device address of the slot array on device dev (each GPU holds its own
+// copy), looked up on the first call on that device.
+hipError_t slot_array_address(int dev, uint32_t** out) {
   constexpr int kMaxDevices = 64;
   static std::once_flag once[kMaxDevices];
   static void* addr[kMaxDevices];
   static hipError_t result[kMaxDevices];
-  int dev = 0;
-  const hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::call_once(once[dev], [dev] {
     void* p = nullptr;
-    result[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(count_slot_array));
+    result[dev] = symbol_address_on(dev, HIP_SYMBOL(count_slot_array), &p);
     addr[dev] = p;
   });
   *out = static_cast<uint32_t*>(addr[dev]);
@@ -81,9 +78,12 @@ std::atomic<uint32_t> next_region{0};
 
 }  // namespace
 
-hipError_t count_slots(uint32_t** slots) {
+hipError_t count_slots(hipStream_t s, uint32_t** slots) {
+  int dev = 0;
+  hipError_t e = stream_device(s, &dev);
+  if (e != hipSuccess) return e;
   uint32_t* base = nullptr;
-  const hipError_t e = slot_array_address(&base);
+  e = slot_array_address(dev, &base);
   if (e != hipSuccess) return e;
   const uint32_t r = next_region.fetch_add(1, std::memory_order_relaxed) % kRegions;
   *slots = base + (size_t)r * kCountSlots;

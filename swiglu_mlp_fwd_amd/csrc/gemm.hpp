@@ -64,6 +64,32 @@ hipError_t allow_lds(size_t lds) {
   return result[dev];
 }
 
+// The device a stream belongs to (the current device for the null stream).
+inline hipError_t stream_device(hipStream_t s, int* dev) {
+  if (s == nullptr) return hipGetDevice(dev);
+  hipDevice_t d = 0;
+  const hipError_t e = hipStreamGetDevice(s, &d);
+  if (e != hipSuccess) return e;
+  *dev = (int)d;
+  return hipSuccess;
+}
+
+// The address of a file-scope __device__ array on device `dev` (each GPU
+// holds its own copy at its own address): dev is made current for the
+// lookup and the caller's current device restored.
+inline hipError_t symbol_address_on(int dev, const void* symbol, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+  e = hipGetSymbolAddress(out, symbol);
+  if (cur != dev) {
+    const hipError_t r = hipSetDevice(cur);
+    if (e == hipSuccess) e = r;
+  }
+  return e;
+}
+
 hipError_t launch_fwd_dual(Dt dt, Act act, const GemmArgs& a, hipStream_t s);  // h = act(g) * u
 // bf16 inputs, h = act(g) * u quantised per 1x32 block (n % 32 == 0).
 hipError_t launch_fwd_dual_fp8(Act act, const GemmArgs& a, hipStream_t s);
@@ -87,7 +113,7 @@ hipError_t launch_gemv_read_twin(int M, int N, int K, const void* x, const void*
 // of at most kCountSlots workgroups writes workgroup b's count to slots[b],
 // then launch_count_sum adds slots[0, nblocks) into *count (overwriting it).
 constexpr int kCountSlots = 8192;
-hipError_t count_slots(uint32_t** slots);   // this call's slots on the current device
+hipError_t count_slots(hipStream_t s, uint32_t** slots);   // this call's slots on the stream's device
 hipError_t launch_count_sum(const uint32_t* slots, int nblocks, uint64_t* count, hipStream_t s);
 
 hipError_t launch_act_bwd(Dt dt, int64_t rows, int64_t cols, const void* gate, const void* up,
