@@ -87,7 +87,8 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="headline only")
     p.add_argument("--only", default=None,
                    choices=["step", "fwd", "train_fwd", "train_bwd", "decode", "act_quant", "act_bwd", "fp32", "tiny",
-                            "fwd_k_sweep", "traffic", "traffic_decode", "traffic_act_quant", "traffic_act_fwd", "traffic_act_bwd"],
+                            "fwd_k_sweep", "traffic", "traffic_bwd", "traffic_decode", "traffic_act_quant", "traffic_act_fwd",
+                            "traffic_act_bwd"],
                    help="profiling aid: run one leg only (no JSON contract); 'traffic*' runs a kernel and a 1 GiB "
                         "copy (the counter calibration) for the --pmc runs")
     p.add_argument("--digest-traffic", nargs=3, metavar=("NAME", "FETCH_CSV", "WRITE_CSV"), default=None,
@@ -112,6 +113,12 @@ TRAFFIC_KERNELS = {
     "fwd_dual_gemm_bf16_8192x14336x4096": (
         ("gemm_dma_kernelIDF16bLNS0_3EpiE0E",), FWD_KERNEL_SOURCES,
         (M4 * K4 + 2 * N4 * K4 + M4 * N4) * 2),
+    # The recompute of the backward: x, Wg, Wu and dh read once; D = [dg | du]
+    # [M, 2N] and its transpose written once (N is a multiple of 64 here, so
+    # neither carries padding).
+    "bwd_recompute_bf16_8192x14336x4096": (
+        ("gemm_dma_kernelIDF16bLNS0_3EpiE2E",), FWD_KERNEL_SOURCES,
+        (M4 * K4 + 2 * N4 * K4 + M4 * N4 + 2 * (2 * M4 * N4)) * 2),
     "gemv_bf16_M8_11008x4096": (
         ("gemv_mfma_kernelILNS_3ActE0ELb0E", "gemv_mfma_kernel<(swg::Act)0, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
         2 * 11008 * 4096 * 2 + 8 * 4096 * 2 + 8 * 11008 * 2, 11008 // 16 * 512),
@@ -406,13 +413,13 @@ def main():
         S.fwd(x, wg, wu, out=h)
         S.bwd(x, wg, wu, dh, workspace=ws, out=grads)
 
-    if args.only in ("step", "fwd", "traffic"):
+    if args.only in ("step", "fwd", "traffic", "traffic_bwd"):
         for _ in range(args.warmup + args.steps):
-            if args.only == "step":
+            if args.only in ("step", "traffic_bwd"):
                 step()
             else:
                 S.fwd(x, wg, wu, out=h)
-        if args.only == "traffic":
+        if args.only in ("traffic", "traffic_bwd"):
             del ws, grads
             torch.cuda.empty_cache()
             copy_calibration(torch, dev, args.steps)

@@ -34,10 +34,9 @@
 // Tiling: a workgroup owns a BM x BN block tile (rows of A x rows of each
 //   B), k-steps of 128 bytes per row (64 bf16 or 32 fp32), and its waves form
 //   a grid in which each wave owns a sub-tile of every B operand made of
-//   MFMA tiles: 16 x 16 x 32 for the bf16 forward and the single-operand
-//   products (that form sustains about 10 % more throughput on this chip than
-//   32 x 32 x 16), 32 x 32 for the bf16 dSwiGLU recompute (whose dh prefetch
-//   leaves no registers for the larger 16 x 16 fragment set) and for fp32.
+//   MFMA tiles: 16 x 16 x 32 for every bf16 product (that form sustains
+//   about 10 % more throughput on this chip than 32 x 32 x 16), 32 x 32 x 2
+//   for fp32.
 //   In bf16 the dual GEMMs use 256 x 128 with 8 waves (4 x 2, 64 x 64 per
 //   wave per weight), the single-operand GEMMs 256 x 256 with 8 waves
 //   (64 x 128 per wave); both were the fastest of the tile shapes measured
@@ -83,11 +82,12 @@ constexpr bool gated_bwd(Epi e) { return e == Epi::kDSwiGLU || e == Epi::kDGeGLU
 // Tile raster: consecutive workgroups walk groups of kGroupM row-tiles down
 // the columns, so the 32 tiles an XCD runs at once share kGroupM tiles of
 // the first operand and 32 / kGroupM of the second.  Measured side by side
-// on the bf16 products at 8192 x 14336 x 4096: 8 for the forward (4: 0.5 %
-// slower, 2: 2.5 %, 16: 3 %, 32: 20 %), 4 for the backward's (2.0 % faster
-// than 8 over the whole backward).  The fp32 products keep 8.
+// on the bf16 products at 8192 x 14336 x 4096: 8 for the dual products
+// (forward: 4 is 0.5 % slower, 2: 2.5 %, 16: 3 %, 32: 20 %; the recompute of
+// the backward: 4 is 1 % slower), 4 for the single products dX and dW (2.0 %
+// faster than 8 over the whole backward).  The fp32 products keep 8.
 template <typename T, Epi E>
-constexpr int kGroupM = (sizeof(T) == 2 && !gated_fwd(E) && !gated_q(E)) ? 4 : 8;
+constexpr int kGroupM = (sizeof(T) == 2 && E == Epi::kStore) ? 4 : 8;
 
 // act(z) and act'(z) for the backward epilogues.  SiLU: a = z s,
 // a' = s (1 + z (1 - s)), s = sigma(z).  GELU (tanh form): a = z s and
@@ -245,10 +245,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p,
 // Epilogue through LDS for 16-bit outputs (used by the DMA kernel once its
 // LDS ring is idle).  The MFMA accumulator layout gives each lane one column
 // and runs of 4 rows, so direct stores are 2 bytes per lane.  Instead:
-//   - dSwiGLU only: the dh tile is staged in LDS with 16-byte coalesced
-//     loads and read back in accumulator layout with ds_read_b64_tr_b16
-//     (16 lanes addressing a 4-row x 16-column block receive one column each,
-//     4 rows deep -- exactly a lane's run of 4 accumulator rows);
+//   - dSwiGLU only: the dh tile, staged in LDS (DhLds below), is read back
+//     in accumulator layout with ds_read_b64_tr_b16 (16 lanes addressing a
+//     4-row x 16-column block receive one column each, 4 rows deep --
+//     exactly a lane's run of 4 accumulator rows);
 //   - results are written to LDS (2-byte writes, rows padded so the two
 //     half-waves hit different banks) and read back as 16-byte row chunks
 //     that are stored with coalesced 16-byte global stores.
@@ -266,43 +266,29 @@ typedef __attribute__((ext_vector_type(4))) short short4_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
-// dSwiGLU: the 16-byte chunks of the dh tile a thread stages (chunk
-// c = tid + k * threads, row c / (BN / 8), column chunk c % (BN / 8)).  Whole
-// chunks inside the matrix are loaded into registers by dh_prefetch, issued
-// before the last k-step so the HBM latency hides behind its MFMAs; the
-// epilogue then only has to write them to LDS.  Other chunks (past the last
-// row, or straddling the last column) are handled in the epilogue.
+// dSwiGLU: the dh tile (BM rows x BN columns of bf16) is staged densely in
+// the ring slot that the last k-step leaves unused: row r at r * 2 BN bytes,
+// its 16-byte chunk c at physical chunk c ^ (r & 15).  When dh's row pitch
+// and base allow 16-byte chunks (dh_dma below), the main loop moves the tile
+// there with the LDS DMA at its last step boundary, in place of the refill
+// that would have no step to fill, so the tile needs no registers while the
+// accumulators and operand fragments are live; the epilogue then only fixes
+// the chunks that straddle or pass the last column.  Otherwise the epilogue
+// loads the whole tile element by element.
 template <class TL>
-struct DhPre {
-  static constexpr int kCPR = TL::kBN / 8;
-  static constexpr int kPer = TL::kBM * kCPR / TL::kThreads;
-  u32x4 v[kPer];
-};
-
-template <class TL>
-__device__ __forceinline__ bool dh_whole(const GemmArgs& p, int grow, int gcol) {
-  return grow < p.m && gcol + 8 <= p.ncols && p.lddh % 8 == 0;
-}
-
-template <class TL>
-__device__ __forceinline__ void dh_prefetch(const GemmArgs& p, int tm, int tn, int tid, DhPre<TL>& pre) {
-  constexpr int kCPR = DhPre<TL>::kCPR;
-  const bf16* dh = static_cast<const bf16*>(p.dh);
-#pragma unroll
-  for (int k = 0; k < DhPre<TL>::kPer; ++k) {
-    const int c = tid + k * TL::kThreads;
-    const int grow = tm * TL::kBM + c / kCPR, gcol = tn * TL::kBN + (c % kCPR) * 8;
-    pre.v[k] = u32x4{0, 0, 0, 0};
-    if (dh_whole<TL>(p, grow, gcol))
-      pre.v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dh + (int64_t)grow * p.lddh + gcol));
+struct DhLds {
+  static constexpr int kCPR = TL::kBN / 8;                  // 16-byte chunks per row
+  static constexpr int kPitch = TL::kBN * 2;
+  __device__ static int offset(int row, int col) {          // byte offset of element (row, col)
+    return row * kPitch + (((col >> 3) ^ (row & 15)) << 4) + (col & 7) * 2;
   }
-}
+};
 
 template <Epi E, int NB, class TL, int kMN>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs& p,
                                                typename AccL<kMN>::V (&acc)[NB][TL::kWM / kMN][TL::kWN / kMN],
                                                int tm, int tn, int wm, int wn, int lane, int tid,
-                                               char* lds, const DhPre<TL>& pre) {
+                                               char* lds, const char* dh_lds, bool dh_dma) {
   constexpr int kBM = TL::kBM, kWM = TL::kWM, kWN = TL::kWN;
   constexpr int kTM = kWM / kMN, kTN = kWN / kMN, kE = AccL<kMN>::kE;
   constexpr int kThreads = TL::kThreads;
@@ -317,24 +303,28 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p,
 
   float dhv[kTM][kTN][kE];
   if constexpr (gated_bwd(E)) {
-    static_assert(DhPre<TL>::kCPR == kCPR && DhPre<TL>::kPer * kThreads == kBM * kCPR, "dh chunk mapping");
+    static_assert(DhLds<TL>::kCPR == kCPR && kCPR == 16, "dh chunk mapping; the swizzle spans 16 chunks");
     const bf16* dh = static_cast<const bf16*>(p.dh);
-#pragma unroll
-    for (int k = 0; k < DhPre<TL>::kPer; ++k) {
-      const int c = tid + k * kThreads;
-      const int r = c / kCPR, ch = c % kCPR;
-      const int grow = grow0 + r, gcol = gcol0 + ch * 8;
-      u32x4 v = pre.v[k];
-      if (!dh_whole<TL>(p, grow, gcol) && grow < p.m && gcol < p.ncols) {
-        const bf16* src = dh + (int64_t)grow * p.lddh + gcol;
+    char* const dst = const_cast<char*>(dh_lds);
+    // Chunks the DMA did not get right: with the DMA only those of rows
+    // inside the matrix that reach past the last column (rows past the end
+    // came in as zeros); without it every chunk.
+    const bool tail = gcol0 + kCols > p.ncols;
+    if (!dh_dma || tail) {
+      for (int c = tid; c < kBM * kCPR; c += kThreads) {
+        const int r = c / kCPR, ch = c % kCPR;
+        const int grow = grow0 + r, gcol = gcol0 + ch * 8;
+        if (dh_dma && (grow >= p.m || gcol + 8 <= p.ncols)) continue;
         uint16_t tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        const int nq = min(8, p.ncols - gcol);
-        for (int q = 0; q < nq; ++q) tmp[q] = __builtin_bit_cast(uint16_t, src[q]);
-        v = __builtin_bit_cast(u32x4, tmp);
+        if (grow < p.m && gcol < p.ncols) {
+          const bf16* src = dh + (int64_t)grow * p.lddh + gcol;
+          const int nq = min(8, p.ncols - gcol);
+          for (int q = 0; q < nq; ++q) tmp[q] = __builtin_bit_cast(uint16_t, src[q]);
+        }
+        *reinterpret_cast<u32x4*>(dst + DhLds<TL>::offset(r, ch * 8)) = __builtin_bit_cast(u32x4, tmp);
       }
-      *reinterpret_cast<u32x4*>(at(0, r, ch * 8)) = v;
+      __syncthreads();
     }
-    __syncthreads();
     // dh in accumulator layout: one transposing read per 4 consecutive rows
     // of a 16-column run (lane s16 of the group addresses row s16 / 4,
     // columns 4 (s16 % 4) .. + 3 of the 4 x 16 block; lane i receives
@@ -350,7 +340,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p,
           const int row = wm * kWM + i * kMN + AccL<kMN>::row(lane, 4 * eq) + (s16 >> 2);
           const int col = wn * kWN + j * kMN + run0 + 4 * (s16 & 3);
           const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_short4_t*)(lds_char_t*)(at(0, row, col)));
+              (lds_short4_t*)(lds_char_t*)(dh_lds + DhLds<TL>::offset(row, col)));
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             dhv[i][j][4 * eq + q] = bits_f32((uint32_t)(uint16_t)v[q] << 16);
@@ -687,6 +677,49 @@ void gemm_dma_kernel(GemmArgs p) {
     }
   };
 
+  // dSwiGLU (bf16): the dh tile goes by DMA into the ring slot of step
+  // nk - 2, which no step refills, when dh's pitch and base allow whole
+  // 16-byte chunks; the epilogue writes D from the fp32 accumulators only
+  // through the LDS path (vec), so the tile is not moved otherwise.
+  constexpr bool kDhDma = gated_bwd(E) && sizeof(T) == 2;
+  const bool dh_dma = kDhDma && nk >= 1 && p.lddh % 8 == 0 && (reinterpret_cast<uintptr_t>(p.dh) & 15) == 0 &&
+                      p.ldo % 8 == 0 && p.du_off % 8 == 0;
+  const int dh_slot = nk % S;   // S == 2: the slot of step nk - 2 (slot 1 when nk == 1)
+  // Wave w moves rows 32 w .. 32 w + 31 of the tile (the same 8 KiB of the
+  // slot as its ring slab): DMA d takes rows 32 w + 4 d .. + 3, lane i lands
+  // in row 32 w + 4 d + i / 16, physical chunk i % 16, and fetches logical
+  // chunk (i % 16) ^ (row & 15).  Rows past the matrix read as zero through
+  // the descriptor; chunks past the last column are fixed by the epilogue.
+  auto issue_dh = [&]() {
+    static_assert(!kDhDma || (S == 2 && kBM * DhLds<TL>::kPitch == kStageBytes &&
+                              kBM * DhLds<TL>::kPitch / kWaves == kDma * 1024),
+                  "the dh tile fills one ring slot, 8 DMAs per wave");
+    const bf16* dh_tile = static_cast<const bf16*>(p.dh) + (int64_t)tm * kBM * p.lddh + (int64_t)tn * kBN;
+    int rows = p.m - tm * kBM;
+    rows = rows < 0 ? 0 : (rows > kBM ? kBM : rows);
+    int cols = p.ncols - tn * kBN;
+    cols = cols < 0 ? 0 : (cols > kBN ? kBN : cols);
+    // The descriptor ends at the tile's last element inside dh, so no read
+    // leaves dh: earlier rows' chunks past the last column read the next
+    // row (fixed by the epilogue), the last row's read zeros.
+    const int64_t bytes = (rows > 0 && cols > 0) ? ((int64_t)(rows - 1) * p.lddh + cols) * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rd = uniform_rsrc(dh_tile, bytes);
+    char* dst = lds_bytes + dh_slot * kStageBytes + wave * (kBM / kWaves) * DhLds<TL>::kPitch;
+    const int pc = lane & 15, rq = lane >> 4;
+    const uint32_t rowb = (uint32_t)(p.lddh * 2);
+    const uint32_t base = (uint32_t)(wave * (kBM / kWaves) + rq) * rowb;
+#pragma unroll
+    for (int d = 0; d < kDma; ++d) {
+      const uint32_t off = base + (uint32_t)(4 * d) * rowb + (uint32_t)((pc ^ ((4 * d + rq) & 15)) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void_t*)(dst + d * 1024), 16, off, 0, 0, 0);
+    }
+  };
+  // The refill at a step boundary, or at the last boundary the dh tile.
+  auto refill = [&](int ks, bool last) {
+    if (kDhDma && last && dh_dma) issue_dh();
+    else issue(ks);
+  };
+
   static_assert(sizeof(T) == 2 || kMN == 32, "fp32 operands use the 32 x 32 x 2 MFMA");
   typename AccL<kMN>::V acc[NB][kTM][kTN];
 #pragma unroll
@@ -772,7 +805,7 @@ void gemm_dma_kernel(GemmArgs p) {
   // branch around the next step's fragment reads: at such a join the
   // compiler's LDS wait counts would have to cover both paths, and the last
   // MFMAs of every step would wait for the next step's reads.
-  auto kstep = [&](int ks, bool more) {
+  auto kstep = [&](int ks, bool more, bool last) {
     const char* L = lds_bytes + (ks % S) * kStageBytes;
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk) {
@@ -805,11 +838,12 @@ void gemm_dma_kernel(GemmArgs p) {
             // The next step's first fragment reads go between the MFMAs
             // with the refill DMAs (one read and one DMA per group of
             // MFMAs) instead of all at once after the barrier: 3.3 % faster
-            // for the forward dual GEMM at 8192 x 14336 x 4096, 0.9 % slower
-            // for the backward's products, bit-identical either way.
+            // for the forward dual GEMM at 8192 x 14336 x 4096 and 1.5 % for
+            // the whole backward through its recompute, 0.9 % slower for the
+            // single products, bit-identical either way.
             __builtin_amdgcn_sched_barrier(0);
             read_frags(0, lds_bytes + ((ks + 1) % S) * kStageBytes, 0);
-            issue(ks + S);
+            refill(ks + S, last);
             mfmas(kk & 1);
             constexpr int kPerDma = kMf / kDma > 0 ? kMf / kDma : 1;
 #pragma unroll
@@ -827,7 +861,7 @@ void gemm_dma_kernel(GemmArgs p) {
           // The DMA instructions of the refill go one by one between the
           // MFMAs of this sub-step instead of stalling the matrix core.
           __builtin_amdgcn_sched_barrier(0);
-          issue(ks + S);
+          refill(ks + S, last);
           mfmas(kk & 1);
           constexpr int kPerDma = kMf / kDma > 0 ? kMf / kDma : 1;
 #pragma unroll
@@ -850,10 +884,18 @@ void gemm_dma_kernel(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  DhPre<TL> dpre;
-  for (int ks = 0; ks + 1 < nk; ++ks) kstep(ks, true);
-  if constexpr (gated_bwd(E) && sizeof(T) == 2) dh_prefetch<TL>(p, tm, tn, tid, dpre);
-  if (nk > 0) kstep(nk - 1, false);
+  if constexpr (kDhDma) {
+    // The last step boundary (that of step nk - 2) is peeled off to move the
+    // dh tile; with a single step the tile goes after the prologue, whose
+    // barrier has retired every wave's DMA into the unused slot.
+    static_assert(kIL >= 1, "the refill at the last boundary is unconditional");
+    for (int ks = 0; ks + 2 < nk; ++ks) kstep(ks, true, false);
+    if (nk >= 2) kstep(nk - 2, true, true);
+    else if (nk == 1 && dh_dma) issue_dh();
+  } else {
+    for (int ks = 0; ks + 1 < nk; ++ks) kstep(ks, true, false);
+  }
+  if (nk > 0) kstep(nk - 1, false, false);
 
   if constexpr (gated_q(E)) {
     wait_vmcnt<0>();
@@ -867,10 +909,14 @@ void gemm_dma_kernel(GemmArgs p) {
         wait_vmcnt<0>();                      // no DMA still landing in the ring
         __builtin_amdgcn_s_waitcnt(0xC07F);   // own LDS reads done
         barrier_no_fence();                   // every wave is done with the ring
-        store_tile_lds<E, NB, TL, kMN>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes, dpre);
+        store_tile_lds<E, NB, TL, kMN>(p, acc, tm, tn, wm, wn, lane, tid, lds_bytes,
+                                       lds_bytes + dh_slot * kStageBytes, dh_dma);
         return;
       }
     }
+    // No ring DMA (a refill with no step to fill) may still be landing in
+    // this workgroup's LDS when its waves end.
+    wait_vmcnt<0>();
     store_tile<T, E, NB, TL, kMN>(p, acc, tm, tn, wm, wn, lane);
   }
 }
@@ -901,8 +947,9 @@ using TileSingleF32 = Tile<128, 128, 2, 2, 2>;  // 64 x 64 per wave
 
 }  // namespace
 
-// The bf16 forward products use the interleaved step boundary (kIL = 3),
-// the backward's the plain one (kIL = 2): each the faster at the training shape.
+// The bf16 dual products (forward and recompute) use the interleaved step
+// boundary (kIL = 3), the single products the plain one (kIL = 2): each the
+// faster at the training shape.
 hipError_t launch_fwd_dual(Dt dt, Act act, const GemmArgs& a, hipStream_t s) {
   if (act == Act::kGeluTanh)
     return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kGeGLU, 2, TileDual, 8, 2, 3>(a, s)
@@ -917,12 +964,10 @@ hipError_t launch_fwd_dual_fp8(Act act, const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dswiglu(Dt dt, Act act, const GemmArgs& a, hipStream_t s) {
-  // 32 x 32 MFMAs here: with the 16 x 16 fragments (twice the registers per
-  // sub-step) the dh tile prefetched into registers would spill.
   if (act == Act::kGeluTanh)
-    return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDGeGLU, 2, TileDual, 8, 2, 2, 32>(a, s)
+    return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDGeGLU, 2, TileDual, 8, 2, 3>(a, s)
                            : launch_dma<float, Epi::kDGeGLU, 2, TileDualF32, 8, 2, 2, 32>(a, s);
-  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, 2, 32>(a, s)
+  return dt == Dt::kBF16 ? launch_dma<bf16, Epi::kDSwiGLU, 2, TileDual, 8, 2, 3>(a, s)
                          : launch_dma<float, Epi::kDSwiGLU, 2, TileDualF32, 8, 2, 2, 32>(a, s);
 }
 

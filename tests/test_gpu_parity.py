@@ -230,6 +230,17 @@ def test_bwd_bf16_full_8192x14336x4096_sampled():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
+@pytest.mark.parametrize("shape", [(257, 136, 72), (24, 48, 64), (40, 8, 8), (300, 1032, 136)])
+def test_bwd_dh_tile_edges(shape, act):
+    """N % 8 == 0, so the recompute moves the dh tile to LDS by DMA: a column
+    tail (chunks past N fixed in LDS), a row tail (rows past M read as zero),
+    a single reduction step (K <= 64: the tile moves after the prologue) and
+    two steps (it replaces the last refill)."""
+    M, N, K = shape
+    check_bwd(synth.train_bf16(M, N, K, seed=5), "bf16", act=act, what=f"bwd bf16 {act} {shape}")
+
+
 def test_bwd_empty_sums_are_zero():
     K = 16
     x = torch.empty((0, K), dtype=torch.bfloat16, device=DEV)
