@@ -91,6 +91,9 @@ def parse():
                             "traffic_act_bwd"],
                    help="profiling aid: run one leg only (no JSON contract); 'traffic*' runs a kernel and a 1 GiB "
                         "copy (the counter calibration) for the --pmc runs")
+    p.add_argument("--digest-cycles", nargs=2, metavar=("NAME", "PMC_CSV"), default=None,
+                   help="read the counter_collection.csv of a rocprofv3 --pmc run with GRBM_GUI_ACTIVE (and "
+                        "SQ_VALU_MFMA_BUSY_CYCLES) and record NAME's cycles per launch in profiles/cycles.json")
     p.add_argument("--digest-traffic", nargs=3, metavar=("NAME", "FETCH_CSV", "WRITE_CSV"), default=None,
                    help="read the counter_collection.csv files of two rocprofv3 --pmc runs of a 'traffic*' leg "
                         "(FETCH_SIZE, then WRITE_SIZE) and record NAME in profiles/traffic.json")
@@ -228,6 +231,69 @@ def load_traffic(name: str):
     return e.get("bytes_per_launch")
 
 
+# MI355X: 8 XCDs (GRBM_GUI_ACTIVE counts per XCD), 256 CUs of 4 SIMDs.
+N_XCD, N_SIMD = 8, 1024
+NOMINAL_SCLK_GHZ = 2.4        # the clock the published peaks assume
+
+
+def digest_cycles(name: str, csv_path: str) -> None:
+    """Shader-clock cycles per launch of one kernel from a --pmc run that
+    collected GRBM_GUI_ACTIVE (and, if present, SQ_VALU_MFMA_BUSY_CYCLES):
+    the mean over its dispatches, per XCD (and per SIMD for the MFMA count)."""
+    import csv
+    tags, files = TRAFFIC_KERNELS[name][:2]
+    grid = TRAFFIC_KERNELS[name][3] if len(TRAFFIC_KERNELS[name]) > 3 else None
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if not any(t in r["Kernel_Name"] for t in tags) or (grid is not None and int(r["Grid_Size"]) != grid):
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per or any("GRBM_GUI_ACTIVE" not in d for d in per.values()):
+        raise SystemExit(f"{csv_path}: no GRBM_GUI_ACTIVE for {name}")
+    n = len(per)
+    entry = {"source_hash": kernel_source_hash(files), "dispatches": n,
+             "cycles_per_launch": round(sum(d["GRBM_GUI_ACTIVE"] for d in per.values()) / n / N_XCD)}
+    if all("SQ_VALU_MFMA_BUSY_CYCLES" in d for d in per.values()):
+        entry["mfma_busy_cycles_per_simd"] = round(sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in per.values()) / n / N_SIMD)
+    path = os.path.join(ROOT, "profiles", "cycles.json")
+    try:
+        with open(path) as fh:
+            out = json.load(fh)
+    except (OSError, ValueError):
+        out = {}
+    out[name] = entry
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({name: entry}))
+
+
+def clock_adjusted(name: str, achieved_tflops: float, launch_s: float):
+    """The roofline at the clock the kernel actually ran at.  A launch of this
+    kernel takes a nearly fixed number of shader cycles whatever the clock
+    (the counter runs put it within 4 % over 1.46-1.92 GHz), so the mean
+    clock of a timed launch is those cycles over its measured duration, and
+    the dense-bf16 peak at that clock is the published one scaled by
+    clock / 2.4 GHz.  None unless the cycles were counted on the current
+    sources of the kernel."""
+    p = os.path.join(ROOT, "profiles", "cycles.json")
+    try:
+        with open(p) as f:
+            e = json.load(f).get(name)
+    except (OSError, ValueError):
+        return None
+    if not e or e.get("source_hash") != kernel_source_hash(TRAFFIC_KERNELS[name][1]) or launch_s <= 0:
+        return None
+    ghz = e["cycles_per_launch"] / launch_s / 1e9
+    peak = PEAK_BF16_TFLOPS * ghz / NOMINAL_SCLK_GHZ
+    out = {"sclk_GHz": round(ghz, 3), "peak": round(peak, 1), "frac": round(achieved_tflops / peak, 4),
+           "cycles_per_launch": e["cycles_per_launch"]}
+    if "mfma_busy_cycles_per_simd" in e:
+        out["mfma_busy_frac"] = round(e["mfma_busy_cycles_per_simd"] / e["cycles_per_launch"], 4)
+    return out
+
+
 def traffic_table():
     """Every counter-measured kernel whose sources are unchanged since the
     measurement: HBM bytes per launch against its algorithmic bytes."""
@@ -359,6 +425,9 @@ def main():
     args = parse()
     if args.digest_traffic:
         digest_traffic(*args.digest_traffic)
+        return
+    if args.digest_cycles:
+        digest_cycles(*args.digest_cycles)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -506,6 +575,7 @@ def main():
             "launch_ms_samples": [round(v * 1e3, 4) for v in fwd_samples],
             "mfma_probe_TFLOPs": round(mfma_tf, 1),
             "frac_of_mfma_probe": round(fwd_tflops / mfma_tf, 4),
+            "clock_adjusted": clock_adjusted("fwd_dual_gemm_bf16_8192x14336x4096", fwd_tflops, t_fwd),
         },
         "fwd_ms": round(t_fwd * 1e3, 4),
         "bwd_ms": round((t_step - t_fwd) * 1e3, 4),

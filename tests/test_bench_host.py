@@ -52,3 +52,20 @@ def test_traffic_is_reported_only_for_the_measured_sources(fake_root):
     assert bench.load_traffic(name) is None
     (fake_root / "profiles" / "traffic.json").unlink()
     assert bench.load_traffic(name) is None
+
+
+def test_clock_adjusted_roofline_needs_cycles_counted_on_the_current_sources(fake_root):
+    name = "fwd_dual_gemm_bf16_8192x14336x4096"
+    entry = {"source_hash": bench.kernel_source_hash(), "cycles_per_launch": 2_400_000,
+             "mfma_busy_cycles_per_simd": 1_800_000}
+    (fake_root / "profiles" / "cycles.json").write_text(json.dumps({name: entry}))
+    r = bench.clock_adjusted(name, 1000.0, 1.5e-3)     # 2.4 M cycles in 1.5 ms: 1.6 GHz
+    assert r["sclk_GHz"] == 1.6
+    assert abs(r["peak"] - bench.PEAK_BF16_TFLOPS * 1.6 / 2.4) < 0.1
+    assert abs(r["frac"] - 1000.0 / (bench.PEAK_BF16_TFLOPS * 1.6 / 2.4)) < 1e-4
+    assert r["mfma_busy_frac"] == 0.75
+    entry["source_hash"] = "0" * 16
+    (fake_root / "profiles" / "cycles.json").write_text(json.dumps({name: entry}))
+    assert bench.clock_adjusted(name, 1000.0, 1.5e-3) is None
+    (fake_root / "profiles" / "cycles.json").unlink()
+    assert bench.clock_adjusted(name, 1000.0, 1.5e-3) is None
