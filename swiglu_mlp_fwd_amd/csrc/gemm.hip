@@ -835,25 +835,26 @@ void gemm_dma_kernel(GemmArgs p) {
           wait_dma(S - 2);
           barrier_no_fence();
           if constexpr (kIL == 3) {
-            // The next step's first fragment reads go between the MFMAs
-            // with the refill DMAs (one read and one DMA per group of
-            // MFMAs) instead of all at once after the barrier: 3.3 % faster
-            // for the forward dual GEMM at 8192 x 14336 x 4096 and 1.5 % for
-            // the whole backward through its recompute, 0.9 % slower for the
-            // single products, bit-identical either way.
+            // After the barrier: a few MFMAs of this sub-step, then the next
+            // step's first fragment reads, then the refill DMAs, then the
+            // rest of the MFMAs.  The compiler keeps every fragment read
+            // before every refill DMA (it cannot tell the two ring slots
+            // apart), so the reads and DMAs go in bursts.  Against the plain
+            // boundary below: 3.3 % faster for the forward dual GEMM at
+            // 8192 x 14336 x 4096 and 1.5 % for the whole backward through
+            // its recompute, 0.9 % slower for the single products,
+            // bit-identical either way.  Other orders, written in source
+            // order, were slower or equal: a read and a DMA between each
+            // group of MFMAs, or the DMAs first.
             __builtin_amdgcn_sched_barrier(0);
             read_frags(0, lds_bytes + ((ks + 1) % S) * kStageBytes, 0);
             refill(ks + S, last);
             mfmas(kk & 1);
-            constexpr int kPerDma = kMf / kDma > 0 ? kMf / kDma : 1;
-#pragma unroll
-            for (int t = 0; t < kDma; ++t) {
-              __builtin_amdgcn_sched_group_barrier(0x008, kPerDma, 0);
-              if (t < kRd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            }
+            constexpr int kLead = kMf / kDma > 0 ? kMf / kDma : 1;
+            __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, kDma, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, kMf - kLead, 0);
             __builtin_amdgcn_sched_barrier(0);
             continue;
           }
