@@ -123,13 +123,13 @@ TRAFFIC_KERNELS = {
         ("gemm_dma_kernelIDF16bLNS0_3EpiE2E",), FWD_KERNEL_SOURCES,
         (M4 * K4 + 2 * N4 * K4 + M4 * N4 + 2 * (2 * M4 * N4)) * 2),
     "gemv_bf16_M8_11008x4096": (
-        ("gemv_mfma_kernelILNS_3ActE0ELb0E", "gemv_mfma_kernel<(swg::Act)0, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
+        ("gemv_mfma_kernelILNS_3ActE0ELb0ELb0E", "gemv_mfma_kernel<(swg::Act)0, false, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
         2 * 11008 * 4096 * 2 + 8 * 4096 * 2 + 8 * 11008 * 2, 11008 // 16 * 512),
     "gemv_bf16_M1_11008x4096": (
         ("gemv_kernelILi1ELNS_3ActE0ELb0E", "gemv_kernel<1, (swg::Act)0, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
         2 * 11008 * 4096 * 2 + 4096 * 2 + 11008 * 2),
     "gemv_bf16_M8_24576x6144": (
-        ("gemv_mfma_kernelILNS_3ActE0ELb0E", "gemv_mfma_kernel<(swg::Act)0, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
+        ("gemv_mfma_kernelILNS_3ActE0ELb0ELb0E", "gemv_mfma_kernel<(swg::Act)0, false, false>"), ("common.hpp", "gemv.hip", "gemm.hpp"),
         2 * 24576 * 6144 * 2 + 8 * 6144 * 2 + 8 * 24576 * 2, 24576 // 16 * 512),
     "act_quant_4001x3584": (
         ("act_quant_kernelILNS_3ActE0ELb0ELb0ELb0ELb0E", "act_quant_kernel<(swg::Act)0, false, false, false, false>"),

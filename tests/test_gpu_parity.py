@@ -317,6 +317,28 @@ def test_gemv_long_reductions(M, N, K):
     assert np.all(got[N:] == np.uint32(0xFFFFFFFF))
 
 
+@pytest.mark.parametrize("M,N,K", [(8, 200, 1664), (4, 77, 3968), (8, 33, 2048), (5, 130, 896), (8, 16, 1544),
+                                   (6, 48, 3920)])
+def test_gemv_short_reductions(M, N, K):
+    """Short reductions (fewer than 32 slabs of 128) on the matrix cores run
+    as many waves as divide the slab count (at most 8), each taking its slabs
+    two at a time: 13 slabs (one wave, 6 pairs and a single), 31 (one wave),
+    16 (8 waves of a pair), 7 (7 waves of one slab), 13 and 31 with a
+    partial last slab (1 and 10 chunks).  The read-only twin
+    takes the same path and reads every weight once."""
+    d = synth.decode_bf16(M, N, K, seed=9)
+    check_fwd(d, "bf16", what=f"gemv M={M} N={N} K={K}", via="gemv")
+    t = to_dev(d)
+    sink = torch.full((N + 64,), -1, dtype=torch.int32, device=DEV)
+    S.probe_gemv_read(t["x"], t["wg"], t["wu"], sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    want = (np.bitwise_xor.reduce(d["wg"].view(np.uint32), axis=1) ^
+            np.bitwise_xor.reduce(d["wu"].view(np.uint32), axis=1))
+    assert np.array_equal(got[:N], want)
+    assert np.all(got[N:] == np.uint32(0xFFFFFFFF))
+
+
 def test_gemv_rotated_copies_agree():
     """The bench rotates weight copies; every copy gives the same bits."""
     d = synth.decode_bf16(4, 6912, 1536, seed=0)
