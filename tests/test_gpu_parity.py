@@ -1391,3 +1391,39 @@ def test_forward_on_small_integers_is_exact_up_to_the_activation(shape, dt):
         assert np.all(np.abs(yk - rk) <= sp * (1 + 1e-9)), "bf16 h off by more than one step"
         log(f"small-integer fwd bf16 {shape}: RNE-exact on {int(safe.sum())} of {safe.size}, "
             f"{int(tail.sum())} tail elements")
+
+
+def _random_case(i):
+    """Case i of the seeded random-shape sweep: sizes drawn so that the GEMM
+    tiles (256 x 128, 256 x 256, 128 x 64), the 64-wide reduction steps and
+    the decode slabs all see ragged tails."""
+    rs = np.random.default_rng(20260 + i)
+    M, N, K = int(rs.integers(1, 700)), int(rs.integers(1, 700)), 8 * int(rs.integers(1, 200))
+    dt = "f32" if i % 3 == 0 else "bf16"
+    act = "gelu_tanh" if i % 2 else "silu"
+    mult = (1.0, 1.0) if i % 4 < 2 else (float(rs.uniform(0.5, 2.0)), float(rs.uniform(0.5, 2.0)))
+    return M, N, K, dt, act, mult
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shapes_forward_and_backward(i):
+    M, N, K, dt, act, mult = _random_case(i)
+    what = f"random {i}: {dt} {act} mult={mult} ({M}, {N}, {K})"
+    if dt == "bf16":
+        d = synth.train_bf16(M, N, K, seed=30 + i)
+    else:
+        d = synth.gemm_fp32(M, N, K, seed=30 + i)
+        d["dh"] = synth.normal_f32((M, N), 1.0, 30 + i, synth.STREAM_DH)
+    fwd_d = {k: v for k, v in d.items() if k != "dh"}
+    check_fwd(fwd_d, dt, what=what + " fwd", act=act, mult=mult)
+    check_bwd(d, dt, what=what + " bwd", act=act, mult=mult)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_shapes_decode(i):
+    rs = np.random.default_rng(30260 + i)
+    M, N, K = int(rs.integers(1, 9)), int(rs.integers(1, 3000)), 8 * int(rs.integers(1, 1200))
+    act = "gelu_tanh" if i % 2 else "silu"
+    mult = (1.0, 1.0) if i % 4 < 2 else (float(rs.uniform(0.5, 2.0)), float(rs.uniform(0.5, 2.0)))
+    d = synth.decode_bf16(M, N, K, seed=40 + i)
+    check_fwd(d, "bf16", what=f"random decode {i}: {act} mult={mult} ({M}, {N}, {K})", via="gemv", act=act, mult=mult)
