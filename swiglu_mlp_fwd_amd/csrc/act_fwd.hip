@@ -10,10 +10,12 @@
 // output type.
 //
 // Mapping as in the quantiser: the array is flat (the activation is
-// elementwise), each lane takes 8 consecutive elements (two 16-byte loads
-// per input) with kUnroll chunks' loads issued before any is used; the clamp
-// count is reduced per workgroup into the workgroup's slot and the slots are
-// summed by a second launch (count.hip).
+// elementwise) and walked in spans of 512 elements, one per wave, lane l
+// taking 16-byte vectors 128 s + l and 128 s + 64 + l of span s, so each
+// load and store instruction of a wave covers one contiguous range; kUnroll
+// units' loads are issued before any is used.  The clamp count is reduced
+// per workgroup into the workgroup's slot and the slots are summed by a
+// second launch (count.hip).
 #include "common.hpp"
 #include "fp8.hpp"
 #include "gemm.hpp"
@@ -27,17 +29,13 @@ constexpr int kMaxBlocks = 8192;
 static_assert(kMaxBlocks <= kCountSlots, "one count slot per workgroup");
 constexpr int kUnroll = 4;
 
-template <typename TO> __device__ __forceinline__ void store8(TO* h, int64_t c, const double (&v)[8]);
-template <> __device__ __forceinline__ void store8<float>(float* h, int64_t c, const double (&v)[8]) {
-  f32x4* p = reinterpret_cast<f32x4*>(h) + 2 * c;
-  __builtin_nontemporal_store(f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}, p);
-  __builtin_nontemporal_store(f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]}, p + 1);
+template <typename TO> __device__ __forceinline__ void store4(TO* h, int64_t v, const double (&r)[4]);
+template <> __device__ __forceinline__ void store4<float>(float* h, int64_t v, const double (&r)[4]) {
+  __builtin_nontemporal_store(f32x4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]}, reinterpret_cast<f32x4*>(h) + v);
 }
-template <> __device__ __forceinline__ void store8<bf16>(bf16* h, int64_t c, const double (&v)[8]) {
-  u32x4 w;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = bf16_bits_rne(v[2 * i]) | (bf16_bits_rne(v[2 * i + 1]) << 16);
-  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(h) + c);
+template <> __device__ __forceinline__ void store4<bf16>(bf16* h, int64_t v, const double (&r)[4]) {
+  const u32x2 w = {bf16_bits_rne(r[0]) | (bf16_bits_rne(r[1]) << 16), bf16_bits_rne(r[2]) | (bf16_bits_rne(r[3]) << 16)};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(h) + v);
 }
 
 template <Act A, typename TO, bool kClamp, bool kCount>
@@ -45,42 +43,50 @@ __global__ __launch_bounds__(kThreads) void act_fwd_kernel(const float* __restri
                                                            const float* __restrict__ up, float L,
                                                            TO* __restrict__ h,
                                                            unsigned long long* __restrict__ count,
-                                                           uint32_t* __restrict__ slots, int64_t nchunks) {
+                                                           uint32_t* __restrict__ slots, int64_t nvec, int64_t units) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const f32x4* g4 = reinterpret_cast<const f32x4*>(gate);
+  const f32x4* u4 = reinterpret_cast<const f32x4*>(up);
   uint32_t cnt = 0;
   if (!kCount && count != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *count = 0ull;
-  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < nchunks; c0 += kUnroll * stride) {
-    f32x4 G0[kUnroll], G1[kUnroll], U0[kUnroll], U1[kUnroll];
+  // Unit c is lane c % 64 of span c / 64 (the quantiser's walk).
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < units; c0 += kUnroll * stride) {
+    f32x4 G[kUnroll][2], U[kUnroll][2];
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
       const int64_t c = c0 + j * stride;
-      if (c < nchunks) {
-        const f32x4* gp = reinterpret_cast<const f32x4*>(gate) + 2 * c;
-        const f32x4* up4 = reinterpret_cast<const f32x4*>(up) + 2 * c;
-        G0[j] = __builtin_nontemporal_load(gp);
-        G1[j] = __builtin_nontemporal_load(gp + 1);
-        U0[j] = __builtin_nontemporal_load(up4);
-        U1[j] = __builtin_nontemporal_load(up4 + 1);
+      const int64_t v0 = (c >> 6) * 128 + (c & 63);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int64_t v = v0 + 64 * hf;
+        const bool in = c < units && v < nvec;
+        G[j][hf] = in ? __builtin_nontemporal_load(g4 + v) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        U[j][hf] = in ? __builtin_nontemporal_load(u4 + v) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
       const int64_t c = c0 + j * stride;
-      if (c >= nchunks) break;
-      double v[8];
+      if (c >= units) break;
+      const int64_t v0 = (c >> 6) * 128 + (c & 63);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float g = e < 4 ? G0[j][e] : G1[j][e - 4];
-        float u = e < 4 ? U0[j][e] : U1[j][e - 4];
-        if (kClamp) {
-          const bool cg = fabsf(g) > L, cu = fabsf(u) > L;   // false for NaN: passes uncounted
-          if (kCount) cnt += (uint32_t)cg + (uint32_t)cu;
-          g = cg ? copysignf(L, g) : g;
-          u = cu ? copysignf(L, u) : u;
+      for (int hf = 0; hf < 2; ++hf) {
+        const int64_t v = v0 + 64 * hf;
+        if (v >= nvec) continue;
+        double r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float g = G[j][hf][e], u = U[j][hf][e];
+          if (kClamp) {
+            const bool cg = fabsf(g) > L, cu = fabsf(u) > L;   // false for NaN: passes uncounted
+            if (kCount) cnt += (uint32_t)cg + (uint32_t)cu;
+            g = cg ? copysignf(L, g) : g;
+            u = cu ? copysignf(L, u) : u;
+          }
+          r[e] = A == Act::kGeluTanh ? gelu_value_d(g, u) : swiglu_value_d(g, u);
         }
-        v[e] = A == Act::kGeluTanh ? gelu_value_d(g, u) : swiglu_value_d(g, u);
+        store4<TO>(h, v, r);
       }
-      store8<TO>(h, c, v);
     }
   }
   if (kCount) {
@@ -100,18 +106,18 @@ __global__ __launch_bounds__(kThreads) void act_fwd_kernel(const float* __restri
 
 template <Act A, typename TO>
 void launch_typed(bool counting, bool clamp, unsigned grid, const float* gate, const float* up, float L,
-                  void* h, uint64_t* count, uint32_t* slots, int64_t nchunks, hipStream_t s) {
+                  void* h, uint64_t* count, uint32_t* slots, int64_t nvec, int64_t units, hipStream_t s) {
   auto* cnt = reinterpret_cast<unsigned long long*>(count);
   TO* out = static_cast<TO*>(h);
   if (counting)
     hipLaunchKernelGGL((act_fwd_kernel<A, TO, true, true>), dim3(grid), dim3(kThreads), 0, s, gate, up, L, out, cnt,
-                       slots, nchunks);
+                       slots, nvec, units);
   else if (clamp)
     hipLaunchKernelGGL((act_fwd_kernel<A, TO, true, false>), dim3(grid), dim3(kThreads), 0, s, gate, up, L, out, cnt,
-                       slots, nchunks);
+                       slots, nvec, units);
   else
     hipLaunchKernelGGL((act_fwd_kernel<A, TO, false, false>), dim3(grid), dim3(kThreads), 0, s, gate, up, L, out, cnt,
-                       slots, nchunks);
+                       slots, nvec, units);
 }
 
 }  // namespace
@@ -119,8 +125,9 @@ void launch_typed(bool counting, bool clamp, unsigned grid, const float* gate, c
 hipError_t launch_act_fwd(Act act, Dt out, int64_t rows, int64_t cols, const float* gate, const float* up,
                           float limit, bool clamp, void* h, uint64_t* count, hipStream_t s) {
   const bool counting = clamp && count != nullptr;
-  const int64_t nchunks = rows * cols / 8;
-  if (nchunks == 0) {
+  const int64_t nvec = rows * cols / 4;
+  const int64_t units = (nvec + 127) / 128 * 64;
+  if (nvec == 0) {
     // Nothing to walk: a given counter receives 0.
     return count != nullptr ? launch_count_sum(nullptr, 0, count, s) : hipSuccess;
   }
@@ -129,14 +136,14 @@ hipError_t launch_act_fwd(Act act, Dt out, int64_t rows, int64_t cols, const flo
     const hipError_t e = count_slots(s, &slots);
     if (e != hipSuccess) return e;
   }
-  const int64_t want = (nchunks + kThreads - 1) / kThreads;
+  const int64_t want = (units + kThreads - 1) / kThreads;
   const unsigned grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);
   if (act == Act::kGeluTanh) {
-    if (out == Dt::kBF16) launch_typed<Act::kGeluTanh, bf16>(counting, clamp, grid, gate, up, limit, h, count, slots, nchunks, s);
-    else launch_typed<Act::kGeluTanh, float>(counting, clamp, grid, gate, up, limit, h, count, slots, nchunks, s);
+    if (out == Dt::kBF16) launch_typed<Act::kGeluTanh, bf16>(counting, clamp, grid, gate, up, limit, h, count, slots, nvec, units, s);
+    else launch_typed<Act::kGeluTanh, float>(counting, clamp, grid, gate, up, limit, h, count, slots, nvec, units, s);
   } else {
-    if (out == Dt::kBF16) launch_typed<Act::kSilu, bf16>(counting, clamp, grid, gate, up, limit, h, count, slots, nchunks, s);
-    else launch_typed<Act::kSilu, float>(counting, clamp, grid, gate, up, limit, h, count, slots, nchunks, s);
+    if (out == Dt::kBF16) launch_typed<Act::kSilu, bf16>(counting, clamp, grid, gate, up, limit, h, count, slots, nvec, units, s);
+    else launch_typed<Act::kSilu, float>(counting, clamp, grid, gate, up, limit, h, count, slots, nvec, units, s);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || !counting) return e;

@@ -10,11 +10,17 @@
 //
 // Mapping: with cols % 32 == 0 the 1x32 blocks tile the flattened
 // [rows, cols] array, so block b covers elements [32 b, 32 b + 32) and its
-// scale byte sits at scale[b].  Each lane handles 8 consecutive elements
-// (two 16-byte loads per input), a quad of 4 lanes covers one block, and the
-// block amax is reduced across the quad with two xor-shuffles.  The block
-// exponent comes from the bits of amax (integer logic); the codes from the
-// hardware FP8 conversion of h * 2^-E.
+// scale byte sits at scale[b].  The array is walked in spans of 512
+// elements (128 16-byte vectors per input), one span per wave: lane l takes
+// vectors 128 s + l and 128 s + 64 + l of span s, so every load and store
+// instruction of a wave covers one contiguous range (1 KiB of each input).
+// Eight lanes cover one block in each half of the span, and the block amax
+// is reduced across them with three xor-shuffles.  The block exponent comes
+// from the bits of amax (integer logic); the codes from the hardware FP8
+// conversion of h * 2^-E.  (Each lane taking 8 consecutive elements instead,
+// two adjacent 16-byte vectors, covers every 32-byte slot of a wave's range
+// half per instruction: that layout streamed 1.7-1.8 times slower in a
+// probe of the same bytes.)
 #include "common.hpp"
 #include "fp8.hpp"
 #include "gemm.hpp"
@@ -42,71 +48,90 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float* __rest
                                                              unsigned long long* __restrict__ count,
                                                              uint32_t* __restrict__ slots,
                                                              float* __restrict__ hout,
-                                                             int64_t nchunks) {
+                                                             int64_t nvec, int64_t units) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const f32x4* g4 = reinterpret_cast<const f32x4*>(gate);
+  const f32x4* u4 = reinterpret_cast<const f32x4*>(up);
+  const int lane = threadIdx.x & 63;
   uint32_t cnt = 0;
   // Without counting, a given counter just receives 0 (one store, no
   // separate zeroing launch).
   if (!kCount && count != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *count = 0ull;
-  // kUnroll chunks per lane per iteration (grid-stride apart): all their
-  // loads are issued before any is used, for more bytes in flight.
-  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < nchunks; c0 += kUnroll * stride) {
-    f32x4 G0[kUnroll], G1[kUnroll], U0[kUnroll], U1[kUnroll];
+  // Unit c (64 per span, consecutive in a wave) is lane c % 64 of span
+  // c / 64.  kUnroll units per lane per iteration (grid-stride apart): all
+  // their loads are issued before any is used, for more bytes in flight.
+  // units and the strides are multiples of 64, so a wave is either wholly
+  // inside the walk or wholly past it; within the last span a half is live
+  // when its vector lies inside the array (whole blocks, since 32 | n).
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < units; c0 += kUnroll * stride) {
+    f32x4 G[kUnroll][2], U[kUnroll][2];
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
       const int64_t c = c0 + j * stride;
-      if (c < nchunks) {
-        const f32x4* gp = reinterpret_cast<const f32x4*>(gate) + 2 * c;
-        const f32x4* up4 = reinterpret_cast<const f32x4*>(up) + 2 * c;
-        G0[j] = __builtin_nontemporal_load(gp);
-        G1[j] = __builtin_nontemporal_load(gp + 1);
-        U0[j] = __builtin_nontemporal_load(up4);
-        U1[j] = __builtin_nontemporal_load(up4 + 1);
+      const int64_t v0 = (c >> 6) * 128 + (c & 63);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int64_t v = v0 + 64 * hf;
+        const bool in = c < units && v < nvec;
+        G[j][hf] = in ? __builtin_nontemporal_load(g4 + v) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        U[j][hf] = in ? __builtin_nontemporal_load(u4 + v) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
-    const int64_t c = c0 + j * stride;
-    if (c >= nchunks) break;
-    const f32x4 g0 = G0[j], g1 = G1[j], u0 = U0[j], u1 = U1[j];
-    if constexpr (kTwin) {
-      const uint32_t lo = f32_bits(g0[0]) ^ f32_bits(g0[1]) ^ f32_bits(g0[2]) ^ f32_bits(g0[3]) ^ f32_bits(u0[0]) ^
-                          f32_bits(u0[1]) ^ f32_bits(u0[2]) ^ f32_bits(u0[3]);
-      const uint32_t hi = f32_bits(g1[0]) ^ f32_bits(g1[1]) ^ f32_bits(g1[2]) ^ f32_bits(g1[3]) ^ f32_bits(u1[0]) ^
-                          f32_bits(u1[1]) ^ f32_bits(u1[2]) ^ f32_bits(u1[3]);
-      __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(q + 8 * c));
-      if ((threadIdx.x & 3) == 0) scale[c >> 2] = (uint8_t)(lo ^ hi);
-      continue;
-    }
-    float h[8];
-    float amax = 0.0f;
+      const int64_t c = c0 + j * stride;
+      if (c >= units) break;
+      const int64_t v0 = (c >> 6) * 128 + (c & 63);
+      if constexpr (kTwin) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float g = e < 4 ? g0[e] : g1[e - 4];
-      float u = e < 4 ? u0[e] : u1[e - 4];
-      if (kClamp) {
-        // |v| > L is false for NaN, so NaN passes through uncounted.
-        const bool cg = fabsf(g) > L, cu = fabsf(u) > L;
-        if (kCount) cnt += (uint32_t)cg + (uint32_t)cu;
-        g = cg ? copysignf(L, g) : g;
-        u = cu ? copysignf(L, u) : u;
+        for (int hf = 0; hf < 2; ++hf) {
+          const int64_t v = v0 + 64 * hf;      // vector index; elements 4 v .. 4 v + 3, block v / 8
+          const f32x4 g4v = G[j][hf], u4v = U[j][hf];
+          const uint32_t f = f32_bits(g4v[0]) ^ f32_bits(g4v[1]) ^ f32_bits(g4v[2]) ^ f32_bits(g4v[3]) ^
+                             f32_bits(u4v[0]) ^ f32_bits(u4v[1]) ^ f32_bits(u4v[2]) ^ f32_bits(u4v[3]);
+          if (v < nvec) {
+            __builtin_nontemporal_store(f, reinterpret_cast<uint32_t*>(q + 4 * v));
+            if ((lane & 7) == 0) scale[v >> 3] = (uint8_t)f;
+          }
+        }
+        continue;
       }
-      h[e] = A == Act::kGeluTanh ? gelu_value(g, u) : swiglu_value(g, u);
-      amax = fmaxf(amax, fabsf(h[e]));  // maxNum: NaN operands are ignored
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const int E = block_exponent(amax);
-    const float sc = ldexpf(1.0f, -E);
-    const uint32_t lo = e4m3_pair(h[0], h[1], sc) | (e4m3_pair(h[2], h[3], sc) << 16);
-    const uint32_t hi = e4m3_pair(h[4], h[5], sc) | (e4m3_pair(h[6], h[7], sc) << 16);
-    __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(q + 8 * c));
-    if ((threadIdx.x & 3) == 0) scale[c >> 2] = (uint8_t)(E + 127);
-    if (kHout) {
-      f32x4* hp = reinterpret_cast<f32x4*>(hout) + 2 * c;
-      hp[0] = f32x4{h[0], h[1], h[2], h[3]};
-      hp[1] = f32x4{h[4], h[5], h[6], h[7]};
-    }
+      // Both halves' values first, then their two amax reductions side by
+      // side, then the codes: the halves' work interleaves.
+      float h[2][4];
+      float amax[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float g = G[j][hf][e], u = U[j][hf][e];
+          if (kClamp) {
+            // |v| > L is false for NaN, so NaN passes through uncounted.
+            const bool cg = fabsf(g) > L, cu = fabsf(u) > L;
+            if (kCount) cnt += (uint32_t)cg + (uint32_t)cu;
+            g = cg ? copysignf(L, g) : g;
+            u = cu ? copysignf(L, u) : u;
+          }
+          h[hf][e] = A == Act::kGeluTanh ? gelu_value(g, u) : swiglu_value(g, u);
+          amax[hf] = fmaxf(amax[hf], fabsf(h[hf][e]));   // maxNum: NaN operands are ignored
+        }
+#pragma unroll
+      for (int m = 1; m <= 4; m <<= 1) {
+        amax[0] = fmaxf(amax[0], __shfl_xor(amax[0], m));
+        amax[1] = fmaxf(amax[1], __shfl_xor(amax[1], m));
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int64_t v = v0 + 64 * hf;        // vector index; elements 4 v .. 4 v + 3, block v / 8
+        const int E = block_exponent(amax[hf]);
+        const float sc = ldexpf(1.0f, -E);
+        const uint32_t codes = e4m3_pair(h[hf][0], h[hf][1], sc) | (e4m3_pair(h[hf][2], h[hf][3], sc) << 16);
+        if (v < nvec) {
+          __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t*>(q + 4 * v));
+          if ((lane & 7) == 0) scale[v >> 3] = (uint8_t)(E + 127);
+          if (kHout) reinterpret_cast<f32x4*>(hout)[v] = f32x4{h[hf][0], h[hf][1], h[hf][2], h[hf][3]};
+        }
+      }
     }
   }
   if (kCount) {
@@ -126,29 +151,44 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(const float* __rest
   }
 }
 
+// The walk: nvec 16-byte vectors per input, in spans of 128; 64 units per
+// span; a grid of at most kMaxBlocks workgroups.
+struct Walk {
+  int64_t nvec, units;
+  unsigned grid;
+};
+inline Walk walk_of(int64_t rows, int64_t cols) {
+  Walk w;
+  w.nvec = rows * cols / 4;
+  w.units = (w.nvec + 127) / 128 * 64;
+  const int64_t want = (w.units + kThreads - 1) / kThreads;
+  w.grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);
+  return w;
+}
+
 template <Act A, bool kClamp, bool kCount, bool kHout>
-void launch_aq(unsigned grid, const float* gate, const float* up, float L, uint8_t* q,
-               uint8_t* scale, uint64_t* count, uint32_t* slots, float* hout, int64_t nchunks, hipStream_t s) {
-  hipLaunchKernelGGL((act_quant_kernel<A, kClamp, kCount, kHout>), dim3(grid), dim3(kThreads), 0, s,
+void launch_aq(const Walk& w, const float* gate, const float* up, float L, uint8_t* q,
+               uint8_t* scale, uint64_t* count, uint32_t* slots, float* hout, hipStream_t s) {
+  hipLaunchKernelGGL((act_quant_kernel<A, kClamp, kCount, kHout>), dim3(w.grid), dim3(kThreads), 0, s,
                      gate, up, L, q, scale, reinterpret_cast<unsigned long long*>(count), slots, hout,
-                     nchunks);
+                     w.nvec, w.units);
 }
 
 template <Act A>
-void launch_aq_variant(bool counting, bool clamp, unsigned grid, const float* gate, const float* up,
+void launch_aq_variant(bool counting, bool clamp, const Walk& w, const float* gate, const float* up,
                        float limit, uint8_t* q, uint8_t* scale, uint64_t* count, uint32_t* slots, float* hout,
-                       int64_t nchunks, hipStream_t s) {
+                       hipStream_t s) {
   // The count is only accumulated when a counter is given and the clamp is
   // on; with the clamp off no value can exceed the limit.
   if (counting) {
-    if (hout) launch_aq<A, true, true, true>(grid, gate, up, limit, q, scale, count, slots, hout, nchunks, s);
-    else launch_aq<A, true, true, false>(grid, gate, up, limit, q, scale, count, slots, hout, nchunks, s);
+    if (hout) launch_aq<A, true, true, true>(w, gate, up, limit, q, scale, count, slots, hout, s);
+    else launch_aq<A, true, true, false>(w, gate, up, limit, q, scale, count, slots, hout, s);
   } else if (clamp) {
-    if (hout) launch_aq<A, true, false, true>(grid, gate, up, limit, q, scale, count, slots, hout, nchunks, s);
-    else launch_aq<A, true, false, false>(grid, gate, up, limit, q, scale, count, slots, hout, nchunks, s);
+    if (hout) launch_aq<A, true, false, true>(w, gate, up, limit, q, scale, count, slots, hout, s);
+    else launch_aq<A, true, false, false>(w, gate, up, limit, q, scale, count, slots, hout, s);
   } else {
-    if (hout) launch_aq<A, false, false, true>(grid, gate, up, limit, q, scale, count, slots, hout, nchunks, s);
-    else launch_aq<A, false, false, false>(grid, gate, up, limit, q, scale, count, slots, hout, nchunks, s);
+    if (hout) launch_aq<A, false, false, true>(w, gate, up, limit, q, scale, count, slots, hout, s);
+    else launch_aq<A, false, false, false>(w, gate, up, limit, q, scale, count, slots, hout, s);
   }
 }
 
@@ -156,12 +196,10 @@ void launch_aq_variant(bool counting, bool clamp, unsigned grid, const float* ga
 
 hipError_t launch_act_quant_twin(int64_t rows, int64_t cols, const float* gate, const float* up, uint8_t* q,
                                  uint8_t* scale, hipStream_t s) {
-  const int64_t nchunks = rows * cols / 8;
-  if (nchunks == 0) return hipSuccess;
-  const int64_t want = (nchunks + kThreads - 1) / kThreads;
-  const unsigned grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);
-  hipLaunchKernelGGL((act_quant_kernel<Act::kSilu, false, false, false, true>), dim3(grid), dim3(kThreads), 0, s,
-                     gate, up, 0.0f, q, scale, nullptr, nullptr, nullptr, nchunks);
+  const Walk w = walk_of(rows, cols);
+  if (w.nvec == 0) return hipSuccess;
+  hipLaunchKernelGGL((act_quant_kernel<Act::kSilu, false, false, false, true>), dim3(w.grid), dim3(kThreads), 0, s,
+                     gate, up, 0.0f, q, scale, nullptr, nullptr, nullptr, w.nvec, w.units);
   return hipGetLastError();
 }
 
@@ -169,8 +207,8 @@ hipError_t launch_act_quant(Act act, int64_t rows, int64_t cols, const float* ga
                             float limit, bool clamp, uint8_t* q, uint8_t* scale, uint64_t* count,
                             float* hout, hipStream_t s) {
   const bool counting = clamp && count != nullptr;
-  const int64_t nchunks = rows * cols / 8;
-  if (nchunks == 0) {
+  const Walk w = walk_of(rows, cols);
+  if (w.nvec == 0) {
     // Nothing to walk: a given counter receives 0.
     return count != nullptr ? launch_count_sum(nullptr, 0, count, s) : hipSuccess;
   }
@@ -179,15 +217,13 @@ hipError_t launch_act_quant(Act act, int64_t rows, int64_t cols, const float* ga
     const hipError_t e = count_slots(s, &slots);
     if (e != hipSuccess) return e;
   }
-  const int64_t want = (nchunks + kThreads - 1) / kThreads;
-  const unsigned grid = (unsigned)(want < kMaxBlocks ? want : kMaxBlocks);
   if (act == Act::kGeluTanh)
-    launch_aq_variant<Act::kGeluTanh>(counting, clamp, grid, gate, up, limit, q, scale, count, slots, hout, nchunks, s);
+    launch_aq_variant<Act::kGeluTanh>(counting, clamp, w, gate, up, limit, q, scale, count, slots, hout, s);
   else
-    launch_aq_variant<Act::kSilu>(counting, clamp, grid, gate, up, limit, q, scale, count, slots, hout, nchunks, s);
+    launch_aq_variant<Act::kSilu>(counting, clamp, w, gate, up, limit, q, scale, count, slots, hout, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || !counting) return e;
-  return launch_count_sum(slots, (int)grid, count, s);
+  return launch_count_sum(slots, (int)w.grid, count, s);
 }
 
 }  // namespace swg

@@ -176,7 +176,7 @@ inline int validate_act_fwd(int out_dtype, int64_t rows, int64_t cols, const flo
   int st = check_dtype(out_dtype);
   if (st) return st;
   if (rows < 0 || cols < 0) return SWIGLU_ERR_SHAPE;
-  if (cols % 8 != 0) return SWIGLU_ERR_SHAPE;         // 8-element chunks of the flat array
+  if (cols % 8 != 0) return SWIGLU_ERR_SHAPE;         // the interface's row granularity (the kernel needs 4)
   if (rows > 0 && cols > (int64_t(1) << 40) / rows) return SWIGLU_ERR_SHAPE;
   if (!(L > 0.0f)) return SWIGLU_ERR_ARG;             // rejects NaN, zero and negatives
   if (count != nullptr && !aligned(count, 8)) return SWIGLU_ERR_ALIGN;

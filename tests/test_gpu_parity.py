@@ -548,23 +548,22 @@ def test_probe_gemv_read_reads_every_weight(M, N, K):
 
 @pytest.mark.parametrize("shape", [(4001, 3584), (3, 384), (1, 32)])
 def test_probe_act_quant_stream_moves_the_quantiser_bytes(shape):
-    """The quantiser's twin writes, for each 8-element chunk, the XOR of the
-    chunk's first four gate and up words and of its last four (8 bytes of q),
-    and for each 1x32 block the low byte of the XOR of its first chunk's two
-    words: every input is read and exactly the quantiser's outputs written."""
+    """The quantiser's twin writes, for each 4 consecutive elements, the XOR
+    of their gate and up words (4 bytes of q), and for each 1x32 block the
+    low byte of that fold of its first 4 elements: every input is read and
+    exactly the quantiser's outputs written."""
     R, C = shape
     d = synth.act_quant_f32(R, C, seed=6)
     gs = [guarded((R, C), torch.uint8), guarded((R, C // 32), torch.uint8)]
     S.probe_act_quant_stream(dev_f32(d["gate"]), dev_f32(d["up"]), gs[0].t, gs[1].t)
     torch.cuda.synchronize()
     check_guards(f"act_quant twin {shape}", *gs)
-    gw = d["gate"].view(np.uint32).reshape(-1, 2, 4)
-    uw = d["up"].view(np.uint32).reshape(-1, 2, 4)
-    fold = np.bitwise_xor.reduce(gw, axis=2) ^ np.bitwise_xor.reduce(uw, axis=2)      # [chunks, 2]
-    got = gs[0].t.cpu().numpy().reshape(-1).view(np.uint32).reshape(-1, 2)
+    gw = d["gate"].view(np.uint32).reshape(-1, 4)
+    uw = d["up"].view(np.uint32).reshape(-1, 4)
+    fold = np.bitwise_xor.reduce(gw, axis=1) ^ np.bitwise_xor.reduce(uw, axis=1)      # [elements / 4]
+    got = gs[0].t.cpu().numpy().reshape(-1).view(np.uint32)
     assert np.array_equal(got, fold)
-    first = fold.reshape(-1, 4, 2)[:, 0, :]                                            # first chunk of each block
-    want_s = ((first[:, 0] ^ first[:, 1]) & 0xFF).astype(np.uint8)
+    want_s = (fold.reshape(-1, 8)[:, 0] & 0xFF).astype(np.uint8)                      # first 4 of each block
     assert np.array_equal(gs[1].t.cpu().numpy().reshape(-1), want_s)
 
 
