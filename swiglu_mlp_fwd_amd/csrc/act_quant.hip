@@ -32,9 +32,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxBlocks = 8192;
 static_assert(kMaxBlocks <= kCountSlots, "one count slot per workgroup");
-// Chunks per lane per loop iteration.  At 4001 x 3584, 8192 workgroups with
-// 2 chunks in flight and non-temporal code stores measured 24.9 us against
-// 25.8 us for 4096 with 4 (the read-only twin moved the same way).
+// Units per lane per loop iteration.  At 4001 x 3584 (one unit per lane),
+// with the earlier lane mapping, 8192 workgroups with 2 chunks in flight
+// and non-temporal code stores measured 24.9 us against 25.8 us for 4096
+// with 4 (the read-only twin moved the same way).
 constexpr int kUnroll = 2;
 
 // kTwin: the same kernel with the same grid, loads and stores and no
