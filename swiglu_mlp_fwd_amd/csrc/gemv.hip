@@ -201,11 +201,15 @@ __global__ __launch_bounds__(kThreads) void gemv_phased_kernel(const bf16* __res
 // partials meet in LDS, and wave 0 adds them in wave order, applies
 // act(g) * u and stores h.  Weight rows past N and k past K load as zero.
 // W is 8, except for short reductions (fewer than 32 slabs, kPairs): there
-// W is the largest count up to 8 that divides S, so every wave walks as many
-// slabs, and a wave requests two slabs' weights before the first goes
-// through its LDS tile.  At (6912, 1536) that is 6 waves of 2 slabs: 1.5-1.8 %
-// faster at M = 8; the same form is up to 2 % slower at the longer
-// reductions, which keep the plain loop.
+// W is the largest count from 4 to 8 that divides S, so every wave walks as
+// many slabs, or, when no such count exists, 8 waves (one per slab below 8)
+// with shares that differ by one slab; a wave requests two slabs' weights
+// before the first goes through its LDS tile.  At (6912, 1536) that is 6
+// waves of 2 slabs: 1.5-1.8 % faster at M = 8; the same form is up to 2 %
+// slower at the longer reductions, which keep the plain loop.  Taking the
+// largest divisor down to 1 left 13, 22 and 31 slabs with 1, 2 and 1 waves:
+// 8 uneven waves run (6400, 1600), (5632, 2816) and (8192, 3968) 1.56, 1.14
+// and 1.64 times faster at M = 4 and 8.
 constexpr int kMxWaves = 8;
 constexpr int kMxThreads = kMxWaves * 64;
 constexpr int kMxSlabK = 128;                    // k per slab
@@ -408,6 +412,7 @@ hipError_t launch_mfma(int M, int N, int K, const void* x, const void* wg, const
   if (nslab < 4 * kMxWaves) {
     int nw = kMxWaves;
     while (nw > 1 && nslab % nw != 0) --nw;
+    if (nw < 4) nw = nslab < kMxWaves ? nslab : kMxWaves;
     const size_t lds = (size_t)nw * 2 * kMxTile * 16;   // the tiles; the reduction needs less
     hipLaunchKernelGGL((gemv_mfma_kernel<A, kTwin, true>), dim3(blocks), dim3(nw * 64), lds, s,
                        static_cast<const bf16*>(x), static_cast<const bf16*>(wg), static_cast<const bf16*>(wu),

@@ -318,14 +318,16 @@ def test_gemv_long_reductions(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 200, 1664), (4, 77, 3968), (8, 33, 2048), (5, 130, 896), (8, 16, 1544),
-                                   (6, 48, 3920)])
+                                   (6, 48, 3920), (8, 64, 2816), (4, 40, 1152), (7, 24, 2560), (8, 18, 384)])
 def test_gemv_short_reductions(M, N, K):
     """Short reductions (fewer than 32 slabs of 128) on the matrix cores run
-    as many waves as divide the slab count (at most 8), each taking its slabs
-    two at a time: 13 slabs (one wave, 6 pairs and a single), 31 (one wave),
-    16 (8 waves of a pair), 7 (7 waves of one slab), 13 and 31 with a
-    partial last slab (1 and 10 chunks).  The read-only twin
-    takes the same path and reads every weight once."""
+    as many waves as divide the slab count when that is 4 to 8, else 8 waves
+    (one per slab below 8) with shares that differ by one slab, each wave
+    taking its slabs two at a time: 13 slabs (8 waves of 1 or 2), 31 (8
+    waves of 3 or 4), 16 (8 waves of a pair), 7 (7 waves of one slab), 13
+    and 31 with a partial last slab (1 and 10 chunks), 22 (8 waves of 2 or
+    3), 9 (8 waves of 1 or 2), 20 (5 waves of 4), 3 (3 waves of one slab).
+    The read-only twin takes the same path and reads every weight once."""
     d = synth.decode_bf16(M, N, K, seed=9)
     check_fwd(d, "bf16", what=f"gemv M={M} N={N} K={K}", via="gemv")
     t = to_dev(d)
