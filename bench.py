@@ -464,7 +464,9 @@ def main():
         res = leg(ctx)
         if args.only.startswith("traffic"):
             copy_calibration(torch, dev, args.steps)
-        log(json.dumps(res)[:2000] if res else "done")
+        if res:
+            print(json.dumps(res), flush=True)
+        log("done")
         return
 
     # ------------------------------------------------------------ headline
@@ -864,6 +866,9 @@ def act_bwd_leg(ctx, oracle_times=None):
              torch.empty(R, dtype=torch.float32, device=dev)) for _ in range(copies)]
     outs16 = [(torch.empty((R, C), dtype=torch.bfloat16, device=dev), torch.empty((R, C), dtype=torch.bfloat16, device=dev))
               for _ in range(copies)]
+    u8 = dict(dtype=torch.uint8, device=dev)
+    outs8 = [(torch.empty((R, C), **u8), torch.empty((R, C // 32), **u8), torch.empty((R, C), **u8),
+              torch.empty((R, C // 32), **u8), None) for _ in range(copies)]
     variants = {
         "f32_clamp_0.5": [(lambda i=i: S.act_bwd(*ins[i][:3], 0.5, out=(outs[i][0], outs[i][1], None)))
                           for _ in range(reps) for i in range(copies)],
@@ -871,9 +876,15 @@ def act_bwd_leg(ctx, oracle_times=None):
                               for _ in range(reps) for i in range(copies)],
         "bf16_clamp_0.5": [(lambda i=i: S.act_bwd(*ins16[i], 0.5, out=(outs16[i][0], outs16[i][1], None)))
                            for _ in range(reps) for i in range(copies)],
+        "f32_in_e4m3_out_clamp_0.5": [(lambda i=i: S.act_bwd_fp8(*ins[i][:3], 0.5, out=outs8[i]))
+                                      for _ in range(reps) for i in range(copies)],
+        "bf16_in_e4m3_out_clamp_0.5": [(lambda i=i: S.act_bwd_fp8(*ins16[i], 0.5, out=outs8[i]))
+                                       for _ in range(reps) for i in range(copies)],
     }
     st = P.run(variants)
-    nb = {"f32_clamp_0.5": 5 * R * C * 4, "f32_weights_wgrad": 5 * R * C * 4 + 2 * R * 4, "bf16_clamp_0.5": 5 * R * C * 2}
+    e4m3_out = 2 * (R * C + R * C // 32)              # codes and scale bytes of dgate and dup
+    nb = {"f32_clamp_0.5": 5 * R * C * 4, "f32_weights_wgrad": 5 * R * C * 4 + 2 * R * 4, "bf16_clamp_0.5": 5 * R * C * 2,
+          "f32_in_e4m3_out_clamp_0.5": 3 * R * C * 4 + e4m3_out, "bf16_in_e4m3_out_clamp_0.5": 3 * R * C * 2 + e4m3_out}
     for k, v in st.items():
         v["bytes_per_call"] = nb[k]
         v["GBs_p50"] = round(nb[k] / (v["p50_us"] * 1e-6) / 1e9, 1)
@@ -889,7 +900,22 @@ def act_bwd_leg(ctx, oracle_times=None):
     if oracle_times is not None:
         oracle_times["act_bwd_f32_clamp_0.5"] = {"seconds": round(secs, 3), "full": True,
                                                  "GBs": round(nb["f32_clamp_0.5"] / secs / 1e9, 3)}
-    del ins, ins16, outs, outs16
+    # E4M3 outputs: the decoded blocks (code x 2^E) against the oracle's exact
+    # dgate and dup, and the share of scale bytes equal to the oracle's.
+    S.act_bwd_fp8(*ins[0][:3], 0.5, out=outs8[0])
+    torch.cuda.synchronize()
+    (rqg, rsg, rqu, rsu, _), secs8 = timed(lambda: oracle.act_bwd_fp8(g, u, dy, 0.5, None))
+    vs = {}
+    for name, q, sc, rs, ref in (("dgate", outs8[0][0], outs8[0][1], rsg, rg), ("dup", outs8[0][2], outs8[0][3], rsu, ru)):
+        qn, scn = q.cpu().numpy(), sc.cpu().numpy()
+        val = oracle.e4m3_decode(qn) * np.exp2(np.repeat(scn.astype(np.float64) - 127.0, 32, axis=1))
+        vs[name] = err_stats(np, val, ref)
+        vs[name]["scale_bytes_equal_frac"] = round(float(np.mean(scn == rs)), 6)
+    st["f32_in_e4m3_out_clamp_0.5"]["vs_oracle"] = vs
+    if oracle_times is not None:
+        oracle_times["act_bwd_fp8_f32_clamp_0.5"] = {"seconds": round(secs8, 3), "full": True,
+                                                     "GBs": round(nb["f32_in_e4m3_out_clamp_0.5"] / secs8 / 1e9, 3)}
+    del ins, ins16, outs, outs16, outs8
     torch.cuda.empty_cache()
     return {"rows": R, "cols": C, "copies": copies, "unit": "GB/s", "variants": st}
 
