@@ -22,8 +22,9 @@ error of one call's output against the fp64 oracle (max / mean absolute
 error, cosine).  The oracle's own time on the host cores is recorded per
 configuration (the headline's on a row sample, extrapolated and labelled).
 Legs:
-  train_fwd   forward variants at the headline shape (SwiGLU, GeGLU, and
-              both with the FP8-quantised output), TFLOP/s;
+  train_fwd   forward variants at the headline shape (SwiGLU, GeGLU, both
+              with the FP8-quantised output, and SwiGLU with gate and up
+              multipliers), TFLOP/s;
   train_bwd   the backward (SwiGLU, GeGLU), TFLOP/s on 8 M N K;
   decode      M = 1, 2, 4, 8 at (N, K) = (6912, 1536), (11008, 4096),
               (13824, 5120), (24576, 6144) with rotated weight copies well
@@ -35,7 +36,8 @@ Legs:
               quantiser's load/store twin, GB/s; the non-quantised forward
               (fp32 and bf16 h);
   act_bwd     the elementwise backward (fp32 with clamp, fp32 with row
-              weights and weight_grad, bf16 with clamp), GB/s;
+              weights and weight_grad, bf16 with clamp, and E4M3 dgate/dup
+              from fp32 and from bf16 inputs), GB/s;
   fp32        the IEEE-fp32 dual GEMM at M=4001, K=2048, N=3584, TFLOP/s;
   tiny_fp32   forward + backward at x[4, 64], W[128, 64].
 """
@@ -500,7 +502,8 @@ def main():
     train = dict(x=x, wg=wg, wu=wu, dh=dh, ws=ws, h=h, grads=grads, d4=d4)
     if args.only in ("train_fwd", "train_bwd"):
         res = (train_fwd_leg if args.only == "train_fwd" else train_bwd_leg)(ctx, train)
-        log(json.dumps(res)[:2000])
+        print(json.dumps(res), flush=True)
+        log("done")
         return
 
     for _ in range(args.warmup):
@@ -625,6 +628,11 @@ def copy_calibration(torch, dev, n):
 
 # ------------------------------------------------------------------ legs
 
+# Gate and up multipliers of the forward leg's multiplier variant (a gate
+# scale below 1 and an up scale above, as in muP-style MLPs).
+FWD_GATE_MULT, FWD_UP_MULT = 0.5, 2.0
+
+
 def train_fwd_leg(ctx, t, oracle_times=None):
     """Forward variants at the headline shape; TFLOP/s and error on sampled rows."""
     torch, S, np, P, args = ctx["torch"], ctx["S"], ctx["np"], ctx["P"], ctx["args"]
@@ -640,6 +648,8 @@ def train_fwd_leg(ctx, t, oracle_times=None):
         "geglu": [lambda: S.fwd(x, wg, wu, out=h2, act="gelu_tanh")] * n,
         "swiglu_fp8": [lambda: S.fwd_fp8(x, wg, wu, out=(q, sc, None))] * n,
         "geglu_fp8": [lambda: S.fwd_fp8(x, wg, wu, act="gelu_tanh", out=(q, sc, None))] * n,
+        # projection multipliers (two more multiplies per output element)
+        "swiglu_mult": [lambda: S.fwd(x, wg, wu, out=h2, gate_mult=FWD_GATE_MULT, up_mult=FWD_UP_MULT)] * n,
     }
     stats = P.run(variants)
     flops = 4.0 * M4 * N4 * K4
@@ -666,6 +676,11 @@ def train_fwd_leg(ctx, t, oracle_times=None):
             oracle_times["train_fwd_sampled"] = {"seconds": round(secs, 3), "rows": len(rows),
                                                  "seconds_full_extrapolated": round(secs * M4 / len(rows), 2),
                                                  "note": "full-size time extrapolated linearly in rows"}
+    S.fwd(x, wg, wu, out=h2, gate_mult=FWD_GATE_MULT, up_mult=FWD_UP_MULT)
+    torch.cuda.synchronize()
+    ref = oracle.glu_fwd(xr, f["wg"], f["wu"], "silu", FWD_GATE_MULT, FWD_UP_MULT)
+    stats["swiglu_mult"]["vs_oracle_sampled_rows"] = err_stats(np, h2[ri].float().cpu().numpy(), ref)
+    stats["swiglu_mult"]["multipliers"] = {"gate": FWD_GATE_MULT, "up": FWD_UP_MULT}
     for act, key in (("silu", "swiglu_fp8"), ("gelu_tanh", "geglu_fp8")):
         S.fwd_fp8(x, wg, wu, act=act, out=(q, sc, None))
         torch.cuda.synchronize()
