@@ -30,7 +30,7 @@ Legs:
               (13824, 5120), (24576, 6144) with rotated weight copies well
               past the 256 MB Infinity Cache, GB/s, beside the kernel's
               read-only twin and a dual-stream read of the same buffers; the
-              floor is the faster of the two;
+              floor is the faster of the two; GeGLU beside SwiGLU at M = 1, 8;
   act_quant   elementwise SwiGLU + 1x32 FP8 quantisation of [4001, 3584] fp32
               (clamp off, L = 7 with count, GELU-tanh), beside the
               quantiser's load/store twin, GB/s; the non-quantised forward
@@ -754,6 +754,10 @@ def decode_leg(ctx, oracle_times=None):
                 "twin": [(lambda a=a, b=b: S.probe_gemv_read(x, a, b, sink)) for _ in range(reps) for (a, b) in W],
                 "stream": [(lambda a=a, b=b: S.probe_read2(a, b, sink)) for _ in range(reps) for (a, b) in W],
             }
+            if M in (1, 8):
+                # the GELU-tanh gate (GeGLU) on the same stream of weights
+                variants["gemv_geglu"] = [(lambda a=a, b=b, o=o: S.gemv_fwd(x, a, b, out=o, act="gelu_tanh"))
+                                          for _ in range(reps) for (a, b), o in zip(W, outs)]
             st = P.run(variants)
             # One byte basis for all three: the decode call's algorithmic
             # bytes over each variant's time, so the floor is the faster of
@@ -772,6 +776,15 @@ def decode_leg(ctx, oracle_times=None):
                  "eager_us_p50": st["gemv"]["eager_p50_us"],
                  "vs_oracle": err_stats(np, outs[0].float().cpu().numpy(), ref),
                  "samples_us": {k: v["samples_us"] for k, v in st.items()}}
+            if "gemv_geglu" in st:
+                S.gemv_fwd(x, W[0][0], W[0][1], out=outs[0], act="gelu_tanh")
+                torch.cuda.synchronize()
+                e["geglu"] = {"us_p50": st["gemv_geglu"]["p50_us"], "GBs": round(gbs["gemv_geglu"], 1),
+                              "frac_of_floor": round(gbs["gemv_geglu"] / floor, 4),
+                              "vs_oracle": err_stats(np, outs[0].float().cpu().numpy(),
+                                                     oracle.glu_fwd(xf, wgf, wuf, "gelu_tanh"))}
+                log(f"decode N={N} K={K} M={M} GeGLU: {e['geglu']['us_p50']:.2f} us, "
+                    f"{e['geglu']['frac_of_floor']:.1%} of the floor")
             entry["per_M"].append(e)
             if oracle_times is not None:
                 oracle_times[f"decode_{N}x{K}_M{M}"] = {"seconds": round(secs, 4), "full": True,
