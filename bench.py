@@ -51,6 +51,7 @@ import os
 import re
 import sys
 import time
+import traceback
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -594,9 +595,20 @@ def main():
         "legs": {},
         "oracle": {},
     }
+    def run_leg(name, fn, *fa):
+        # A leg that raises is recorded with its error (and its traceback on
+        # stderr); the headline line is still printed.
+        try:
+            result["legs"][name] = fn(*fa)
+        except Exception as e:
+            traceback.print_exc()
+            result["legs"][name] = {"error": f"{type(e).__name__}: {e}"}
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
     if not args.no_extra:
-        result["legs"]["train_fwd"] = train_fwd_leg(ctx, train, result["oracle"])
-        result["legs"]["train_bwd"] = train_bwd_leg(ctx, train, result["oracle"])
+        run_leg("train_fwd", train_fwd_leg, ctx, train, result["oracle"])
+        run_leg("train_bwd", train_bwd_leg, ctx, train, result["oracle"])
     del h, grads, train
     sample_inputs = {k: d4[k] for k in ("x", "wg", "wu", "dh")}
     del x, wg, wu, dh, ws, d4
@@ -604,15 +616,19 @@ def main():
 
     # ------------------------------------------------------------ other legs
     if not args.no_extra:
-        result["legs"]["decode"] = decode_leg(ctx, result["oracle"])
-        result["legs"]["act_quant"] = act_quant_leg(ctx, result["oracle"])
-        result["legs"]["act_bwd"] = act_bwd_leg(ctx, result["oracle"])
-        result["legs"]["fp32"] = fp32_leg(ctx, result["oracle"])
-        result["legs"]["tiny_fp32"] = tiny_leg(ctx, result["oracle"])
+        run_leg("decode", decode_leg, ctx, result["oracle"])
+        run_leg("act_quant", act_quant_leg, ctx, result["oracle"])
+        run_leg("act_bwd", act_bwd_leg, ctx, result["oracle"])
+        run_leg("fp32", fp32_leg, ctx, result["oracle"])
+        run_leg("tiny_fp32", tiny_leg, ctx, result["oracle"])
 
     # ------------------------------------------------------------ cpu baseline
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(np, synth, sample_inputs, args.cpu_seconds, value)
+        try:
+            result["cpu_baseline"] = cpu_baseline(np, synth, sample_inputs, args.cpu_seconds, value)
+        except Exception as e:
+            traceback.print_exc()
+            result["cpu_baseline"] = {"error": f"{type(e).__name__}: {e}"}
 
     print(json.dumps(result), flush=True)
 
