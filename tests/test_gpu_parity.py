@@ -230,6 +230,20 @@ def test_bwd_bf16_full_8192x14336x4096_sampled():
     torch.cuda.empty_cache()
 
 
+def test_bwd_fp32_4001x3584x2048_sampled():
+    """The IEEE-fp32 backward at the fp32 workload's size: 4001 tokens (a
+    ragged last row tile), reductions of 2 x 3584 and 4001, on 32 sampled
+    rows of dX and of dWg, dWu."""
+    M, N, K = 4001, 3584, 2048
+    d = synth.gemm_fp32(M, N, K, seed=5)
+    d["dh"] = synth.normal_f32((M, N), 1.0, 5, synth.STREAM_DH)
+    rs = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, M - 1], rs.integers(0, M, 30)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rs.integers(0, N, 30)]))
+    check_bwd(d, "f32", rows=rows, cols=cols, what="bwd fp32 4001x3584x2048 (sampled)")
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
 @pytest.mark.parametrize("shape", [(257, 136, 72), (24, 48, 64), (40, 8, 8), (300, 1032, 136)])
 def test_bwd_dh_tile_edges(shape, act):
