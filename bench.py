@@ -38,7 +38,8 @@ Legs:
   act_bwd     the elementwise backward (fp32 with clamp, fp32 with row
               weights and weight_grad, bf16 with clamp, and E4M3 dgate/dup
               from fp32 and from bf16 inputs), GB/s;
-  fp32        the IEEE-fp32 dual GEMM at M=4001, K=2048, N=3584, TFLOP/s;
+  fp32        the IEEE-fp32 dual GEMM at M=4001, K=2048, N=3584 and its
+              backward, TFLOP/s;
   tiny_fp32   forward + backward at x[4, 64], W[128, 64].
 """
 from __future__ import annotations
@@ -973,14 +974,21 @@ def fp32_leg(ctx, oracle_times=None):
     x, wg, wu = (torch.from_numpy(d[k]).to(dev) for k in ("x", "wg", "wu"))
     h = torch.empty((M, N), dtype=torch.float32, device=dev)
     h2 = torch.empty_like(h)
+    dh = torch.from_numpy(synth.normal_f32((M, N), 1.0, 0, synth.STREAM_DH)).to(dev)
+    ws = torch.empty(S.bwd_workspace_bytes(torch.float32, M, N, K), dtype=torch.uint8, device=dev)
+    grads = (torch.empty((M, K), dtype=torch.float32, device=dev), torch.empty((N, K), dtype=torch.float32, device=dev),
+             torch.empty((N, K), dtype=torch.float32, device=dev))
     n = args.gemm_iters
     st = P.run({"swiglu": [lambda: S.fwd(x, wg, wu, out=h)] * n,
-                "geglu": [lambda: S.fwd(x, wg, wu, out=h2, act="gelu_tanh")] * n})
+                "geglu": [lambda: S.fwd(x, wg, wu, out=h2, act="gelu_tanh")] * n,
+                "swiglu_bwd": [lambda: S.bwd(x, wg, wu, dh, workspace=ws, out=grads)] * n})
     for k, v in st.items():
-        v["TFLOPs_p50"] = round(4.0 * M * N * K / (v["p50_us"] * 1e-6) / 1e12, 2)
+        # the backward is credited with 8 M N K (dX, dWg, dWu), its recompute not
+        flops = (8.0 if k.endswith("_bwd") else 4.0) * M * N * K
+        v["TFLOPs_p50"] = round(flops / (v["p50_us"] * 1e-6) / 1e12, 2)
         v["frac_of_fp32_peak"] = round(v["TFLOPs_p50"] / PEAK_FP32_TFLOPS, 4)
-        v["launches_per_call"] = LAUNCHES["fwd"]
-        log(f"fp32 fwd {M}x{N}x{K} {k}: {v['p50_us'] / 1e3:.3f} ms, {v['TFLOPs_p50']:.1f} TFLOP/s")
+        v["launches_per_call"] = LAUNCHES["bwd_f32"] if k.endswith("_bwd") else LAUNCHES["fwd"]
+        log(f"fp32 {M}x{N}x{K} {k}: {v['p50_us'] / 1e3:.3f} ms, {v['TFLOPs_p50']:.1f} TFLOP/s")
     S.fwd(x, wg, wu, out=h)
     torch.cuda.synchronize()
     ref, secs = timed(lambda: oracle.glu_fwd(d["x"], d["wg"], d["wu"]))
@@ -988,7 +996,23 @@ def fp32_leg(ctx, oracle_times=None):
     if oracle_times is not None:
         oracle_times["fp32_fwd_4001x3584x2048"] = {"seconds": round(secs, 3), "full": True,
                                                    "TFLOPs": round(4.0 * M * N * K / secs / 1e12, 4)}
-    del x, wg, wu, h, h2
+    # the backward against the oracle on 32 sampled rows of dX and of dWg, dWu
+    S.bwd(x, wg, wu, dh, workspace=ws, out=grads)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 30)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 30)]))
+    f = {k: d[k].astype(np.float64) for k in ("x", "wg", "wu")}
+    f["dh"] = dh.cpu().numpy().astype(np.float64)
+    dxr = oracle.swiglu_bwd_dx_rows(f["x"], f["wg"], f["wu"], f["dh"], rows)
+    dwgr, dwur = oracle.swiglu_bwd_dw_rows(f["x"], f["wg"], f["wu"], f["dh"], cols)
+    ri, ci = torch.as_tensor(rows, device=dev), torch.as_tensor(cols, device=dev)
+    st["swiglu_bwd"]["vs_oracle_sampled"] = {
+        "dx_rows": err_stats(np, grads[0][ri].cpu().numpy(), dxr),
+        "dwg_rows": err_stats(np, grads[1][ci].cpu().numpy(), dwgr),
+        "dwu_rows": err_stats(np, grads[2][ci].cpu().numpy(), dwur),
+        "sampled": f"{len(rows)} rows of dX, {len(cols)} rows of dWg and dWu"}
+    del x, wg, wu, h, h2, dh, ws, grads
     torch.cuda.empty_cache()
     return {"M": M, "N": N, "K": K, "variants": st}
 
