@@ -410,6 +410,17 @@ int swiglu_probe_fp8_transitions(int kind, uint32_t first, uint32_t last, uint32
 int swiglu_probe_read2(const void* a, const void* b, size_t bytes,
                        uint32_t* sink, void* stream);
 
+/* Measurement aid: the same dual-stream read with a chosen launch shape,
+ * so that the floor can be the fastest of several: `threads` per workgroup
+ * (256 or 512), `chunks` 16-byte chunks of each buffer in flight per lane
+ * (1, 2, 4 or 8), a grid of at most `max_blocks` workgroups (1..65535;
+ * grid-stride beyond).  `sink` (>= 4096 uint32 words) receives a word only
+ * when a lane's fold of its loaded words equals 0x9E3779B9; it exists so
+ * that the loads cannot be elided.  Other arguments and errors as
+ * swiglu_probe_read2; an unsupported shape is SWIGLU_ERR_ARG. */
+int swiglu_probe_read2_cfg(const void* a, const void* b, size_t bytes, int threads, int chunks, int max_blocks,
+                           uint32_t* sink, void* stream);
+
 /* Measurement aid: the dense bf16 matrix-core rate the chip sustains.
  * `blocks` workgroups of 8 waves each run `iters` iterations of eight
  * independent v_mfma_f32_16x16x32_bf16 (the form the bf16 forward uses) on

@@ -67,6 +67,8 @@ SIGNATURES = {
     "swiglu_probe_fp8_transitions": (ctypes.c_int, [ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32, _c_ptr,
                                                     ctypes.c_uint32, _c_ptr, _c_ptr]),
     "swiglu_probe_read2": (ctypes.c_int, [_c_ptr, _c_ptr, ctypes.c_size_t, _c_ptr, _c_ptr]),
+    "swiglu_probe_read2_cfg": (ctypes.c_int, [_c_ptr, _c_ptr, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, _c_ptr, _c_ptr]),
     "swiglu_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "swiglu_last_hip_error": (ctypes.c_int, []),
     "swiglu_version": (ctypes.c_int, []),

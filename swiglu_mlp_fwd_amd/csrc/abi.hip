@@ -72,6 +72,12 @@ hipError_t scratch_address(hipStream_t stream, void** out) {
 
 }  // namespace
 
+namespace swg {
+// probe.hip: threads in {256, 512}, chunks in {1, 2, 4, 8}, 1 <= max_blocks <= 65535.
+hipError_t launch_probe_read2_cfg(const void* a, const void* b, size_t bytes, int threads, int chunks,
+                                  int max_blocks, uint32_t* sink, hipStream_t s);
+}  // namespace swg
+
 extern "C" {
 
 int swiglu_fwd_mult(int act, int dtype, int64_t M, int64_t N, int64_t K, const void* x,
@@ -357,6 +363,18 @@ int swiglu_probe_read2(const void* a, const void* b, size_t bytes, uint32_t* sin
   if (a == nullptr || b == nullptr || sink == nullptr) return SWIGLU_ERR_NULL;
   if (!swg::aligned(a, 16) || !swg::aligned(b, 16) || !swg::aligned(sink, 4)) return SWIGLU_ERR_ALIGN;
   return hip_status(swg::launch_probe_read2(a, b, bytes, sink, as_stream(stream)));
+}
+
+int swiglu_probe_read2_cfg(const void* a, const void* b, size_t bytes, int threads, int chunks, int max_blocks,
+                           uint32_t* sink, void* stream) {
+  if (threads != 256 && threads != 512) return SWIGLU_ERR_ARG;
+  if (chunks != 1 && chunks != 2 && chunks != 4 && chunks != 8) return SWIGLU_ERR_ARG;
+  if (max_blocks < 1 || max_blocks > 65535) return SWIGLU_ERR_ARG;
+  if (bytes % 16 != 0) return SWIGLU_ERR_SHAPE;
+  if (bytes == 0) return SWIGLU_OK;
+  if (a == nullptr || b == nullptr || sink == nullptr) return SWIGLU_ERR_NULL;
+  if (!swg::aligned(a, 16) || !swg::aligned(b, 16) || !swg::aligned(sink, 4)) return SWIGLU_ERR_ALIGN;
+  return hip_status(swg::launch_probe_read2_cfg(a, b, bytes, threads, chunks, max_blocks, sink, as_stream(stream)));
 }
 
 const char* swiglu_status_str(int status) {

@@ -433,12 +433,21 @@ def probe_act_quant_stream(gate: torch.Tensor, up: torch.Tensor, q: torch.Tensor
                                                                                _p(scale), _stream(gate)))
 
 
-def probe_read2(a: torch.Tensor, b: torch.Tensor, sink: torch.Tensor) -> None:
-    """Pure read of two equally sized buffers (cold-read floor measurement)."""
+def probe_read2(a: torch.Tensor, b: torch.Tensor, sink: torch.Tensor, shape: tuple[int, int, int] | None = None) -> None:
+    """Pure read of two equally sized buffers (cold-read floor measurement);
+    `shape` = (threads, chunks in flight per lane, max workgroups) picks the
+    launch shape of swiglu_probe_read2_cfg."""
     nbytes = a.numel() * a.element_size()
     if b.numel() * b.element_size() != nbytes:
         raise ValueError("probe buffers must have equal size")
-    check("swiglu_probe_read2", lib().swiglu_probe_read2(_p(a), _p(b), nbytes, _p(sink), _stream(a)))
+    if sink.numel() * sink.element_size() < 4096 * 4:
+        raise ValueError("sink must hold at least 4096 words")
+    if shape is None:
+        check("swiglu_probe_read2", lib().swiglu_probe_read2(_p(a), _p(b), nbytes, _p(sink), _stream(a)))
+    else:
+        t, c, m = shape
+        check("swiglu_probe_read2_cfg", lib().swiglu_probe_read2_cfg(_p(a), _p(b), nbytes, int(t), int(c), int(m),
+                                                                     _p(sink), _stream(a)))
 
 
 class SwiGLUFunction(torch.autograd.Function):

@@ -43,6 +43,13 @@ def test_header_declares_the_entry_points():
         assert n in names
 
 
+def test_library_resolves_every_symbol_at_load():
+    """Loading with immediate binding resolves every function the library
+    calls, so no entry point can fail later on an undefined symbol (a
+    declaration given C linkage by mistake, say)."""
+    ctypes.CDLL(_lib.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
 def test_library_exports_every_header_symbol(L):
     names = header_functions()
     assert names
@@ -264,6 +271,16 @@ def test_probe_validation(L):
     assert L.swiglu_probe_read2(A, A, 17, A, None) == ESHAPE
     assert L.swiglu_probe_read2(None, A, 32, A, None) == ENULL
     assert L.swiglu_probe_read2(A, A, 0, A, None) == OK
+
+
+def test_probe_read2_cfg_validation(L):
+    assert L.swiglu_probe_read2_cfg(A, A, 32, 128, 4, 4096, A, None) == EARG
+    assert L.swiglu_probe_read2_cfg(A, A, 32, 256, 3, 4096, A, None) == EARG
+    assert L.swiglu_probe_read2_cfg(A, A, 32, 512, 1, 0, A, None) == EARG
+    assert L.swiglu_probe_read2_cfg(A, A, 32, 512, 1, 65536, A, None) == EARG
+    assert L.swiglu_probe_read2_cfg(A, A, 17, 256, 8, 4096, A, None) == ESHAPE
+    assert L.swiglu_probe_read2_cfg(None, A, 32, 256, 8, 4096, A, None) == ENULL
+    assert L.swiglu_probe_read2_cfg(A, A, 0, 512, 2, 16384, A, None) == OK
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

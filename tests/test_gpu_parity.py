@@ -660,6 +660,19 @@ def test_probe_read2_runs():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("shape", [(256, 1, 65535), (256, 8, 4096), (512, 1, 16384), (512, 2, 64), (512, 8, 1)])
+def test_probe_read2_shapes_run(shape):
+    """Every launch shape of the configurable read, on buffers that leave a
+    grid-stride tail (1 MiB + 48 bytes); the sink stays untouched (no lane's
+    fold of these words equals the marker)."""
+    a = torch.ones((1 << 18) + 12, dtype=torch.int32, device=DEV)
+    b = torch.full(((1 << 18) + 12,), 3, dtype=torch.int32, device=DEV)
+    sink = torch.zeros(4096, dtype=torch.int32, device=DEV)
+    S.probe_read2(a, b, sink, shape=shape)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+
+
 # ---------------------------------------------------------- act_bwd (next f1)
 
 ULP32 = 2.0 ** -24
