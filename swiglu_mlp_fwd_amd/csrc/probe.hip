@@ -47,9 +47,10 @@ __global__ __launch_bounds__(kThreads) void probe_read2_kernel(const u32x4* __re
 // The same pure read with a chosen shape: kT threads per workgroup, kU
 // 16-byte chunks of each buffer in flight per lane, a grid of up to
 // max_blocks workgroups (grid-stride beyond).  The fastest of a few shapes
-// is the floor: at 21 MB per buffer 256 threads with 8 chunks in flight read
-// 10 % faster than the fixed shape above, at 90 MB 512 threads with 1 chunk
-// and a grid covering the buffers in one pass.  A lane stores its fold only
+// is the floor: at 21 MB per buffer 256 or 512 threads with 2-8 chunks in
+// flight read 8-10 % faster than the fixed shape above, at 90 MB 512 threads
+// with 1 chunk and a grid covering the buffers in one pass 9-16 % faster
+// (several runs).  A lane stores its fold only
 // in the practically impossible case that it equals kNever, which keeps the
 // loads from being elided without a reduction at the end of every
 // workgroup (that reduction alone cost 0.5 us of an 8 us read).
